@@ -1,0 +1,205 @@
+/*
+ * CPU oracle for the quantized MoE expert FFN -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library. The GPU path shares no code with it and never calls it.
+ *
+ * Everything is computed slowly and plainly in fp64, one definition at a time:
+ *
+ *  - fp16 / bf16 decoding and bf16 round-to-nearest-even;
+ *  - dequantization of a 144-byte 4-bit super-block. The pages
+ *    (sparkinfer README, opening paragraph and kernel table: Q4_K_M GGUF
+ *    experts kept quantized and dequantized on read) name the format but print
+ *    no bit layout; the canonical block read here is: fp16 d, fp16 dmin,
+ *    sixteen 6-bit fields LSB-first from byte 4 (sub-block scales sc_0..sc_7
+ *    then sub-block mins m_0..m_7), then 128 bytes of 4-bit codes with
+ *    sub-block j in bytes 16+16j..31+16j and element 2i of a sub-block in the
+ *    low nibble of byte i. Weight = d*sc_j*q - dmin*m_j, exact in fp64;
+ *  - the quantized GEMV y = Deq(W) x with fp64 accumulation;
+ *  - the router: logits = W_r x, exact top-k by a full stable sort on
+ *    (logit descending, expert id ascending), and the softmax restricted to
+ *    the selected experts (softmax over all experts then renormalised over
+ *    the top-k, which is the same number);
+ *  - the expert FFN y_e = D_e (SiLU(G_e x) * (U_e x)) and the routing-weighted
+ *    sum over the selected experts (the pages' fused MoE expert FFN: sparkinfer
+ *    README kernel table; sparkinfer CuTe-DSL README, "moe" paragraph, for the
+ *    SiLU-gated form with top-k ids and weights as inputs);
+ *  - the residual add and RMSNorm between stacked layers (weight 1, eps given
+ *    by the caller), rounded to bf16.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+
+#define QK 256
+#define QBLOCK_BYTES 144
+
+/* ---------------------------------------------------------------- numbers */
+double oracle_f16(uint16_t h) {
+  int sign = h >> 15, ex = (h >> 10) & 31, mant = h & 1023;
+  double v;
+  if (ex == 0) v = ldexp((double)mant, -24);                 /* zero / subnormal */
+  else if (ex == 31) v = mant ? NAN : INFINITY;
+  else v = ldexp((double)(1024 + mant), ex - 25);            /* (1 + m/1024) 2^(ex-15) */
+  return sign ? -v : v;
+}
+
+double oracle_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* nearest bf16 to a finite double, ties to even mantissa */
+uint16_t oracle_round_bf16(double v) {
+  if (v == 0) return signbit(v) ? 0x8000 : 0;
+  uint16_t sign = v < 0 ? 0x8000 : 0;
+  double a = fabs(v);
+  int e;
+  frexp(a, &e);
+  int E = e - 1;                                  /* a in [2^E, 2^(E+1)) */
+  if (E < -126) E = -126;                         /* subnormal spacing 2^-133 */
+  double q = a / ldexp(1.0, E - 7);               /* units of the bf16 spacing */
+  double r = floor(q);
+  double frac = q - r;
+  if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  double rv = r * ldexp(1.0, E - 7);
+  /* rebuild bits from the rounded value */
+  float f = (float)rv;                            /* exact: rv has <= 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return sign | (uint16_t)(u >> 16);
+}
+
+/* ---------------------------------------------------------------- dequant */
+static int field6(const uint8_t* blk, int f) {
+  int v = 0;
+  for (int b = 0; b < 6; ++b) {
+    int bit = 6 * f + b;
+    v |= ((blk[4 + bit / 8] >> (bit % 8)) & 1) << b;
+  }
+  return v;
+}
+
+/* one super-block -> 256 weights */
+void oracle_dequant_block(const uint8_t* blk, double* w) {
+  double d = oracle_f16((uint16_t)(blk[0] | (blk[1] << 8)));
+  double dmin = oracle_f16((uint16_t)(blk[2] | (blk[3] << 8)));
+  for (int j = 0; j < 8; ++j) {
+    int sc = field6(blk, j), m = field6(blk, 8 + j);
+    for (int i = 0; i < 32; ++i) {
+      uint8_t byte = blk[16 + 16 * j + i / 2];
+      int q = (i & 1) ? (byte >> 4) : (byte & 15);
+      w[32 * j + i] = d * sc * q - dmin * m;
+    }
+  }
+}
+
+void oracle_dequant_matrix(const uint8_t* blocks, int64_t rows, int64_t cols, double* w) {
+  int64_t nb = cols / QK;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b)
+      oracle_dequant_block(blocks + (r * nb + b) * QBLOCK_BYTES, w + r * cols + b * QK);
+}
+
+/* y[r] = sum_c Deq(W)[r][c] * x[c], fp64 */
+void oracle_qgemv(const uint8_t* blocks, int64_t rows, int64_t cols, const double* x, double* y) {
+  int64_t nb = cols / QK;
+  double w[QK];
+  for (int64_t r = 0; r < rows; ++r) {
+    double acc = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+      oracle_dequant_block(blocks + (r * nb + b) * QBLOCK_BYTES, w);
+      for (int i = 0; i < QK; ++i) acc += w[i] * x[b * QK + i];
+    }
+    y[r] = acc;
+  }
+}
+
+/* ---------------------------------------------------------------- router */
+void oracle_router_logits(const float* wr, int64_t E, int64_t H, const uint16_t* x_bf16, double* logits) {
+  for (int64_t e = 0; e < E; ++e) {
+    double acc = 0.0;
+    for (int64_t i = 0; i < H; ++i) acc += (double)wr[e * H + i] * oracle_bf16(x_bf16[i]);
+    logits[e] = acc;
+  }
+}
+
+typedef struct { double l; int32_t id; } scored;
+
+static int by_logit_desc_id_asc(const void* a, const void* b) {
+  const scored* x = (const scored*)a;
+  const scored* y = (const scored*)b;
+  if (x->l > y->l) return -1;
+  if (x->l < y->l) return 1;
+  return x->id < y->id ? -1 : (x->id > y->id);
+}
+
+/* the k largest logits, descending; equal logits -> lower id first */
+void oracle_topk(const double* logits, int64_t E, int64_t k, int32_t* ids) {
+  scored* s = (scored*)malloc(sizeof(scored) * (size_t)E);
+  for (int64_t e = 0; e < E; ++e) { s[e].l = logits[e]; s[e].id = (int32_t)e; }
+  qsort(s, (size_t)E, sizeof(scored), by_logit_desc_id_asc);
+  for (int64_t i = 0; i < k; ++i) ids[i] = s[i].id;
+  free(s);
+}
+
+/* softmax over the selected logits (= full softmax renormalised over top-k) */
+void oracle_route_weights(const double* logits, const int32_t* ids, int64_t k, double* w) {
+  double mx = -INFINITY;
+  for (int64_t s = 0; s < k; ++s) if (logits[ids[s]] > mx) mx = logits[ids[s]];
+  double den = 0.0;
+  for (int64_t s = 0; s < k; ++s) den += exp(logits[ids[s]] - mx);
+  for (int64_t s = 0; s < k; ++s) w[s] = exp(logits[ids[s]] - mx) / den;
+}
+
+/* ---------------------------------------------------------------- FFN */
+double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* y = D (SiLU(G x) * (U x)); G, U: [I x H] blocks, D: [H x I] blocks */
+void oracle_expert_ffn(const uint8_t* gate, const uint8_t* up, const uint8_t* down,
+                       int64_t H, int64_t I, const double* x, double* y, double* h_out) {
+  double* g = (double*)malloc(sizeof(double) * (size_t)I);
+  double* u = (double*)malloc(sizeof(double) * (size_t)I);
+  oracle_qgemv(gate, I, H, x, g);
+  oracle_qgemv(up, I, H, x, u);
+  for (int64_t i = 0; i < I; ++i) g[i] = oracle_silu(g[i]) * u[i];
+  if (h_out) memcpy(h_out, g, sizeof(double) * (size_t)I);
+  oracle_qgemv(down, H, I, g, y);
+  free(g);
+  free(u);
+}
+
+/* One token through one MoE layer given its selected experts' blocks.
+ * gate/up/down: arrays of k pointers (expert of slot s); w: k routing weights. */
+void oracle_moe_token(const uint8_t* const* gate, const uint8_t* const* up, const uint8_t* const* down,
+                      const double* w, int64_t k, int64_t H, int64_t I, const uint16_t* x_bf16,
+                      double* y) {
+  double* x = (double*)malloc(sizeof(double) * (size_t)H);
+  double* ys = (double*)malloc(sizeof(double) * (size_t)H);
+  for (int64_t i = 0; i < H; ++i) { x[i] = oracle_bf16(x_bf16[i]); y[i] = 0.0; }
+  for (int64_t s = 0; s < k; ++s) {
+    oracle_expert_ffn(gate[s], up[s], down[s], H, I, x, ys, NULL);
+    for (int64_t i = 0; i < H; ++i) y[i] += w[s] * ys[i];
+  }
+  free(x);
+  free(ys);
+}
+
+/* ---------------------------------------------------------------- stack */
+/* r = v / sqrt(mean(v^2) + eps), v = x + y; returned in fp64 and as bf16 */
+void oracle_resid_rmsnorm(const uint16_t* x_bf16, const double* y, int64_t n, double eps,
+                          double* r, uint16_t* r_bf16) {
+  double ss = 0.0;
+  double* v = (double*)malloc(sizeof(double) * (size_t)n);
+  for (int64_t i = 0; i < n; ++i) { v[i] = oracle_bf16(x_bf16[i]) + y[i]; ss += v[i] * v[i]; }
+  double inv = 1.0 / sqrt(ss / (double)n + eps);
+  for (int64_t i = 0; i < n; ++i) {
+    double ri = v[i] * inv;
+    if (r) r[i] = ri;
+    if (r_bf16) r_bf16[i] = oracle_round_bf16(ri);
+  }
+  free(v);
+}

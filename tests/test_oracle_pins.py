@@ -1,0 +1,305 @@
+"""Pins for the CPU oracle: each check ties a piece of it to something other
+than itself (a worked example with exact answers, exhaustive sweeps against a
+library conversion, library matmul/sort/softmax, brute force, closed forms).
+A plausible slip anywhere in the oracle (wrong nibble, swapped scale/min
+fields, sign of the min, dropped term, transposed operand, wrong tie rule)
+fails at least one of these."""
+import itertools
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit, softmax
+
+import oracle
+import synth
+
+QB = oracle.QBLOCK_BYTES
+
+
+def _load_worked_example(golden_dir):
+    blk = None
+    w = None
+    with open(os.path.join(golden_dir, "q4k_worked_example.txt")) as f:
+        for line in f:
+            if line.startswith("block_hex "):
+                blk = np.frombuffer(bytes.fromhex(line.split()[1]), dtype=np.uint8)
+            elif line.startswith("weights "):
+                w = np.array([int(v) for v in line.split()[1:]], dtype=np.float64)
+    return blk, w
+
+
+def _block_from_fields(d_bits, dmin_bits, sc, m, q):
+    """Independent encoder for test blocks (big-integer bit packing)."""
+    blk = bytearray(QB)
+    blk[0:2] = int(d_bits).to_bytes(2, "little")
+    blk[2:4] = int(dmin_bits).to_bytes(2, "little")
+    bits = 0
+    for f, v in enumerate(list(sc) + list(m)):
+        assert 0 <= v < 64
+        bits |= int(v) << (6 * f)
+    blk[4:16] = bits.to_bytes(12, "little")
+    for i in range(256):
+        j, e = divmod(i, 32)
+        byte = 16 + 16 * j + e // 2
+        blk[byte] |= (int(q[i]) << 4) if (e & 1) else int(q[i])
+    return np.frombuffer(bytes(blk), dtype=np.uint8)
+
+
+# ------------------------------------------------------------------ codec
+def test_worked_example_block(golden_dir):
+    blk, w = _load_worked_example(golden_dir)
+    assert blk.size == QB and w.size == 256
+    got = oracle.dequant_block(blk)
+    assert np.array_equal(got, w)
+    assert got[0] == 0 and got[33] == 1 and got[255] == 113
+
+
+def test_six_bit_fields_every_position_every_value():
+    """Each of the 16 packed fields at every value 0..63: scales via q=1,
+    mins via q=0 (d = dmin = 1)."""
+    one = 0x3C00
+    for f in range(16):
+        for v in range(64):
+            sc = [0] * 8
+            m = [0] * 8
+            if f < 8:
+                sc[f] = v
+            else:
+                m[f - 8] = v
+            q = np.ones(256, dtype=np.int64)
+            w = oracle.dequant_block(_block_from_fields(one, one, sc, m, q))
+            exp = np.array([sc[i // 32] * 1 - m[i // 32] for i in range(256)], dtype=np.float64)
+            assert np.array_equal(w, exp), (f, v)
+
+
+def test_codes_every_nibble_position():
+    rng = np.random.default_rng(1)
+    for _ in range(20):
+        q = rng.integers(0, 16, 256)
+        sc = rng.integers(0, 64, 8)
+        m = rng.integers(0, 64, 8)
+        w = oracle.dequant_block(_block_from_fields(0x3C00, 0x3800, sc, m, q))
+        exp = np.array([sc[i // 32] * q[i] - 0.5 * m[i // 32] for i in range(256)], dtype=np.float64)
+        assert np.array_equal(w, exp)
+
+
+def test_f16_all_finite_patterns_match_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    finite = np.isfinite(ref)
+    got = np.array([oracle.f16(int(b)) for b in bits[finite]])
+    assert np.array_equal(got, ref[finite])
+
+
+def test_d_dmin_scaling_and_extremes():
+    q = np.arange(256) % 16
+    for d_bits in (0x0000, 0x0001, 0x03FF, 0x0400, 0x3555, 0x7BFF):
+        for dmin_bits in (0x0000, 0x0001, 0x2E66, 0x7BFF):
+            d = float(np.array([d_bits], dtype=np.uint16).view(np.float16)[0])
+            dmin = float(np.array([dmin_bits], dtype=np.uint16).view(np.float16)[0])
+            sc = [63, 1, 0, 17, 32, 5, 9, 44]
+            m = [0, 63, 12, 1, 2, 33, 60, 7]
+            w = oracle.dequant_block(_block_from_fields(d_bits, dmin_bits, sc, m, q))
+            exp = np.array([d * sc[i // 32] * q[i] - dmin * m[i // 32] for i in range(256)])
+            assert np.array_equal(w, exp)
+
+
+def test_all_zero_block_is_zero():
+    assert np.array_equal(oracle.dequant_block(np.zeros(QB, np.uint8)), np.zeros(256))
+
+
+# ------------------------------------------------------------------ quantizer vs decoder
+def test_decoded_synthetic_weights_within_quantizer_bound():
+    """The shared generator's encoder and the oracle's decoder agree: every
+    decoded weight lies within half a code step (plus the fp16/6-bit scale
+    rounding slack) of the Gaussian value it encodes."""
+    S = synth.TINY
+    w = synth.expert_matrix_f32(S, 0, 3, synth.GATE).astype(np.float64)
+    deq = oracle.dequant_matrix(synth.expert_matrix(S, 0, 3, synth.GATE))
+    rows, cols = w.shape
+    for r in range(0, rows, 37):
+        for b in range(cols // 256):
+            seg = w[r, 256 * b:256 * (b + 1)].reshape(8, 32)
+            err = np.abs(deq[r, 256 * b:256 * (b + 1)].reshape(8, 32) - seg)
+            rng_ = seg.max(1) - np.minimum(seg.min(1), 0)
+            # step ~ range/15; scale rounding (6-bit sc, fp16 d) adds <= ~1 step at the ends
+            assert np.all(err.max(1) <= rng_ / 15 * 1.5 + 1e-6)
+    assert np.abs(deq - w).max() < 0.02 and np.abs(deq - w).mean() < 0.004
+
+
+# ------------------------------------------------------------------ GEMV
+@pytest.mark.parametrize("shape,mat", [(synth.TINY, synth.GATE), (synth.TINY, synth.DOWN),
+                                       (synth.QWEN3_30B_A3B, synth.UP)])
+def test_qgemv_matches_library_matmul(shape, mat):
+    blocks = synth.expert_matrix(shape, 0, 1, mat)
+    W = oracle.dequant_matrix(blocks)
+    x = np.random.default_rng(2).standard_normal(W.shape[1])
+    y = oracle.qgemv(blocks, x)
+    ref = W @ x
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(W).sum(1).max())
+
+
+def test_router_logits_match_library_matmul():
+    S = synth.TINY
+    wr = synth.router(S, 0)
+    xb = synth.x_bf16(S, 0, 0)[0]
+    got = oracle.router_logits(wr, xb)
+    ref = wr.astype(np.float64) @ oracle.bf16_array(xb)
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_bf16_decode_matches_float32_upper_half():
+    bits = np.arange(0, 65536, 7, dtype=np.uint32).astype(np.uint16)
+    ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ok = np.isfinite(ref)
+    got = np.array([oracle.bf16(int(b)) for b in bits[ok]])
+    assert np.array_equal(got, ref[ok])
+
+
+def test_round_bf16_is_nearest_ties_to_even():
+    rng = np.random.default_rng(3)
+    vals = list(rng.standard_normal(3000) * np.exp(rng.uniform(-30, 30, 3000)))
+    # exact midpoints between neighbouring bf16 values, both parities
+    for b in (0x3F80, 0x3F81, 0x4000, 0xC123, 0x0081, 0x0001):
+        lo = oracle.bf16(b)
+        hi = oracle.bf16(b + 1)
+        vals.append((lo + hi) / 2)
+    for v in vals:
+        r = oracle.round_bf16(v)
+        rv = oracle.bf16(r)
+        nb = [oracle.bf16((r + d) & 0xFFFF) for d in (-1, 1)]
+        for n in nb:
+            if np.isfinite(n) and np.sign(n) == np.sign(rv):
+                assert abs(v - rv) <= abs(v - n)
+                if abs(v - rv) == abs(v - n):
+                    assert r % 2 == 0
+
+
+# ------------------------------------------------------------------ top-k
+def test_topk_all_orderings_e8():
+    base = np.array([0.5, -1.0, 2.0, 3.25, -0.75, 1.5, 0.0, -2.5])
+    for perm in itertools.permutations(range(8)):
+        lg = base[list(perm)]
+        ref = np.argsort(-lg, kind="stable")
+        for k in (1, 2, 3, 8):
+            assert np.array_equal(oracle.topk(lg, k), ref[:k])
+
+
+def test_topk_ties_take_lower_id():
+    lg = np.array([1.0, 3.0, 3.0, 2.0, 3.0, -1.0])
+    assert list(oracle.topk(lg, 2)) == [1, 2]
+    assert list(oracle.topk(lg, 4)) == [1, 2, 4, 3]
+    assert list(oracle.topk(np.zeros(5), 3)) == [0, 1, 2]
+
+
+def test_topk_random_large_matches_library_sort():
+    rng = np.random.default_rng(4)
+    for _ in range(200):
+        lg = rng.standard_normal(128)
+        assert np.array_equal(oracle.topk(lg, 8), np.argsort(-lg, kind="stable")[:8])
+
+
+# ------------------------------------------------------------------ softmax-renorm
+def test_route_weights_sum_to_one_and_match_library_softmax():
+    rng = np.random.default_rng(5)
+    for _ in range(100):
+        lg = rng.standard_normal(128) * 3
+        ids = oracle.topk(lg, 8)
+        w = oracle.route_weights(lg, ids)
+        assert abs(w.sum() - 1) <= 1e-15 * 8
+        full = softmax(lg)
+        ref = full[ids] / full[ids].sum()
+        assert np.allclose(w, ref, rtol=1e-13, atol=0)
+        w2 = oracle.route_weights(lg + 17.5, ids)
+        assert np.allclose(w, w2, rtol=1e-13)
+        assert np.all(np.diff(w) <= 0)          # descending logits -> descending weights
+
+
+def test_route_weights_two_expert_closed_form():
+    for a, b in [(0.3, -1.2), (5.0, 4.999), (-3.0, -7.0)]:
+        w = oracle.route_weights(np.array([a, b]), np.array([0, 1], dtype=np.int32))
+        assert np.isclose(w[0], expit(a - b), rtol=1e-14)
+        assert np.isclose(w[1], expit(b - a), rtol=1e-14)
+
+
+# ------------------------------------------------------------------ SiLU
+def test_silu_closed_forms():
+    assert oracle.silu(0.0) == 0.0
+    for z in np.linspace(-20, 20, 81):
+        assert np.isclose(oracle.silu(z) - oracle.silu(-z), z, rtol=1e-13, atol=1e-13)
+        assert np.isclose(oracle.silu(z), z * expit(z), rtol=1e-14, atol=1e-300)
+
+
+# ------------------------------------------------------------------ FFN / MoE
+def _dense_ffn(src, layer, e, x):
+    g, u, d = [oracle.dequant_matrix(b) for b in src.blocks(layer, e)]
+    hg = g @ x
+    return d @ (hg * expit(hg) * (u @ x))
+
+
+def test_expert_ffn_matches_dense_numpy():
+    src = oracle.ExpertSource(synth.TINY)
+    x = oracle.bf16_array(synth.x_bf16(synth.TINY, 0, 0)[0])
+    y = oracle.expert_ffn(*src.blocks(0, 5), x)
+    assert np.allclose(y, _dense_ffn(src, 0, 5, x), rtol=1e-11, atol=1e-12)
+
+
+def test_one_hot_k1_is_dense_ffn_of_argmax_expert():
+    S = synth.Shape("tiny-k1", 1, 256, 8, 1, 512)
+    src = oracle.ExpertSource(S)
+    xb = synth.x_bf16(S, 7, 0, T=3)
+    res = oracle.moe_layer(src, 0, xb)
+    for t in range(3):
+        x = oracle.bf16_array(xb[t])
+        e = int(np.argmax(synth.router(S, 0).astype(np.float64) @ x))
+        assert res["ids"][t, 0] == e and res["w"][t, 0] == 1.0
+        assert np.allclose(res["y"][t], _dense_ffn(src, 0, e, x), rtol=1e-11, atol=1e-12)
+
+
+def test_identical_experts_give_dense_ffn_for_any_k():
+    S = synth.TINY
+    src = oracle.ExpertSource(S)
+    g, u, d = src.blocks(0, 2)
+    xb = synth.x_bf16(S, 8, 0)[0]
+    x = oracle.bf16_array(xb)
+    ref = _dense_ffn(src, 0, 2, x)
+    for k in (1, 2, 5, 8):
+        w = np.random.default_rng(k).dirichlet(np.ones(k))
+        y = oracle.moe_token([g] * k, [u] * k, [d] * k, w, xb)
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_moe_layer_is_weighted_sum_of_selected_experts():
+    S = synth.TINY
+    src = oracle.ExpertSource(S)
+    xb = synth.x_bf16(S, 9, 0)
+    res = oracle.moe_layer(src, 0, xb)
+    x = oracle.bf16_array(xb[0])
+    lg = synth.router(S, 0).astype(np.float64) @ x
+    ids = np.argsort(-lg, kind="stable")[:2]
+    w = softmax(lg)[ids] / softmax(lg)[ids].sum()
+    ref = sum(w[s] * _dense_ffn(src, 0, ids[s], x) for s in range(2))
+    assert np.array_equal(res["ids"][0], ids)
+    assert np.allclose(res["y"][0], ref, rtol=1e-11, atol=1e-13)
+
+
+# ------------------------------------------------------------------ RMSNorm
+def test_rmsnorm_unit_rms_and_scale_invariance():
+    rng = np.random.default_rng(6)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal(2048).astype(np.float32))
+    y = rng.standard_normal(2048) * 0.3
+    r, rb = oracle.resid_rmsnorm(xb, y, eps=0.0)
+    assert np.isclose(np.sqrt(np.mean(r * r)), 1.0, rtol=1e-14)
+    v = oracle.bf16_array(xb) + y
+    assert np.allclose(r, v / np.sqrt(np.mean(v * v)), rtol=1e-14)
+    # scale invariance (eps = 0): RMSNorm(c v) = RMSNorm(v)
+    xz = np.zeros(2048, dtype=np.uint16)
+    r1, _ = oracle.resid_rmsnorm(xz, v, eps=0.0)
+    r2, _ = oracle.resid_rmsnorm(xz, 7.0 * v, eps=0.0)
+    assert np.allclose(r1, r2, rtol=1e-14)
+    # eps shrinks the norm as sqrt(ms / (ms + eps))
+    r3, _ = oracle.resid_rmsnorm(xz, v * 1e-3, eps=1e-6)
+    ms = np.mean((v * 1e-3) ** 2)
+    assert np.isclose(np.sqrt(np.mean(r3 * r3)), np.sqrt(ms / (ms + 1e-6)), rtol=1e-12)
+    assert all(rb[i] == oracle.round_bf16(r[i]) for i in range(0, 2048, 97))
