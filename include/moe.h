@@ -1,0 +1,145 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) quantized mixture-of-experts expert FFN.
+ *
+ * What it computes (sparkinfer README: opening paragraph, "deeper
+ * MoE-bandwidth specialization" item and the kernel/moe rows of the layout
+ * table; sparkinfer CuTe-DSL README, "moe" paragraph and "Using it"):
+ * for each token x (bf16, length hidden),
+ *   logits = W_r x                        (router GEMV, fp32 weights)
+ *   ids    = the top_k largest logits      (descending; equal -> lower id)
+ *   w_s    = softmax over the selected logits (softmax renormalised on top-k)
+ *   y      = sum_s w_s * D_{ids_s} ( SiLU(G_{ids_s} x) * (U_{ids_s} x) )
+ * with every expert matrix G, U [inter x hidden] and D [hidden x inter] kept
+ * resident as 4-bit super-blocks (256 weights = 144 bytes: fp16 d, fp16 dmin,
+ * eight 6-bit sub-block scales and mins, 4-bit codes; weight =
+ * d*sc_j*q - dmin*m_j) and dequantized on read. Optionally the stacked-layer
+ * epilogue x_next = bf16(RMSNorm(x + y)) (weight 1, eps from the config).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_host are host memory; every other buffer pointer is
+ *    device memory owned by the caller. The library never allocates, frees,
+ *    synchronises or reads device memory on the host; device calls only
+ *    enqueue kernels on `stream` and are safe to capture into a hipGraph.
+ *  - Device buffers must be 16-byte aligned; the blob 256-byte aligned.
+ *  - Return value: MOE_OK (0) or a negative moe_status. Errors are detected
+ *    on the host before any launch (nothing is enqueued then), except
+ *    MOE_ERR_HIP, which reports a failed launch. Faults inside kernels surface
+ *    at the caller's next synchronisation.
+ *  - T == 0 is valid and enqueues nothing.
+ *  - Inputs must be finite (not checked).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = -1,
+  MOE_ERR_UNSUPPORTED = -2,
+  MOE_ERR_BLOB_MISMATCH = -3,
+  MOE_ERR_SCRATCH_TOO_SMALL = -4,
+  MOE_ERR_HIP = -5,
+};
+
+/* Routing/FFN path choice for moe_expert_ffn and moe_forward (moe_config.flags). */
+#define MOE_FLAG_FORCE_GEMV 0x1u     /* per-token dequant-on-read GEMV for every T */
+#define MOE_FLAG_FORCE_GROUPED 0x2u  /* grouped MFMA expert GEMM for every T > 0 */
+
+typedef struct moe_config {
+  int32_t hidden;      /* H: multiple of 256; 256, 512, 1024 or a multiple of 2048 up to 8192 */
+  int32_t n_experts;   /* E: 1..256 */
+  int32_t top_k;       /* k: 1..min(E, 16) */
+  int32_t inter;       /* I: expert intermediate size, multiple of 256, up to 4096 */
+  int32_t n_layers;    /* layers held in one blob, >= 1 */
+  int32_t max_tokens;  /* largest T any call will pass, >= 1 */
+  uint32_t flags;      /* MOE_FLAG_* */
+  float rms_eps;       /* RMSNorm epsilon of the stacked-layer epilogue, >= 0 */
+} moe_config;
+
+typedef struct moe_plan moe_plan;
+
+/* 1 if the configuration is supported, else 0. No side effects. */
+int moe_is_supported(const moe_config* cfg);
+
+/* Host-only. Validates cfg and builds an immutable plan (host allocation).
+ * *out is set to NULL on error. Thread-safe to use concurrently once made. */
+int moe_plan_create(const moe_config* cfg, moe_plan** out);
+void moe_plan_destroy(moe_plan* plan);
+
+/* Pure size queries (0 on a NULL plan or T out of range). */
+size_t moe_blob_bytes(const moe_plan* plan);          /* header + n_layers * layer bytes */
+size_t moe_header_bytes(const moe_plan* plan);        /* blob header (4096) */
+size_t moe_layer_bytes(const moe_plan* plan);         /* one packed layer */
+size_t moe_layer_offset(const moe_plan* plan, int32_t layer);  /* byte offset of a layer in the blob */
+size_t moe_scratch_bytes(const moe_plan* plan, int32_t T);     /* device scratch for T tokens */
+
+/* ---------------------------------------------------------------- packing
+ * Canonical input: for one layer, gate_host and up_host are
+ * [E][inter][hidden/256] blocks of 144 bytes, down_host is
+ * [E][hidden][inter/256] blocks, router_host is fp32 [E][hidden]; all
+ * row-major, host memory, read only. The device layout written to
+ * dst_host (moe_layer_bytes, host memory owned by the caller) is private to
+ * the library; the caller copies it to blob + moe_layer_offset(layer).
+ */
+int moe_pack_header(const moe_plan* plan, void* dst_host);
+int moe_pack_layer(const moe_plan* plan, const uint8_t* gate_host, const uint8_t* up_host,
+                   const uint8_t* down_host, const float* router_host, void* dst_host);
+/* Inverse of moe_pack_layer (host-only; used to verify the layout). */
+int moe_unpack_layer(const moe_plan* plan, const void* src_host, uint8_t* gate_host, uint8_t* up_host,
+                     uint8_t* down_host, float* router_host);
+/* Checks a host copy of the blob header against the plan:
+ * MOE_OK or MOE_ERR_BLOB_MISMATCH. */
+int moe_blob_check(const moe_plan* plan, const void* header_host);
+
+/* ---------------------------------------------------------------- device calls
+ * Buffers for routing results. topk_ids int32 [T][k] and topk_w fp32 [T][k]
+ * are always written. counts int32 [E], offsets int32 [E+1] and pairs int32
+ * [T*k] (pair index t*k+s, ordered by expert, then token, then slot) are the
+ * on-device dispatch lists; they may be NULL (all three together) when not
+ * wanted.
+ */
+typedef struct moe_route_out {
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* pairs;
+} moe_route_out;
+
+/* Router for T tokens of layer `layer`. If logits is NULL the logits are the
+ * router GEMV of x_bf16 ([T][hidden] bf16) with the layer's fp32 router
+ * weights; otherwise logits (fp32 [T][E], device) are used and x_bf16 is
+ * ignored (may be NULL). */
+int moe_route(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16,
+              const float* logits, int32_t T, const moe_route_out* out, void* scratch,
+              size_t scratch_bytes, hipStream_t stream);
+
+/* Expert FFN and weighted sum for T tokens given routing results r (the
+ * dispatch lists are required when the grouped path runs, i.e. T > 1 without
+ * MOE_FLAG_FORCE_GEMV). out: fp32 [T][hidden]. */
+int moe_expert_ffn(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16,
+                   int32_t T, const moe_route_out* r, float* out, void* scratch, size_t scratch_bytes,
+                   hipStream_t stream);
+
+/* Router + expert FFN for T tokens: out = y (fp32 [T][hidden]). If x_next is
+ * not NULL it also writes x_next = bf16(RMSNorm(x + y)) ([T][hidden] bf16),
+ * the input of the next stacked layer. route_out may be NULL; if given, the
+ * routing results are written there too. Routing comes from the router GEMV. */
+int moe_forward(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16,
+                int32_t T, float* out, uint16_t* x_next, const moe_route_out* route_out,
+                void* scratch, size_t scratch_bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

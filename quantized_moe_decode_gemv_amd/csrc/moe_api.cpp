@@ -1,0 +1,289 @@
+// C ABI of the quantized MoE expert FFN: plan, size queries, host-side
+// packing of canonical 4-bit super-blocks into the device layout, argument
+// validation and kernel launches. No device allocation, no synchronisation,
+// no host reads of device memory.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "moe_internal.h"
+
+using namespace qmoe;
+
+struct moe_plan {
+  Layout d;
+};
+
+static bool cfg_ok(const moe_config* c) {
+  if (!c) return false;
+  const int H = c->hidden, E = c->n_experts, k = c->top_k, I = c->inter;
+  if (H <= 0 || H % QK || E < 1 || E > 256 || k < 1 || k > 16 || k > E || I <= 0 || I % QK) return false;
+  if (c->n_layers < 1 || c->max_tokens < 1 || !(c->rms_eps >= 0.0f)) return false;
+  // gate/up lane mapping: hidden/32 sub-blocks per row either fill a
+  // power-of-two lane group (256, 512, 1024) or whole waves (2048 * {1..4})
+  const bool h_ok = H == 256 || H == 512 || H == 1024 || (H % 2048 == 0 && H / 2048 <= 4);
+  if (!h_ok) return false;
+  // down: k * inter/32 items per output row spread over at most 4 per lane
+  if ((long long)k * (I / 32) > 256) return false;
+  if ((c->flags & (MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GROUPED)) == (MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GROUPED))
+    return false;
+  if (c->flags & ~(MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GROUPED)) return false;
+  return true;
+}
+
+extern "C" int moe_is_supported(const moe_config* cfg) { return cfg_ok(cfg) ? 1 : 0; }
+
+extern "C" int moe_plan_create(const moe_config* cfg, moe_plan** out) {
+  if (!out) return MOE_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (!cfg) return MOE_ERR_INVALID_ARGUMENT;
+  if (!cfg_ok(cfg)) return MOE_ERR_UNSUPPORTED;
+  moe_plan* p = new (std::nothrow) moe_plan;
+  if (!p) return MOE_ERR_INVALID_ARGUMENT;
+  p->d.init(*cfg);
+  *out = p;
+  return MOE_OK;
+}
+
+extern "C" void moe_plan_destroy(moe_plan* plan) { delete plan; }
+
+extern "C" size_t moe_header_bytes(const moe_plan* plan) { return plan ? HEADER_BYTES : 0; }
+extern "C" size_t moe_layer_bytes(const moe_plan* plan) { return plan ? plan->d.layer_bytes : 0; }
+extern "C" size_t moe_blob_bytes(const moe_plan* plan) {
+  return plan ? HEADER_BYTES + (size_t)plan->d.L * plan->d.layer_bytes : 0;
+}
+extern "C" size_t moe_layer_offset(const moe_plan* plan, int32_t layer) {
+  if (!plan || layer < 0 || layer >= plan->d.L) return 0;
+  return HEADER_BYTES + (size_t)layer * plan->d.layer_bytes;
+}
+extern "C" size_t moe_scratch_bytes(const moe_plan* plan, int32_t T) {
+  if (!plan || T < 0 || T > plan->d.maxT) return 0;
+  Scratch s;
+  s.init(plan->d, T);
+  return s.total;
+}
+
+// ---------------------------------------------------------------- packing
+extern "C" int moe_pack_header(const moe_plan* plan, void* dst_host) {
+  if (!plan || !dst_host) return MOE_ERR_INVALID_ARGUMENT;
+  memset(dst_host, 0, HEADER_BYTES);
+  BlobHeader h;
+  memset(&h, 0, sizeof(h));
+  h.magic = BLOB_MAGIC;
+  h.version = BLOB_VERSION;
+  h.hidden = plan->d.H;
+  h.n_experts = plan->d.E;
+  h.top_k = plan->d.k;
+  h.inter = plan->d.I;
+  h.n_layers = plan->d.L;
+  h.layer_bytes = plan->d.layer_bytes;
+  h.header_bytes = HEADER_BYTES;
+  memcpy(dst_host, &h, sizeof(h));
+  return MOE_OK;
+}
+
+extern "C" int moe_blob_check(const moe_plan* plan, const void* header_host) {
+  if (!plan || !header_host) return MOE_ERR_INVALID_ARGUMENT;
+  BlobHeader h;
+  memcpy(&h, header_host, sizeof(h));
+  const Layout& d = plan->d;
+  if (h.magic != BLOB_MAGIC || h.version != BLOB_VERSION || h.hidden != d.H || h.n_experts != d.E ||
+      h.inter != d.I || h.n_layers != d.L || h.layer_bytes != d.layer_bytes || h.header_bytes != HEADER_BYTES)
+    return MOE_ERR_BLOB_MISMATCH;
+  return MOE_OK;
+}
+
+// canonical block -> (16-byte header, 128 code bytes) and back
+static inline void split_block(const uint8_t* blk, uint8_t* hdr, uint8_t* codes) {
+  memcpy(hdr, blk, QHDR);
+  memcpy(codes, blk + QHDR, QCODES);
+}
+static inline void join_block(const uint8_t* hdr, const uint8_t* codes, uint8_t* blk) {
+  memcpy(blk, hdr, QHDR);
+  memcpy(blk + QHDR, codes, QCODES);
+}
+
+extern "C" int moe_pack_layer(const moe_plan* plan, const uint8_t* gate, const uint8_t* up, const uint8_t* down,
+                              const float* router, void* dst_host) {
+  if (!plan || !gate || !up || !down || !router || !dst_host) return MOE_ERR_INVALID_ARGUMENT;
+  const Layout& d = plan->d;
+  uint8_t* dst = static_cast<uint8_t*>(dst_host);
+  memset(dst, 0, d.layer_bytes);
+  memcpy(dst + d.router_off, router, (size_t)d.E * d.H * 4);
+  const size_t grow = (size_t)d.nbH * QBYTES;   // canonical bytes of one gate/up row
+  const size_t drow = (size_t)d.nbI * QBYTES;   // canonical bytes of one down row
+  for (int e = 0; e < d.E; ++e) {
+    for (int r = 0; r < d.I; ++r) {
+      const uint8_t* g = gate + ((size_t)e * d.I + r) * grow;
+      const uint8_t* u = up + ((size_t)e * d.I + r) * grow;
+      uint8_t* rp = dst + d.gu_off + (size_t)e * d.gu_expert_bytes + (size_t)r * d.rp_bytes;
+      uint8_t* gcodes = rp;
+      uint8_t* ucodes = rp + (size_t)d.nbH * QCODES;
+      uint8_t* ghdr = rp + (size_t)2 * d.nbH * QCODES;
+      uint8_t* uhdr = ghdr + (size_t)d.nbH * QHDR;
+      for (int b = 0; b < d.nbH; ++b) {
+        split_block(g + (size_t)b * QBYTES, ghdr + (size_t)b * QHDR, gcodes + (size_t)b * QCODES);
+        split_block(u + (size_t)b * QBYTES, uhdr + (size_t)b * QHDR, ucodes + (size_t)b * QCODES);
+      }
+    }
+    for (int n = 0; n < d.H; ++n) {
+      const uint8_t* s = down + ((size_t)e * d.H + n) * drow;
+      uint8_t* row = dst + d.dn_off + (size_t)e * d.dn_expert_bytes + (size_t)n * d.drow_bytes;
+      for (int b = 0; b < d.nbI; ++b)
+        split_block(s + (size_t)b * QBYTES, row + (size_t)d.nbI * QCODES + (size_t)b * QHDR, row + (size_t)b * QCODES);
+    }
+  }
+  return MOE_OK;
+}
+
+extern "C" int moe_unpack_layer(const moe_plan* plan, const void* src_host, uint8_t* gate, uint8_t* up,
+                                uint8_t* down, float* router) {
+  if (!plan || !src_host || !gate || !up || !down || !router) return MOE_ERR_INVALID_ARGUMENT;
+  const Layout& d = plan->d;
+  const uint8_t* src = static_cast<const uint8_t*>(src_host);
+  memcpy(router, src + d.router_off, (size_t)d.E * d.H * 4);
+  const size_t grow = (size_t)d.nbH * QBYTES;
+  const size_t drow = (size_t)d.nbI * QBYTES;
+  for (int e = 0; e < d.E; ++e) {
+    for (int r = 0; r < d.I; ++r) {
+      uint8_t* g = gate + ((size_t)e * d.I + r) * grow;
+      uint8_t* u = up + ((size_t)e * d.I + r) * grow;
+      const uint8_t* rp = src + d.gu_off + (size_t)e * d.gu_expert_bytes + (size_t)r * d.rp_bytes;
+      const uint8_t* gcodes = rp;
+      const uint8_t* ucodes = rp + (size_t)d.nbH * QCODES;
+      const uint8_t* ghdr = rp + (size_t)2 * d.nbH * QCODES;
+      const uint8_t* uhdr = ghdr + (size_t)d.nbH * QHDR;
+      for (int b = 0; b < d.nbH; ++b) {
+        join_block(ghdr + (size_t)b * QHDR, gcodes + (size_t)b * QCODES, g + (size_t)b * QBYTES);
+        join_block(uhdr + (size_t)b * QHDR, ucodes + (size_t)b * QCODES, u + (size_t)b * QBYTES);
+      }
+    }
+    for (int n = 0; n < d.H; ++n) {
+      uint8_t* s = down + ((size_t)e * d.H + n) * drow;
+      const uint8_t* row = src + d.dn_off + (size_t)e * d.dn_expert_bytes + (size_t)n * d.drow_bytes;
+      for (int b = 0; b < d.nbI; ++b)
+        join_block(row + (size_t)d.nbI * QCODES + (size_t)b * QHDR, row + (size_t)b * QCODES, s + (size_t)b * QBYTES);
+    }
+  }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- device calls
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static int common_checks(const moe_plan* plan, const void* blob, int32_t layer, int32_t T, void* scratch,
+                         size_t scratch_bytes, Scratch* sc) {
+  if (!plan || !blob || !aligned(blob, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (layer < 0 || layer >= plan->d.L) return MOE_ERR_INVALID_ARGUMENT;
+  if (T < 0 || T > plan->d.maxT) return MOE_ERR_INVALID_ARGUMENT;
+  sc->init(plan->d, T);
+  if (T > 0) {
+    if (!scratch || !aligned(scratch, 256)) return MOE_ERR_INVALID_ARGUMENT;
+    if (scratch_bytes < sc->total) return MOE_ERR_SCRATCH_TOO_SMALL;
+  }
+  return MOE_OK;
+}
+
+static const uint8_t* layer_ptr(const moe_plan* plan, const void* blob, int32_t layer) {
+  return static_cast<const uint8_t*>(blob) + HEADER_BYTES + (size_t)layer * plan->d.layer_bytes;
+}
+
+static bool use_grouped(const moe_plan* plan, int32_t T) {
+  (void)T;
+  (void)plan;
+  return false;  // grouped MFMA path not enabled in this build
+}
+
+static int route_impl(const moe_plan* plan, const uint8_t* L, const uint16_t* x, const float* logits, int32_t T,
+                      int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* pairs, uint8_t* scr,
+                      const Scratch& sc, hipStream_t stream) {
+  const Layout& d = plan->d;
+  const float* lg = logits;
+  if (!lg) {
+    float* tmp = reinterpret_cast<float*>(scr + sc.logits);
+    if (launch_router(d, reinterpret_cast<const float*>(L + d.router_off), x, tmp, T, stream) != hipSuccess)
+      return MOE_ERR_HIP;
+    lg = tmp;
+  }
+  if (launch_topk(d, lg, ids, w, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (counts && launch_dispatch(d, ids, counts, offsets, pairs, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+extern "C" int moe_route(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16,
+                         const float* logits, int32_t T, const moe_route_out* out, void* scratch,
+                         size_t scratch_bytes, hipStream_t stream) {
+  Scratch sc;
+  int st = common_checks(plan, blob, layer, T, scratch, scratch_bytes, &sc);
+  if (st) return st;
+  if (!out || !out->topk_ids || !out->topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  const bool lists = out->counts || out->offsets || out->pairs;
+  if (lists && !(out->counts && out->offsets && out->pairs)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!logits && (!x_bf16 || !aligned(x_bf16, 16))) return MOE_ERR_INVALID_ARGUMENT;
+  if (logits && !aligned(logits, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  return route_impl(plan, layer_ptr(plan, blob, layer), x_bf16, logits, T, out->topk_ids, out->topk_w,
+                    lists ? out->counts : nullptr, out->offsets, out->pairs, static_cast<uint8_t*>(scratch), sc,
+                    stream);
+}
+
+extern "C" int moe_expert_ffn(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16,
+                              int32_t T, const moe_route_out* r, float* out, void* scratch, size_t scratch_bytes,
+                              hipStream_t stream) {
+  Scratch sc;
+  int st = common_checks(plan, blob, layer, T, scratch, scratch_bytes, &sc);
+  if (st) return st;
+  if (!r || !r->topk_ids || !r->topk_w || !x_bf16 || !aligned(x_bf16, 16) || !out || !aligned(out, 16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  const Layout& d = plan->d;
+  const uint8_t* L = layer_ptr(plan, blob, layer);
+  uint8_t* scr = static_cast<uint8_t*>(scratch);
+  float* h = reinterpret_cast<float*>(scr + sc.h);
+  if (use_grouped(plan, T)) return MOE_ERR_UNSUPPORTED;
+  if (launch_gateup(d, L, x_bf16, r->topk_ids, nullptr, nullptr, nullptr, h, T, false, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (launch_down(d, L, r->topk_ids, r->topk_w, h, out, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+extern "C" int moe_forward(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16, int32_t T,
+                           float* out, uint16_t* x_next, const moe_route_out* route_out, void* scratch,
+                           size_t scratch_bytes, hipStream_t stream) {
+  Scratch sc;
+  int st = common_checks(plan, blob, layer, T, scratch, scratch_bytes, &sc);
+  if (st) return st;
+  if (!x_bf16 || !aligned(x_bf16, 16) || !out || !aligned(out, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (x_next && !aligned(x_next, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (route_out && (!route_out->topk_ids || !route_out->topk_w)) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  const Layout& d = plan->d;
+  const uint8_t* L = layer_ptr(plan, blob, layer);
+  uint8_t* scr = static_cast<uint8_t*>(scratch);
+  int32_t* ids = route_out ? route_out->topk_ids : reinterpret_cast<int32_t*>(scr + sc.ids);
+  float* w = route_out ? route_out->topk_w : reinterpret_cast<float*>(scr + sc.w);
+  float* lg = reinterpret_cast<float*>(scr + sc.logits);
+  float* h = reinterpret_cast<float*>(scr + sc.h);
+  if (launch_router(d, reinterpret_cast<const float*>(L + d.router_off), x_bf16, lg, T, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (use_grouped(plan, T)) return MOE_ERR_UNSUPPORTED;
+  const bool fused = (T == 1);
+  if (!fused && launch_topk(d, lg, ids, w, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_gateup(d, L, x_bf16, ids, lg, ids, w, h, T, fused, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_down(d, L, ids, w, h, out, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (x_next && launch_resid_norm(d, x_bf16, out, x_next, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+extern "C" const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_BLOB_MISMATCH: return "weight blob does not match the plan";
+    case MOE_ERR_SCRATCH_TOO_SMALL: return "scratch buffer too small";
+    case MOE_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,587 @@
+// gfx950 kernels of the single-stream (per-token) path: router GEMV, top-k
+// routing, dequant-on-read gate/up GEMV with SiLU(gate)*up, dequant-on-read
+// down GEMV with the routing-weighted combine, residual + RMSNorm, and the
+// on-device expert dispatch lists.
+//
+// The expert GEMVs follow the pages' decode design goal -- experts stay
+// resident as 4-bit super-blocks and are dequantized on read, so the bytes per
+// token are the encoded weight bytes (sparkinfer README, opening paragraph and
+// the MoE-bandwidth item; kernel table: decode GEMV, fused quantized MoE
+// expert FFN, GGUF dequant). Their shape on CDNA4 is our own: one wave64 owns
+// whole weight rows, each lane owns fixed 32-weight sub-blocks of every row it
+// touches, so its slice of the activation vector and that slice's sum stay in
+// registers for all rows; weights are streamed with 128-bit non-temporal loads
+// and the sub-block affine (d*sc*q - dmin*m) is applied once per sub-block:
+//   sum_i (a*q_i - b) x_i = a * sum_i q_i x_i - b * sum_i x_i.
+// Gate/up use the exact trick bf16(128 + q) = 0x4300 | q, so two codes per
+// v_dot2_f32_bf16 against the bf16 activations, with 128*sum(x) removed after.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace qmoe {
+
+typedef unsigned int u32;
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+constexpr int BLOCK = 256;
+
+__device__ __forceinline__ u32x4 load_nt(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ float dot2_bf16(u32 a, u32 b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+__device__ __forceinline__ float half_bits_to_float(u32 bits) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)bits);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(u32 bits) { return __builtin_bit_cast(float, bits << 16); }
+
+// Reinterpret a 32-bit value as fp32. Takes the value (not a vector element
+// lvalue) so the cast always sees the intended component.
+__device__ __forceinline__ float as_f32(u32 v) { return __builtin_bit_cast(float, v); }
+
+// Nearest-even bf16 of a finite fp32.
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
+  u32 b = __builtin_bit_cast(u32, f);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+// Sum over groups of W adjacent lanes (W a power of two <= 64); every lane of
+// a group ends with the group's sum. Fixed butterfly order -> deterministic.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = W / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, WAVE);
+  return v;
+}
+
+// Six-bit field at bit position p of the 96-bit little-endian field area
+// (header dwords 1..3).
+__device__ __forceinline__ u32 field6(const u32x4& h, int p) {
+  const int idx = p >> 5, sh = p & 31;
+  const u32 lo = idx == 0 ? h.y : (idx == 1 ? h.z : h.w);
+  const u32 hi = idx == 0 ? h.z : (idx == 1 ? h.w : 0u);
+  return __builtin_amdgcn_alignbit(hi, lo, sh) & 63u;
+}
+
+// Sub-block affine of sub-block jj (0..7) of a super-block header:
+// weight = a*q - b.
+struct Affine { float a, b; };
+__device__ __forceinline__ Affine header_affine(const u32x4& h, int jj) {
+  const float d = half_bits_to_float(h.x & 0xFFFFu);
+  const float dmin = half_bits_to_float(h.x >> 16);
+  const u32 sc = field6(h, 6 * jj), m = field6(h, 48 + 6 * jj);
+  return {d * (float)sc, dmin * (float)m};   // both products exact in fp32
+}
+
+// sum_i (128 + q_i) * x_i over one 32-code sub-block, two codes per dot2.
+// X[4d+c] holds the bf16 pair matching the nibble pair extracted at shift 4c
+// from code dword d (elements 8d+c' and 8d+c'+4, see load_x_pairs).
+__device__ __forceinline__ float dot_codes_bf16(const u32x4& c, const u32* X) {
+  const u32 M = 0x000F000Fu, B = 0x43004300u;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  const u32 w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32 v = w[d];
+    a0 = dot2_bf16((v & M) | B, X[4 * d + 0], a0);
+    a1 = dot2_bf16(((v >> 4) & M) | B, X[4 * d + 1], a1);
+    a2 = dot2_bf16(((v >> 8) & M) | B, X[4 * d + 2], a2);
+    a3 = dot2_bf16(((v >> 12) & M) | B, X[4 * d + 3], a3);
+  }
+  return (a0 + a1) + (a2 + a3);
+}
+
+// Load the 32 bf16 activations of one sub-block and arrange them in the pair
+// order of dot_codes_bf16. Code dword d covers elements 8d..8d+7: shift 0
+// gives (8d, 8d+4), shift 4 gives (8d+1, 8d+5), shift 8 gives (8d+2, 8d+6),
+// shift 12 gives (8d+3, 8d+7). Returns sum(x) in fp32.
+__device__ __forceinline__ float load_x_pairs(const uint16_t* xs, u32* X) {
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 r = load16(xs + 8 * q);   // elements 8q .. 8q+7
+    X[4 * q + 0] = (r.x & 0xFFFFu) | (r.z << 16);
+    X[4 * q + 1] = (r.x >> 16) | (r.z & 0xFFFF0000u);
+    X[4 * q + 2] = (r.y & 0xFFFFu) | (r.w << 16);
+    X[4 * q + 3] = (r.y >> 16) | (r.w & 0xFFFF0000u);
+    s += (bf16_bits_to_float(r.x & 0xFFFFu) + bf16_bits_to_float(r.x >> 16)) +
+         (bf16_bits_to_float(r.y & 0xFFFFu) + bf16_bits_to_float(r.y >> 16)) +
+         (bf16_bits_to_float(r.z & 0xFFFFu) + bf16_bits_to_float(r.z >> 16)) +
+         (bf16_bits_to_float(r.w & 0xFFFFu) + bf16_bits_to_float(r.w >> 16));
+  }
+  return s;
+}
+
+// sum_i q_i * h_i over one 32-code sub-block with fp32 h (32 values).
+__device__ __forceinline__ float dot_codes_f32(const u32x4& c, const float* hv) {
+  float a0 = 0.f, a1 = 0.f;
+  const u32 w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32 lo = w[d] & 0x0F0F0F0Fu, hi = (w[d] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      a0 = fmaf((float)((lo >> (8 * b)) & 0xFFu), hv[8 * d + 2 * b], a0);
+      a1 = fmaf((float)((hi >> (8 * b)) & 0xFFu), hv[8 * d + 2 * b + 1], a1);
+    }
+  }
+  return a0 + a1;
+}
+
+// ------------------------------------------------------------------ top-k
+// One wave selects the k largest of E <= 256 logits (descending; equal values
+// -> lower id) and their softmax restricted to the selection. Result in
+// sid/sw (k entries, any memory the wave can write).
+__device__ void wave_topk(const float* __restrict__ lg, int E, int k, int32_t* sid, float* sw) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  float v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + WAVE * q;
+    v[q] = e < E ? lg[e] : -INFINITY;
+  }
+  bool taken[4] = {false, false, false, false};
+  float top0 = 0.f, den = 0.f;
+  for (int s = 0; s < k; ++s) {
+    // lane-local best (value desc, id asc)
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + WAVE * q;
+      if (e < E && !taken[q] && (v[q] > bv || (v[q] == bv && e < bi))) { bv = v[q]; bi = e; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, WAVE);
+      const int oi = __shfl_xor(bi, off, WAVE);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (lane + WAVE * q == bi) taken[q] = true;
+    if (s == 0) top0 = bv;
+    const float ex = expf(bv - top0);
+    den += ex;
+    if (lane == 0) { sid[s] = bi; sw[s] = ex; }
+  }
+  // all lanes hold the same den; lane 0 wrote the numerators
+  __builtin_amdgcn_wave_barrier();
+  if (lane == 0) {
+    const float inv = 1.0f / den;
+    for (int s = 0; s < k; ++s) sw[s] *= inv;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+__global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ logits, int32_t* __restrict__ ids,
+                                                     float* __restrict__ w, int E, int k, int T) {
+  const int t = blockIdx.x * (BLOCK / WAVE) + (threadIdx.x / WAVE);
+  if (t >= T) return;
+  wave_topk(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+}
+
+// ------------------------------------------------------------------ router GEMV
+// One block per expert row; the 256 threads split the hidden dimension
+// (4 consecutive fp32 weights each per chunk). Tokens loop inside with the
+// weight slice held in registers. Block reduction in a fixed order.
+template <int CH>  // chunks of 4 weights per thread: H = CH * 1024
+__global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__ wr, const uint16_t* __restrict__ x,
+                                                       float* __restrict__ logits, int E, int H, int T) {
+  __shared__ float part[BLOCK / WAVE];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x;
+  float w[CH][4];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + (size_t)e * H + 4 * (tid + BLOCK * c)));
+    w[c][0] = as_f32(v.x); w[c][1] = as_f32(v.y);
+    w[c][2] = as_f32(v.z); w[c][3] = as_f32(v.w);
+  }
+  for (int t = 0; t < T; ++t) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * H + 4 * (tid + BLOCK * c));
+      acc = fmaf(w[c][0], bf16_bits_to_float(xv.x & 0xFFFFu), acc);
+      acc = fmaf(w[c][1], bf16_bits_to_float(xv.x >> 16), acc);
+      acc = fmaf(w[c][2], bf16_bits_to_float(xv.y & 0xFFFFu), acc);
+      acc = fmaf(w[c][3], bf16_bits_to_float(xv.y >> 16), acc);
+    }
+    acc = group_sum<WAVE>(acc);
+    if ((tid & (WAVE - 1)) == 0) part[tid / WAVE] = acc;
+    __syncthreads();
+    if (tid == 0) logits[(size_t)t * E + e] = (part[0] + part[1]) + (part[2] + part[3]);
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ gate/up GEMV
+// Wave work unit: RPS*U consecutive intermediate rows of one (token, slot);
+// RPS = 64/LPR rows per step, LPR lanes per row, IPL sub-blocks per lane.
+// h[(t*k + s)*I + r] = SiLU(G_e[r]·x_t) * (U_e[r]·x_t).
+template <int IPL, int LPR, int U>
+__global__ __launch_bounds__(BLOCK) void gateup_kernel(
+    const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int E, int k,
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids_in, const float* __restrict__ logits,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ h, int T, int fused_topk) {
+  constexpr int RPS = WAVE / LPR;
+  __shared__ int32_t s_ids[16];
+  __shared__ float s_w[16];
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wid = threadIdx.x / WAVE;
+  if (fused_topk) {
+    // T == 1: every block derives the same routing from the logits.
+    if (wid == 0) wave_topk(logits, E, k, s_ids, s_w);
+    __syncthreads();
+    if (blockIdx.x == 0 && threadIdx.x < k) { ids_out[threadIdx.x] = s_ids[threadIdx.x]; w_out[threadIdx.x] = s_w[threadIdx.x]; }
+  }
+  const int unit = blockIdx.x * (BLOCK / WAVE) + wid;
+  const int rows_per_unit = RPS * U;
+  const int total_units = T * k * I / rows_per_unit;
+  if (unit >= total_units) return;
+  const int flat0 = unit * rows_per_unit;   // flat row index over (t, s, r)
+  const int ts = flat0 / I;                 // t*k + s
+  const int r0 = flat0 % I;
+  const int t = ts / k;
+  const int e = fused_topk ? s_ids[ts] : ids_in[ts];
+  const int rho = lane / LPR, lam = lane % LPR;
+
+  u32 X[IPL][16];
+  float S[IPL];
+#pragma unroll
+  for (int q = 0; q < IPL; ++q) {
+    const int j = lam + LPR * q;
+    S[q] = load_x_pairs(x + (size_t)t * H + 32 * j, X[q]);
+  }
+  const uint8_t* base = gu + (size_t)e * gu_expert_bytes;
+  const int half = H / 2;                 // code bytes per matrix row
+  const int hdr = H / 2 * 2;              // headers start after both code areas
+  const int nb = H / QK;
+  u32x4 cg[U][IPL], cu[U][IPL], hg[U][IPL], hu[U][IPL];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint8_t* rp = base + (size_t)(r0 + u * RPS + rho) * rp_bytes;
+#pragma unroll
+    for (int q = 0; q < IPL; ++q) {
+      const int j = lam + LPR * q;
+      cg[u][q] = load_nt(rp + 16 * j);
+      cu[u][q] = load_nt(rp + half + 16 * j);
+      hg[u][q] = load_nt(rp + hdr + QHDR * (j >> 3));
+      hu[u][q] = load_nt(rp + hdr + QHDR * nb + QHDR * (j >> 3));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float pg = 0.f, pu = 0.f;
+#pragma unroll
+    for (int q = 0; q < IPL; ++q) {
+      const int jj = (lam + LPR * q) & 7;
+      const Affine ag = header_affine(hg[u][q], jj);
+      const Affine au = header_affine(hu[u][q], jj);
+      const float Ag = dot_codes_bf16(cg[u][q], X[q]);
+      const float Au = dot_codes_bf16(cu[u][q], X[q]);
+      pg += ag.a * Ag - (128.f * ag.a + ag.b) * S[q];
+      pu += au.a * Au - (128.f * au.a + au.b) * S[q];
+    }
+    pg = group_sum<LPR>(pg);
+    pu = group_sum<LPR>(pu);
+    if (lam == 0) {
+      const float silu = pg / (1.0f + expf(-pg));
+      h[(size_t)ts * I + r0 + u * RPS + rho] = silu * pu;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ down GEMV + combine
+// Items of an output row: (slot s, sub-block j) for s < k, j < I/32, i.e.
+// G = k*I/32 items; item i = lam + LPR*q. Wave work unit: RPS*U consecutive
+// output rows of one token. y[t*H + n] = sum_s w_s * D_{e_s}[n]·h_{t,s}.
+template <int IPL, int LPR, int U>
+__global__ __launch_bounds__(BLOCK) void down_kernel(
+    const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I, int k,
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, const float* __restrict__ h,
+    float* __restrict__ y, int T) {
+  constexpr int RPS = WAVE / LPR;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wid = threadIdx.x / WAVE;
+  const int unit = blockIdx.x * (BLOCK / WAVE) + wid;
+  const int rows_per_unit = RPS * U;
+  const int total_units = T * H / rows_per_unit;
+  if (unit >= total_units) return;
+  const int flat0 = unit * rows_per_unit;
+  const int t = flat0 / H;
+  const int n0 = flat0 % H;
+  const int rho = lane / LPR, lam = lane % LPR;
+  const int nsb = I / 32;
+  const int G = k * nsb;
+
+  float hv[IPL][32];
+  float Sh[IPL], ws[IPL];
+  const uint8_t* eb[IPL];
+  int jq[IPL];
+  bool valid[IPL];
+#pragma unroll
+  for (int q = 0; q < IPL; ++q) {
+    const int i = lam + LPR * q;
+    valid[q] = i < G;
+    const int s = valid[q] ? i / nsb : 0;
+    const int j = valid[q] ? i % nsb : 0;
+    jq[q] = j;
+    const int ts = t * k + s;
+    ws[q] = valid[q] ? wts[ts] : 0.f;
+    eb[q] = dn + (size_t)ids[ts] * dn_expert_bytes;
+    const float* hp = h + (size_t)ts * I + 32 * j;
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const u32x4 v = load16(hp + 4 * c);
+      hv[q][4 * c + 0] = as_f32(v.x);
+      hv[q][4 * c + 1] = as_f32(v.y);
+      hv[q][4 * c + 2] = as_f32(v.z);
+      hv[q][4 * c + 3] = as_f32(v.w);
+      sum += (hv[q][4 * c + 0] + hv[q][4 * c + 1]) + (hv[q][4 * c + 2] + hv[q][4 * c + 3]);
+    }
+    Sh[q] = sum;
+  }
+  const int half = I / 2;
+  u32x4 cd[U][IPL], hd[U][IPL];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int n = n0 + u * RPS + rho;
+#pragma unroll
+    for (int q = 0; q < IPL; ++q) {
+      if (valid[q]) {
+        const uint8_t* row = eb[q] + (size_t)n * drow_bytes;
+        cd[u][q] = load_nt(row + 16 * jq[q]);
+        hd[u][q] = load_nt(row + half + QHDR * (jq[q] >> 3));
+      } else {
+        cd[u][q] = u32x4{0u, 0u, 0u, 0u};
+        hd[u][q] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float p = 0.f;
+#pragma unroll
+    for (int q = 0; q < IPL; ++q) {
+      const Affine a = header_affine(hd[u][q], jq[q] & 7);
+      const float dq = dot_codes_f32(cd[u][q], hv[q]);
+      p += ws[q] * (a.a * dq - a.b * Sh[q]);
+    }
+    p = group_sum<LPR>(p);
+    if (lam == 0) y[(size_t)t * H + n0 + u * RPS + rho] = p;
+  }
+}
+
+// ------------------------------------------------------------------ residual + RMSNorm
+// One block per token: v = x + y (fp32), x_next = bf16(v / sqrt(mean(v^2) + eps)).
+__global__ __launch_bounds__(BLOCK) void resid_norm_kernel(const uint16_t* __restrict__ x, const float* __restrict__ y,
+                                                           uint16_t* __restrict__ xn, int H, float eps) {
+  __shared__ float part[BLOCK / WAVE];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  float ss = 0.f;
+  for (int i = tid; i < H; i += BLOCK) {
+    const float v = bf16_bits_to_float(x[(size_t)t * H + i]) + y[(size_t)t * H + i];
+    ss = fmaf(v, v, ss);
+  }
+  ss = group_sum<WAVE>(ss);
+  if ((tid & (WAVE - 1)) == 0) part[tid / WAVE] = ss;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int i = tid; i < H; i += BLOCK) {
+    const float v = bf16_bits_to_float(x[(size_t)t * H + i]) + y[(size_t)t * H + i];
+    xn[(size_t)t * H + i] = float_to_bf16_rne(v * inv);
+  }
+}
+
+// ------------------------------------------------------------------ dispatch lists
+// Single block of 1024 threads (16 waves). counts[e] = #pairs routed to e,
+// offsets = exclusive scan, pairs = pair indices p = t*k+s ordered by
+// (expert, p). Deterministic: ranks come from ballots, not from atomics order.
+constexpr int DISP_THREADS = 1024;
+constexpr int DISP_WAVES = DISP_THREADS / WAVE;
+__global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets, int32_t* __restrict__ pairs,
+                                                                int E, int P) {
+  __shared__ int cnt[DISP_WAVES][256];
+  __shared__ int off[257];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
+  for (int i = tid; i < DISP_WAVES * 256; i += DISP_THREADS) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int chunk = (P + DISP_WAVES - 1) / DISP_WAVES;
+  const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
+  for (int p = p0 + lane; p < p1; p += WAVE) atomicAdd(&cnt[wid][ids[p]], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      off[e] = run;
+      for (int w = 0; w < DISP_WAVES; ++w) { const int c = cnt[w][e]; cnt[w][e] = run; run += c; }
+    }
+    off[E] = run;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += DISP_THREADS) { counts[e] = off[e + 1] - off[e]; offsets[e] = off[e]; }
+  if (tid == 0) offsets[E] = off[E];
+  // cnt[w][e] is now the first output slot of wave w's pairs for expert e
+  for (int pb = p0; pb < p1; pb += WAVE) {
+    const int p = pb + lane;
+    const bool act = p < p1;
+    const int e = act ? ids[p] : -1;
+    unsigned long long same = __ballot(act);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const unsigned long long bal = __ballot(act && ((e >> b) & 1));
+      same &= ((e >> b) & 1) ? bal : ~bal;
+    }
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
+    const int rank = __popcll(same & below);
+    const int n = __popcll(same);
+    int base = 0;
+    if (act) base = cnt[wid][e];
+    __builtin_amdgcn_wave_barrier();
+    if (act) pairs[base + rank] = p;
+    if (act && rank == n - 1) cnt[wid][e] = base + n;
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+static int pow2ceil(int v) { int p = 1; while (p < v) p <<= 1; return p; }
+
+static hipError_t launch_router_big(const Layout& d, const float* wr, const uint16_t* x, float* logits, int T, hipStream_t s) {
+  const int CH = d.H / 1024;
+  dim3 grid(d.E), block(BLOCK);
+  switch (CH) {
+    case 1: hipLaunchKernelGGL(router_kernel<1>, grid, block, 0, s, wr, x, logits, d.E, d.H, T); break;
+    case 2: hipLaunchKernelGGL(router_kernel<2>, grid, block, 0, s, wr, x, logits, d.E, d.H, T); break;
+    case 4: hipLaunchKernelGGL(router_kernel<4>, grid, block, 0, s, wr, x, logits, d.E, d.H, T); break;
+    case 6: hipLaunchKernelGGL(router_kernel<6>, grid, block, 0, s, wr, x, logits, d.E, d.H, T); break;
+    case 8: hipLaunchKernelGGL(router_kernel<8>, grid, block, 0, s, wr, x, logits, d.E, d.H, T); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Router for hidden sizes that are not a multiple of 1024: wave per row.
+__global__ __launch_bounds__(BLOCK) void router_small_kernel(const float* __restrict__ wr, const uint16_t* __restrict__ x,
+                                                             float* __restrict__ logits, int E, int H, int T) {
+  const int e = blockIdx.x * (BLOCK / WAVE) + threadIdx.x / WAVE;
+  const int lane = threadIdx.x & (WAVE - 1);
+  if (e >= E) return;
+  for (int t = 0; t < T; ++t) {
+    float acc = 0.f;
+    for (int i = lane; i < H; i += WAVE) acc = fmaf(wr[(size_t)e * H + i], bf16_bits_to_float(x[(size_t)t * H + i]), acc);
+    acc = group_sum<WAVE>(acc);
+    if (lane == 0) logits[(size_t)t * E + e] = acc;
+  }
+}
+
+hipError_t launch_router(const Layout& d, const float* wr, const uint16_t* x, float* logits, int T, hipStream_t s) {
+  if (d.H % 1024 == 0 && d.H <= 8192 && (d.H / 1024 <= 2 || d.H / 1024 == 4 || d.H / 1024 == 6 || d.H / 1024 == 8))
+    return launch_router_big(d, wr, x, logits, T, s);
+  hipLaunchKernelGGL(router_small_kernel, dim3((d.E + 3) / 4), dim3(BLOCK), 0, s, wr, x, logits, d.E, d.H, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const Layout& d, const float* logits, int32_t* ids, float* w, int T, hipStream_t s) {
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(BLOCK), 0, s, logits, ids, w, d.E, d.k, T);
+  return hipGetLastError();
+}
+
+template <int IPL, int LPR, int U>
+static void gateup_go(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids, const float* logits,
+                      int32_t* ids_out, float* w_out, float* h, int T, bool fused, hipStream_t s) {
+  constexpr int RPS = WAVE / LPR;
+  const long long units = (long long)T * d.k * d.I / (RPS * U);
+  const int blocks = (int)((units + 3) / 4);
+  hipLaunchKernelGGL((gateup_kernel<IPL, LPR, U>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s,
+                     layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
+                     ids_out, w_out, h, T, fused ? 1 : 0);
+}
+
+hipError_t launch_gateup(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids,
+                         const float* logits, int32_t* ids_out, float* w_out, float* h, int T, bool fused_topk,
+                         hipStream_t s) {
+  const int nsb = d.H / 32;
+  // rows per wave unit must divide I (a multiple of 256): RPS*U <= 256
+  if (nsb >= 64) {
+    switch (nsb / 64) {
+      case 1: gateup_go<1, 64, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
+      case 2: gateup_go<2, 64, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
+      case 3: gateup_go<3, 64, 1>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
+      case 4: gateup_go<4, 64, 1>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (nsb) {
+      case 8: gateup_go<1, 8, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
+      case 16: gateup_go<1, 16, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
+      case 32: gateup_go<1, 32, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int IPL, int LPR, int U>
+static void down_go(const Layout& d, const uint8_t* layer, const int32_t* ids, const float* w, const float* h, float* y,
+                    int T, hipStream_t s) {
+  constexpr int RPS = WAVE / LPR;
+  const long long units = (long long)T * d.H / (RPS * U);
+  const int blocks = (int)((units + 3) / 4);
+  hipLaunchKernelGGL((down_kernel<IPL, LPR, U>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s, layer + d.dn_off,
+                     d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
+}
+
+hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids, const float* w, const float* h,
+                       float* y, int T, hipStream_t s) {
+  const int G = d.k * (d.I / 32);
+  const int LPR = G >= WAVE ? WAVE : pow2ceil(G);
+  const int IPL = (G + LPR - 1) / LPR;
+  // RPS*U must divide H (a multiple of 256)
+  if (LPR == 64) {
+    switch (IPL) {
+      case 1: down_go<1, 64, 2>(d, layer, ids, w, h, y, T, s); break;
+      case 2: down_go<2, 64, 2>(d, layer, ids, w, h, y, T, s); break;
+      case 3: down_go<3, 64, 2>(d, layer, ids, w, h, y, T, s); break;
+      case 4: down_go<4, 64, 1>(d, layer, ids, w, h, y, T, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (LPR) {
+      case 8: down_go<1, 8, 2>(d, layer, ids, w, h, y, T, s); break;
+      case 16: down_go<1, 16, 2>(d, layer, ids, w, h, y, T, s); break;
+      case 32: down_go<1, 32, 2>(d, layer, ids, w, h, y, T, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y, uint16_t* x_next, int T, hipStream_t s) {
+  hipLaunchKernelGGL(resid_norm_kernel, dim3(T), dim3(BLOCK), 0, s, x, y, x_next, d.H, d.eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* pairs, int T,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs, d.E, T * d.k);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -1,0 +1,96 @@
+// Internal layout and launcher declarations shared by the C-ABI layer and the
+// kernels. Not part of the public ABI.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/moe.h"
+
+namespace qmoe {
+
+constexpr int QK = 256;            // weights per super-block
+constexpr int QBYTES = 144;        // bytes per super-block
+constexpr int QHDR = 16;           // header bytes (d, dmin, 12 bytes of 6-bit fields)
+constexpr int QCODES = 128;        // code bytes
+constexpr size_t HEADER_BYTES = 4096;
+constexpr uint64_t BLOB_MAGIC = 0x31424F4C42454F4DULL;  // "MOEBLOB1" little-endian
+constexpr uint32_t BLOB_VERSION = 1;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Device layout of one layer (all offsets from the layer base, 256-aligned):
+//   router   fp32 [E][H]
+//   gate/up  per expert, per intermediate row r, one "row pair" record:
+//            [gate codes H/2 B][up codes H/2 B][gate headers H/256*16 B][up headers H/256*16 B]
+//            (codes of super-block b, sub-block j' at byte 128*b + 16*j'; canonical nibble order)
+//   down     per expert, per output row n: [codes I/2 B][headers I/256*16 B]
+struct Layout {
+  int H, E, k, I, L, maxT;
+  uint32_t flags;
+  float eps;
+  int nbH, nbI;                 // super-blocks per gate/up row and per down row
+  size_t rp_bytes;              // gate/up row-pair record
+  size_t gu_expert_bytes;
+  size_t drow_bytes;            // down row record
+  size_t dn_expert_bytes;
+  size_t router_off, gu_off, dn_off, layer_bytes;
+
+  void init(const moe_config& c) {
+    H = c.hidden; E = c.n_experts; k = c.top_k; I = c.inter; L = c.n_layers; maxT = c.max_tokens;
+    flags = c.flags; eps = c.rms_eps;
+    nbH = H / QK; nbI = I / QK;
+    rp_bytes = (size_t)2 * nbH * QBYTES;
+    gu_expert_bytes = (size_t)I * rp_bytes;
+    drow_bytes = (size_t)nbI * QBYTES;
+    dn_expert_bytes = (size_t)H * drow_bytes;
+    router_off = 0;
+    gu_off = align_up((size_t)E * H * 4, 256);
+    dn_off = align_up(gu_off + (size_t)E * gu_expert_bytes, 256);
+    layer_bytes = align_up(dn_off + (size_t)E * dn_expert_bytes, 256);
+  }
+};
+
+struct BlobHeader {
+  uint64_t magic;
+  uint32_t version;
+  int32_t hidden, n_experts, top_k, inter, n_layers;
+  uint64_t layer_bytes;
+  uint64_t header_bytes;
+};
+
+// Scratch carve-up for T tokens (offsets 256-aligned).
+struct Scratch {
+  size_t logits, ids, w, h, counts, offsets, pairs, tiles, total;
+  void init(const Layout& d, int T) {
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
+    logits = take((size_t)T * d.E * 4);
+    ids = take((size_t)T * d.k * 4);
+    w = take((size_t)T * d.k * 4);
+    h = take((size_t)T * d.k * d.I * 4);
+    counts = take((size_t)d.E * 4);
+    offsets = take((size_t)(d.E + 1) * 4);
+    pairs = take((size_t)T * d.k * 4);
+    tiles = take(((size_t)T * d.k + (size_t)d.E) * 4 + 64);
+    total = o;
+  }
+};
+
+// ---------------------------------------------------------------- launchers
+// All return hipSuccess or the launch error. Pointers are device pointers.
+hipError_t launch_router(const Layout& d, const float* wr, const uint16_t* x, float* logits, int T,
+                         hipStream_t s);
+hipError_t launch_topk(const Layout& d, const float* logits, int32_t* ids, float* w, int T, hipStream_t s);
+// ids/w given (fused_topk == false), or computed per block from logits (T == 1 only).
+hipError_t launch_gateup(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids,
+                         const float* logits, int32_t* ids_out, float* w_out, float* h, int T,
+                         bool fused_topk, hipStream_t s);
+hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids, const float* w,
+                       const float* h, float* y, int T, hipStream_t s);
+hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y, uint16_t* x_next, int T,
+                             hipStream_t s);
+hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets,
+                           int32_t* pairs, int T, hipStream_t s);
+
+}  // namespace qmoe
