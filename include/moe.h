@@ -136,6 +136,37 @@ int moe_forward(const moe_plan* plan, const void* blob, int32_t layer, const uin
                 int32_t T, float* out, uint16_t* x_next, const moe_route_out* route_out,
                 void* scratch, size_t scratch_bytes, hipStream_t stream);
 
+/* One decode step of the whole stack for T tokens: for l = 0..n_layers-1,
+ * moe_forward(layer l, x = xs[l], out = ys[l], x_next = xs[(l+1) % n_layers]),
+ * so the last layer's normalised output becomes the next step's layer-0
+ * input. xs: bf16 [n_layers][T][hidden]; ys: fp32 [n_layers][T][hidden];
+ * ids/w: int32/fp32 [n_layers][T][k] routing record, both or neither (NULL).
+ * Routing of every layer comes from its router GEMV. */
+int moe_stack_step(const moe_plan* plan, const void* blob, uint16_t* xs, float* ys, int32_t* ids, float* w,
+                   int32_t T, void* scratch, size_t scratch_bytes, hipStream_t stream);
+
+/* A decode step captured once as a hipGraph and replayed per token. Capture
+ * is a set-up call (like plan creation: it may allocate runtime resources)
+ * and needs a non-default `stream`; it records moe_stack_step with exactly
+ * these buffers, which must stay alive and in place for the graph's life.
+ * moe_graph_launch enqueues one step on `stream`. */
+typedef struct moe_graph moe_graph;
+int moe_graph_capture_step(const moe_plan* plan, const void* blob, uint16_t* xs, float* ys, int32_t* ids,
+                           float* w, int32_t T, void* scratch, size_t scratch_bytes, hipStream_t stream,
+                           moe_graph** out);
+int moe_graph_launch(const moe_graph* graph, hipStream_t stream);
+void moe_graph_destroy(moe_graph* graph);
+
+/* Measurement hook (for benchmarks and profilers; not graph-capturable):
+ * enqueues the launches moe_forward makes for the same arguments up to and
+ * including the gate/up GEMV kernel (router GEMV, routing, then
+ * h = SiLU(G x) * (U x) for every routed (token, slot), into scratch), with
+ * the caller's HIP events start/stop recorded around the gate/up kernel's
+ * execution only (hipExtLaunchKernel). start and stop must be valid events. */
+int moe_profile_gate_up(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16,
+                        int32_t T, void* scratch, size_t scratch_bytes, hipEvent_t start, hipEvent_t stop,
+                        hipStream_t stream);
+
 /* Static description of a status code. */
 const char* moe_status_string(int status);
 

@@ -25,7 +25,8 @@ FLAG_FORCE_GROUPED = 0x2
 EXPORTS = [
     "moe_is_supported", "moe_plan_create", "moe_plan_destroy", "moe_blob_bytes", "moe_header_bytes",
     "moe_layer_bytes", "moe_layer_offset", "moe_scratch_bytes", "moe_pack_header", "moe_pack_layer",
-    "moe_unpack_layer", "moe_blob_check", "moe_route", "moe_expert_ffn", "moe_forward", "moe_status_string",
+    "moe_unpack_layer", "moe_blob_check", "moe_route", "moe_expert_ffn", "moe_forward", "moe_stack_step",
+    "moe_graph_capture_step", "moe_graph_launch", "moe_graph_destroy", "moe_profile_gate_up", "moe_status_string",
 ]
 
 
@@ -90,6 +91,16 @@ def load():
     L.moe_expert_ffn.argtypes = [P, vp, i32, vp, i32, ctypes.POINTER(RouteOut), vp, vp, sz, vp]
     L.moe_forward.restype = ctypes.c_int
     L.moe_forward.argtypes = [P, vp, i32, vp, i32, vp, vp, ctypes.POINTER(RouteOut), vp, sz, vp]
+    L.moe_stack_step.restype = ctypes.c_int
+    L.moe_stack_step.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.moe_graph_capture_step.restype = ctypes.c_int
+    L.moe_graph_capture_step.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, sz, vp, ctypes.POINTER(P)]
+    L.moe_graph_launch.restype = ctypes.c_int
+    L.moe_graph_launch.argtypes = [P, vp]
+    L.moe_graph_destroy.restype = None
+    L.moe_graph_destroy.argtypes = [P]
+    L.moe_profile_gate_up.restype = ctypes.c_int
+    L.moe_profile_gate_up.argtypes = [P, vp, i32, vp, i32, vp, sz, vp, vp, vp]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [ctypes.c_int]
     _lib = L
@@ -228,15 +239,35 @@ class Plan:
         _check(load().moe_forward(self._h, _dptr(blob), layer, _dptr(x), T, _dptr(out), _dptr(x_next), ro,
                                   _dptr(scratch), sb, _stream(stream)), "moe_forward")
 
+    def profile_gate_up(self, blob, layer, x, T, start, stop, scratch=None, stream=None):
+        """moe_forward's launches up to the gate/up GEMV kernel, whose
+        execution is bracketed by torch.cuda.Event objects start/stop
+        (created with enable_timing=True)."""
+        sb = scratch.numel() * scratch.element_size() if scratch is not None else 0
+        _check(load().moe_profile_gate_up(self._h, _dptr(blob), layer, _dptr(x), T, _dptr(scratch), sb,
+                                          ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event),
+                                          _stream(stream)), "moe_profile_gate_up")
+
+    def stack_step(self, blob, xs, ys, T=1, ids=None, w=None, scratch=None, stream=None):
+        """One decode step through every layer (see moe_stack_step)."""
+        sb = scratch.numel() * scratch.element_size() if scratch is not None else 0
+        _check(load().moe_stack_step(self._h, _dptr(blob), _dptr(xs), _dptr(ys), _dptr(ids), _dptr(w), T,
+                                     _dptr(scratch), sb, _stream(stream)), "moe_stack_step")
+
+    def capture_step(self, blob, xs, ys, T=1, ids=None, w=None, scratch=None, stream=None):
+        """Capture one decode step as a hipGraph (returns a StepGraph)."""
+        return StepGraph(self, blob, xs, ys, T, ids, w, scratch, stream)
+
     # ---- convenience
     def new_scratch(self, T=None, device="cuda"):
         import torch
         n = self.scratch_bytes(self.max_tokens if T is None else T)
         return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
-    def upload_blob(self, layer_source, device="cuda", blob=None):
+    def upload_blob(self, layer_source, device="cuda", blob=None, progress=None):
         """Pack every layer on the host and copy it into a device blob.
-        ``layer_source(layer)`` returns canonical (gate, up, down, router)."""
+        ``layer_source(layer)`` returns canonical (gate, up, down, router);
+        ``progress(layer)`` is called after each layer when given."""
         import torch
         if blob is None:
             blob = torch.empty(self.blob_bytes(), dtype=torch.uint8, device=device)
@@ -247,4 +278,32 @@ class Plan:
             self.pack_layer(*layer_source(layer), out=host)
             off = self.layer_offset(layer)
             blob[off:off + self.layer_bytes()].copy_(staging, non_blocking=False)
+            if progress is not None:
+                progress(layer)
         return blob
+
+
+class StepGraph:
+    """A captured decode step (moe_graph_capture_step); keeps its buffers alive."""
+
+    def __init__(self, plan, blob, xs, ys, T, ids, w, scratch, stream):
+        import torch
+        if stream is None:
+            raise ValueError("capture needs an explicit non-default stream")
+        self._keep = (plan, blob, xs, ys, ids, w, scratch)
+        sb = scratch.numel() * scratch.element_size() if scratch is not None else 0
+        h = ctypes.c_void_p()
+        torch.cuda.synchronize()
+        _check(load().moe_graph_capture_step(plan.handle, _dptr(blob), _dptr(xs), _dptr(ys), _dptr(ids), _dptr(w), T,
+                                             _dptr(scratch), sb, _stream(stream), ctypes.byref(h)),
+               "moe_graph_capture_step")
+        self._h = h
+
+    def launch(self, stream=None):
+        _check(load().moe_graph_launch(self._h, _stream(stream)), "moe_graph_launch")
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.moe_graph_destroy(h)
+            self._h = None

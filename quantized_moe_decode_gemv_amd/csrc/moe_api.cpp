@@ -276,6 +276,100 @@ extern "C" int moe_forward(const moe_plan* plan, const void* blob, int32_t layer
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- stacked decode step
+extern "C" int moe_stack_step(const moe_plan* plan, const void* blob, uint16_t* xs, float* ys, int32_t* ids, float* w,
+                              int32_t T, void* scratch, size_t scratch_bytes, hipStream_t stream) {
+  Scratch sc;
+  int st = common_checks(plan, blob, 0, T, scratch, scratch_bytes, &sc);
+  if (st) return st;
+  if (!xs || !ys || !aligned(xs, 16) || !aligned(ys, 16) || (!ids) != (!w)) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  const Layout& d = plan->d;
+  const size_t xstride = (size_t)T * d.H, rstride = (size_t)T * d.k;
+  for (int l = 0; l < d.L; ++l) {
+    moe_route_out ro = {ids ? ids + l * rstride : nullptr, w ? w + l * rstride : nullptr, nullptr, nullptr, nullptr};
+    st = moe_forward(plan, blob, l, xs + l * xstride, T, ys + l * xstride, xs + ((l + 1) % d.L) * xstride,
+                     ids ? &ro : nullptr, scratch, scratch_bytes, stream);
+    if (st) return st;
+  }
+  return MOE_OK;
+}
+
+struct moe_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+extern "C" int moe_graph_capture_step(const moe_plan* plan, const void* blob, uint16_t* xs, float* ys, int32_t* ids,
+                                      float* w, int32_t T, void* scratch, size_t scratch_bytes, hipStream_t stream,
+                                      moe_graph** out) {
+  if (!out) return MOE_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (!stream) return MOE_ERR_INVALID_ARGUMENT;  // the legacy default stream cannot be captured
+  Scratch sc;
+  int st = common_checks(plan, blob, 0, T, scratch, scratch_bytes, &sc);
+  if (st) return st;
+  if (T < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal) != hipSuccess) return MOE_ERR_HIP;
+  st = moe_stack_step(plan, blob, xs, ys, ids, w, T, scratch, scratch_bytes, stream);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(stream, &g);
+  if (st || e != hipSuccess || !g) {
+    if (g) hipGraphDestroy(g);
+    return st ? st : MOE_ERR_HIP;
+  }
+  hipGraphExec_t x = nullptr;
+  if (hipGraphInstantiate(&x, g, nullptr, nullptr, 0) != hipSuccess) {
+    hipGraphDestroy(g);
+    return MOE_ERR_HIP;
+  }
+  moe_graph* mg = new (std::nothrow) moe_graph{g, x};
+  if (!mg) {
+    hipGraphExecDestroy(x);
+    hipGraphDestroy(g);
+    return MOE_ERR_INVALID_ARGUMENT;
+  }
+  *out = mg;
+  return MOE_OK;
+}
+
+extern "C" int moe_graph_launch(const moe_graph* g, hipStream_t stream) {
+  if (!g) return MOE_ERR_INVALID_ARGUMENT;
+  return hipGraphLaunch(g->exec, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" void moe_graph_destroy(moe_graph* g) {
+  if (!g) return;
+  hipGraphExecDestroy(g->exec);
+  hipGraphDestroy(g->graph);
+  delete g;
+}
+
+extern "C" int moe_profile_gate_up(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16,
+                                   int32_t T, void* scratch, size_t scratch_bytes, hipEvent_t start, hipEvent_t stop,
+                                   hipStream_t stream) {
+  Scratch sc;
+  int st = common_checks(plan, blob, layer, T, scratch, scratch_bytes, &sc);
+  if (st) return st;
+  if (!x_bf16 || !aligned(x_bf16, 16) || !start || !stop) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  const Layout& d = plan->d;
+  const uint8_t* L = layer_ptr(plan, blob, layer);
+  uint8_t* scr = static_cast<uint8_t*>(scratch);
+  int32_t* ids = reinterpret_cast<int32_t*>(scr + sc.ids);
+  float* w = reinterpret_cast<float*>(scr + sc.w);
+  float* lg = reinterpret_cast<float*>(scr + sc.logits);
+  float* h = reinterpret_cast<float*>(scr + sc.h);
+  // same launches as moe_forward up to and including the gate/up kernel
+  if (launch_router(d, reinterpret_cast<const float*>(L + d.router_off), x_bf16, lg, T, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  const bool fused = (T == 1);
+  if (!fused && launch_topk(d, lg, ids, w, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_gateup(d, L, x_bf16, ids, lg, ids, w, h, T, fused, stream, start, stop) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 extern "C" const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -16,6 +16,7 @@
 // Gate/up use the exact trick bf16(128 + q) = 0x4300 | q, so two codes per
 // v_dot2_f32_bf16 against the bf16 activations, with 128*sum(x) removed after.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "moe_internal.h"
@@ -505,10 +506,18 @@ hipError_t launch_topk(const Layout& d, const float* logits, int32_t* ids, float
 
 template <int IPL, int LPR, int U>
 static void gateup_go(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids, const float* logits,
-                      int32_t* ids_out, float* w_out, float* h, int T, bool fused, hipStream_t s) {
+                      int32_t* ids_out, float* w_out, float* h, int T, bool fused, hipStream_t s, hipEvent_t ev0,
+                      hipEvent_t ev1) {
   constexpr int RPS = WAVE / LPR;
   const long long units = (long long)T * d.k * d.I / (RPS * U);
   const int blocks = (int)((units + 3) / 4);
+  if (ev0 || ev1) {
+    // measurement launch: the events bracket this kernel's execution
+    hipExtLaunchKernelGGL((gateup_kernel<IPL, LPR, U>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s, ev0, ev1, 0,
+                          layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
+                          ids_out, w_out, h, T, fused ? 1 : 0);
+    return;
+  }
   hipLaunchKernelGGL((gateup_kernel<IPL, LPR, U>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s,
                      layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
                      ids_out, w_out, h, T, fused ? 1 : 0);
@@ -516,22 +525,22 @@ static void gateup_go(const Layout& d, const uint8_t* layer, const uint16_t* x, 
 
 hipError_t launch_gateup(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids,
                          const float* logits, int32_t* ids_out, float* w_out, float* h, int T, bool fused_topk,
-                         hipStream_t s) {
+                         hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int nsb = d.H / 32;
   // rows per wave unit must divide I (a multiple of 256): RPS*U <= 256
   if (nsb >= 64) {
     switch (nsb / 64) {
-      case 1: gateup_go<1, 64, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
-      case 2: gateup_go<2, 64, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
-      case 3: gateup_go<3, 64, 1>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
-      case 4: gateup_go<4, 64, 1>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
+      case 1: gateup_go<1, 64, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
+      case 2: gateup_go<2, 64, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
+      case 3: gateup_go<3, 64, 1>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
+      case 4: gateup_go<4, 64, 1>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (nsb) {
-      case 8: gateup_go<1, 8, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
-      case 16: gateup_go<1, 16, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
-      case 32: gateup_go<1, 32, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s); break;
+      case 8: gateup_go<1, 8, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
+      case 16: gateup_go<1, 16, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
+      case 32: gateup_go<1, 32, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
       default: return hipErrorInvalidValue;
     }
   }

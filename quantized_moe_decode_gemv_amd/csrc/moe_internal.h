@@ -85,7 +85,7 @@ hipError_t launch_topk(const Layout& d, const float* logits, int32_t* ids, float
 // ids/w given (fused_topk == false), or computed per block from logits (T == 1 only).
 hipError_t launch_gateup(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids,
                          const float* logits, int32_t* ids_out, float* w_out, float* h, int T,
-                         bool fused_topk, hipStream_t s);
+                         bool fused_topk, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids, const float* w,
                        const float* h, float* y, int T, hipStream_t s);
 hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y, uint16_t* x_next, int T,

@@ -9,9 +9,10 @@
  *
  * Random numbers: Philox4x32-10, the counter-based generator of Salmon,
  * Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
- * (SC 2011), keyed per stream; uniforms are turned into normals with the
- * Box-Muller transform. Element i of a stream uses counter block i/4, so any
- * slice of any stream can be regenerated independently.
+ * (SC 2011), keyed per stream; each 32-bit output becomes a uniform that is
+ * mapped to a normal by the inverse normal CDF. Element i of a stream uses
+ * counter block i/4, so any slice of any stream can be regenerated
+ * independently.
  *
  * Encoding. The pages name the Q4_K super-block but print no bit layout, so
  * this canonical block is our reading of it: 144 bytes per 256 weights, made
@@ -70,20 +71,44 @@ uint64_t synth_key(int64_t a, int64_t b, int64_t c, int64_t d, int64_t e) {
   return h;
 }
 
+/* Standard normal quantile by P. J. Acklam's rational approximation of the
+ * inverse normal CDF (relative error below 1.2e-9): a rational function of
+ * (p - 1/2) in the central region, of sqrt(-2 log p) in the tails. */
+static inline double normal_quantile(double p) {
+  static const double a[6] = {-3.969683028665376e+01, 2.209460984245205e+02, -2.759285104469687e+02,
+                              1.383577518672690e+02, -3.066479806614716e+01, 2.506628277459239e+00};
+  static const double b[5] = {-5.447609879822406e+01, 1.615858368580409e+02, -1.556989798598866e+02,
+                              6.680131188771972e+01, -1.328068155288572e+01};
+  static const double c[6] = {-7.784894002430293e-03, -3.223964580411365e-01, -2.400758277161838e+00,
+                              -2.549732539343734e+00, 4.374664141464968e+00, 2.938163982698783e+00};
+  static const double d[4] = {7.784695709041462e-03, 3.224671290700398e-01, 2.445134137142996e+00,
+                              3.754408661907416e+00};
+  const double plow = 0.02425;
+  if (p < plow) {
+    double q = sqrt(-2.0 * log(p));
+    return (((((c[0] * q + c[1]) * q + c[2]) * q + c[3]) * q + c[4]) * q + c[5]) /
+           ((((d[0] * q + d[1]) * q + d[2]) * q + d[3]) * q + 1.0);
+  }
+  if (p > 1.0 - plow) {
+    double q = sqrt(-2.0 * log(1.0 - p));
+    return -(((((c[0] * q + c[1]) * q + c[2]) * q + c[3]) * q + c[4]) * q + c[5]) /
+           ((((d[0] * q + d[1]) * q + d[2]) * q + d[3]) * q + 1.0);
+  }
+  double q = p - 0.5, r = q * q;
+  return (((((a[0] * r + a[1]) * r + a[2]) * r + a[3]) * r + a[4]) * r + a[5]) * q /
+         (((((b[0] * r + b[1]) * r + b[2]) * r + b[3]) * r + b[4]) * r + 1.0);
+}
+
 /* four standard normals from counter block `blk` of stream `key` */
 static inline void normals4(uint64_t key, uint64_t blk, float z[4]) {
   uint32_t ctr[4] = {(uint32_t)blk, (uint32_t)(blk >> 32), 0x4E4F524Du, 0x414C5321u};
   uint32_t k[2] = {(uint32_t)key, (uint32_t)(key >> 32)};
   uint32_t r[4];
   synth_philox4x32_10(ctr, k, r);
-  for (int p = 0; p < 2; ++p) {
-    /* uniforms strictly inside (0,1): 24-bit grid offset by half a step */
-    float u1 = ((float)(r[2 * p] >> 8) + 0.5f) * (1.0f / 16777216.0f);
-    float u2 = ((float)(r[2 * p + 1] >> 8) + 0.5f) * (1.0f / 16777216.0f);
-    float rad = sqrtf(-2.0f * logf(u1));
-    float th = 6.28318530717958647692f * u2;
-    z[2 * p] = rad * cosf(th);
-    z[2 * p + 1] = rad * sinf(th);
+  for (int j = 0; j < 4; ++j) {
+    /* uniform strictly inside (0,1) on a 2^-32 grid offset by half a step */
+    double u = ((double)r[j] + 0.5) * (1.0 / 4294967296.0);
+    z[j] = (float)normal_quantile(u);
   }
 }
 

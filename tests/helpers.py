@@ -53,3 +53,23 @@ def check_routing(ids_gpu, w_gpu, ref, exact=False, tau=TAU):
         for i, e in enumerate(gs):
             assert abs(w_gpu[t, i] - wr[e]) <= W_TOL, f"token {t}: weight of expert {e}: {w_gpu[t, i]} vs {wr[e]}"
     return exempt
+
+
+def bf16_step(bits):
+    """Spacing of the bf16 grid at each value (the ulp of a bf16)."""
+    v = np.abs((np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def check_bf16_vector(got_bits, ref_bits, tol=REL_TOL):
+    """A bf16 vector derived from fp32 outputs (the normalised next-layer
+    input): each element must be within one bf16 step of the oracle's value or
+    within tol * max|ref| (the output tolerance, which covers elements where
+    x + y nearly cancels). Returns the number of elements that differ."""
+    g = (np.asarray(got_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    r = (np.asarray(ref_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bound = np.maximum(bf16_step(ref_bits), tol * np.abs(r).max())
+    bad = np.nonzero(np.abs(g - r) > bound)[0]
+    assert bad.size == 0, f"elements {bad[:8]}: {g[bad[:8]]} vs {r[bad[:8]]}"
+    return int(np.count_nonzero(g != r))

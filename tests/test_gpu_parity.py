@@ -9,7 +9,7 @@ import torch
 import oracle
 import synth
 import quantized_moe_decode_gemv_amd as q
-from helpers import REL_TOL, check_routing, layer_source, rel_err
+from helpers import REL_TOL, check_bf16_vector, check_routing, layer_source, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -161,8 +161,9 @@ def test_route_from_logits_and_dispatch_lists(qwen, T, zipf):
 def test_resid_rmsnorm_epilogue(tiny):
     """x_next = bf16(RMSNorm(x + y)) against the oracle's own y and norm: the
     GPU's y differs from the oracle's by ~1e-6 relative, so an element may
-    land on the other side of a bf16 rounding boundary; then it must be the
-    adjacent bf16 value, and such flips must be rare."""
+    land on the other side of a bf16 rounding boundary (then it must be the
+    adjacent bf16 value, or within the output tolerance where x + y nearly
+    cancels), and such differences must be rare."""
     S = tiny.shape
     flips = 0
     for step in range(8):
@@ -170,10 +171,7 @@ def test_resid_rmsnorm_epilogue(tiny):
         got = tiny.forward(xb, with_next=True)
         ref = oracle.moe_layer(tiny.src, 0, xb)
         _, ref_bits = oracle.resid_rmsnorm(xb[0], ref["y"][0], eps=1e-6)
-        diff = np.nonzero(got["xn"][0] != ref_bits)[0]
-        for i in diff:
-            assert abs(int(got["xn"][0][i]) - int(ref_bits[i])) == 1, i
-        flips += diff.size
+        flips += check_bf16_vector(got["xn"][0], ref_bits)
     assert flips <= 8 * S.hidden // 100
 
 
