@@ -248,6 +248,33 @@ extern "C" int moe_expert_ffn(const moe_plan* plan, const void* blob, int32_t la
   return MOE_OK;
 }
 
+// Router + expert FFN for one layer. With y_prev the layer input is formed
+// inside the router kernel as bf16(RMSNorm(x_in + y_prev)) and stored to
+// x_formed; otherwise x_in is the layer input.
+static int forward_impl(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_in,
+                        const float* y_prev, uint16_t* x_formed, int32_t T, float* out, uint16_t* x_next,
+                        int32_t* ids, float* w, uint8_t* scr, const Scratch& sc, hipStream_t stream) {
+  const Layout& d = plan->d;
+  const uint8_t* L = layer_ptr(plan, blob, layer);
+  float* lg = reinterpret_cast<float*>(scr + sc.logits);
+  float* h = reinterpret_cast<float*>(scr + sc.h);
+  const float* wr = reinterpret_cast<const float*>(L + d.router_off);
+  const uint16_t* x = x_in;
+  if (y_prev) {
+    if (launch_router_norm(d, wr, x_in, y_prev, x_formed, lg, T, stream) != hipSuccess) return MOE_ERR_HIP;
+    x = x_formed;
+  } else if (launch_router(d, wr, x_in, lg, T, stream) != hipSuccess) {
+    return MOE_ERR_HIP;
+  }
+  if (use_grouped(plan, T)) return MOE_ERR_UNSUPPORTED;
+  const bool fused = (T == 1);
+  if (!fused && launch_topk(d, lg, ids, w, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_gateup(d, L, x, ids, lg, ids, w, h, T, fused, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_down(d, L, ids, w, h, out, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (x_next && launch_resid_norm(d, x, out, x_next, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 extern "C" int moe_forward(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16, int32_t T,
                            float* out, uint16_t* x_next, const moe_route_out* route_out, void* scratch,
                            size_t scratch_bytes, hipStream_t stream) {
@@ -258,22 +285,10 @@ extern "C" int moe_forward(const moe_plan* plan, const void* blob, int32_t layer
   if (x_next && !aligned(x_next, 16)) return MOE_ERR_INVALID_ARGUMENT;
   if (route_out && (!route_out->topk_ids || !route_out->topk_w)) return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
-  const Layout& d = plan->d;
-  const uint8_t* L = layer_ptr(plan, blob, layer);
   uint8_t* scr = static_cast<uint8_t*>(scratch);
   int32_t* ids = route_out ? route_out->topk_ids : reinterpret_cast<int32_t*>(scr + sc.ids);
   float* w = route_out ? route_out->topk_w : reinterpret_cast<float*>(scr + sc.w);
-  float* lg = reinterpret_cast<float*>(scr + sc.logits);
-  float* h = reinterpret_cast<float*>(scr + sc.h);
-  if (launch_router(d, reinterpret_cast<const float*>(L + d.router_off), x_bf16, lg, T, stream) != hipSuccess)
-    return MOE_ERR_HIP;
-  if (use_grouped(plan, T)) return MOE_ERR_UNSUPPORTED;
-  const bool fused = (T == 1);
-  if (!fused && launch_topk(d, lg, ids, w, T, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_gateup(d, L, x_bf16, ids, lg, ids, w, h, T, fused, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_down(d, L, ids, w, h, out, T, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (x_next && launch_resid_norm(d, x_bf16, out, x_next, T, stream) != hipSuccess) return MOE_ERR_HIP;
-  return MOE_OK;
+  return forward_impl(plan, blob, layer, x_bf16, nullptr, nullptr, T, out, x_next, ids, w, scr, sc, stream);
 }
 
 // ---------------------------------------------------------------- stacked decode step
@@ -285,11 +300,22 @@ extern "C" int moe_stack_step(const moe_plan* plan, const void* blob, uint16_t* 
   if (!xs || !ys || !aligned(xs, 16) || !aligned(ys, 16) || (!ids) != (!w)) return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
   const Layout& d = plan->d;
+  uint8_t* scr = static_cast<uint8_t*>(scratch);
   const size_t xstride = (size_t)T * d.H, rstride = (size_t)T * d.k;
+  // The epilogue of layer l (x_{l+1} = bf16(RMSNorm(x_l + y_l))) runs inside
+  // layer l+1's router kernel when that kernel supports it; the last layer's
+  // epilogue, which feeds the next step, runs as its own kernel.
+  const bool fold = router_has_norm_prologue(d);
   for (int l = 0; l < d.L; ++l) {
-    moe_route_out ro = {ids ? ids + l * rstride : nullptr, w ? w + l * rstride : nullptr, nullptr, nullptr, nullptr};
-    st = moe_forward(plan, blob, l, xs + l * xstride, T, ys + l * xstride, xs + ((l + 1) % d.L) * xstride,
-                     ids ? &ro : nullptr, scratch, scratch_bytes, stream);
+    int32_t* li = ids ? ids + l * rstride : reinterpret_cast<int32_t*>(scr + sc.ids);
+    float* lw = w ? w + l * rstride : reinterpret_cast<float*>(scr + sc.w);
+    uint16_t* xl = xs + l * xstride;
+    float* yl = ys + l * xstride;
+    const bool folded_in = fold && l > 0;
+    const bool last = (l == d.L - 1);
+    uint16_t* x_next = (!fold || last) ? xs + ((l + 1) % d.L) * xstride : nullptr;
+    st = forward_impl(plan, blob, l, folded_in ? xl - xstride : xl, folded_in ? yl - xstride : nullptr, xl, T, yl,
+                      x_next, li, lw, scr, sc, stream);
     if (st) return st;
   }
   return MOE_OK;

@@ -140,65 +140,124 @@ __device__ __forceinline__ float dot_codes_f32(const u32x4& c, const float* hv) 
 }
 
 // ------------------------------------------------------------------ top-k
-// One wave selects the k largest of E <= 256 logits (descending; equal values
-// -> lower id) and their softmax restricted to the selection. Result in
-// sid/sw (k entries, any memory the wave can write).
-__device__ void wave_topk(const float* __restrict__ lg, int E, int k, int32_t* sid, float* sw) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  float v[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + WAVE * q;
-    v[q] = e < E ? lg[e] : -INFINITY;
-  }
-  bool taken[4] = {false, false, false, false};
-  float top0 = 0.f, den = 0.f;
-  for (int s = 0; s < k; ++s) {
-    // lane-local best (value desc, id asc)
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + WAVE * q;
-      if (e < E && !taken[q] && (v[q] > bv || (v[q] == bv && e < bi))) { bv = v[q]; bi = e; }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, WAVE);
-      const int oi = __shfl_xor(bi, off, WAVE);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (lane + WAVE * q == bi) taken[q] = true;
-    if (s == 0) top0 = bv;
-    const float ex = expf(bv - top0);
-    den += ex;
-    if (lane == 0) { sid[s] = bi; sw[s] = ex; }
-  }
-  // all lanes hold the same den; lane 0 wrote the numerators
-  __builtin_amdgcn_wave_barrier();
-  if (lane == 0) {
-    const float inv = 1.0f / den;
-    for (int s = 0; s < k; ++s) sw[s] *= inv;
-  }
-  __builtin_amdgcn_wave_barrier();
+// Order-preserving map fp32 -> u32 (a > b  <=>  key(a) > key(b) for non-NaN).
+__device__ __forceinline__ u32 order_key(float f) {
+  const u32 b = __builtin_bit_cast(u32, f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// LDS workspace of block_topk.
+struct TopkSmem {
+  unsigned long long key[BLOCK];   // unique keys: (order_key(logit) << 32) | ~id, 0 past E
+  unsigned long long gmax[32];     // maxima of groups of 8 consecutive ids
+  unsigned long long ckey[64];     // candidates
+  unsigned long long thr;
+  int wcnt[BLOCK / WAVE];
+  float val[16];                   // selected logits, descending
+  int32_t sid[16];
+  float sw[16];
+};
+
+// Block-wide top-k of E <= 256 logits (descending; equal values -> lower id)
+// and the softmax restricted to the selection, into sm.sid / sm.sw (k <= 16).
+// Every logit gets a unique 64-bit key, larger for a larger logit and, among
+// equal logits, for the lower id, so its rank is the number of larger keys.
+// To keep the comparisons few, the k-th largest of the maxima of groups of 8
+// consecutive ids is taken as a threshold: at least k keys reach it, so the
+// whole top-k does, and at most 8k keys (those of the k leading groups) can;
+// only those candidates are ranked, against each other. Every thread of the
+// block must call it.
+__device__ void block_topk(const float* __restrict__ lg, int E, int k, TopkSmem& sm) {
+  const int t = threadIdx.x;
+  const int lane = t & (WAVE - 1), wid = t / WAVE;
+  float v = 0.f;
+  if (t < E) v = lg[t];
+  const unsigned long long key = t < E ? (((unsigned long long)order_key(v) << 32) | (u32)~(u32)t) : 0ull;
+  sm.key[t] = key;
+  if (t == 0) sm.thr = 0ull;
+  __syncthreads();
+  const int ng = (E + 7) / 8;
+  if (t < ng) {
+    unsigned long long m = 0ull;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = sm.key[8 * t + j] > m ? sm.key[8 * t + j] : m;
+    sm.gmax[t] = m;
+  }
+  __syncthreads();
+  if (ng >= k && t < ng) {
+    const unsigned long long g = sm.gmax[t];
+    int r = 0;
+    for (int j = 0; j < ng; ++j) r += sm.gmax[j] > g ? 1 : 0;
+    if (r == k - 1) sm.thr = g;
+  }
+  __syncthreads();
+  const bool cand = t < E && key >= sm.thr;
+  const unsigned long long m = __ballot(cand);
+  const unsigned long long below = lane ? (~0ull >> (WAVE - lane)) : 0ull;
+  if (lane == 0) sm.wcnt[wid] = __popcll(m);
+  __syncthreads();
+  int base = 0, nc = 0;
+#pragma unroll
+  for (int w = 0; w < BLOCK / WAVE; ++w) {
+    base += w < wid ? sm.wcnt[w] : 0;
+    nc += sm.wcnt[w];
+  }
+  if (cand) sm.ckey[base + __popcll(m & below)] = key;
+  __syncthreads();
+  if (cand) {
+    int rank = 0;
+    for (int j = 0; j < nc; ++j) rank += sm.ckey[j] > key ? 1 : 0;
+    if (rank < k) { sm.sid[rank] = t; sm.val[rank] = v; }
+  }
+  __syncthreads();
+  // softmax over the selection: lane s < k forms every term itself (same
+  // order in every lane, so all lanes agree on the denominator)
+  if (t < k) {
+    const float l0 = sm.val[0];
+    float den = 0.f;
+    for (int j = 0; j < k; ++j) den += __expf(sm.val[j] - l0);
+    sm.sw[t] = __expf(sm.val[t] - l0) / den;
+  }
+  __syncthreads();
+}
+
+// One block per token.
 __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ logits, int32_t* __restrict__ ids,
                                                      float* __restrict__ w, int E, int k, int T) {
-  const int t = blockIdx.x * (BLOCK / WAVE) + (threadIdx.x / WAVE);
-  if (t >= T) return;
-  wave_topk(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+  __shared__ TopkSmem sm;
+  const int t = blockIdx.x;
+  block_topk(logits + (size_t)t * E, E, k, sm);
+  if (threadIdx.x < k) {
+    ids[(size_t)t * k + threadIdx.x] = sm.sid[threadIdx.x];
+    w[(size_t)t * k + threadIdx.x] = sm.sw[threadIdx.x];
+  }
+}
+
+// ------------------------------------------------------------------ residual + RMSNorm
+// Element order shared by the standalone norm kernel and the router prologue
+// (so both produce the same bits): thread tid owns the 4-element chunks
+// starting at 4*(tid + 256c); the sum of squares is accumulated chunk by
+// chunk, then reduced over the wave (butterfly) and over the 4 waves.
+__device__ __forceinline__ float block_sum4(float v, float* part) {
+  v = group_sum<WAVE>(v);
+  if ((threadIdx.x & (WAVE - 1)) == 0) part[threadIdx.x / WAVE] = v;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  __syncthreads();
+  return tot;
 }
 
 // ------------------------------------------------------------------ router GEMV
 // One block per expert row; the 256 threads split the hidden dimension
 // (4 consecutive fp32 weights each per chunk). Tokens loop inside with the
 // weight slice held in registers. Block reduction in a fixed order.
+// With y_prev != nullptr the block first forms its input as
+// x = bf16(RMSNorm(x_in + y_prev)) (the stacked-layer epilogue of the
+// previous layer, recomputed by every block) and block 0 stores it to x_out.
 template <int CH>  // chunks of 4 weights per thread: H = CH * 1024
 __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__ wr, const uint16_t* __restrict__ x,
-                                                       float* __restrict__ logits, int E, int H, int T) {
+                                                       const float* __restrict__ y_prev, uint16_t* __restrict__ x_out,
+                                                       float eps, float* __restrict__ logits, int E, int H, int T) {
   __shared__ float part[BLOCK / WAVE];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
@@ -206,24 +265,46 @@ __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + (size_t)e * H + 4 * (tid + BLOCK * c)));
-    w[c][0] = as_f32(v.x); w[c][1] = as_f32(v.y);
-    w[c][2] = as_f32(v.z); w[c][3] = as_f32(v.w);
+    w[c][0] = as_f32(v.x); w[c][1] = as_f32(v.y); w[c][2] = as_f32(v.z); w[c][3] = as_f32(v.w);
   }
   for (int t = 0; t < T; ++t) {
-    float acc = 0.f;
+    float xv[CH][4];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * H + 4 * (tid + BLOCK * c));
-      acc = fmaf(w[c][0], bf16_bits_to_float(xv.x & 0xFFFFu), acc);
-      acc = fmaf(w[c][1], bf16_bits_to_float(xv.x >> 16), acc);
-      acc = fmaf(w[c][2], bf16_bits_to_float(xv.y & 0xFFFFu), acc);
-      acc = fmaf(w[c][3], bf16_bits_to_float(xv.y >> 16), acc);
+      const uint2 q = *reinterpret_cast<const uint2*>(x + (size_t)t * H + 4 * (tid + BLOCK * c));
+      xv[c][0] = bf16_bits_to_float(q.x & 0xFFFFu); xv[c][1] = bf16_bits_to_float(q.x >> 16);
+      xv[c][2] = bf16_bits_to_float(q.y & 0xFFFFu); xv[c][3] = bf16_bits_to_float(q.y >> 16);
     }
-    acc = group_sum<WAVE>(acc);
-    if ((tid & (WAVE - 1)) == 0) part[tid / WAVE] = acc;
-    __syncthreads();
-    if (tid == 0) logits[(size_t)t * E + e] = (part[0] + part[1]) + (part[2] + part[3]);
-    __syncthreads();
+    if (y_prev) {
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const u32x4 q = load16(y_prev + (size_t)t * H + 4 * (tid + BLOCK * c));
+        xv[c][0] += as_f32(q.x); xv[c][1] += as_f32(q.y); xv[c][2] += as_f32(q.z); xv[c][3] += as_f32(q.w);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss = fmaf(xv[c][i], xv[c][i], ss);
+      }
+      const float inv = 1.0f / sqrtf(block_sum4(ss, part) / (float)H + eps);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        uint16_t b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          b[i] = float_to_bf16_rne(xv[c][i] * inv);
+          xv[c][i] = bf16_bits_to_float(b[i]);
+        }
+        if (e == 0)
+          *reinterpret_cast<uint2*>(x_out + (size_t)t * H + 4 * (tid + BLOCK * c)) =
+              make_uint2((u32)b[0] | ((u32)b[1] << 16), (u32)b[2] | ((u32)b[3] << 16));
+      }
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf(w[c][i], xv[c][i], acc);
+    const float tot = block_sum4(acc, part);
+    if (tid == 0) logits[(size_t)t * E + e] = tot;
   }
 }
 
@@ -237,15 +318,16 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids_in, const float* __restrict__ logits,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ h, int T, int fused_topk) {
   constexpr int RPS = WAVE / LPR;
-  __shared__ int32_t s_ids[16];
-  __shared__ float s_w[16];
+  __shared__ TopkSmem s_topk;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x / WAVE;
   if (fused_topk) {
     // T == 1: every block derives the same routing from the logits.
-    if (wid == 0) wave_topk(logits, E, k, s_ids, s_w);
-    __syncthreads();
-    if (blockIdx.x == 0 && threadIdx.x < k) { ids_out[threadIdx.x] = s_ids[threadIdx.x]; w_out[threadIdx.x] = s_w[threadIdx.x]; }
+    block_topk(logits, E, k, s_topk);
+    if (blockIdx.x == 0 && threadIdx.x < k) {
+      ids_out[threadIdx.x] = s_topk.sid[threadIdx.x];
+      w_out[threadIdx.x] = s_topk.sw[threadIdx.x];
+    }
   }
   const int unit = blockIdx.x * (BLOCK / WAVE) + wid;
   const int rows_per_unit = RPS * U;
@@ -255,7 +337,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
   const int ts = flat0 / I;                 // t*k + s
   const int r0 = flat0 % I;
   const int t = ts / k;
-  const int e = fused_topk ? s_ids[ts] : ids_in[ts];
+  const int e = fused_topk ? s_topk.sid[ts] : ids_in[ts];
   const int rho = lane / LPR, lam = lane % LPR;
 
   u32 X[IPL][16];
@@ -386,26 +468,35 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
   }
 }
 
-// ------------------------------------------------------------------ residual + RMSNorm
-// One block per token: v = x + y (fp32), x_next = bf16(v / sqrt(mean(v^2) + eps)).
+// ------------------------------------------------------------------ standalone residual + RMSNorm
+// One block per token: v = x + y (fp32), x_next = bf16(v / sqrt(mean(v^2) + eps)),
+// in the element order of the router prologue (H a multiple of 4).
 __global__ __launch_bounds__(BLOCK) void resid_norm_kernel(const uint16_t* __restrict__ x, const float* __restrict__ y,
                                                            uint16_t* __restrict__ xn, int H, float eps) {
   __shared__ float part[BLOCK / WAVE];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   float ss = 0.f;
-  for (int i = tid; i < H; i += BLOCK) {
-    const float v = bf16_bits_to_float(x[(size_t)t * H + i]) + y[(size_t)t * H + i];
-    ss = fmaf(v, v, ss);
+  for (int c = 0; 4 * (tid + BLOCK * c) < H; ++c) {
+    const int i0 = 4 * (tid + BLOCK * c);
+    const uint2 q = *reinterpret_cast<const uint2*>(x + (size_t)t * H + i0);
+    const u32x4 yv = load16(y + (size_t)t * H + i0);
+    const float v0 = bf16_bits_to_float(q.x & 0xFFFFu) + as_f32(yv.x);
+    const float v1 = bf16_bits_to_float(q.x >> 16) + as_f32(yv.y);
+    const float v2 = bf16_bits_to_float(q.y & 0xFFFFu) + as_f32(yv.z);
+    const float v3 = bf16_bits_to_float(q.y >> 16) + as_f32(yv.w);
+    ss = fmaf(v0, v0, ss); ss = fmaf(v1, v1, ss); ss = fmaf(v2, v2, ss); ss = fmaf(v3, v3, ss);
   }
-  ss = group_sum<WAVE>(ss);
-  if ((tid & (WAVE - 1)) == 0) part[tid / WAVE] = ss;
-  __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int i = tid; i < H; i += BLOCK) {
-    const float v = bf16_bits_to_float(x[(size_t)t * H + i]) + y[(size_t)t * H + i];
-    xn[(size_t)t * H + i] = float_to_bf16_rne(v * inv);
+  const float inv = 1.0f / sqrtf(block_sum4(ss, part) / (float)H + eps);
+  for (int c = 0; 4 * (tid + BLOCK * c) < H; ++c) {
+    const int i0 = 4 * (tid + BLOCK * c);
+    const uint2 q = *reinterpret_cast<const uint2*>(x + (size_t)t * H + i0);
+    const u32x4 yv = load16(y + (size_t)t * H + i0);
+    const u32 b0 = float_to_bf16_rne((bf16_bits_to_float(q.x & 0xFFFFu) + as_f32(yv.x)) * inv);
+    const u32 b1 = float_to_bf16_rne((bf16_bits_to_float(q.x >> 16) + as_f32(yv.y)) * inv);
+    const u32 b2 = float_to_bf16_rne((bf16_bits_to_float(q.y & 0xFFFFu) + as_f32(yv.z)) * inv);
+    const u32 b3 = float_to_bf16_rne((bf16_bits_to_float(q.y >> 16) + as_f32(yv.w)) * inv);
+    *reinterpret_cast<uint2*>(xn + (size_t)t * H + i0) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
   }
 }
 
@@ -464,18 +555,32 @@ __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* _
 // ------------------------------------------------------------------ launchers
 static int pow2ceil(int v) { int p = 1; while (p < v) p <<= 1; return p; }
 
-static hipError_t launch_router_big(const Layout& d, const float* wr, const uint16_t* x, float* logits, int T, hipStream_t s) {
+static hipError_t launch_router_big(const Layout& d, const float* wr, const uint16_t* x, const float* y_prev,
+                                    uint16_t* x_out, float* logits, int T, hipStream_t s) {
   const int CH = d.H / 1024;
   dim3 grid(d.E), block(BLOCK);
+#define QMOE_ROUTER(C) hipLaunchKernelGGL(router_kernel<C>, grid, block, 0, s, wr, x, y_prev, x_out, d.eps, logits, d.E, d.H, T)
   switch (CH) {
-    case 1: hipLaunchKernelGGL(router_kernel<1>, grid, block, 0, s, wr, x, logits, d.E, d.H, T); break;
-    case 2: hipLaunchKernelGGL(router_kernel<2>, grid, block, 0, s, wr, x, logits, d.E, d.H, T); break;
-    case 4: hipLaunchKernelGGL(router_kernel<4>, grid, block, 0, s, wr, x, logits, d.E, d.H, T); break;
-    case 6: hipLaunchKernelGGL(router_kernel<6>, grid, block, 0, s, wr, x, logits, d.E, d.H, T); break;
-    case 8: hipLaunchKernelGGL(router_kernel<8>, grid, block, 0, s, wr, x, logits, d.E, d.H, T); break;
+    case 1: QMOE_ROUTER(1); break;
+    case 2: QMOE_ROUTER(2); break;
+    case 4: QMOE_ROUTER(4); break;
+    case 6: QMOE_ROUTER(6); break;
+    case 8: QMOE_ROUTER(8); break;
     default: return hipErrorInvalidValue;
   }
+#undef QMOE_ROUTER
   return hipGetLastError();
+}
+
+bool router_has_norm_prologue(const Layout& d) {
+  const int CH = d.H / 1024;
+  return d.H % 1024 == 0 && (CH == 1 || CH == 2 || CH == 4 || CH == 6 || CH == 8);
+}
+
+hipError_t launch_router_norm(const Layout& d, const float* wr, const uint16_t* x_prev, const float* y_prev,
+                              uint16_t* x_out, float* logits, int T, hipStream_t s) {
+  if (!router_has_norm_prologue(d)) return hipErrorInvalidValue;
+  return launch_router_big(d, wr, x_prev, y_prev, x_out, logits, T, s);
 }
 
 // Router for hidden sizes that are not a multiple of 1024: wave per row.
@@ -493,14 +598,13 @@ __global__ __launch_bounds__(BLOCK) void router_small_kernel(const float* __rest
 }
 
 hipError_t launch_router(const Layout& d, const float* wr, const uint16_t* x, float* logits, int T, hipStream_t s) {
-  if (d.H % 1024 == 0 && d.H <= 8192 && (d.H / 1024 <= 2 || d.H / 1024 == 4 || d.H / 1024 == 6 || d.H / 1024 == 8))
-    return launch_router_big(d, wr, x, logits, T, s);
+  if (router_has_norm_prologue(d)) return launch_router_big(d, wr, x, nullptr, nullptr, logits, T, s);
   hipLaunchKernelGGL(router_small_kernel, dim3((d.E + 3) / 4), dim3(BLOCK), 0, s, wr, x, logits, d.E, d.H, T);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const Layout& d, const float* logits, int32_t* ids, float* w, int T, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(BLOCK), 0, s, logits, ids, w, d.E, d.k, T);
+  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(BLOCK), 0, s, logits, ids, w, d.E, d.k, T);
   return hipGetLastError();
 }
 

@@ -81,6 +81,11 @@ struct Scratch {
 // All return hipSuccess or the launch error. Pointers are device pointers.
 hipError_t launch_router(const Layout& d, const float* wr, const uint16_t* x, float* logits, int T,
                          hipStream_t s);
+// Router whose input is formed as bf16(RMSNorm(x_prev + y_prev)) inside the
+// kernel (stored to x_out by block 0); available when router_has_norm_prologue.
+bool router_has_norm_prologue(const Layout& d);
+hipError_t launch_router_norm(const Layout& d, const float* wr, const uint16_t* x_prev, const float* y_prev,
+                              uint16_t* x_out, float* logits, int T, hipStream_t s);
 hipError_t launch_topk(const Layout& d, const float* logits, int32_t* ids, float* w, int T, hipStream_t s);
 // ids/w given (fused_topk == false), or computed per block from logits (T == 1 only).
 hipError_t launch_gateup(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids,
