@@ -189,10 +189,25 @@ static const uint8_t* layer_ptr(const moe_plan* plan, const void* blob, int32_t 
   return static_cast<const uint8_t*>(blob) + HEADER_BYTES + (size_t)layer * plan->d.layer_bytes;
 }
 
+// Path choice by the host-known token count: the per-token GEMV streams every
+// routed expert once per token, the grouped MFMA path once per batch.
+constexpr int32_t GROUPED_MIN_TOKENS = 8;
 static bool use_grouped(const moe_plan* plan, int32_t T) {
-  (void)T;
-  (void)plan;
-  return false;  // grouped MFMA path not enabled in this build
+  if (T < 2 || (plan->d.flags & MOE_FLAG_FORCE_GEMV)) return false;
+  if (plan->d.flags & MOE_FLAG_FORCE_GROUPED) return true;
+  return T >= GROUPED_MIN_TOKENS;
+}
+
+static int grouped_impl(const moe_plan* plan, const uint8_t* L, const uint16_t* x, int32_t T, const float* w,
+                        const int32_t* offsets, const int32_t* pairs, float* out, uint8_t* scr, const Scratch& sc,
+                        hipStream_t stream) {
+  const Layout& d = plan->d;
+  int32_t* tile_off = reinterpret_cast<int32_t*>(scr + sc.tile_off);
+  if (launch_tile_offsets(d, offsets, tile_off, GROUPED_MT, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_grouped_ffn(d, L, x, w, offsets, pairs, tile_off, reinterpret_cast<_Float16*>(scr + sc.h16),
+                         reinterpret_cast<float*>(scr + sc.ypair), out, T, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 static int route_impl(const moe_plan* plan, const uint8_t* L, const uint16_t* x, const float* logits, int32_t T,
@@ -241,7 +256,10 @@ extern "C" int moe_expert_ffn(const moe_plan* plan, const void* blob, int32_t la
   const uint8_t* L = layer_ptr(plan, blob, layer);
   uint8_t* scr = static_cast<uint8_t*>(scratch);
   float* h = reinterpret_cast<float*>(scr + sc.h);
-  if (use_grouped(plan, T)) return MOE_ERR_UNSUPPORTED;
+  if (use_grouped(plan, T)) {
+    if (!r->offsets || !r->pairs) return MOE_ERR_INVALID_ARGUMENT;
+    return grouped_impl(plan, L, x_bf16, T, r->topk_w, r->offsets, r->pairs, out, scr, sc, stream);
+  }
   if (launch_gateup(d, L, x_bf16, r->topk_ids, nullptr, nullptr, nullptr, h, T, false, stream) != hipSuccess)
     return MOE_ERR_HIP;
   if (launch_down(d, L, r->topk_ids, r->topk_w, h, out, T, stream) != hipSuccess) return MOE_ERR_HIP;
@@ -266,11 +284,19 @@ static int forward_impl(const moe_plan* plan, const void* blob, int32_t layer, c
   } else if (launch_router(d, wr, x_in, lg, T, stream) != hipSuccess) {
     return MOE_ERR_HIP;
   }
-  if (use_grouped(plan, T)) return MOE_ERR_UNSUPPORTED;
   const bool fused = (T == 1);
   if (!fused && launch_topk(d, lg, ids, w, T, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_gateup(d, L, x, ids, lg, ids, w, h, T, fused, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_down(d, L, ids, w, h, out, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (use_grouped(plan, T)) {
+    int32_t* counts = reinterpret_cast<int32_t*>(scr + sc.counts);
+    int32_t* offsets = reinterpret_cast<int32_t*>(scr + sc.offsets);
+    int32_t* pairs = reinterpret_cast<int32_t*>(scr + sc.pairs);
+    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream) != hipSuccess) return MOE_ERR_HIP;
+    const int st = grouped_impl(plan, L, x, T, w, offsets, pairs, out, scr, sc, stream);
+    if (st) return st;
+  } else {
+    if (launch_gateup(d, L, x, ids, lg, ids, w, h, T, fused, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_down(d, L, ids, w, h, out, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  }
   if (x_next && launch_resid_norm(d, x, out, x_next, T, stream) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }

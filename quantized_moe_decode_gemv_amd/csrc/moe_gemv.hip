@@ -697,4 +697,20 @@ hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts,
   return hipGetLastError();
 }
 
+// tile_off[e] = number of `mt`-pair tiles of experts before e (E + 1 entries).
+__global__ void tile_offsets_kernel(const int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int E, int mt) {
+  if (threadIdx.x != 0) return;
+  int run = 0;
+  for (int e = 0; e < E; ++e) {
+    tile_off[e] = run;
+    run += (offsets[e + 1] - offsets[e] + mt - 1) / mt;
+  }
+  tile_off[E] = run;
+}
+
+hipError_t launch_tile_offsets(const Layout& d, const int32_t* offsets, int32_t* tile_off, int mt, hipStream_t s) {
+  hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(WAVE), 0, s, offsets, tile_off, d.E, mt);
+  return hipGetLastError();
+}
+
 }  // namespace qmoe

@@ -61,7 +61,7 @@ struct BlobHeader {
 
 // Scratch carve-up for T tokens (offsets 256-aligned).
 struct Scratch {
-  size_t logits, ids, w, h, counts, offsets, pairs, tiles, total;
+  size_t logits, ids, w, h, counts, offsets, pairs, tile_off, h16, ypair, total;
   void init(const Layout& d, int T) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
@@ -72,7 +72,10 @@ struct Scratch {
     counts = take((size_t)d.E * 4);
     offsets = take((size_t)(d.E + 1) * 4);
     pairs = take((size_t)T * d.k * 4);
-    tiles = take(((size_t)T * d.k + (size_t)d.E) * 4 + 64);
+    tile_off = take((size_t)(d.E + 1) * 4);
+    // grouped path only (T > 1): fp16 h in expert-sorted pair order, one fp32 output row per pair
+    h16 = take(T > 1 ? (size_t)T * d.k * d.I * 2 : 0);
+    ypair = take(T > 1 ? (size_t)T * d.k * d.H * 4 : 0);
     total = o;
   }
 };
@@ -97,5 +100,13 @@ hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y,
                              hipStream_t s);
 hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets,
                            int32_t* pairs, int T, hipStream_t s);
+hipError_t launch_tile_offsets(const Layout& d, const int32_t* offsets, int32_t* tile_off, int mt, hipStream_t s);
+
+// grouped MFMA path (T > 1)
+constexpr int GROUPED_MT = 64;
+int grouped_max_tiles(const Layout& d, int T);
+hipError_t launch_grouped_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
+                              const int32_t* offsets, const int32_t* pairs, const int32_t* tile_off, _Float16* h16,
+                              float* ypair, float* out, int T, hipStream_t s);
 
 }  // namespace qmoe

@@ -98,7 +98,7 @@ def test_qwen_forward_single_tokens(qwen):
 
 def test_qwen_expert_ffn_with_oracle_routing(qwen):
     S = qwen.shape
-    for T in (1, 8):
+    for T in (1, 4):
         xb = synth.x_bf16(S, 2, T, T=T)
         ref = oracle.moe_layer(qwen.src, 0, xb)
         ids = torch.from_numpy(ref["ids"]).to(qwen.dev)
@@ -109,24 +109,88 @@ def test_qwen_expert_ffn_with_oracle_routing(qwen):
         assert rel_err(out.cpu().numpy(), ref["y"]) <= REL_TOL
 
 
+def _route_lists(plan, blob, lg_dev, T, S, dev, scratch):
+    ids = torch.empty(T, S.top_k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, S.top_k, dtype=torch.float32, device=dev)
+    counts = torch.empty(S.n_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(S.n_experts + 1, dtype=torch.int32, device=dev)
+    pairs = torch.empty(T * S.top_k, dtype=torch.int32, device=dev)
+    plan.route(blob, 0, None, lg_dev, T, ids, w, counts, offsets, pairs, scratch=scratch)
+    return ids, w, counts, offsets, pairs
+
+
 @pytest.mark.parametrize("T", [8, 32, 128])
-def test_qwen_per_token_gemv_path_small_batch(qwen, T):
-    """Small-batch decode on the per-token GEMV path, routing from given
-    N(0,1) logits (shared fp32 inputs -> ids must match exactly)."""
+def test_small_batch_gemv_and_grouped_paths(qwen, T):
+    """Small-batch decode / short prefill on the Qwen3-30B-A3B-shaped layer:
+    routing from given N(0,1) logits (shared fp32 inputs -> ids must match
+    exactly), expert FFN on both the per-token GEMV path and the grouped
+    MFMA path, each against the oracle (all tokens up to 32, else every 4th)."""
     S = qwen.shape
+    d = qwen.dev
     xb = synth.x_bf16(S, 3, T, T=T)
     lg = synth.logits_f32(S, 3, T)
-    d = qwen.dev
-    ids = torch.empty(T, S.top_k, dtype=torch.int32, device=d)
-    w = torch.empty(T, S.top_k, dtype=torch.float32, device=d)
-    out = torch.empty(T, S.hidden, dtype=torch.float32, device=d)
-    qwen.plan.route(qwen.blob, 0, None, torch.from_numpy(lg).to(d), T, ids, w, scratch=qwen.scratch)
-    qwen.plan.expert_ffn(qwen.blob, 0, qwen.xdev(xb), T, ids, w, out, scratch=qwen.scratch)
-    torch.cuda.synchronize()
-    sample = list(range(T)) if T <= 32 else list(range(0, T, 8))
+    x = qwen.xdev(xb)
+    outs = {}
+    for name, flag in (("gemv", q.FLAG_FORCE_GEMV), ("grouped", q.FLAG_FORCE_GROUPED)):
+        plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=T, flags=flag)
+        scratch = plan.new_scratch(T, device=d)
+        ids, w, counts, offsets, pairs = _route_lists(plan, qwen.blob, torch.from_numpy(lg).to(d), T, S, d, scratch)
+        out = torch.empty(T, S.hidden, dtype=torch.float32, device=d)
+        plan.expert_ffn(qwen.blob, 0, x, T, ids, w, out, counts, offsets, pairs, scratch=scratch)
+        torch.cuda.synchronize()
+        outs[name] = (ids.cpu().numpy(), w.cpu().numpy(), out.cpu().numpy())
+    sample = list(range(T)) if T <= 32 else list(range(0, T, 4))
     ref = oracle.moe_layer(qwen.src, 0, xb[sample], logits=lg[sample])
-    check_routing(ids.cpu().numpy()[sample], w.cpu().numpy()[sample], ref, exact=True)
-    assert rel_err(out.cpu().numpy()[sample], ref["y"]) <= REL_TOL
+    for name, (gi, gw, gy) in outs.items():
+        check_routing(gi[sample], gw[sample], ref, exact=True)
+        err = rel_err(gy[sample], ref["y"])
+        assert err <= REL_TOL, f"{name}: {err:.3e}"
+    assert rel_err(outs["grouped"][2], outs["gemv"][2]) <= REL_TOL
+
+
+def test_zipf_skewed_prefill_4096_grouped(qwen):
+    """4096-token chunk with Zipf(1.1)-biased logits: a handful of experts get
+    most tokens (load-imbalanced grouped GEMM, some experts empty). Sampled
+    tokens cover the hottest expert, cold experts and every tile position."""
+    S = qwen.shape
+    d = qwen.dev
+    T = 4096
+    xb = synth.x_bf16(S, 4, T, T=T)
+    lg = synth.logits_f32(S, 4, T, zipf_s=1.1)
+    plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=T)
+    scratch = plan.new_scratch(T, device=d)
+    ids, w, counts, offsets, pairs = _route_lists(plan, qwen.blob, torch.from_numpy(lg).to(d), T, S, d, scratch)
+    out = torch.empty(T, S.hidden, dtype=torch.float32, device=d)
+    plan.expert_ffn(qwen.blob, 0, qwen.xdev(xb), T, ids, w, out, counts, offsets, pairs, scratch=scratch)
+    torch.cuda.synchronize()
+    cnt = counts.cpu().numpy()
+    assert cnt.max() > 2000 and (cnt == 0).sum() >= 1          # the skew the workload asks for
+    gi = ids.cpu().numpy()
+    hot = int(np.argmax(cnt))
+    cold = [int(e) for e in np.nonzero((cnt > 0) & (cnt < 8))[0][:4]]
+    sample = sorted(set([0, 1, 63, 64, 65, T - 1] + list(range(0, T, 257))
+                        + [int(np.nonzero((gi == e).any(1))[0][0]) for e in cold]
+                        + [int(np.nonzero((gi == hot).any(1))[0][-1])]))
+    ref = oracle.moe_layer(qwen.src, 0, xb[sample], logits=lg[sample])
+    check_routing(gi[sample], w.cpu().numpy()[sample], ref, exact=True)
+    err = rel_err(out.cpu().numpy()[sample], ref["y"])
+    assert err <= REL_TOL, f"{err:.3e}"
+    print(f"T=4096 zipf: hot expert {hot} has {cnt.max()} tokens, {int((cnt == 0).sum())} empty; "
+          f"sampled {len(sample)} tokens, max|err|/max|ref| = {err:.3e}")
+
+
+def test_forward_batched_auto_grouped_tiny(tiny):
+    """moe_forward with T >= 8 takes the grouped path on its own (router GEMV,
+    top-k, dispatch, grouped GEMMs, combine) and keeps the norm epilogue."""
+    S = tiny.shape
+    xb = synth.x_bf16(S, 9, 40, T=40)
+    got = tiny.forward(xb, with_next=True)
+    ref, err, exempt = _check_layer(tiny, xb, got)
+    for t in range(40):
+        if t in exempt:
+            continue
+        _, ref_next = oracle.resid_rmsnorm(xb[t], ref["y"][t])
+        check_bf16_vector(got["xn"][t], ref_next)
 
 
 # ------------------------------------------------------------------ routing and dispatch lists
@@ -229,6 +293,14 @@ def test_edge_shapes(dev, shape):
     st = Setup(shape, dev, n_layers=1, max_tokens=4)
     for T in (1, 3):
         xb = synth.x_bf16(shape, 8, T, T=T)
+        _check_layer(st, xb, st.forward(xb))
+
+
+@pytest.mark.parametrize("shape", EDGE, ids=[s.name for s in EDGE])
+def test_edge_shapes_grouped_path(dev, shape):
+    st = Setup(shape, dev, n_layers=1, max_tokens=70, flags=q.FLAG_FORCE_GROUPED)
+    for T in (2, 5, 70):          # ragged tiles: 70 tokens * k pairs over E experts
+        xb = synth.x_bf16(shape, 12, T, T=T)
         _check_layer(st, xb, st.forward(xb))
 
 
