@@ -46,6 +46,9 @@ def main():
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=4, help="passes over all layers for the kernel timing")
+    ap.add_argument("--no-batched", action="store_true", help="skip the small-batch / prefill measurements")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device copy (reference kernel for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
@@ -62,6 +65,13 @@ def main():
     L = args.layers
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 268435456 bytes read, 268435456 bytes written")
+        del src, dst
     plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=L, max_tokens=1)
 
     # ------------------------------------------------------------ weights
@@ -151,6 +161,12 @@ def main():
         if tr.get("kernel_source_hash") == kernel_source_hash():
             traffic = tr.get("hbm_bytes_per_launch")
 
+    # ------------------------------------------------------------ batched workloads on the same layers
+    batched = None
+    if not args.no_batched:
+        batched = batched_measurements(S, blob, L, dev, stream, q, np, torch, synth)
+        log(f"batched: {json.dumps(batched)}")
+
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = parity = None
     if not args.no_cpu_baseline:
@@ -195,10 +211,78 @@ def main():
             "avg_launch_us": round(gu_us, 3),
         },
         "cpu_baseline": cpu,
+        "batched": batched,
         "parity_step0": parity,
         "outputs_finite": finite,
     }
     print(json.dumps(result), flush=True)
+
+
+MFMA_FP16_PEAK_TFLOPS = 2500.0
+
+
+def batched_measurements(S, blob, L, dev, stream, q, np, torch, synth):
+    """Small-batch decode / short prefill (T = 8, 32, 128; N(0,1) logits) on
+    the per-token GEMV path and the grouped MFMA path, and the Zipf-skewed
+    4096-token chunk on the grouped path. Routing from given logits, expert
+    FFN only, each call on a different layer of the stack in turn (so a
+    layer's experts are not cache-resident from the previous call); captured
+    in a graph, timed with HIP events. Unique expert bytes = experts with at
+    least one routed pair x 2,654,208 B."""
+    res = {}
+    n_rot = min(L, 16)
+
+    def run_case(T, zipf, flag, case):
+        plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=L, max_tokens=T, flags=flag)
+        scratch = plan.new_scratch(T, device=dev)
+        xb = synth.x_bf16(S, case, T, T=T)
+        x = torch.from_numpy(xb.view(np.int16)).to(dev)
+        lg = torch.from_numpy(synth.logits_f32(S, case, T, zipf_s=zipf)).to(dev)
+        k, E = S.top_k, S.n_experts
+        ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+        w = torch.empty(T, k, dtype=torch.float32, device=dev)
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        pairs = torch.empty(T * k, dtype=torch.int32, device=dev)
+        out = torch.empty(T, S.hidden, dtype=torch.float32, device=dev)
+
+        def calls(l):
+            plan.route(blob, l, None, lg, T, ids, w, counts, offsets, pairs, scratch=scratch, stream=stream)
+            plan.expert_ffn(blob, l, x, T, ids, w, out, counts, offsets, pairs, scratch=scratch, stream=stream)
+
+        with torch.cuda.stream(stream):
+            calls(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for l in range(n_rot):
+                    calls(l)
+        reps = 3 if T >= 1024 else 10
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):          # replay() launches on the current stream
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * n_rot)
+        uniq = int((counts.cpu().numpy() > 0).sum())
+        ubytes = uniq * S.expert_bytes
+        flops = 2.0 * T * k * 3 * S.hidden * S.inter
+        return {"us": round(us, 2), "unique_experts": uniq, "unique_expert_gbps": round(ubytes / (us * 1e-6) / 1e9, 1),
+                "tflops": round(flops / (us * 1e-6) / 1e12, 2)}
+
+    for T in (8, 32, 128):
+        res[f"T{T}"] = {"gemv": run_case(T, None, q.FLAG_FORCE_GEMV, 3),
+                        "grouped": run_case(T, None, q.FLAG_FORCE_GROUPED, 3)}
+    z = run_case(4096, 1.1, q.FLAG_FORCE_GROUPED, 4)
+    z["mfma_util"] = round(z["tflops"] / MFMA_FP16_PEAK_TFLOPS, 4)
+    res["T4096_zipf"] = z
+    res["note"] = "route (given logits) + expert FFN per call; us per call averaged over rotating layers"
+    return res
 
 
 def cpu_baseline(S, L, x0, gpu):
