@@ -125,18 +125,18 @@ __device__ __forceinline__ float load_x_pairs(const uint16_t* xs, u32* X) {
 
 // sum_i q_i * h_i over one 32-code sub-block with fp32 h (32 values).
 __device__ __forceinline__ float dot_codes_f32(const u32x4& c, const float* hv) {
-  float a0 = 0.f, a1 = 0.f;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
   const u32 w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const u32 lo = w[d] & 0x0F0F0F0Fu, hi = (w[d] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      a0 = fmaf((float)((lo >> (8 * b)) & 0xFFu), hv[8 * d + 2 * b], a0);
-      a1 = fmaf((float)((hi >> (8 * b)) & 0xFFu), hv[8 * d + 2 * b + 1], a1);
+      a[(2 * b) & 3] = fmaf((float)((lo >> (8 * b)) & 0xFFu), hv[8 * d + 2 * b], a[(2 * b) & 3]);
+      a[(2 * b + 1) & 3] = fmaf((float)((hi >> (8 * b)) & 0xFFu), hv[8 * d + 2 * b + 1], a[(2 * b + 1) & 3]);
     }
   }
-  return a0 + a1;
+  return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
 // ------------------------------------------------------------------ top-k
@@ -321,6 +321,24 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
   __shared__ TopkSmem s_topk;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x / WAVE;
+  const int unit = blockIdx.x * (BLOCK / WAVE) + wid;
+  const int rows_per_unit = RPS * U;
+  const int total_units = T * k * I / rows_per_unit;
+  const bool active = unit < total_units;
+  const int flat0 = active ? unit * rows_per_unit : 0;   // flat row index over (t, s, r)
+  const int ts = flat0 / I;                               // t*k + s
+  const int r0 = flat0 % I;
+  const int t = ts / k;
+  const int rho = lane / LPR, lam = lane % LPR;
+  // the activation slice does not depend on the routing: load it first so
+  // its round trip overlaps the routing's
+  u32 X[IPL][16];
+  float S[IPL];
+#pragma unroll
+  for (int q = 0; q < IPL; ++q) {
+    const int j = lam + LPR * q;
+    S[q] = load_x_pairs(x + (size_t)t * H + 32 * j, X[q]);
+  }
   if (fused_topk) {
     // T == 1: every block derives the same routing from the logits.
     block_topk(logits, E, k, s_topk);
@@ -329,24 +347,8 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
       w_out[threadIdx.x] = s_topk.sw[threadIdx.x];
     }
   }
-  const int unit = blockIdx.x * (BLOCK / WAVE) + wid;
-  const int rows_per_unit = RPS * U;
-  const int total_units = T * k * I / rows_per_unit;
-  if (unit >= total_units) return;
-  const int flat0 = unit * rows_per_unit;   // flat row index over (t, s, r)
-  const int ts = flat0 / I;                 // t*k + s
-  const int r0 = flat0 % I;
-  const int t = ts / k;
+  if (!active) return;
   const int e = fused_topk ? s_topk.sid[ts] : ids_in[ts];
-  const int rho = lane / LPR, lam = lane % LPR;
-
-  u32 X[IPL][16];
-  float S[IPL];
-#pragma unroll
-  for (int q = 0; q < IPL; ++q) {
-    const int j = lam + LPR * q;
-    S[q] = load_x_pairs(x + (size_t)t * H + 32 * j, X[q]);
-  }
   const uint8_t* base = gu + (size_t)e * gu_expert_bytes;
   const int half = H / 2;                 // code bytes per matrix row
   const int hdr = H / 2 * 2;              // headers start after both code areas
@@ -389,22 +391,34 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
 // ------------------------------------------------------------------ down GEMV + combine
 // Items of an output row: (slot s, sub-block j) for s < k, j < I/32, i.e.
 // G = k*I/32 items; item i = lam + LPR*q. Wave work unit: RPS*U consecutive
-// output rows of one token. y[t*H + n] = sum_s w_s * D_{e_s}[n]·h_{t,s}.
+// output rows of one token; a block's 4 units share the token, whose k*I
+// values of h are staged once in LDS. y[t*H + n] = sum_s w_s * D_{e_s}[n]·h_{t,s}.
+constexpr int DOWN_H_MAX = 8192;   // k * I floats staged per block (k * I / 32 <= 256)
 template <int IPL, int LPR, int U>
 __global__ __launch_bounds__(BLOCK) void down_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I, int k,
     const int32_t* __restrict__ ids, const float* __restrict__ wts, const float* __restrict__ h,
     float* __restrict__ y, int T) {
   constexpr int RPS = WAVE / LPR;
+  __shared__ float sh[DOWN_H_MAX];
+  __shared__ int32_t s_ids[16];
+  __shared__ float s_w[16];
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x / WAVE;
-  const int unit = blockIdx.x * (BLOCK / WAVE) + wid;
   const int rows_per_unit = RPS * U;
-  const int total_units = T * H / rows_per_unit;
-  if (unit >= total_units) return;
-  const int flat0 = unit * rows_per_unit;
-  const int t = flat0 / H;
-  const int n0 = flat0 % H;
+  const int rows_per_block = rows_per_unit * (BLOCK / WAVE);
+  const int t = blockIdx.x * rows_per_block / H;          // every row of the block belongs to token t
+  const int unit = blockIdx.x * (BLOCK / WAVE) + wid;
+  const int n0 = (unit * rows_per_unit) % H;
+  const int KI = k * I;
+  // stage h of token t (k*I floats, a multiple of 1024) and its routing
+  for (int i = 4 * threadIdx.x; i < KI; i += 4 * BLOCK)
+    *reinterpret_cast<u32x4*>(sh + i) = load16(h + (size_t)t * KI + i);
+  if (threadIdx.x < k) {
+    s_ids[threadIdx.x] = ids[(size_t)t * k + threadIdx.x];
+    s_w[threadIdx.x] = wts[(size_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
   const int rho = lane / LPR, lam = lane % LPR;
   const int nsb = I / 32;
   const int G = k * nsb;
@@ -421,19 +435,15 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
     const int s = valid[q] ? i / nsb : 0;
     const int j = valid[q] ? i % nsb : 0;
     jq[q] = j;
-    const int ts = t * k + s;
-    ws[q] = valid[q] ? wts[ts] : 0.f;
-    eb[q] = dn + (size_t)ids[ts] * dn_expert_bytes;
-    const float* hp = h + (size_t)ts * I + 32 * j;
+    ws[q] = valid[q] ? s_w[s] : 0.f;
+    eb[q] = dn + (size_t)s_ids[s] * dn_expert_bytes;
+    const float* hp = sh + s * I + 32 * j;
     float sum = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const u32x4 v = load16(hp + 4 * c);
-      hv[q][4 * c + 0] = as_f32(v.x);
-      hv[q][4 * c + 1] = as_f32(v.y);
-      hv[q][4 * c + 2] = as_f32(v.z);
-      hv[q][4 * c + 3] = as_f32(v.w);
-      sum += (hv[q][4 * c + 0] + hv[q][4 * c + 1]) + (hv[q][4 * c + 2] + hv[q][4 * c + 3]);
+      const float4 v = *reinterpret_cast<const float4*>(hp + 4 * c);
+      hv[q][4 * c + 0] = v.x; hv[q][4 * c + 1] = v.y; hv[q][4 * c + 2] = v.z; hv[q][4 * c + 3] = v.w;
+      sum += (v.x + v.y) + (v.z + v.w);
     }
     Sh[q] = sum;
   }
@@ -655,8 +665,7 @@ template <int IPL, int LPR, int U>
 static void down_go(const Layout& d, const uint8_t* layer, const int32_t* ids, const float* w, const float* h, float* y,
                     int T, hipStream_t s) {
   constexpr int RPS = WAVE / LPR;
-  const long long units = (long long)T * d.H / (RPS * U);
-  const int blocks = (int)((units + 3) / 4);
+  const int blocks = T * d.H / (RPS * U * (BLOCK / WAVE));   // H is a multiple of every rows-per-block used
   hipLaunchKernelGGL((down_kernel<IPL, LPR, U>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s, layer + d.dn_off,
                      d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
 }
