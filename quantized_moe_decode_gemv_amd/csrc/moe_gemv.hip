@@ -39,6 +39,11 @@ __device__ __forceinline__ float dot2_bf16(u32 a, u32 b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_f16(u32 a, u32 b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c, false);
+}
+
 __device__ __forceinline__ float half_bits_to_float(u32 bits) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)bits);
 }
@@ -56,12 +61,34 @@ __device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
   return (uint16_t)(b >> 16);
 }
 
+// Cross-lane move by a DPP pattern (all lanes of the wave active).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float read_lane(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
 // Sum over groups of W adjacent lanes (W a power of two <= 64); every lane of
-// a group ends with the group's sum. Fixed butterfly order -> deterministic.
+// a group ends with the same value, the group's sum. Within a row of 16
+// lanes: quad swaps (lane ^ 1, lane ^ 2), then the half-row and row mirrors,
+// each pairing a lane with one holding the other half's partial sum (a + b
+// and b + a are the same float, so all lanes agree); the four row sums are
+// then combined through scalar reads of lanes 0, 16, 32, 48. DPP moves stay
+// in the VALU instead of the LDS crossbar. Must be called with the whole
+// wave active.
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = W / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, WAVE);
+  if (W >= 2) v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+  if (W >= 4) v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+  if (W >= 8) v += dpp_mov<0x141>(v);   // row_half_mirror
+  if (W >= 16) v += dpp_mov<0x140>(v);  // row_mirror
+  if (W >= 32) {
+    const float r0 = read_lane(v, 0), r1 = read_lane(v, 16), r2 = read_lane(v, 32), r3 = read_lane(v, 48);
+    if (W == 32) v = (threadIdx.x & (WAVE - 1)) < 32 ? r0 + r1 : r2 + r3;
+    else v = (r0 + r1) + (r2 + r3);
+  }
   return v;
 }
 
@@ -137,6 +164,25 @@ __device__ __forceinline__ float dot_codes_f32(const u32x4& c, const float* hv) 
     }
   }
   return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// sum_i (1024 + q_i) * h_i over one 32-code sub-block with fp16 h, two codes
+// per v_dot2_f32_f16: fp16 0x6400|q is exactly 1024 + q, and (1024 + q) * h is
+// exact in fp32. X[4d+c] holds the fp16 pair (h[8d+c], h[8d+c+4]) matching the
+// nibble pair extracted at shift 4c from code dword d.
+__device__ __forceinline__ float dot_codes_f16(const u32x4& c, const u32* X) {
+  const u32 M = 0x000F000Fu, B = 0x64006400u;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  const u32 w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32 v = w[d];
+    a0 = dot2_f16((v & M) | B, X[4 * d + 0], a0);
+    a1 = dot2_f16(((v >> 4) & M) | B, X[4 * d + 1], a1);
+    a2 = dot2_f16(((v >> 8) & M) | B, X[4 * d + 2], a2);
+    a3 = dot2_f16(((v >> 12) & M) | B, X[4 * d + 3], a3);
+  }
+  return (a0 + a1) + (a2 + a3);
 }
 
 // ------------------------------------------------------------------ top-k
@@ -390,91 +436,81 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
 
 // ------------------------------------------------------------------ down GEMV + combine
 // Items of an output row: (slot s, sub-block j) for s < k, j < I/32, i.e.
-// G = k*I/32 items; item i = lam + LPR*q. Wave work unit: RPS*U consecutive
-// output rows of one token; a block's 4 units share the token, whose k*I
-// values of h are staged once in LDS. y[t*H + n] = sum_s w_s * D_{e_s}[n]·h_{t,s}.
-constexpr int DOWN_H_MAX = 8192;   // k * I floats staged per block (k * I / 32 <= 256)
-template <int IPL, int LPR, int U>
+// G = k*I/32 <= 256 items. A block computes R consecutive output rows of one
+// token; wave w takes the contiguous item range [w*IW, (w+1)*IW), IW =
+// ceil(G/4) <= 64, one item per lane, for all R rows, so a lane loads its
+// 32 values of h once (straight into registers) and one 16-byte code chunk
+// and header per row. The routing is read directly, so the weight loads
+// leave as soon as the expert ids arrive. The four wave partials of a row are
+// added in wave order. h is rounded to fp16 for v_dot2_f32_f16 (relative
+// rounding 2^-11 per value); products and sums are fp32.
+// y[t*H + n] = sum_s w_s * D_{e_s}[n]·h_{t,s}.
+template <int R>
 __global__ __launch_bounds__(BLOCK) void down_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I, int k,
     const int32_t* __restrict__ ids, const float* __restrict__ wts, const float* __restrict__ h,
     float* __restrict__ y, int T) {
-  constexpr int RPS = WAVE / LPR;
-  __shared__ float sh[DOWN_H_MAX];
-  __shared__ int32_t s_ids[16];
-  __shared__ float s_w[16];
+  __shared__ float part[BLOCK / WAVE][R];
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x / WAVE;
-  const int rows_per_unit = RPS * U;
-  const int rows_per_block = rows_per_unit * (BLOCK / WAVE);
-  const int t = blockIdx.x * rows_per_block / H;          // every row of the block belongs to token t
-  const int unit = blockIdx.x * (BLOCK / WAVE) + wid;
-  const int n0 = (unit * rows_per_unit) % H;
-  const int KI = k * I;
-  // stage h of token t (k*I floats, a multiple of 1024) and its routing
-  for (int i = 4 * threadIdx.x; i < KI; i += 4 * BLOCK)
-    *reinterpret_cast<u32x4*>(sh + i) = load16(h + (size_t)t * KI + i);
-  if (threadIdx.x < k) {
-    s_ids[threadIdx.x] = ids[(size_t)t * k + threadIdx.x];
-    s_w[threadIdx.x] = wts[(size_t)t * k + threadIdx.x];
-  }
-  __syncthreads();
-  const int rho = lane / LPR, lam = lane % LPR;
+  const int bpt = H / R;                           // blocks per token
+  const int t = blockIdx.x / bpt;
+  const int n0 = (blockIdx.x % bpt) * R;
   const int nsb = I / 32;
   const int G = k * nsb;
-
-  float hv[IPL][32];
-  float Sh[IPL], ws[IPL];
-  const uint8_t* eb[IPL];
-  int jq[IPL];
-  bool valid[IPL];
+  const int IW = (G + 3) / 4;
+  const int i = wid * IW + lane;
+  const bool valid = lane < IW && i < G;
+  const int s = valid ? i / nsb : 0;
+  const int j = valid ? i % nsb : 0;
+  const int e = valid ? ids[(size_t)t * k + s] : 0;
+  const float ws = valid ? wts[(size_t)t * k + s] : 0.f;
+  u32x4 hr[8];
+  const float* hp = h + ((size_t)t * k + s) * I + 32 * j;
 #pragma unroll
-  for (int q = 0; q < IPL; ++q) {
-    const int i = lam + LPR * q;
-    valid[q] = i < G;
-    const int s = valid[q] ? i / nsb : 0;
-    const int j = valid[q] ? i % nsb : 0;
-    jq[q] = j;
-    ws[q] = valid[q] ? s_w[s] : 0.f;
-    eb[q] = dn + (size_t)s_ids[s] * dn_expert_bytes;
-    const float* hp = sh + s * I + 32 * j;
-    float sum = 0.f;
+  for (int c = 0; c < 8; ++c) hr[c] = valid ? load16(hp + 4 * c) : u32x4{0u, 0u, 0u, 0u};
+  const uint8_t* row0 = dn + (size_t)e * dn_expert_bytes + (size_t)n0 * drow_bytes;
+  const int hdr = I / 2 + QHDR * (j >> 3);
+  u32x4 cd[R], hd[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint8_t* row = row0 + (size_t)r * drow_bytes;
+    cd[r] = valid ? load_nt(row + 16 * j) : u32x4{0u, 0u, 0u, 0u};
+    hd[r] = valid ? load_nt(row + hdr) : u32x4{0u, 0u, 0u, 0u};
+  }
+  // h -> fp16 pairs in nibble order; S is the sum of the rounded values
+  u32 X[16];
+  float S = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32 v[8] = {hr[2 * d].x, hr[2 * d].y, hr[2 * d].z, hr[2 * d].w,
+                      hr[2 * d + 1].x, hr[2 * d + 1].y, hr[2 * d + 1].z, hr[2 * d + 1].w};
+    _Float16 hh[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float4 v = *reinterpret_cast<const float4*>(hp + 4 * c);
-      hv[q][4 * c + 0] = v.x; hv[q][4 * c + 1] = v.y; hv[q][4 * c + 2] = v.z; hv[q][4 * c + 3] = v.w;
-      sum += (v.x + v.y) + (v.z + v.w);
+      hh[c] = (_Float16)as_f32(v[c]);
+      S += (float)hh[c];
     }
-    Sh[q] = sum;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      X[4 * d + c] = (u32)__builtin_bit_cast(unsigned short, hh[c]) |
+                     ((u32)__builtin_bit_cast(unsigned short, hh[c + 4]) << 16);
   }
-  const int half = I / 2;
-  u32x4 cd[U][IPL], hd[U][IPL];
+  float p[R];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int n = n0 + u * RPS + rho;
-#pragma unroll
-    for (int q = 0; q < IPL; ++q) {
-      if (valid[q]) {
-        const uint8_t* row = eb[q] + (size_t)n * drow_bytes;
-        cd[u][q] = load_nt(row + 16 * jq[q]);
-        hd[u][q] = load_nt(row + half + QHDR * (jq[q] >> 3));
-      } else {
-        cd[u][q] = u32x4{0u, 0u, 0u, 0u};
-        hd[u][q] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+  for (int r = 0; r < R; ++r) {
+    const Affine a = header_affine(hd[r], j & 7);
+    const float dq = dot_codes_f16(cd[r], X);
+    p[r] = group_sum<WAVE>(ws * (a.a * dq - (1024.f * a.a + a.b) * S));
   }
+  if (lane == 0) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    float p = 0.f;
-#pragma unroll
-    for (int q = 0; q < IPL; ++q) {
-      const Affine a = header_affine(hd[u][q], jq[q] & 7);
-      const float dq = dot_codes_f32(cd[u][q], hv[q]);
-      p += ws[q] * (a.a * dq - a.b * Sh[q]);
-    }
-    p = group_sum<LPR>(p);
-    if (lam == 0) y[(size_t)t * H + n0 + u * RPS + rho] = p;
+    for (int r = 0; r < R; ++r) part[wid][r] = p[r];
+  }
+  __syncthreads();
+  if (threadIdx.x < R) {
+    const int r = threadIdx.x;
+    y[(size_t)t * H + n0 + r] = ((part[0][r] + part[1][r]) + part[2][r]) + part[3][r];
   }
 }
 
@@ -563,7 +599,6 @@ __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* _
 }
 
 // ------------------------------------------------------------------ launchers
-static int pow2ceil(int v) { int p = 1; while (p < v) p <<= 1; return p; }
 
 static hipError_t launch_router_big(const Layout& d, const float* wr, const uint16_t* x, const float* y_prev,
                                     uint16_t* x_out, float* logits, int T, hipStream_t s) {
@@ -661,37 +696,13 @@ hipError_t launch_gateup(const Layout& d, const uint8_t* layer, const uint16_t* 
   return hipGetLastError();
 }
 
-template <int IPL, int LPR, int U>
-static void down_go(const Layout& d, const uint8_t* layer, const int32_t* ids, const float* w, const float* h, float* y,
-                    int T, hipStream_t s) {
-  constexpr int RPS = WAVE / LPR;
-  const int blocks = T * d.H / (RPS * U * (BLOCK / WAVE));   // H is a multiple of every rows-per-block used
-  hipLaunchKernelGGL((down_kernel<IPL, LPR, U>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s, layer + d.dn_off,
-                     d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
-}
-
 hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids, const float* w, const float* h,
                        float* y, int T, hipStream_t s) {
-  const int G = d.k * (d.I / 32);
-  const int LPR = G >= WAVE ? WAVE : pow2ceil(G);
-  const int IPL = (G + LPR - 1) / LPR;
-  // RPS*U must divide H (a multiple of 256)
-  if (LPR == 64) {
-    switch (IPL) {
-      case 1: down_go<1, 64, 2>(d, layer, ids, w, h, y, T, s); break;
-      case 2: down_go<2, 64, 2>(d, layer, ids, w, h, y, T, s); break;
-      case 3: down_go<3, 64, 2>(d, layer, ids, w, h, y, T, s); break;
-      case 4: down_go<4, 64, 1>(d, layer, ids, w, h, y, T, s); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (LPR) {
-      case 8: down_go<1, 8, 2>(d, layer, ids, w, h, y, T, s); break;
-      case 16: down_go<1, 16, 2>(d, layer, ids, w, h, y, T, s); break;
-      case 32: down_go<1, 32, 2>(d, layer, ids, w, h, y, T, s); break;
-      default: return hipErrorInvalidValue;
-    }
-  }
+  constexpr int R = 8;                       // divides every supported H
+  if (d.k * (d.I / 32) > 4 * WAVE || d.H % R) return hipErrorInvalidValue;
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL((down_kernel<R>), dim3(T * (d.H / R)), dim3(BLOCK), 0, s, layer + d.dn_off,
+                     d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
   return hipGetLastError();
 }
 
