@@ -192,87 +192,110 @@ __device__ __forceinline__ u32 order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// LDS workspace of block_topk.
+// LDS workspace of wave_topk (one per wave that runs it).
 struct TopkSmem {
-  unsigned long long key[BLOCK];   // unique keys: (order_key(logit) << 32) | ~id, 0 past E
-  unsigned long long gmax[32];     // maxima of groups of 8 consecutive ids
-  unsigned long long ckey[64];     // candidates
-  unsigned long long thr;
-  int wcnt[BLOCK / WAVE];
+  unsigned long long ckey[16];     // selected keys (order_key(logit) << 32 | ~id), id order
+  float cval[16];                  // their logits
   float val[16];                   // selected logits, descending
-  int32_t sid[16];
-  float sw[16];
+  int32_t sid[16];                 // selected ids, descending logit (equal logits: lower id first)
+  float sw[16];                    // softmax over the selection
 };
 
-// Block-wide top-k of E <= 256 logits (descending; equal values -> lower id)
-// and the softmax restricted to the selection, into sm.sid / sm.sw (k <= 16).
-// Every logit gets a unique 64-bit key, larger for a larger logit and, among
-// equal logits, for the lower id, so its rank is the number of larger keys.
-// To keep the comparisons few, the k-th largest of the maxima of groups of 8
-// consecutive ids is taken as a threshold: at least k keys reach it, so the
-// whole top-k does, and at most 8k keys (those of the k leading groups) can;
-// only those candidates are ranked, against each other. Every thread of the
-// block must call it.
-__device__ void block_topk(const float* __restrict__ lg, int E, int k, TopkSmem& sm) {
-  const int t = threadIdx.x;
-  const int lane = t & (WAVE - 1), wid = t / WAVE;
-  float v = 0.f;
-  if (t < E) v = lg[t];
-  const unsigned long long key = t < E ? (((unsigned long long)order_key(v) << 32) | (u32)~(u32)t) : 0ull;
-  sm.key[t] = key;
-  if (t == 0) sm.thr = 0ull;
-  __syncthreads();
-  const int ng = (E + 7) / 8;
-  if (t < ng) {
-    unsigned long long m = 0ull;
+// Orders the LDS accesses of one wave (the LDS serves a wave's requests in
+// program order; this keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Top-k of E <= 64*NC logits by one wave (k <= 16 <= E; descending, equal
+// logits -> lower id first), into sm.sid / sm.val, and with want_weights the
+// softmax restricted to the selection into sm.sw. Lane l holds the logits of
+// ids l + 64c (c < NC) as order keys (a > b <=> key(a) > key(b)).
+// A threshold T is built bit by bit from the top: a bit stays set when at
+// least k keys reach the prefix with it set (ballot + popcount per 64 keys);
+// the search stops early once exactly k keys reach T. Every key above T is
+// selected and keys equal to T fill the remaining places in id order (after
+// a full search T is the k-th largest key; after an early stop the keys
+// reaching T are exactly the k largest). Only the k selected keys are then
+// ranked, against each other. Ids >= E are never selected.
+template <int NC>
+__device__ void wave_topk(const float* __restrict__ lg, int E, int k, bool want_weights, TopkSmem& sm) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  float v[NC];
+  u32 key[NC];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = sm.key[8 * t + j] > m ? sm.key[8 * t + j] : m;
-    sm.gmax[t] = m;
+  for (int c = 0; c < NC; ++c) {
+    const int id = lane + WAVE * c;
+    v[c] = id < E ? lg[id] : 0.f;
+    key[c] = id < E ? order_key(v[c]) : 0u;
   }
-  __syncthreads();
-  if (ng >= k && t < ng) {
-    const unsigned long long g = sm.gmax[t];
-    int r = 0;
-    for (int j = 0; j < ng; ++j) r += sm.gmax[j] > g ? 1 : 0;
-    if (r == k - 1) sm.thr = g;
+  u32 thr = 0u;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const u32 cand = thr | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) cnt += __popcll(__ballot(key[c] >= cand));
+    if (cnt >= k) {
+      thr = cand;
+      if (cnt == k) break;
+    }
   }
-  __syncthreads();
-  const bool cand = t < E && key >= sm.thr;
-  const unsigned long long m = __ballot(cand);
   const unsigned long long below = lane ? (~0ull >> (WAVE - lane)) : 0ull;
-  if (lane == 0) sm.wcnt[wid] = __popcll(m);
-  __syncthreads();
-  int base = 0, nc = 0;
+  int gt = 0;
 #pragma unroll
-  for (int w = 0; w < BLOCK / WAVE; ++w) {
-    base += w < wid ? sm.wcnt[w] : 0;
-    nc += sm.wcnt[w];
+  for (int c = 0; c < NC; ++c) gt += __popcll(__ballot(key[c] > thr));
+  const int need = k - gt;                         // >= 1 places left for keys equal to T
+  int ties_before = 0, base = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int id = lane + WAVE * c;
+    const bool eq = key[c] == thr && id < E;
+    const unsigned long long em = __ballot(eq);
+    const bool sel = key[c] > thr || (eq && ties_before + __popcll(em & below) < need);
+    ties_before += __popcll(em);
+    const unsigned long long sm_mask = __ballot(sel);
+    if (sel) {
+      const int pos = base + __popcll(sm_mask & below);
+      sm.ckey[pos] = ((unsigned long long)key[c] << 32) | (u32)~(u32)id;
+      sm.cval[pos] = v[c];
+    }
+    base += __popcll(sm_mask);
   }
-  if (cand) sm.ckey[base + __popcll(m & below)] = key;
-  __syncthreads();
-  if (cand) {
-    int rank = 0;
-    for (int j = 0; j < nc; ++j) rank += sm.ckey[j] > key ? 1 : 0;
-    if (rank < k) { sm.sid[rank] = t; sm.val[rank] = v; }
+  wave_lds_sync();
+  if (lane < k) {
+    const unsigned long long mk = sm.ckey[lane];
+    int r = 0;
+    for (int j = 0; j < k; ++j) r += sm.ckey[j] > mk ? 1 : 0;
+    sm.sid[r] = (int32_t)~(u32)mk;
+    sm.val[r] = sm.cval[lane];
   }
-  __syncthreads();
-  // softmax over the selection: lane s < k forms every term itself (same
-  // order in every lane, so all lanes agree on the denominator)
-  if (t < k) {
+  wave_lds_sync();
+  if (want_weights && lane < k) {
+    // every lane forms the denominator in the same order
     const float l0 = sm.val[0];
     float den = 0.f;
     for (int j = 0; j < k; ++j) den += __expf(sm.val[j] - l0);
-    sm.sw[t] = __expf(sm.val[t] - l0) / den;
+    sm.sw[lane] = __expf(sm.val[lane] - l0) / den;
   }
-  __syncthreads();
+  wave_lds_sync();
 }
 
-// One block per token.
-__global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ logits, int32_t* __restrict__ ids,
-                                                     float* __restrict__ w, int E, int k, int T) {
+__device__ __forceinline__ void wave_topk_any(const float* __restrict__ lg, int E, int k, bool want_weights,
+                                              TopkSmem& sm) {
+  if (E <= WAVE) wave_topk<1>(lg, E, k, want_weights, sm);
+  else if (E <= 2 * WAVE) wave_topk<2>(lg, E, k, want_weights, sm);
+  else if (E <= 3 * WAVE) wave_topk<3>(lg, E, k, want_weights, sm);
+  else wave_topk<4>(lg, E, k, want_weights, sm);
+}
+
+// One wave per token.
+__global__ __launch_bounds__(WAVE) void topk_kernel(const float* __restrict__ logits, int32_t* __restrict__ ids,
+                                                    float* __restrict__ w, int E, int k, int T) {
   __shared__ TopkSmem sm;
   const int t = blockIdx.x;
-  block_topk(logits + (size_t)t * E, E, k, sm);
+  wave_topk_any(logits + (size_t)t * E, E, k, true, sm);
   if (threadIdx.x < k) {
     ids[(size_t)t * k + threadIdx.x] = sm.sid[threadIdx.x];
     w[(size_t)t * k + threadIdx.x] = sm.sw[threadIdx.x];
@@ -386,12 +409,16 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
     S[q] = load_x_pairs(x + (size_t)t * H + 32 * j, X[q]);
   }
   if (fused_topk) {
-    // T == 1: every block derives the same routing from the logits.
-    block_topk(logits, E, k, s_topk);
-    if (blockIdx.x == 0 && threadIdx.x < k) {
-      ids_out[threadIdx.x] = s_topk.sid[threadIdx.x];
-      w_out[threadIdx.x] = s_topk.sw[threadIdx.x];
+    // T == 1: wave 0 of every block derives the same routing from the logits;
+    // block 0 also publishes it with the weights.
+    if (wid == 0) {
+      wave_topk_any(logits, E, k, blockIdx.x == 0, s_topk);
+      if (blockIdx.x == 0 && lane < k) {
+        ids_out[lane] = s_topk.sid[lane];
+        w_out[lane] = s_topk.sw[lane];
+      }
     }
+    __syncthreads();
   }
   if (!active) return;
   const int e = fused_topk ? s_topk.sid[ts] : ids_in[ts];
@@ -649,7 +676,7 @@ hipError_t launch_router(const Layout& d, const float* wr, const uint16_t* x, fl
 }
 
 hipError_t launch_topk(const Layout& d, const float* logits, int32_t* ids, float* w, int T, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(BLOCK), 0, s, logits, ids, w, d.E, d.k, T);
+  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(WAVE), 0, s, logits, ids, w, d.E, d.k, T);
   return hipGetLastError();
 }
 
