@@ -198,12 +198,13 @@ static bool use_grouped(const moe_plan* plan, int32_t T) {
   return T >= GROUPED_MIN_TOKENS;
 }
 
+// tiles_ready: the dispatch kernel already wrote the tile offsets into scratch.
 static int grouped_impl(const moe_plan* plan, const uint8_t* L, const uint16_t* x, int32_t T, const float* w,
                         const int32_t* offsets, const int32_t* pairs, float* out, uint8_t* scr, const Scratch& sc,
-                        hipStream_t stream) {
+                        hipStream_t stream, bool tiles_ready = false) {
   const Layout& d = plan->d;
   int32_t* tile_off = reinterpret_cast<int32_t*>(scr + sc.tile_off);
-  if (launch_tile_offsets(d, offsets, tile_off, GROUPED_MT, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (!tiles_ready && launch_tile_offsets(d, offsets, tile_off, GROUPED_MT, stream) != hipSuccess) return MOE_ERR_HIP;
   if (launch_grouped_ffn(d, L, x, w, offsets, pairs, tile_off, reinterpret_cast<_Float16*>(scr + sc.h16),
                          reinterpret_cast<float*>(scr + sc.ypair), out, T, stream) != hipSuccess)
     return MOE_ERR_HIP;
@@ -290,8 +291,10 @@ static int forward_impl(const moe_plan* plan, const void* blob, int32_t layer, c
     int32_t* counts = reinterpret_cast<int32_t*>(scr + sc.counts);
     int32_t* offsets = reinterpret_cast<int32_t*>(scr + sc.offsets);
     int32_t* pairs = reinterpret_cast<int32_t*>(scr + sc.pairs);
-    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream) != hipSuccess) return MOE_ERR_HIP;
-    const int st = grouped_impl(plan, L, x, T, w, offsets, pairs, out, scr, sc, stream);
+    int32_t* tile_off = reinterpret_cast<int32_t*>(scr + sc.tile_off);
+    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream, tile_off, GROUPED_MT) != hipSuccess)
+      return MOE_ERR_HIP;
+    const int st = grouped_impl(plan, L, x, T, w, offsets, pairs, out, scr, sc, stream, true);
     if (st) return st;
   } else {
     if (launch_gateup(d, L, x, ids, lg, ids, w, h, T, fused, stream) != hipSuccess) return MOE_ERR_HIP;

@@ -574,16 +574,42 @@ __global__ __launch_bounds__(BLOCK) void resid_norm_kernel(const uint16_t* __res
 }
 
 // ------------------------------------------------------------------ dispatch lists
+// Exclusive scans of a and b over threads 0..255 of the block (threads past
+// 255 take part in the calls but their results are unspecified); totals in
+// tot_a / tot_b. Wave inclusive scans (shfl_up), then the four wave totals
+// through LDS. Every thread of the block must call it.
+__device__ __forceinline__ void excl_scan256x2(int a, int b, int& ea, int& eb, int& tot_a, int& tot_b, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
+  int ia = a, ib = b;
+#pragma unroll
+  for (int dl = 1; dl < WAVE; dl <<= 1) {
+    const int ta = __shfl_up(ia, dl, WAVE), tb = __shfl_up(ib, dl, WAVE);
+    if (lane >= dl) { ia += ta; ib += tb; }
+  }
+  if (tid < 4 * WAVE && lane == WAVE - 1) { wsum[wid] = ia; wsum[4 + wid] = ib; }
+  __syncthreads();
+  int ba = 0, bb = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    if (w < wid) { ba += wsum[w]; bb += wsum[4 + w]; }
+  ea = ba + ia - a;
+  eb = bb + ib - b;
+  tot_a = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  tot_b = (wsum[4] + wsum[5]) + (wsum[6] + wsum[7]);
+}
+
 // Single block of 1024 threads (16 waves). counts[e] = #pairs routed to e,
-// offsets = exclusive scan, pairs = pair indices p = t*k+s ordered by
-// (expert, p). Deterministic: ranks come from ballots, not from atomics order.
+// offsets = exclusive scan (E+1 entries), pairs = pair indices p = t*k+s
+// ordered by (expert, p), and with tile_off != nullptr the exclusive scan of
+// ceil(counts[e] / mt) (E+1 entries: the grouped GEMMs' tile list).
+// Deterministic: ranks come from ballots, not from the order of atomics.
 constexpr int DISP_THREADS = 1024;
 constexpr int DISP_WAVES = DISP_THREADS / WAVE;
 __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
                                                                 int32_t* __restrict__ offsets, int32_t* __restrict__ pairs,
-                                                                int E, int P) {
+                                                                int32_t* __restrict__ tile_off, int E, int P, int mt) {
   __shared__ int cnt[DISP_WAVES][256];
-  __shared__ int off[257];
+  __shared__ int wsum[8];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
   for (int i = tid; i < DISP_WAVES * 256; i += DISP_THREADS) (&cnt[0][0])[i] = 0;
   __syncthreads();
@@ -591,17 +617,25 @@ __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* _
   const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
   for (int p = p0 + lane; p < p1; p += WAVE) atomicAdd(&cnt[wid][ids[p]], 1);
   __syncthreads();
+  // thread e: its expert's column over the waves (exclusive within the expert)
+  int tot = 0;
+  if (tid < E) {
+    for (int w = 0; w < DISP_WAVES; ++w) { const int c = cnt[w][tid]; cnt[w][tid] = tot; tot += c; }
+  }
+  const int tiles = tid < E ? (tot + mt - 1) / mt : 0;
+  int ex_tot, ex_tiles, all_tot, all_tiles;
+  excl_scan256x2(tid < E ? tot : 0, tiles, ex_tot, ex_tiles, all_tot, all_tiles, wsum);
+  if (tid < E) {
+    counts[tid] = tot;
+    offsets[tid] = ex_tot;
+    if (tile_off) tile_off[tid] = ex_tiles;
+    for (int w = 0; w < DISP_WAVES; ++w) cnt[w][tid] += ex_tot;
+  }
   if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      off[e] = run;
-      for (int w = 0; w < DISP_WAVES; ++w) { const int c = cnt[w][e]; cnt[w][e] = run; run += c; }
-    }
-    off[E] = run;
+    offsets[E] = all_tot;
+    if (tile_off) tile_off[E] = all_tiles;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += DISP_THREADS) { counts[e] = off[e + 1] - off[e]; offsets[e] = off[e]; }
-  if (tid == 0) offsets[E] = off[E];
   // cnt[w][e] is now the first output slot of wave w's pairs for expert e
   for (int pb = p0; pb < p1; pb += WAVE) {
     const int p = pb + lane;
@@ -739,24 +773,29 @@ hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y,
 }
 
 hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* pairs, int T,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs, d.E, T * d.k);
+                           hipStream_t s, int32_t* tile_off, int mt) {
+  if (tile_off && mt < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs, tile_off, d.E,
+                     T * d.k, tile_off ? mt : 1);
   return hipGetLastError();
 }
 
 // tile_off[e] = number of `mt`-pair tiles of experts before e (E + 1 entries).
-__global__ void tile_offsets_kernel(const int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off, int E, int mt) {
-  if (threadIdx.x != 0) return;
-  int run = 0;
-  for (int e = 0; e < E; ++e) {
-    tile_off[e] = run;
-    run += (offsets[e + 1] - offsets[e] + mt - 1) / mt;
-  }
-  tile_off[E] = run;
+// tile_off = exclusive scan of ceil((offsets[e+1] - offsets[e]) / mt), E+1
+// entries; one block of 256 threads.
+__global__ __launch_bounds__(BLOCK) void tile_offsets_kernel(const int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ tile_off, int E, int mt) {
+  __shared__ int wsum[8];
+  const int tid = threadIdx.x;
+  const int n = tid < E ? offsets[tid + 1] - offsets[tid] : 0;
+  int ex, ex2, tot, tot2;
+  excl_scan256x2((n + mt - 1) / mt, 0, ex, ex2, tot, tot2, wsum);
+  if (tid < E) tile_off[tid] = ex;
+  if (tid == 0) tile_off[E] = tot;
 }
 
 hipError_t launch_tile_offsets(const Layout& d, const int32_t* offsets, int32_t* tile_off, int mt, hipStream_t s) {
-  hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(WAVE), 0, s, offsets, tile_off, d.E, mt);
+  hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(BLOCK), 0, s, offsets, tile_off, d.E, mt);
   return hipGetLastError();
 }
 

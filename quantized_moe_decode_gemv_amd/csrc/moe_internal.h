@@ -99,7 +99,7 @@ hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids
 hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y, uint16_t* x_next, int T,
                              hipStream_t s);
 hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets,
-                           int32_t* pairs, int T, hipStream_t s);
+                           int32_t* pairs, int T, hipStream_t s, int32_t* tile_off = nullptr, int mt = 1);
 hipError_t launch_tile_offsets(const Layout& d, const int32_t* offsets, int32_t* tile_off, int mt, hipStream_t s);
 
 // grouped MFMA path (T > 1)
