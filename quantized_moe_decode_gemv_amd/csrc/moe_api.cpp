@@ -204,7 +204,8 @@ static int grouped_impl(const moe_plan* plan, const uint8_t* L, const uint16_t* 
                         hipStream_t stream, bool tiles_ready = false) {
   const Layout& d = plan->d;
   int32_t* tile_off = reinterpret_cast<int32_t*>(scr + sc.tile_off);
-  if (!tiles_ready && launch_tile_offsets(d, offsets, tile_off, GROUPED_MT, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (!tiles_ready && launch_tile_offsets(d, offsets, tile_off, grouped_mt(d, T), stream) != hipSuccess)
+    return MOE_ERR_HIP;
   if (launch_grouped_ffn(d, L, x, w, offsets, pairs, tile_off, reinterpret_cast<_Float16*>(scr + sc.h16),
                          reinterpret_cast<float*>(scr + sc.ypair), out, T, stream) != hipSuccess)
     return MOE_ERR_HIP;
@@ -292,7 +293,7 @@ static int forward_impl(const moe_plan* plan, const void* blob, int32_t layer, c
     int32_t* offsets = reinterpret_cast<int32_t*>(scr + sc.offsets);
     int32_t* pairs = reinterpret_cast<int32_t*>(scr + sc.pairs);
     int32_t* tile_off = reinterpret_cast<int32_t*>(scr + sc.tile_off);
-    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream, tile_off, GROUPED_MT) != hipSuccess)
+    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream, tile_off, grouped_mt(d, T)) != hipSuccess)
       return MOE_ERR_HIP;
     const int st = grouped_impl(plan, L, x, T, w, offsets, pairs, out, scr, sc, stream, true);
     if (st) return st;

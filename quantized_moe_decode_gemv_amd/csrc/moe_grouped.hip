@@ -1,24 +1,26 @@
 // gfx950 kernels of the batched path: grouped expert GEMMs on the MFMA
 // units for token batches routed to the same expert.
 //
-// The pages' batched prefill dequantizes 4-bit weights into the GEMM operand
-// and shares one weight read across a chunk of tokens (SP⚡RKINFER README,
-// Qwen3.8-27B prefill notes; sparkinfer-k3 release log, batched prompt
-// ingestion); this is our CDNA4 form of it. Tokens are grouped by expert on
-// the device (dispatch lists); a workgroup takes a (expert, 64-pair tile,
-// feature block) and runs v_mfma_f32_16x16x32_f16 with
+// The pages' batched prefill dequantizes the 4-bit super-blocks into the GEMM
+// operand and shares one weight read across a chunk of tokens (SP⚡RKINFER
+// README, Qwen3.8-27B prefill notes; sparkinfer-k3 release log, batched
+// prompt ingestion); this is our CDNA4 form of it. Tokens are grouped by
+// expert on the device (dispatch lists); a workgroup takes (expert, tile of
+// MT = 32*WR routed pairs, block of output features) and runs
+// v_mfma_f32_32x32x16_f16 with
 //   A = activations in fp16 (bf16 inputs are exact in fp16 above 2^-14),
-//   B = q * sc, the 4-bit code times its 6-bit sub-block scale (<= 945,
-//       exact in fp16), built with the exact fp16 identity 0x6400|q = 1024+q,
-// accumulated over one 256-weight super-block, then scaled by the block's d.
-// The min term sum_j dmin*m_j*sum_{i in j} x_i is one more MFMA per
-// super-block with A = the sub-block sums split into fp16 hi + lo parts and
-// B = m_j, scaled by dmin. Activations are staged in LDS with each group of 8
-// stored in the order the code nibbles are unpacked (0,4,1,5,2,6,3,7), two
-// super-blocks in flight (LDS double buffer, next weights in registers).
-// h = SiLU(gate) * up is kept in fp16 between the two GEMMs; the down GEMM
-// writes one fp32 row per (token, slot) pair and the routing-weighted combine
-// sums them in slot order (deterministic).
+//   B = the dequantized weight d*sc*q - dmin*m rounded once to fp16: the
+//       code q comes out exact as fp16(0x6400|q) - 1024, then one packed fp16
+//       fma with (d*sc, -dmin*m) per sub-block (relative rounding 2^-11),
+// accumulated in fp32 over the whole K. Lane (n = l%32, kg = l/32) of a
+// weight row owns the 16-byte code chunks at 32j + 16kg (j = 0..3) of every
+// super-block, i.e. sub-blocks 2j + kg, so four consecutive MFMAs cover 64
+// consecutive K; activations are staged in LDS half a super-block (128 K) at
+// a time, double buffered, with each group of 8 stored in the order the code
+// nibbles are unpacked (0,2,4,6,1,3,5,7). h = SiLU(gate) * up is written in
+// fp16 in that same order, so the down GEMM stages it by plain copies; the
+// down GEMM writes one fp32 row per (token, slot) pair and the
+// routing-weighted combine sums them in slot order (deterministic).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,15 +33,15 @@ typedef unsigned int u32;
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int WAVE = 64;
 constexpr int BLOCK = 256;
-constexpr int MT = 64;       // pairs per tile
-constexpr int XS = 256 + 8;  // LDS row stride (halfs) of a staged 256-wide K slice
-
-__device__ __forceinline__ float bf16_to_f32(u32 bits) { return __builtin_bit_cast(float, bits << 16); }
-__device__ __forceinline__ float half_bits(u32 b) { return (float)__builtin_bit_cast(_Float16, (unsigned short)b); }
+constexpr int KH = 128;            // K per stage (half a super-block)
+constexpr int XS = KH + 8;         // LDS row stride (halfs): 272 B = 16 mod 128, conflict-free 16-byte reads
+constexpr int NN = 2;              // 32-feature column blocks per wave
+constexpr int FB = 4 * NN * 32 / 2;   // gate/up: output features (h) per workgroup = 128
+constexpr int FD = 4 * NN * 32;       // down: output features per workgroup = 256
 
 __device__ __forceinline__ u32 field6(const u32x4& h, int p) {
   const int idx = p >> 5, sh = p & 31;
@@ -48,270 +50,299 @@ __device__ __forceinline__ u32 field6(const u32x4& h, int p) {
   return __builtin_amdgcn_alignbit(hi, lo, sh) & 63u;
 }
 
+__device__ __forceinline__ float half_bits(u32 b) { return (float)__builtin_bit_cast(_Float16, (unsigned short)b); }
+
 // tile -> (expert, first pair in the expert's group); -1 if past the last tile
-__device__ __forceinline__ int find_tile(const int32_t* __restrict__ tile_off, int E, int tile, int* m0) {
+__device__ __forceinline__ int find_tile(const int32_t* __restrict__ tile_off, int E, int tile, int mt, int* m0) {
   if (tile >= tile_off[E]) return -1;
   int lo = 0, hi = E;            // tile_off[lo] <= tile < tile_off[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (tile_off[mid] <= tile) lo = mid; else hi = mid;
   }
-  *m0 = (tile - tile_off[lo]) * MT;
+  *m0 = (tile - tile_off[lo]) * mt;
   return lo;
 }
 
-// B fragment of one sub-block for this lane: its 8 codes (4 bytes) times the
-// sub-block scale, as fp16, in nibble-unpack order (0,4,1,5,2,6,3,7).
-// 0x6400|q is 1024+q exactly; subtracting 1024 and multiplying by sc <= 63
-// stay exact (q*sc <= 945).
-__device__ __forceinline__ half8 codes_times_scale(u32 c4, u32 sc) {
-  const u32 M = 0x000F000Fu, B = 0x64006400u;
+// Work unit of a workgroup: units are dealt so that each XCD (workgroup i
+// runs on XCD i % 8) gets a contiguous run of (feature block, tile) units,
+// tiles fastest: consecutive tiles of one expert's feature block share the
+// XCD's L2.
+__device__ __forceinline__ void unit_of_block(int ntiles, int* tile, int* fb) {
+  const int per = gridDim.x >> 3;
+  const int u = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  *tile = u % ntiles;
+  *fb = u / ntiles;
+}
+
+// Per-sub-block dequantization constants (a, -b) as fp16 pairs:
+// weight = a*q - b with a = d*sc, b = dmin*m (products exact in fp32, then
+// rounded to fp16). The 6-bit fields sit at bit 6*sb (scales) and 48 + 6*sb
+// (mins) of header dwords 1..3, read with one 64-bit shift each.
+struct SubScale { half2 a2, nb2; };
+__device__ __forceinline__ SubScale sub_scale(const u32x4& h, int sb) {
+  const float d = half_bits(h.x & 0xFFFFu), dmin = half_bits(h.x >> 16);
+  const unsigned long long lo = (unsigned long long)h.y | ((unsigned long long)h.z << 32);
+  const unsigned long long hi = (unsigned long long)h.z | ((unsigned long long)h.w << 32);
+  const u32 sc = (u32)(lo >> (6 * sb)) & 63u;
+  const u32 m = (u32)(hi >> (16 + 6 * sb)) & 63u;
+  const _Float16 a = (_Float16)(d * (float)sc);
+  const _Float16 nb = (_Float16)(-(dmin * (float)m));
+  return {half2{a, a}, half2{nb, nb}};
+}
+
+// The 8 weights of one code dword in unpack order (0,2,4,6,1,3,5,7): the low
+// and high nibbles of the 4 bytes are split into bytes, and each pair of
+// bytes becomes two fp16 values 0x64qq = 1024 + q with one byte permute
+// against a register of 0x64 bytes; 1024 is then removed exactly and one
+// packed fma applies the sub-block's (a, -b).
+__device__ __forceinline__ half8 dequant8(u32 v, const SubScale& s) {
+  const u32 K64 = 0x64646464u;
+  const u32 lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;   // bytes: e0 e2 e4 e6 / e1 e3 e5 e7
+  const u32 p[4] = {__builtin_amdgcn_perm(K64, lo, 0x04010400u), __builtin_amdgcn_perm(K64, lo, 0x04030402u),
+                    __builtin_amdgcn_perm(K64, hi, 0x04010400u), __builtin_amdgcn_perm(K64, hi, 0x04030402u)};
   const half2 bias = {(_Float16)1024.0f, (_Float16)1024.0f};
-  const half2 s2 = {(_Float16)(float)sc, (_Float16)(float)sc};
   half8 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32 p = ((c4 >> (4 * i)) & M) | B;
-    const half2 v = (__builtin_bit_cast(half2, p) - bias) * s2;
-    r[2 * i] = v[0];
-    r[2 * i + 1] = v[1];
+    const half2 q = __builtin_bit_cast(half2, p[i]) - bias;   // exact
+    const half2 w = __builtin_elementwise_fma(q, s.a2, s.nb2);
+    r[2 * i] = w[0];
+    r[2 * i + 1] = w[1];
   }
   return r;
 }
 
-// Activation slice staging: thread -> (row i = tid/4, 64 columns).
-// Loaded values are held in registers between the load and the LDS write so
-// the next slice's loads overlap the current slice's MFMAs.
-struct StageRegs {
-  u32x4 v[8];
-};
+// Position of element e (0..7) of an 8-group in unpack order.
+__device__ __forceinline__ int nib_pos(int e) { return (e >> 1) + 4 * (e & 1); }
 
-template <bool SRC_BF16>
+// Staging of one 128-wide K half of the A tile (MT rows): thread -> chunks of
+// 8 values (16 bytes), chunk c = tid + 256*q: row c/16, columns 8*(c%16).
+template <int MT>
+struct StageRegs { u32x4 v[MT / 16]; };
+
+template <int MT, bool SRC_BF16>
 __device__ __forceinline__ void stage_load(const void* __restrict__ src, const int* __restrict__ row_index, int rows,
-                                           int ld, int k0, StageRegs& r) {
-  const int tid = threadIdx.x;
-  const int i = tid >> 2, q = tid & 3;
-  const bool ok = i < rows;
+                                           int ld, int k0, StageRegs<MT>& r) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    r.v[c] = u32x4{0u, 0u, 0u, 0u};
-    if (ok) {
-      const size_t off = (size_t)row_index[i] * ld + k0 + 64 * q + 8 * c;
-      r.v[c] = SRC_BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + off)
+  for (int q = 0; q < MT / 16; ++q) {
+    const int c = (int)threadIdx.x + BLOCK * q;
+    const int row = c >> 4, c8 = c & 15;
+    r.v[q] = u32x4{0u, 0u, 0u, 0u};
+    if (row < rows) {
+      const size_t off = (size_t)row_index[row] * ld + k0 + 8 * c8;
+      r.v[q] = SRC_BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + off)
                         : *reinterpret_cast<const u32x4*>(static_cast<const _Float16*>(src) + off);
     }
   }
 }
 
-// Write the staged slice as fp16 in nibble order and the per-row sub-block
-// sums (fp16 hi + lo) of sub-blocks 2q, 2q+1.
-template <bool SRC_BF16>
-__device__ __forceinline__ void stage_store(const StageRegs& r, _Float16* xs, _Float16* shi, _Float16* slo) {
-  const int tid = threadIdx.x;
-  const int i = tid >> 2, q = tid & 3;
-  float s0 = 0.f, s1 = 0.f;
+// bf16 sources are converted to fp16 (exact for normal values; the
+// round-toward-zero conversion only matters below 2^-14 or above 65504) and
+// permuted into unpack order; fp16 sources (h) are already in that order.
+template <int MT, bool SRC_BF16>
+__device__ __forceinline__ void stage_store(const StageRegs<MT>& r, _Float16* a) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const u32 w[4] = {r.v[c].x, r.v[c].y, r.v[c].z, r.v[c].w};
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (SRC_BF16) { f[2 * e] = bf16_to_f32(w[e] & 0xFFFFu); f[2 * e + 1] = bf16_to_f32(w[e] >> 16); }
-      else { f[2 * e] = half_bits(w[e] & 0xFFFFu); f[2 * e + 1] = half_bits(w[e] >> 16); }
+  for (int q = 0; q < MT / 16; ++q) {
+    const int c = (int)threadIdx.x + BLOCK * q;
+    const int row = c >> 4, c8 = c & 15;
+    u32x4 o = r.v[q];
+    if (SRC_BF16) {
+      const u32 w0 = r.v[q].x, w1 = r.v[q].y, w2 = r.v[q].z, w3 = r.v[q].w;   // (e0,e1) (e2,e3) (e4,e5) (e6,e7)
+      auto lo = [](u32 w) { return __builtin_bit_cast(float, w << 16); };
+      auto hi = [](u32 w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); };
+      o.x = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_pkrtz(lo(w0), lo(w1)));   // (e0, e2)
+      o.y = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_pkrtz(lo(w2), lo(w3)));   // (e4, e6)
+      o.z = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_pkrtz(hi(w0), hi(w1)));   // (e1, e3)
+      o.w = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_pkrtz(hi(w2), hi(w3)));   // (e5, e7)
     }
-    half8 hv;
-    // nibble order: 0,4,1,5,2,6,3,7
-    hv[0] = (_Float16)f[0]; hv[1] = (_Float16)f[4]; hv[2] = (_Float16)f[1]; hv[3] = (_Float16)f[5];
-    hv[4] = (_Float16)f[2]; hv[5] = (_Float16)f[6]; hv[6] = (_Float16)f[3]; hv[7] = (_Float16)f[7];
-    *reinterpret_cast<half8*>(xs + i * XS + 64 * q + 8 * c) = hv;
-    const float part = ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
-    if (c < 4) s0 += part; else s1 += part;
+    *reinterpret_cast<u32x4*>(a + row * XS + 8 * c8) = o;
   }
-  const _Float16 h0 = (_Float16)s0, h1 = (_Float16)s1;
-  shi[i * 8 + 2 * q] = h0;
-  slo[i * 8 + 2 * q] = (_Float16)(s0 - (float)h0);
-  shi[i * 8 + 2 * q + 1] = h1;
-  slo[i * 8 + 2 * q + 1] = (_Float16)(s1 - (float)h1);
 }
 
-struct SliceSmem {
-  _Float16 x[MT * XS];
-  _Float16 shi[MT * 8];
-  _Float16 slo[MT * 8];
-};
+// One lane's weights for one super-block: the four 16-byte code chunks at
+// 32j + 16kg (j = 0..3) of its row, i.e. sub-blocks 2j + kg. The four loads
+// of a row's 128-byte line leave together, so the line is fetched from HBM
+// once; ordinary (cached) loads, since each instruction covers 32 bytes of
+// 32 different rows.
+struct SbCodes { u32x4 c[4]; };
 
-// Weights of one lane's row for one super-block: the lane's 4 code bytes of
-// each of the 8 sub-blocks and the 16-byte header.
-struct WRegs {
-  u32 c4[8];
-  u32x4 hd;
-};
-
-__device__ __forceinline__ void load_w(const uint8_t* __restrict__ row, int codes_bytes, int b, int kg, WRegs& w) {
+__device__ __forceinline__ void load_sb(const uint8_t* __restrict__ row, int b, int kg, SbCodes& w) {
+  const uint8_t* p = row + (size_t)b * QCODES + 16 * kg;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) w.c4[s] = *reinterpret_cast<const u32*>(row + (size_t)b * QCODES + 16 * s + 4 * kg);
-  w.hd = *reinterpret_cast<const u32x4*>(row + codes_bytes + (size_t)b * QHDR);
+  for (int j = 0; j < 4; ++j) w.c[j] = *reinterpret_cast<const u32x4*>(p + 32 * j);
 }
 
-// NM weight matrices (row pointers per lane) x the staged slice: accumulate
-// one super-block into tot[m][r] (lane: rows 16r + 4*(l/16) + i, column l%16).
-template <int NM>
-__device__ __forceinline__ void slice_mfma(const SliceSmem& sm, const WRegs* w, f32x4 (*tot)[4]) {
+// Grouped GEMM core: MT x (NN*32) outputs per wave over K, NN weight rows
+// per lane (rowp[n] = start of the lane's row in column block n, header
+// offset hdr_off[n] from that start). The weights of super-block b + 1 are
+// requested when super-block b starts; activations are staged half a
+// super-block at a time through a double-buffered LDS tile, the next half
+// requested before the current one is multiplied.
+template <int WR, bool SRC_BF16>
+__device__ __forceinline__ void tile_gemm(const uint8_t* const* rowp, const int* hdr_off, int K, const void* __restrict__ src,
+                                          const int* __restrict__ row_index, int rows, int ld, _Float16 (*a)[32 * WR * XS],
+                                          f32x16 (*acc)[NN]) {
+  constexpr int MT = 32 * WR;
   const int lane = threadIdx.x & (WAVE - 1);
-  const int j = lane & 15, kg = lane >> 4;
-  f32x4 acc[NM][4];
+  const int i = lane & 31, kg = lane >> 5;
 #pragma unroll
-  for (int m = 0; m < NM; ++m)
+  for (int r = 0; r < WR; ++r)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[m][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NN; ++n)
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    half8 bf[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) bf[m] = codes_times_scale(w[m].c4[s], field6(w[m].hd, 6 * s));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const half8 af = *reinterpret_cast<const half8*>(sm.x + (16 * r + j) * XS + 32 * s + 8 * kg);
-#pragma unroll
-      for (int m = 0; m < NM; ++m) acc[m][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[m], acc[m][r], 0, 0, 0);
-    }
-  }
-  // min term: A' = [sum_hi(8) | sum_lo(8) | 0], B' = [m(8) | m(8) | 0]
-  half8 am[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (kg < 2) am[r] = *reinterpret_cast<const half8*>((kg == 0 ? sm.shi : sm.slo) + (16 * r + j) * 8);
-    else am[r] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    half8 bm;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) bm[s] = kg < 2 ? (_Float16)(float)field6(w[m].hd, 48 + 6 * s) : (_Float16)0.f;
-    const float d = half_bits(w[m].hd.x & 0xFFFFu), dmin = half_bits(w[m].hd.x >> 16);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const f32x4 mt = __builtin_amdgcn_mfma_f32_16x16x32_f16(am[r], bm, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tot[m][r][i] += d * acc[m][r][i] - dmin * mt[i];
-    }
-  }
-}
-
-// Pipelined K loop over super-blocks for NM weight matrices.
-template <bool SRC_BF16, int NM>
-__device__ __forceinline__ void tile_gemm(const uint8_t* const* rows, const int* codes_bytes, int K,
-                                          const void* __restrict__ src, const int* __restrict__ row_index, int rows_n,
-                                          int ld, SliceSmem* sm, f32x4 (*tot)[4]) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int kg = lane >> 4;
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) tot[m][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < 16; ++q) acc[r][n][q] = 0.f;
   const int nb = K / QK;
-  StageRegs st;
-  WRegs w[NM], wn[NM];
-  stage_load<SRC_BF16>(src, row_index, rows_n, ld, 0, st);
+  SbCodes w[NN], wn[NN];
+  u32x4 hd[NN], hdn[NN];
+  StageRegs<MT> st;
 #pragma unroll
-  for (int m = 0; m < NM; ++m) load_w(rows[m], codes_bytes[m], 0, kg, w[m]);
-  stage_store<SRC_BF16>(st, sm[0].x, sm[0].shi, sm[0].slo);
+  for (int n = 0; n < NN; ++n) {
+    load_sb(rowp[n], 0, kg, w[n]);
+    hd[n] = *reinterpret_cast<const u32x4*>(rowp[n] + hdr_off[n]);
+  }
+  stage_load<MT, SRC_BF16>(src, row_index, rows, ld, 0, st);
+  stage_store<MT, SRC_BF16>(st, a[0]);
   for (int b = 0; b < nb; ++b) {
-    __syncthreads();                                   // slice b is in sm[b & 1]
-    const bool more = b + 1 < nb;
-    if (more) {
-      stage_load<SRC_BF16>(src, row_index, rows_n, ld, (b + 1) * QK, st);
+    if (b + 1 < nb) {
 #pragma unroll
-      for (int m = 0; m < NM; ++m) load_w(rows[m], codes_bytes[m], b + 1, kg, wn[m]);
+      for (int n = 0; n < NN; ++n) {
+        load_sb(rowp[n], b + 1, kg, wn[n]);
+        hdn[n] = *reinterpret_cast<const u32x4*>(rowp[n] + hdr_off[n] + (size_t)(b + 1) * QHDR);
+      }
     }
-    slice_mfma<NM>(sm[b & 1], w, tot);
-    if (more) {
-      stage_store<SRC_BF16>(st, sm[(b + 1) & 1].x, sm[(b + 1) & 1].shi, sm[(b + 1) & 1].slo);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) w[m] = wn[m];
+    for (int hs = 0; hs < 2; ++hs) {
+      const int s = 2 * b + hs;
+      __syncthreads();                                 // half s is in a[s & 1]
+      const bool more = s + 1 < 2 * nb;
+      if (more) stage_load<MT, SRC_BF16>(src, row_index, rows, ld, (s + 1) * KH, st);
+      const _Float16* as = a[s & 1];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * hs + jj;
+        const int sb = 2 * j + kg;                     // sub-block of this lane's chunk
+        SubScale sc[NN];
+#pragma unroll
+        for (int n = 0; n < NN; ++n) sc[n] = sub_scale(hd[n], sb);
+#pragma unroll
+        for (int wq = 0; wq < 4; ++wq) {
+          half8 bf[NN];
+#pragma unroll
+          for (int n = 0; n < NN; ++n) {
+            const u32x4& c = w[n].c[j];
+            const u32 dw = wq == 0 ? c.x : (wq == 1 ? c.y : (wq == 2 ? c.z : c.w));
+            bf[n] = dequant8(dw, sc[n]);
+          }
+          const int col = 64 * jj + 32 * kg + 8 * wq;
+#pragma unroll
+          for (int r = 0; r < WR; ++r) {
+            const half8 af = *reinterpret_cast<const half8*>(as + (32 * r + i) * XS + col);
+#pragma unroll
+            for (int n = 0; n < NN; ++n) acc[r][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[n], acc[r][n], 0, 0, 0);
+          }
+        }
+      }
+      if (more) stage_store<MT, SRC_BF16>(st, a[(s + 1) & 1]);
     }
+#pragma unroll
+    for (int n = 0; n < NN; ++n) { w[n] = wn[n]; hd[n] = hdn[n]; }
   }
 }
+
+template <int WR>
+struct Smem {
+  _Float16 a[2][32 * WR * XS];
+  int rowidx[32 * WR];
+};
 
 // ------------------------------------------------------------------ gate/up + SiLU
-// Work item: blockIdx.x = tile * nnb + nb (nb fastest, so workgroups reading
-// the same weights cycle through the same XCD). Features [64nb, 64nb+64),
-// 16 per wave; each wave computes gate and up of its features.
+// Workgroup: one tile (MT pairs of one expert) x 128 features of h; wave w
+// computes gate (column block 0) and up (column block 1) of features
+// [f0, f0 + 32), f0 = 128*fb + 32*w, and writes h in fp16 at the pairs'
+// sorted positions, in unpack order within each group of 8.
+template <int WR>
 __global__ __launch_bounds__(BLOCK, 2) void gateup_grouped_kernel(
-    const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int E, int k,
+    const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int E, int k, int ntiles,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
     const int32_t* __restrict__ tile_off, _Float16* __restrict__ h16) {
-  __shared__ SliceSmem sm[2];
-  __shared__ int rowtok[MT];
-  const int nnb = I / 64;
-  const int nb = blockIdx.x % nnb, tile = blockIdx.x / nnb;
+  constexpr int MT = 32 * WR;
+  __shared__ Smem<WR> sm;
+  int tile, fb;
+  unit_of_block(ntiles, &tile, &fb);
+  if (fb >= I / FB) return;
   int m0 = 0;
-  const int e = find_tile(tile_off, E, tile, &m0);
+  const int e = find_tile(tile_off, E, tile, MT, &m0);
   if (e < 0) return;
   const int n_e = offsets[e + 1] - offsets[e];
   const int rows = min(MT, n_e - m0);
   const int tid = threadIdx.x, wid = tid / WAVE, lane = tid & (WAVE - 1);
-  if (tid < MT) rowtok[tid] = tid < rows ? pairs[offsets[e] + m0 + tid] / k : 0;
+  if (tid < MT) sm.rowidx[tid] = tid < rows ? pairs[offsets[e] + m0 + tid] / k : 0;
   __syncthreads();
-  const int j = lane & 15, kg = lane >> 4;
-  const int f0 = 64 * nb + 16 * wid;       // first feature of this wave
+  const int f0 = FB * fb + 32 * wid;
   // row-pair record: gate codes at 0, up codes at H/2, gate headers at H, up headers at H + H/16
-  const uint8_t* rec = gu + (size_t)e * gu_expert_bytes + (size_t)(f0 + j) * rp_bytes;
-  const uint8_t* rowp[2] = {rec, rec + H / 2};
-  const int cb[2] = {H, H / 2 + H / 16};
-  f32x4 tot[2][4];
-  tile_gemm<true, 2>(rowp, cb, H, x, rowtok, rows, H, sm, tot);
+  const uint8_t* rec = gu + (size_t)e * gu_expert_bytes + (size_t)(f0 + (lane & 31)) * rp_bytes;
+  const uint8_t* rowp[NN] = {rec, rec + H / 2};
+  const int hdr[NN] = {H, H / 2 + H / 16};
+  f32x16 acc[WR][NN];
+  tile_gemm<WR, true>(rowp, hdr, H, x, sm.rowidx, rows, H, sm.a, acc);
+  const int kg = lane >> 5;
+  const int col = f0 + 8 * ((lane & 31) >> 3) + nib_pos(lane & 7);
+  const size_t pos0 = (size_t)offsets[e] + m0;
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < WR; ++r)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * r + 4 * kg + i;
+    for (int q = 0; q < 16; ++q) {
+      const int row = 32 * r + 8 * (q >> 2) + 4 * kg + (q & 3);
       if (row < rows) {
-        const float g = tot[0][r][i];
-        h16[(size_t)(offsets[e] + m0 + row) * I + f0 + j] = (_Float16)(g / (1.0f + expf(-g)) * tot[1][r][i]);
+        const float g = acc[r][0][q], u = acc[r][1][q];
+        h16[(pos0 + row) * I + col] = (_Float16)(g / (1.0f + expf(-g)) * u);
       }
     }
 }
 
 // ------------------------------------------------------------------ down
-// Work item: blockIdx.x = tile * nnb + nb; features [128nb, 128nb+128), 32
-// per wave (two 16-column MFMA blocks sharing each A fragment). Output rows
-// go to their pair index (t*k + s).
+// Workgroup: one tile x 256 output features; wave w computes features
+// [f0, f0 + 64), f0 = 256*fb + 64*w (two column blocks), rows to ypair at
+// the pair index t*k + s.
+template <int WR>
 __global__ __launch_bounds__(BLOCK, 2) void down_grouped_kernel(
-    const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I, int E,
+    const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I, int E, int ntiles,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs, const int32_t* __restrict__ tile_off,
     const _Float16* __restrict__ h16, float* __restrict__ ypair) {
-  __shared__ SliceSmem sm[2];
-  __shared__ int rowpos[MT];
+  constexpr int MT = 32 * WR;
+  __shared__ Smem<WR> sm;
   __shared__ int rowpair[MT];
-  const int nnb = H / 128;
-  const int nb = blockIdx.x % nnb, tile = blockIdx.x / nnb;
+  int tile, fb;
+  unit_of_block(ntiles, &tile, &fb);
+  if (fb >= H / FD) return;
   int m0 = 0;
-  const int e = find_tile(tile_off, E, tile, &m0);
+  const int e = find_tile(tile_off, E, tile, MT, &m0);
   if (e < 0) return;
   const int n_e = offsets[e + 1] - offsets[e];
   const int rows = min(MT, n_e - m0);
   const int tid = threadIdx.x, wid = tid / WAVE, lane = tid & (WAVE - 1);
   if (tid < MT) {
-    rowpos[tid] = tid < rows ? offsets[e] + m0 + tid : 0;     // row of h16 (sorted order)
+    sm.rowidx[tid] = tid < rows ? offsets[e] + m0 + tid : 0;     // row of h16 (sorted order)
     rowpair[tid] = tid < rows ? pairs[offsets[e] + m0 + tid] : 0;
   }
   __syncthreads();
-  const int j = lane & 15, kg = lane >> 4;
-  const int f0 = 128 * nb + 32 * wid;
+  const int f0 = FD * fb + 64 * wid;
   const uint8_t* base = dn + (size_t)e * dn_expert_bytes;
-  const uint8_t* rowp[2] = {base + (size_t)(f0 + j) * drow_bytes, base + (size_t)(f0 + 16 + j) * drow_bytes};
-  const int cb[2] = {I / 2, I / 2};
-  f32x4 tot[2][4];
-  tile_gemm<false, 2>(rowp, cb, I, h16, rowpos, rows, I, sm, tot);
+  const uint8_t* rowp[NN] = {base + (size_t)(f0 + (lane & 31)) * drow_bytes,
+                             base + (size_t)(f0 + 32 + (lane & 31)) * drow_bytes};
+  const int hdr[NN] = {I / 2, I / 2};
+  f32x16 acc[WR][NN];
+  tile_gemm<WR, false>(rowp, hdr, I, h16, sm.rowidx, rows, I, sm.a, acc);
+  const int kg = lane >> 5;
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int r = 0; r < WR; ++r)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int n = 0; n < NN; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * r + 4 * kg + i;
-        if (row < rows) ypair[(size_t)rowpair[row] * H + f0 + 16 * m + j] = tot[m][r][i];
+      for (int q = 0; q < 16; ++q) {
+        const int row = 32 * r + 8 * (q >> 2) + 4 * kg + (q & 3);
+        if (row < rows) ypair[(size_t)rowpair[row] * H + f0 + 32 * n + (lane & 31)] = acc[r][n][q];
       }
 }
 
@@ -333,22 +364,38 @@ __global__ __launch_bounds__(BLOCK) void combine_kernel(const float* __restrict_
   *reinterpret_cast<float4*>(out + (size_t)t * H + 4 * c) = acc;
 }
 
+template <int WR>
+static hipError_t launch_wr(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* offsets,
+                            const int32_t* pairs, const int32_t* tile_off, _Float16* h16, float* ypair, int T,
+                            hipStream_t s) {
+  const int tiles = grouped_max_tiles(d, T);
+  const int gu_units = tiles * (d.I / FB), dn_units = tiles * (d.H / FD);
+  // grids padded to a multiple of 8 (the unit dealing assumes it); extra blocks exit
+  hipLaunchKernelGGL((gateup_grouped_kernel<WR>), dim3((gu_units + 7) / 8 * 8), dim3(BLOCK), 0, s, layer + d.gu_off,
+                     d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, tiles, x, offsets, pairs, tile_off, h16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((down_grouped_kernel<WR>), dim3((dn_units + 7) / 8 * 8), dim3(BLOCK), 0, s, layer + d.dn_off,
+                     d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.E, tiles, offsets, pairs, tile_off, h16, ypair);
+  return hipGetLastError();
+}
+
 }  // namespace grouped
 
-int grouped_max_tiles(const Layout& d, int T) { return (T * d.k + grouped::MT - 1) / grouped::MT + d.E; }
+int grouped_mt(const Layout& d, int T) { return (long long)T * d.k >= 64LL * d.E ? 96 : 32; }
+
+int grouped_max_tiles(const Layout& d, int T) {
+  const int mt = grouped_mt(d, T);
+  return (T * d.k + mt - 1) / mt + d.E;
+}
 
 hipError_t launch_grouped_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
                               const int32_t* offsets, const int32_t* pairs, const int32_t* tile_off, _Float16* h16,
                               float* ypair, float* out, int T, hipStream_t s) {
   using namespace grouped;
-  const int tiles = grouped_max_tiles(d, T);
-  hipLaunchKernelGGL(gateup_grouped_kernel, dim3(tiles * (d.I / 64)), dim3(BLOCK), 0, s, layer + d.gu_off,
-                     d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, offsets, pairs, tile_off, h16);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(down_grouped_kernel, dim3(tiles * (d.H / 128)), dim3(BLOCK), 0, s, layer + d.dn_off,
-                     d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.E, offsets, pairs, tile_off, h16, ypair);
-  e = hipGetLastError();
+  if (d.I % FB || d.H % FD) return hipErrorInvalidValue;
+  const hipError_t e = grouped_mt(d, T) == 96 ? launch_wr<3>(d, layer, x, offsets, pairs, tile_off, h16, ypair, T, s)
+                                               : launch_wr<1>(d, layer, x, offsets, pairs, tile_off, h16, ypair, T, s);
   if (e != hipSuccess) return e;
   const int n4 = T * (d.H / 4);
   hipLaunchKernelGGL(combine_kernel, dim3((n4 + BLOCK - 1) / BLOCK), dim3(BLOCK), 0, s, ypair, w, out, d.H, d.k, T);

@@ -103,7 +103,7 @@ hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts,
 hipError_t launch_tile_offsets(const Layout& d, const int32_t* offsets, int32_t* tile_off, int mt, hipStream_t s);
 
 // grouped MFMA path (T > 1)
-constexpr int GROUPED_MT = 64;
+int grouped_mt(const Layout& d, int T);          // pairs per tile of the grouped GEMMs for a T-token call
 int grouped_max_tiles(const Layout& d, int T);
 hipError_t launch_grouped_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
                               const int32_t* offsets, const int32_t* pairs, const int32_t* tile_off, _Float16* h16,
