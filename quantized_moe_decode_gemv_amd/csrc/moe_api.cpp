@@ -191,7 +191,7 @@ static const uint8_t* layer_ptr(const moe_plan* plan, const void* blob, int32_t 
 
 // Path choice by the host-known token count: the per-token GEMV streams every
 // routed expert once per token, the grouped MFMA path once per batch.
-constexpr int32_t GROUPED_MIN_TOKENS = 8;
+constexpr int32_t GROUPED_MIN_TOKENS = 16;   // measured crossover: between 8 and 32 tokens
 static bool use_grouped(const moe_plan* plan, int32_t T) {
   if (T < 2 || (plan->d.flags & MOE_FLAG_FORCE_GEMV)) return false;
   if (plan->d.flags & MOE_FLAG_FORCE_GROUPED) return true;

@@ -180,7 +180,7 @@ def test_zipf_skewed_prefill_4096_grouped(qwen):
 
 
 def test_forward_batched_auto_grouped_tiny(tiny):
-    """moe_forward with T >= 8 takes the grouped path on its own (router GEMV,
+    """moe_forward with T >= 16 takes the grouped path on its own (router GEMV,
     top-k, dispatch, grouped GEMMs, combine) and keeps the norm epilogue."""
     S = tiny.shape
     xb = synth.x_bf16(S, 9, 40, T=40)
