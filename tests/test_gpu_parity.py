@@ -193,6 +193,15 @@ def test_forward_batched_auto_grouped_tiny(tiny):
         check_bf16_vector(got["xn"][t], ref_next)
 
 
+def test_forward_auto_path_boundary_qwen(qwen):
+    """Without flags moe_forward runs the per-token GEMV path below 16 tokens
+    and the grouped path from 16 on: both sides of the switch against the
+    oracle."""
+    for T in (15, 16):
+        xb = synth.x_bf16(qwen.shape, 10, T, T=T)
+        _check_layer(qwen, xb, qwen.forward(xb))
+
+
 # ------------------------------------------------------------------ routing and dispatch lists
 @pytest.mark.parametrize("T,zipf", [(8, None), (128, None), (4096, 1.1)])
 def test_route_from_logits_and_dispatch_lists(qwen, T, zipf):
