@@ -132,6 +132,17 @@ def main():
     gbps = expert_bytes_per_token * tok_s / 1e9
     log(f"decode: {ms_per_step * 1e3:.1f} us/step, {tok_s:.1f} tok/s, expert bytes {gbps:.0f} GB/s")
     finite = bool(torch.isfinite(ys).all().item())
+    # spread of single steps (after the timed region, each replay between its own events)
+    step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(64)]
+    for a, b in step_evs:
+        a.record(stream)
+        graph.launch(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    st_us = np.array([a.elapsed_time(b) * 1e3 for a, b in step_evs])
+    step_pct = {"p10_us": round(float(np.percentile(st_us, 10)), 1), "p50_us": round(float(np.percentile(st_us, 50)), 1),
+                "p90_us": round(float(np.percentile(st_us, 90)), 1), "replays": len(st_us)}
+    log(f"single steps: {step_pct}")
 
     # ------------------------------------------------------------ dominant kernel (gate/up GEMV)
     # same launches as the decode step, with HIP events around the gate/up
@@ -153,6 +164,9 @@ def main():
     gu_gbps = gu_bytes / (gu_us * 1e-6) / 1e9
     log(f"gate/up kernel: {gu_us:.2f} us avg over {len(times)} launches, {gu_gbps:.0f} GB/s")
 
+    single = single_layer_measurements(S, blob, L, dev, stream, q, np, torch, synth)
+    log(f"single layer calls: {json.dumps(single)}")
+
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "gateup_kernel_traffic.json")
     if os.path.exists(tpath):
@@ -173,6 +187,8 @@ def main():
         cpu, parity = cpu_baseline(S, L, x0, step0)
         log(f"cpu oracle: {cpu}")
         log(f"step-0 parity: {parity}")
+        cpu["all_cores"] = cpu_baseline_all_cores(S, L)
+        log(f"cpu oracle, all cores: {cpu['all_cores']}")
 
     result = {
         "metric": METRIC,
@@ -210,6 +226,8 @@ def main():
             "bytes_per_launch": gu_bytes,
             "avg_launch_us": round(gu_us, 3),
         },
+        "step_time": step_pct,
+        "single_layer": single,
         "cpu_baseline": cpu,
         "batched": batched,
         "parity_step0": parity,
@@ -219,6 +237,62 @@ def main():
 
 
 MFMA_FP16_PEAK_TFLOPS = 2500.0
+
+
+def _graph_us(calls, n_rot, reps, stream, torch):
+    """Capture calls(0..n_rot-1) in one CUDA graph on `stream`, replay it, and
+    return the average time per call in microseconds (HIP events on `stream`)."""
+    with torch.cuda.stream(stream):
+        calls(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for l in range(n_rot):
+                calls(l)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):          # replay() launches on the current stream
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * n_rot)
+
+
+def single_layer_measurements(S, blob, L, dev, stream, q, np, torch, synth):
+    """One token through one layer (router GEMV, top-k, gate/up, down; no
+    norm), graph-replayed: the tiny layer (hidden 256, 8 experts, top-2,
+    inter 512: 442,368 expert bytes per call) and the Qwen3-30B-A3B-shaped
+    layer rotating over 16 layers of the stack (21,233,664 expert bytes per
+    call, so no layer's experts are cache-resident from the previous call)."""
+    res = {}
+    T = synth.TINY
+    tplan = q.Plan(T.hidden, T.n_experts, T.top_k, T.inter, n_layers=1, max_tokens=1)
+    tblob = torch.empty(tplan.blob_bytes(), dtype=torch.uint8, device=dev)
+    tblob[: tplan.header_bytes()].copy_(torch.from_numpy(tplan.pack_header()))
+    host = np.empty(tplan.layer_bytes(), dtype=np.uint8)
+    tplan.pack_layer(synth.layer_experts(T, 0, synth.GATE), synth.layer_experts(T, 0, synth.UP),
+                     synth.layer_experts(T, 0, synth.DOWN), synth.router(T, 0), out=host)
+    off = tplan.layer_offset(0)
+    tblob[off:off + tplan.layer_bytes()].copy_(torch.from_numpy(host))
+    tscr = tplan.new_scratch(1, device=dev)
+    tx = torch.from_numpy(synth.x_bf16(T, 0, 0).view(np.int16)).to(dev)
+    ty = torch.empty(1, T.hidden, dtype=torch.float32, device=dev)
+    us = _graph_us(lambda l: tplan.forward(tblob, 0, tx, 1, ty, scratch=tscr, stream=stream), 16, 20, stream, torch)
+    res["tiny_layer"] = {"us_per_call": round(us, 2), "expert_bytes": T.top_k * T.expert_bytes}
+    plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=L, max_tokens=1)
+    scr = plan.new_scratch(1, device=dev)
+    x = torch.from_numpy(synth.x_bf16(S, 3, 1).view(np.int16)).to(dev)
+    y = torch.empty(1, S.hidden, dtype=torch.float32, device=dev)
+    n_rot = min(L, 16)
+    us = _graph_us(lambda l: plan.forward(blob, l, x, 1, y, scratch=scr, stream=stream), n_rot, 20, stream, torch)
+    eb = S.top_k * S.expert_bytes
+    res["qwen3_30b_a3b_layer"] = {"us_per_call": round(us, 2), "expert_bytes": eb,
+                                 "expert_gbps": round(eb / (us * 1e-6) / 1e9, 1)}
+    return res
 
 
 def batched_measurements(S, blob, L, dev, stream, q, np, torch, synth):
@@ -269,11 +343,17 @@ def batched_measurements(S, blob, L, dev, stream, q, np, torch, synth):
             e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (reps * n_rot)
-        uniq = int((counts.cpu().numpy() > 0).sum())
+        cnt = counts.cpu().numpy()
+        uniq = int((cnt > 0).sum())
         ubytes = uniq * S.expert_bytes
         flops = 2.0 * T * k * 3 * S.hidden * S.inter
-        return {"us": round(us, 2), "unique_experts": uniq, "unique_expert_gbps": round(ubytes / (us * 1e-6) / 1e9, 1),
-                "tflops": round(flops / (us * 1e-6) / 1e12, 2)}
+        r = {"us": round(us, 2), "unique_experts": uniq, "unique_expert_gbps": round(ubytes / (us * 1e-6) / 1e9, 1),
+             "tflops": round(flops / (us * 1e-6) / 1e12, 2)}
+        if zipf:
+            top = np.sort(cnt)[::-1]
+            r["expert_pairs"] = {"largest": [int(v) for v in top[:8]], "experts_ge_88": int((cnt >= 88).sum()),
+                                 "empty": int((cnt == 0).sum()), "top8_share": round(float(top[:8].sum() / cnt.sum()), 3)}
+        return r
 
     for T in (8, 32, 128):
         res[f"T{T}"] = {"gemv": run_case(T, None, q.FLAG_FORCE_GEMV, 3),
@@ -349,6 +429,46 @@ def cpu_baseline(S, L, x0, gpu):
               "worst_rel_err": float(f"{worst:.3e}"), "x_next_bf16_differences": flips, "tolerance": tol,
               "stopped": stopped}
     return cpu, parity
+
+
+def cpu_baseline_all_cores(S, L):
+    """The same oracle, unchanged, on every usable host core at once (up to
+    16): one thread per core, each taking independent tokens (its own seeded input)
+    through layers 0-7 of the stack (router, top-k, softmax, expert FFNs,
+    weighted sum, RMSNorm; the oracle's C routines release the interpreter
+    lock). Expert blocks are generated beforehand and not timed. tok/s is the
+    number of (token, layer) items finished per second of wall time divided by
+    the stack's layer count (the items are run four times over)."""
+    import concurrent.futures as cf
+    import numpy as np
+    import oracle
+    import synth
+
+    cores = min(len(os.sched_getaffinity(0)), 16)    # the process's CPU share, at most 16 threads
+    layers = list(range(8))
+    src = oracle.ExpertSource(S, max_cached=4 * S.n_experts)
+    items = []
+    for l in layers:
+        wr = synth.router(S, l)
+        for i in range(cores):
+            x = synth.x_bf16(S, 5, i)[0]
+            rid, rw, _ = oracle.route(oracle.router_logits(wr, x), S.top_k)
+            items.append((wr, x, [src.blocks(l, e) for e in rid]))
+
+    def run(item):
+        wr, x, bl = item
+        rid, rw, _ = oracle.route(oracle.router_logits(wr, x), S.top_k)
+        y = oracle.moe_token([b[0] for b in bl], [b[1] for b in bl], [b[2] for b in bl], rw, x)
+        return oracle.resid_rmsnorm(x, y)[1]
+
+    reps = 4
+    t = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+        list(ex.map(run, items * reps))
+    wall = time.perf_counter() - t
+    return {"value": round(reps * len(items) / wall / L, 5), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} x {len(items)} (token, layer) items ({cores} independent tokens x layers 0-7), "
+                      f"{wall:.2f} s wall; tok/s = items per second / {L} layers"}
 
 
 if __name__ == "__main__":
