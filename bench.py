@@ -47,6 +47,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=4, help="passes over all layers for the kernel timing")
     ap.add_argument("--no-batched", action="store_true", help="skip the small-batch / prefill measurements")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the single-step percentiles and the single-layer calls (for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (reference kernel for hardware byte counters)")
     args = ap.parse_args()
@@ -133,16 +135,19 @@ def main():
     log(f"decode: {ms_per_step * 1e3:.1f} us/step, {tok_s:.1f} tok/s, expert bytes {gbps:.0f} GB/s")
     finite = bool(torch.isfinite(ys).all().item())
     # spread of single steps (after the timed region, each replay between its own events)
-    step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(64)]
-    for a, b in step_evs:
-        a.record(stream)
-        graph.launch(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    st_us = np.array([a.elapsed_time(b) * 1e3 for a, b in step_evs])
-    step_pct = {"p10_us": round(float(np.percentile(st_us, 10)), 1), "p50_us": round(float(np.percentile(st_us, 50)), 1),
-                "p90_us": round(float(np.percentile(st_us, 90)), 1), "replays": len(st_us)}
-    log(f"single steps: {step_pct}")
+    step_pct = None
+    if not args.no_extras:
+        step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(64)]
+        for a, b in step_evs:
+            a.record(stream)
+            graph.launch(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        st_us = np.array([a.elapsed_time(b) * 1e3 for a, b in step_evs])
+        step_pct = {"p10_us": round(float(np.percentile(st_us, 10)), 1),
+                    "p50_us": round(float(np.percentile(st_us, 50)), 1),
+                    "p90_us": round(float(np.percentile(st_us, 90)), 1), "replays": len(st_us)}
+        log(f"single steps: {step_pct}")
 
     # ------------------------------------------------------------ dominant kernel (gate/up GEMV)
     # same launches as the decode step, with HIP events around the gate/up
@@ -164,8 +169,10 @@ def main():
     gu_gbps = gu_bytes / (gu_us * 1e-6) / 1e9
     log(f"gate/up kernel: {gu_us:.2f} us avg over {len(times)} launches, {gu_gbps:.0f} GB/s")
 
-    single = single_layer_measurements(S, blob, L, dev, stream, q, np, torch, synth)
-    log(f"single layer calls: {json.dumps(single)}")
+    single = None
+    if not args.no_extras:
+        single = single_layer_measurements(S, blob, L, dev, stream, q, np, torch, synth)
+        log(f"single layer calls: {json.dumps(single)}")
 
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "gateup_kernel_traffic.json")
