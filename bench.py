@@ -32,7 +32,7 @@ def log(msg):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("moe_gemv.hip", "moe_internal.h"):
+    for f in ("moe_gemv.hip", "moe_device.h", "moe_internal.h"):
         with open(os.path.join(ROOT, "quantized_moe_decode_gemv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -303,9 +303,9 @@ def single_layer_measurements(S, blob, L, dev, stream, q, np, torch, synth):
 
 
 def batched_measurements(S, blob, L, dev, stream, q, np, torch, synth):
-    """Small-batch decode / short prefill (T = 8, 32, 128; N(0,1) logits) on
-    the per-token GEMV path and the grouped MFMA path, and the Zipf-skewed
-    4096-token chunk on the grouped path. Routing from given logits, expert
+    """Small-batch decode / short prefill (T = 2 ... 256; N(0,1) logits) on
+    the per-token GEMV path, the expert-major GEMV path and the grouped MFMA
+    path, and the Zipf-skewed 4096-token chunk on the grouped path. Routing from given logits, expert
     FFN only, each call on a different layer of the stack in turn (so a
     layer's experts are not cache-resident from the previous call); captured
     in a graph, timed with HIP events. Unique expert bytes = experts with at
@@ -362,9 +362,11 @@ def batched_measurements(S, blob, L, dev, stream, q, np, torch, synth):
                                  "empty": int((cnt == 0).sum()), "top8_share": round(float(top[:8].sum() / cnt.sum()), 3)}
         return r
 
-    for T in (8, 32, 128):
-        res[f"T{T}"] = {"gemv": run_case(T, None, q.FLAG_FORCE_GEMV, 3),
-                        "grouped": run_case(T, None, q.FLAG_FORCE_GROUPED, 3)}
+    flags = {"gemv": q.FLAG_FORCE_GEMV, "expert_gemv": q.FLAG_FORCE_EXPERT_GEMV, "grouped": q.FLAG_FORCE_GROUPED}
+    paths = {2: ("gemv", "expert_gemv"), 8: tuple(flags), 32: tuple(flags), 128: tuple(flags),
+             256: ("expert_gemv", "grouped")}
+    for T, names in paths.items():
+        res[f"T{T}"] = {name: run_case(T, None, flags[name], 3) for name in names}
     z = run_case(4096, 1.1, q.FLAG_FORCE_GROUPED, 4)
     z["mfma_util"] = round(z["tflops"] / MFMA_FP16_PEAK_TFLOPS, 4)
     res["T4096_zipf"] = z

@@ -48,12 +48,15 @@ enum moe_status {
   MOE_ERR_HIP = -5,
 };
 
-/* Routing/FFN path choice for moe_expert_ffn and moe_forward (moe_config.flags).
- * Without either flag the per-token GEMV path runs for T < 16 and the grouped
- * MFMA path for T >= 16 (the measured crossover on the Qwen3-30B-A3B-shaped
- * layer lies between 8 and 32 tokens). */
-#define MOE_FLAG_FORCE_GEMV 0x1u     /* per-token dequant-on-read GEMV for every T */
-#define MOE_FLAG_FORCE_GROUPED 0x2u  /* grouped MFMA expert GEMM for every T > 0 */
+/* Routing/FFN path choice for moe_expert_ffn and moe_forward (moe_config.flags,
+ * at most one of them). T = 1 always takes the per-token GEMV. Without a flag
+ * the choice goes by routed pairs per expert, T*top_k/n_experts: below 1/2 the
+ * per-token GEMV (each routed expert streamed once per token), up to 9/4 the
+ * expert-major GEMV (each routed expert streamed once, its tokens held in
+ * registers; needs inter <= 2048), beyond that the grouped MFMA GEMMs. */
+#define MOE_FLAG_FORCE_GEMV 0x1u         /* per-token dequant-on-read GEMV for every T */
+#define MOE_FLAG_FORCE_GROUPED 0x2u      /* grouped MFMA expert GEMM for every T >= 2 */
+#define MOE_FLAG_FORCE_EXPERT_GEMV 0x4u  /* expert-major GEMV for every T >= 2; needs inter <= 2048 */
 
 typedef struct moe_config {
   int32_t hidden;      /* H: multiple of 256; 256, 512, 1024 or a multiple of 2048 up to 8192 */
@@ -124,10 +127,10 @@ int moe_route(const moe_plan* plan, const void* blob, int32_t layer, const uint1
               const float* logits, int32_t T, const moe_route_out* out, void* scratch,
               size_t scratch_bytes, hipStream_t stream);
 
-/* Expert FFN and weighted sum for T tokens given routing results r (the
- * dispatch lists are required when the grouped path runs: T >= 16 without
- * MOE_FLAG_FORCE_GEMV, or any T with MOE_FLAG_FORCE_GROUPED). out: fp32
- * [T][hidden]. */
+/* Expert FFN and weighted sum for T tokens given routing results r. The
+ * batched paths read the dispatch lists (r->offsets, r->pairs); without them
+ * the per-token GEMV path runs, unless a batched path is forced, which is
+ * then an invalid argument. out: fp32 [T][hidden]. */
 int moe_expert_ffn(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16,
                    int32_t T, const moe_route_out* r, float* out, void* scratch, size_t scratch_bytes,
                    hipStream_t stream);

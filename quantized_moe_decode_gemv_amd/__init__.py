@@ -12,7 +12,7 @@ import numpy as np
 
 __all__ = [
     "MoeError", "Config", "RouteOut", "Plan", "load", "is_supported", "status_string",
-    "FLAG_FORCE_GEMV", "FLAG_FORCE_GROUPED", "LIB_PATH",
+    "FLAG_FORCE_GEMV", "FLAG_FORCE_GROUPED", "FLAG_FORCE_EXPERT_GEMV", "LIB_PATH",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libqmoe.so")
 
 FLAG_FORCE_GEMV = 0x1
 FLAG_FORCE_GROUPED = 0x2
+FLAG_FORCE_EXPERT_GEMV = 0x4
 
 # Every symbol include/moe.h declares.
 EXPORTS = [

@@ -26,9 +26,11 @@ static bool cfg_ok(const moe_config* c) {
   if (!h_ok) return false;
   // down: k * inter/32 items per output row spread over at most 4 per lane
   if ((long long)k * (I / 32) > 256) return false;
-  if ((c->flags & (MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GROUPED)) == (MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GROUPED))
-    return false;
-  if (c->flags & ~(MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GROUPED)) return false;
+  const uint32_t force = c->flags & (MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_EXPERT_GEMV);
+  if (c->flags & ~force) return false;
+  if (force & (force - 1)) return false;          // at most one path may be forced
+  // expert-major GEMV: one 32-code sub-block of a down row per lane of a wave
+  if ((force & MOE_FLAG_FORCE_EXPERT_GEMV) && I > 2048) return false;
   return true;
 }
 
@@ -189,27 +191,53 @@ static const uint8_t* layer_ptr(const moe_plan* plan, const void* blob, int32_t 
   return static_cast<const uint8_t*>(blob) + HEADER_BYTES + (size_t)layer * plan->d.layer_bytes;
 }
 
-// Path choice by the host-known token count: the per-token GEMV streams every
-// routed expert once per token, the grouped MFMA path once per batch.
-constexpr int32_t GROUPED_MIN_TOKENS = 16;   // measured crossover: between 8 and 32 tokens
-static bool use_grouped(const moe_plan* plan, int32_t T) {
-  if (T < 2 || (plan->d.flags & MOE_FLAG_FORCE_GEMV)) return false;
-  if (plan->d.flags & MOE_FLAG_FORCE_GROUPED) return true;
-  return T >= GROUPED_MIN_TOKENS;
+// Path choice by the host-known token count T. The per-token GEMV streams
+// every routed expert once per token; the expert-major GEMV and the grouped
+// MFMA GEMMs stream each routed expert once per batch, the former with the
+// tokens of an expert held in registers, the latter on MFMA tiles of 32 or 96
+// pairs, which pay off once experts carry many pairs.
+// The switches are in routed pairs per expert, T*k/E (measured crossovers on
+// the Qwen3-30B-A3B-shaped layer: per-token GEMV ahead up to 6 tokens, 0.375
+// pairs per expert, the expert-major GEMV from 8 tokens, 0.5, the grouped
+// GEMMs from about 36 tokens, 2.25).
+enum class Path { Gemv, ExpertGemv, Grouped };
+static Path choose_path(const moe_plan* plan, int32_t T) {
+  const Layout& d = plan->d;
+  if (T < 2 || (d.flags & MOE_FLAG_FORCE_GEMV)) return Path::Gemv;
+  if (d.flags & MOE_FLAG_FORCE_GROUPED) return Path::Grouped;
+  if (d.flags & MOE_FLAG_FORCE_EXPERT_GEMV) return Path::ExpertGemv;
+  const long long pairs4 = 4LL * T * d.k;            // 4 * T*k, against multiples of E/4
+  if (pairs4 < 2LL * d.E) return Path::Gemv;         // T*k < E/2
+  if (egemv_supported(d) && pairs4 <= 9LL * d.E) return Path::ExpertGemv;   // T*k <= 9E/4
+  return Path::Grouped;
 }
 
-// tiles_ready: the dispatch kernel already wrote the tile offsets into scratch.
-static int grouped_impl(const moe_plan* plan, const uint8_t* L, const uint16_t* x, int32_t T, const float* w,
+// Work list of each batched path in scratch: the grouped GEMMs' tile offsets
+// or the expert-major GEMV's routed-expert records.
+struct WorkList {
+  int32_t* tile_off;
+  void* slots;
+  int mt;
+};
+static WorkList work_list(const Layout& d, Path p, int32_t T, uint8_t* scr, const Scratch& sc) {
+  if (p == Path::Grouped) return {reinterpret_cast<int32_t*>(scr + sc.tile_off), nullptr, grouped_mt(d, T)};
+  return {nullptr, scr + sc.slots, 1};
+}
+
+// lists_ready: the dispatch kernel already wrote the work list into scratch.
+static int batched_impl(const moe_plan* plan, Path path, const uint8_t* L, const uint16_t* x, int32_t T, const float* w,
                         const int32_t* offsets, const int32_t* pairs, float* out, uint8_t* scr, const Scratch& sc,
-                        hipStream_t stream, bool tiles_ready = false) {
+                        hipStream_t stream, bool lists_ready = false) {
   const Layout& d = plan->d;
-  int32_t* tile_off = reinterpret_cast<int32_t*>(scr + sc.tile_off);
-  if (!tiles_ready && launch_tile_offsets(d, offsets, tile_off, grouped_mt(d, T), stream) != hipSuccess)
+  const WorkList wl = work_list(d, path, T, scr, sc);
+  if (!lists_ready && launch_work_list(d, offsets, wl.tile_off, wl.mt, wl.slots, stream) != hipSuccess)
     return MOE_ERR_HIP;
-  if (launch_grouped_ffn(d, L, x, w, offsets, pairs, tile_off, reinterpret_cast<_Float16*>(scr + sc.h16),
-                         reinterpret_cast<float*>(scr + sc.ypair), out, T, stream) != hipSuccess)
-    return MOE_ERR_HIP;
-  return MOE_OK;
+  _Float16* h16 = reinterpret_cast<_Float16*>(scr + sc.h16);
+  float* ypair = reinterpret_cast<float*>(scr + sc.ypair);
+  const hipError_t e = path == Path::ExpertGemv
+                           ? launch_egemv_ffn(d, L, x, w, pairs, wl.slots, h16, ypair, out, T, stream)
+                           : launch_grouped_ffn(d, L, x, w, offsets, pairs, wl.tile_off, h16, ypair, out, T, stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 static int route_impl(const moe_plan* plan, const uint8_t* L, const uint16_t* x, const float* logits, int32_t T,
@@ -258,10 +286,15 @@ extern "C" int moe_expert_ffn(const moe_plan* plan, const void* blob, int32_t la
   const uint8_t* L = layer_ptr(plan, blob, layer);
   uint8_t* scr = static_cast<uint8_t*>(scratch);
   float* h = reinterpret_cast<float*>(scr + sc.h);
-  if (use_grouped(plan, T)) {
-    if (!r->offsets || !r->pairs) return MOE_ERR_INVALID_ARGUMENT;
-    return grouped_impl(plan, L, x_bf16, T, r->topk_w, r->offsets, r->pairs, out, scr, sc, stream);
+  Path path = choose_path(plan, T);
+  if (path != Path::Gemv && (!r->offsets || !r->pairs)) {
+    // without dispatch lists only the per-token path can run, and only if
+    // no batched path was forced
+    if (d.flags & (MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_EXPERT_GEMV)) return MOE_ERR_INVALID_ARGUMENT;
+    path = Path::Gemv;
   }
+  if (path != Path::Gemv)
+    return batched_impl(plan, path, L, x_bf16, T, r->topk_w, r->offsets, r->pairs, out, scr, sc, stream);
   if (launch_gateup(d, L, x_bf16, r->topk_ids, nullptr, nullptr, nullptr, h, T, false, stream) != hipSuccess)
     return MOE_ERR_HIP;
   if (launch_down(d, L, r->topk_ids, r->topk_w, h, out, T, stream) != hipSuccess) return MOE_ERR_HIP;
@@ -288,14 +321,15 @@ static int forward_impl(const moe_plan* plan, const void* blob, int32_t layer, c
   }
   const bool fused = (T == 1);
   if (!fused && launch_topk(d, lg, ids, w, T, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (use_grouped(plan, T)) {
+  const Path path = choose_path(plan, T);
+  if (path != Path::Gemv) {
     int32_t* counts = reinterpret_cast<int32_t*>(scr + sc.counts);
     int32_t* offsets = reinterpret_cast<int32_t*>(scr + sc.offsets);
     int32_t* pairs = reinterpret_cast<int32_t*>(scr + sc.pairs);
-    int32_t* tile_off = reinterpret_cast<int32_t*>(scr + sc.tile_off);
-    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream, tile_off, grouped_mt(d, T)) != hipSuccess)
+    const WorkList wl = work_list(d, path, T, scr, sc);
+    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream, wl.tile_off, wl.mt, wl.slots) != hipSuccess)
       return MOE_ERR_HIP;
-    const int st = grouped_impl(plan, L, x, T, w, offsets, pairs, out, scr, sc, stream, true);
+    const int st = batched_impl(plan, path, L, x, T, w, offsets, pairs, out, scr, sc, stream, true);
     if (st) return st;
   } else {
     if (launch_gateup(d, L, x, ids, lg, ids, w, h, T, fused, stream) != hipSuccess) return MOE_ERR_HIP;

@@ -19,171 +19,9 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
-#include "moe_internal.h"
+#include "moe_device.h"
 
 namespace qmoe {
-
-typedef unsigned int u32;
-typedef u32 u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int WAVE = 64;
-constexpr int BLOCK = 256;
-
-__device__ __forceinline__ u32x4 load_nt(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-__device__ __forceinline__ float dot2_bf16(u32 a, u32 b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float dot2_f16(u32 a, u32 b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c, false);
-}
-
-__device__ __forceinline__ float half_bits_to_float(u32 bits) {
-  return (float)__builtin_bit_cast(_Float16, (unsigned short)bits);
-}
-
-__device__ __forceinline__ float bf16_bits_to_float(u32 bits) { return __builtin_bit_cast(float, bits << 16); }
-
-// Reinterpret a 32-bit value as fp32. Takes the value (not a vector element
-// lvalue) so the cast always sees the intended component.
-__device__ __forceinline__ float as_f32(u32 v) { return __builtin_bit_cast(float, v); }
-
-// Nearest-even bf16 of a finite fp32.
-__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
-  u32 b = __builtin_bit_cast(u32, f);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
-}
-
-// Cross-lane move by a DPP pattern (all lanes of the wave active).
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float read_lane(float v, int l) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-
-// Sum over groups of W adjacent lanes (W a power of two <= 64); every lane of
-// a group ends with the same value, the group's sum. Within a row of 16
-// lanes: quad swaps (lane ^ 1, lane ^ 2), then the half-row and row mirrors,
-// each pairing a lane with one holding the other half's partial sum (a + b
-// and b + a are the same float, so all lanes agree); the four row sums are
-// then combined through scalar reads of lanes 0, 16, 32, 48. DPP moves stay
-// in the VALU instead of the LDS crossbar. Must be called with the whole
-// wave active.
-template <int W>
-__device__ __forceinline__ float group_sum(float v) {
-  if (W >= 2) v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
-  if (W >= 4) v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
-  if (W >= 8) v += dpp_mov<0x141>(v);   // row_half_mirror
-  if (W >= 16) v += dpp_mov<0x140>(v);  // row_mirror
-  if (W >= 32) {
-    const float r0 = read_lane(v, 0), r1 = read_lane(v, 16), r2 = read_lane(v, 32), r3 = read_lane(v, 48);
-    if (W == 32) v = (threadIdx.x & (WAVE - 1)) < 32 ? r0 + r1 : r2 + r3;
-    else v = (r0 + r1) + (r2 + r3);
-  }
-  return v;
-}
-
-// Six-bit field at bit position p of the 96-bit little-endian field area
-// (header dwords 1..3).
-__device__ __forceinline__ u32 field6(const u32x4& h, int p) {
-  const int idx = p >> 5, sh = p & 31;
-  const u32 lo = idx == 0 ? h.y : (idx == 1 ? h.z : h.w);
-  const u32 hi = idx == 0 ? h.z : (idx == 1 ? h.w : 0u);
-  return __builtin_amdgcn_alignbit(hi, lo, sh) & 63u;
-}
-
-// Sub-block affine of sub-block jj (0..7) of a super-block header:
-// weight = a*q - b.
-struct Affine { float a, b; };
-__device__ __forceinline__ Affine header_affine(const u32x4& h, int jj) {
-  const float d = half_bits_to_float(h.x & 0xFFFFu);
-  const float dmin = half_bits_to_float(h.x >> 16);
-  const u32 sc = field6(h, 6 * jj), m = field6(h, 48 + 6 * jj);
-  return {d * (float)sc, dmin * (float)m};   // both products exact in fp32
-}
-
-// sum_i (128 + q_i) * x_i over one 32-code sub-block, two codes per dot2.
-// X[4d+c] holds the bf16 pair matching the nibble pair extracted at shift 4c
-// from code dword d (elements 8d+c' and 8d+c'+4, see load_x_pairs).
-__device__ __forceinline__ float dot_codes_bf16(const u32x4& c, const u32* X) {
-  const u32 M = 0x000F000Fu, B = 0x43004300u;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  const u32 w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const u32 v = w[d];
-    a0 = dot2_bf16((v & M) | B, X[4 * d + 0], a0);
-    a1 = dot2_bf16(((v >> 4) & M) | B, X[4 * d + 1], a1);
-    a2 = dot2_bf16(((v >> 8) & M) | B, X[4 * d + 2], a2);
-    a3 = dot2_bf16(((v >> 12) & M) | B, X[4 * d + 3], a3);
-  }
-  return (a0 + a1) + (a2 + a3);
-}
-
-// Load the 32 bf16 activations of one sub-block and arrange them in the pair
-// order of dot_codes_bf16. Code dword d covers elements 8d..8d+7: shift 0
-// gives (8d, 8d+4), shift 4 gives (8d+1, 8d+5), shift 8 gives (8d+2, 8d+6),
-// shift 12 gives (8d+3, 8d+7). Returns sum(x) in fp32.
-__device__ __forceinline__ float load_x_pairs(const uint16_t* xs, u32* X) {
-  float s = 0.f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const u32x4 r = load16(xs + 8 * q);   // elements 8q .. 8q+7
-    X[4 * q + 0] = (r.x & 0xFFFFu) | (r.z << 16);
-    X[4 * q + 1] = (r.x >> 16) | (r.z & 0xFFFF0000u);
-    X[4 * q + 2] = (r.y & 0xFFFFu) | (r.w << 16);
-    X[4 * q + 3] = (r.y >> 16) | (r.w & 0xFFFF0000u);
-    s += (bf16_bits_to_float(r.x & 0xFFFFu) + bf16_bits_to_float(r.x >> 16)) +
-         (bf16_bits_to_float(r.y & 0xFFFFu) + bf16_bits_to_float(r.y >> 16)) +
-         (bf16_bits_to_float(r.z & 0xFFFFu) + bf16_bits_to_float(r.z >> 16)) +
-         (bf16_bits_to_float(r.w & 0xFFFFu) + bf16_bits_to_float(r.w >> 16));
-  }
-  return s;
-}
-
-// sum_i q_i * h_i over one 32-code sub-block with fp32 h (32 values).
-__device__ __forceinline__ float dot_codes_f32(const u32x4& c, const float* hv) {
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
-  const u32 w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const u32 lo = w[d] & 0x0F0F0F0Fu, hi = (w[d] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      a[(2 * b) & 3] = fmaf((float)((lo >> (8 * b)) & 0xFFu), hv[8 * d + 2 * b], a[(2 * b) & 3]);
-      a[(2 * b + 1) & 3] = fmaf((float)((hi >> (8 * b)) & 0xFFu), hv[8 * d + 2 * b + 1], a[(2 * b + 1) & 3]);
-    }
-  }
-  return (a[0] + a[1]) + (a[2] + a[3]);
-}
-
-// sum_i (1024 + q_i) * h_i over one 32-code sub-block with fp16 h, two codes
-// per v_dot2_f32_f16: fp16 0x6400|q is exactly 1024 + q, and (1024 + q) * h is
-// exact in fp32. X[4d+c] holds the fp16 pair (h[8d+c], h[8d+c+4]) matching the
-// nibble pair extracted at shift 4c from code dword d.
-__device__ __forceinline__ float dot_codes_f16(const u32x4& c, const u32* X) {
-  const u32 M = 0x000F000Fu, B = 0x64006400u;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  const u32 w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const u32 v = w[d];
-    a0 = dot2_f16((v & M) | B, X[4 * d + 0], a0);
-    a1 = dot2_f16(((v >> 4) & M) | B, X[4 * d + 1], a1);
-    a2 = dot2_f16(((v >> 8) & M) | B, X[4 * d + 2], a2);
-    a3 = dot2_f16(((v >> 12) & M) | B, X[4 * d + 3], a3);
-  }
-  return (a0 + a1) + (a2 + a3);
-}
 
 // ------------------------------------------------------------------ top-k
 // Order-preserving map fp32 -> u32 (a > b  <=>  key(a) > key(b) for non-NaN).
@@ -600,14 +438,17 @@ __device__ __forceinline__ void excl_scan256x2(int a, int b, int& ea, int& eb, i
 
 // Single block of 1024 threads (16 waves). counts[e] = #pairs routed to e,
 // offsets = exclusive scan (E+1 entries), pairs = pair indices p = t*k+s
-// ordered by (expert, p), and with tile_off != nullptr the exclusive scan of
-// ceil(counts[e] / mt) (E+1 entries: the grouped GEMMs' tile list).
+// ordered by (expert, p), and the batched paths' work list: with tile_off
+// the exclusive scan of ceil(counts[e] / mt) (E+1 entries: the grouped
+// GEMMs' tiles), with slots the routed experts' records {e, offsets[e],
+// counts[e], 0} in expert order, then zero records up to E.
 // Deterministic: ranks come from ballots, not from the order of atomics.
 constexpr int DISP_THREADS = 1024;
 constexpr int DISP_WAVES = DISP_THREADS / WAVE;
 __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
                                                                 int32_t* __restrict__ offsets, int32_t* __restrict__ pairs,
-                                                                int32_t* __restrict__ tile_off, int E, int P, int mt) {
+                                                                int32_t* __restrict__ tile_off,
+                                                                int4* __restrict__ slots, int E, int P, int mt) {
   __shared__ int cnt[DISP_WAVES][256];
   __shared__ int wsum[8];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
@@ -622,13 +463,16 @@ __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* _
   if (tid < E) {
     for (int w = 0; w < DISP_WAVES; ++w) { const int c = cnt[w][tid]; cnt[w][tid] = tot; tot += c; }
   }
-  const int tiles = tid < E ? (tot + mt - 1) / mt : 0;
+  // second scan: tiles of the grouped GEMMs, or routed experts for the slots
+  const int tiles = tid >= E ? 0 : (slots ? (tot > 0) : (tot + mt - 1) / mt);
   int ex_tot, ex_tiles, all_tot, all_tiles;
   excl_scan256x2(tid < E ? tot : 0, tiles, ex_tot, ex_tiles, all_tot, all_tiles, wsum);
   if (tid < E) {
     counts[tid] = tot;
     offsets[tid] = ex_tot;
     if (tile_off) tile_off[tid] = ex_tiles;
+    if (slots && tot > 0) slots[ex_tiles] = make_int4(tid, ex_tot, tot, 0);
+    if (slots && tid >= all_tiles) slots[tid] = make_int4(0, 0, 0, 0);
     for (int w = 0; w < DISP_WAVES; ++w) cnt[w][tid] += ex_tot;
   }
   if (tid == 0) {
@@ -773,29 +617,39 @@ hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y,
 }
 
 hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* pairs, int T,
-                           hipStream_t s, int32_t* tile_off, int mt) {
-  if (tile_off && mt < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs, tile_off, d.E,
-                     T * d.k, tile_off ? mt : 1);
+                           hipStream_t s, int32_t* tile_off, int mt, void* slots) {
+  if ((tile_off && mt < 1) || (tile_off && slots)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs, tile_off,
+                     static_cast<int4*>(slots), d.E, T * d.k, tile_off ? mt : 1);
   return hipGetLastError();
 }
 
-// tile_off[e] = number of `mt`-pair tiles of experts before e (E + 1 entries).
-// tile_off = exclusive scan of ceil((offsets[e+1] - offsets[e]) / mt), E+1
-// entries; one block of 256 threads.
-__global__ __launch_bounds__(BLOCK) void tile_offsets_kernel(const int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ tile_off, int E, int mt) {
+// The batched paths' work list from given dispatch offsets (E+1 entries),
+// as the dispatch kernel writes it: tile_off = exclusive scan of
+// ceil(count / mt) (E+1 entries), or the routed experts' slot records. One
+// block of 256 threads.
+__global__ __launch_bounds__(BLOCK) void work_list_kernel(const int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ tile_off, int4* __restrict__ slots,
+                                                         int E, int mt) {
   __shared__ int wsum[8];
   const int tid = threadIdx.x;
   const int n = tid < E ? offsets[tid + 1] - offsets[tid] : 0;
+  const int units = tid >= E ? 0 : (slots ? (n > 0) : (n + mt - 1) / mt);
   int ex, ex2, tot, tot2;
-  excl_scan256x2((n + mt - 1) / mt, 0, ex, ex2, tot, tot2, wsum);
-  if (tid < E) tile_off[tid] = ex;
-  if (tid == 0) tile_off[E] = tot;
+  excl_scan256x2(units, 0, ex, ex2, tot, tot2, wsum);
+  if (tid < E) {
+    if (tile_off) tile_off[tid] = ex;
+    if (slots && n > 0) slots[ex] = make_int4(tid, offsets[tid], n, 0);
+    if (slots && tid >= tot) slots[tid] = make_int4(0, 0, 0, 0);
+  }
+  if (tid == 0 && tile_off) tile_off[E] = tot;
 }
 
-hipError_t launch_tile_offsets(const Layout& d, const int32_t* offsets, int32_t* tile_off, int mt, hipStream_t s) {
-  hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(BLOCK), 0, s, offsets, tile_off, d.E, mt);
+hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int32_t* tile_off, int mt, void* slots,
+                            hipStream_t s) {
+  if ((!tile_off) == (!slots) || (tile_off && mt < 1)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(work_list_kernel, dim3(1), dim3(BLOCK), 0, s, offsets, tile_off, static_cast<int4*>(slots), d.E,
+                     mt);
   return hipGetLastError();
 }
 

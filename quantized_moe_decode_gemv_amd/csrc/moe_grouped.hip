@@ -397,6 +397,12 @@ hipError_t launch_grouped_ffn(const Layout& d, const uint8_t* layer, const uint1
   const hipError_t e = grouped_mt(d, T) == 96 ? launch_wr<3>(d, layer, x, offsets, pairs, tile_off, h16, ypair, T, s)
                                                : launch_wr<1>(d, layer, x, offsets, pairs, tile_off, h16, ypair, T, s);
   if (e != hipSuccess) return e;
+  return launch_combine(d, ypair, w, out, T, s);
+}
+
+hipError_t launch_combine(const Layout& d, const float* ypair, const float* w, float* out, int T, hipStream_t s) {
+  using namespace grouped;
+  if (T <= 0) return hipSuccess;
   const int n4 = T * (d.H / 4);
   hipLaunchKernelGGL(combine_kernel, dim3((n4 + BLOCK - 1) / BLOCK), dim3(BLOCK), 0, s, ypair, w, out, d.H, d.k, T);
   return hipGetLastError();

@@ -61,7 +61,7 @@ struct BlobHeader {
 
 // Scratch carve-up for T tokens (offsets 256-aligned).
 struct Scratch {
-  size_t logits, ids, w, h, counts, offsets, pairs, tile_off, h16, ypair, total;
+  size_t logits, ids, w, h, counts, offsets, pairs, tile_off, slots, h16, ypair, total;
   void init(const Layout& d, int T) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
@@ -73,7 +73,8 @@ struct Scratch {
     offsets = take((size_t)(d.E + 1) * 4);
     pairs = take((size_t)T * d.k * 4);
     tile_off = take((size_t)(d.E + 1) * 4);
-    // grouped path only (T > 1): fp16 h in expert-sorted pair order, one fp32 output row per pair
+    slots = take((size_t)d.E * 16);        // routed-expert records of the expert-major GEMV path
+    // batched paths only (T > 1): fp16 h in expert-sorted pair order, one fp32 output row per pair
     h16 = take(T > 1 ? (size_t)T * d.k * d.I * 2 : 0);
     ypair = take(T > 1 ? (size_t)T * d.k * d.H * 4 : 0);
     total = o;
@@ -98,9 +99,16 @@ hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids
                        const float* h, float* y, int T, hipStream_t s);
 hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y, uint16_t* x_next, int T,
                              hipStream_t s);
+// Batched-path work lists, written by the dispatch or, from given dispatch
+// lists, by launch_work_list: with tile_off the grouped GEMMs' tile offsets
+// (exclusive scan of ceil(counts[e] / mt), E+1 entries); with slots the
+// expert-major GEMV's records {expert, first pair, pairs} of the routed
+// experts in expert order, then {0, 0, 0} up to E records.
 hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets,
-                           int32_t* pairs, int T, hipStream_t s, int32_t* tile_off = nullptr, int mt = 1);
-hipError_t launch_tile_offsets(const Layout& d, const int32_t* offsets, int32_t* tile_off, int mt, hipStream_t s);
+                           int32_t* pairs, int T, hipStream_t s, int32_t* tile_off = nullptr, int mt = 1,
+                           void* slots = nullptr);
+hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int32_t* tile_off, int mt, void* slots,
+                            hipStream_t s);
 
 // grouped MFMA path (T > 1)
 int grouped_mt(const Layout& d, int T);          // pairs per tile of the grouped GEMMs for a T-token call
@@ -108,5 +116,13 @@ int grouped_max_tiles(const Layout& d, int T);
 hipError_t launch_grouped_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
                               const int32_t* offsets, const int32_t* pairs, const int32_t* tile_off, _Float16* h16,
                               float* ypair, float* out, int T, hipStream_t s);
+// out[t] = sum_s w[t][s] * ypair[t*k + s], slot order
+hipError_t launch_combine(const Layout& d, const float* ypair, const float* w, float* out, int T, hipStream_t s);
+
+// expert-major GEMV path (T > 1, few pairs per expert); slots from the dispatch
+bool egemv_supported(const Layout& d);
+hipError_t launch_egemv_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
+                            const int32_t* pairs, const void* slots, _Float16* h16, float* ypair, float* out,
+                            int T, hipStream_t s);
 
 }  // namespace qmoe

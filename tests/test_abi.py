@@ -40,7 +40,13 @@ def test_status_strings():
     ((256, 8, 2, 512, 1, 1, 0, 1e-6), True),
     ((2048, 128, 8, 768, 48, 1, 0, 1e-6), True),
     ((4096, 64, 4, 1024, 1, 4096, 0, 1e-6), True),
-    ((2048, 128, 8, 768, 1, 1, 3, 1e-6), False),    # both force flags
+    ((2048, 128, 8, 768, 1, 1, 3, 1e-6), False),    # two force flags
+    ((2048, 128, 8, 768, 1, 1, 5, 1e-6), False),    # two force flags
+    ((2048, 128, 8, 768, 1, 1, 6, 1e-6), False),    # two force flags
+    ((2048, 128, 8, 768, 1, 1, 4, 1e-6), True),     # expert-major GEMV forced
+    ((256, 8, 2, 2048, 1, 1, 4, 1e-6), True),       # expert-major GEMV: inter up to 2048
+    ((256, 8, 2, 2304, 1, 1, 4, 1e-6), False),      # expert-major GEMV: inter above 2048
+    ((256, 8, 2, 2304, 1, 1, 0, 1e-6), True),       # same shape without the flag
     ((2048, 128, 8, 768, 1, 1, 8, 1e-6), False),    # unknown flag
     ((300, 8, 2, 512, 1, 1, 0, 1e-6), False),       # hidden not a multiple of 256
     ((768, 8, 2, 512, 1, 1, 0, 1e-6), False),       # hidden lane mapping unsupported

@@ -63,7 +63,11 @@ def qwen(dev):
     return Setup(synth.QWEN3_30B_A3B, dev, n_layers=1, max_tokens=256)
 
 
-def _check_layer(setup, xb, got, layer=0, exact=False):
+def _check_layer(setup, xb, got, layer=0, exact=False, sample=None):
+    """Routing and output of the tokens in `sample` (default: all) against the oracle."""
+    if sample is not None:
+        xb = xb[sample]
+        got = {key: val[sample] for key, val in got.items()}
     ref = oracle.moe_layer(setup.src, layer, xb)
     exempt = check_routing(got["ids"], got["w"], ref, exact=exact)
     keep = [t for t in range(xb.shape[0]) if t not in exempt]
@@ -119,19 +123,24 @@ def _route_lists(plan, blob, lg_dev, T, S, dev, scratch):
     return ids, w, counts, offsets, pairs
 
 
+PATH_FLAGS = (("gemv", q.FLAG_FORCE_GEMV), ("expert_gemv", q.FLAG_FORCE_EXPERT_GEMV),
+              ("grouped", q.FLAG_FORCE_GROUPED))
+
+
 @pytest.mark.parametrize("T", [8, 32, 128])
-def test_small_batch_gemv_and_grouped_paths(qwen, T):
+def test_small_batch_all_paths(qwen, T):
     """Small-batch decode / short prefill on the Qwen3-30B-A3B-shaped layer:
     routing from given N(0,1) logits (shared fp32 inputs -> ids must match
-    exactly), expert FFN on both the per-token GEMV path and the grouped
-    MFMA path, each against the oracle (all tokens up to 32, else every 4th)."""
+    exactly), expert FFN on the per-token GEMV path, the expert-major GEMV
+    path and the grouped MFMA path, each against the oracle (all tokens up to
+    32, else every 4th)."""
     S = qwen.shape
     d = qwen.dev
     xb = synth.x_bf16(S, 3, T, T=T)
     lg = synth.logits_f32(S, 3, T)
     x = qwen.xdev(xb)
     outs = {}
-    for name, flag in (("gemv", q.FLAG_FORCE_GEMV), ("grouped", q.FLAG_FORCE_GROUPED)):
+    for name, flag in PATH_FLAGS:
         plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=T, flags=flag)
         scratch = plan.new_scratch(T, device=d)
         ids, w, counts, offsets, pairs = _route_lists(plan, qwen.blob, torch.from_numpy(lg).to(d), T, S, d, scratch)
@@ -146,6 +155,38 @@ def test_small_batch_gemv_and_grouped_paths(qwen, T):
         err = rel_err(gy[sample], ref["y"])
         assert err <= REL_TOL, f"{name}: {err:.3e}"
     assert rel_err(outs["grouped"][2], outs["gemv"][2]) <= REL_TOL
+    assert rel_err(outs["expert_gemv"][2], outs["gemv"][2]) <= REL_TOL
+
+
+def test_expert_gemv_skewed_routing(qwen):
+    """Expert-major GEMV with Zipf(1.1)-biased logits at T = 64: the hottest
+    experts hold far more pairs than one register chunk of tokens, so their
+    waves loop over many chunks; sampled tokens cover the hottest expert's
+    first and last pairs and a cold expert."""
+    S = qwen.shape
+    d = qwen.dev
+    T = 64
+    xb = synth.x_bf16(S, 5, T, T=T)
+    lg = synth.logits_f32(S, 5, T, zipf_s=1.1)
+    plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=T, flags=q.FLAG_FORCE_EXPERT_GEMV)
+    scratch = plan.new_scratch(T, device=d)
+    ids, w, counts, offsets, pairs = _route_lists(plan, qwen.blob, torch.from_numpy(lg).to(d), T, S, d, scratch)
+    out = torch.empty(T, S.hidden, dtype=torch.float32, device=d)
+    plan.expert_ffn(qwen.blob, 0, qwen.xdev(xb), T, ids, w, out, counts, offsets, pairs, scratch=scratch)
+    torch.cuda.synchronize()
+    cnt = counts.cpu().numpy()
+    assert cnt.max() >= 24                      # many chunks of 4 tokens for the hottest expert
+    gi = ids.cpu().numpy()
+    hot = int(np.argmax(cnt))
+    hot_tokens = np.nonzero((gi == hot).any(1))[0]
+    cold = [int(e) for e in np.nonzero(cnt == 1)[0][:2]]
+    sample = sorted(set([0, T - 1, int(hot_tokens[0]), int(hot_tokens[-1])] + list(range(0, T, 7))
+                        + [int(np.nonzero((gi == e).any(1))[0][0]) for e in cold]))
+    ref = oracle.moe_layer(qwen.src, 0, xb[sample], logits=lg[sample])
+    check_routing(gi[sample], w.cpu().numpy()[sample], ref, exact=True)
+    err = rel_err(out.cpu().numpy()[sample], ref["y"])
+    assert err <= REL_TOL, f"{err:.3e}"
+    print(f"T=64 zipf: hot expert {hot} has {cnt.max()} pairs; max|err|/max|ref| = {err:.3e}")
 
 
 def test_zipf_skewed_prefill_4096_grouped(qwen):
@@ -180,8 +221,9 @@ def test_zipf_skewed_prefill_4096_grouped(qwen):
 
 
 def test_forward_batched_auto_grouped_tiny(tiny):
-    """moe_forward with T >= 16 takes the grouped path on its own (router GEMV,
-    top-k, dispatch, grouped GEMMs, combine) and keeps the norm epilogue."""
+    """moe_forward with T*k > 8*E (40 tokens, 80 pairs over 8 experts) takes
+    the grouped path on its own (router GEMV, top-k, dispatch, grouped GEMMs,
+    combine) and keeps the norm epilogue."""
     S = tiny.shape
     xb = synth.x_bf16(S, 9, 40, T=40)
     got = tiny.forward(xb, with_next=True)
@@ -193,13 +235,15 @@ def test_forward_batched_auto_grouped_tiny(tiny):
         check_bf16_vector(got["xn"][t], ref_next)
 
 
-def test_forward_auto_path_boundary_qwen(qwen):
-    """Without flags moe_forward runs the per-token GEMV path below 16 tokens
-    and the grouped path from 16 on: both sides of the switch against the
-    oracle."""
-    for T in (15, 16):
-        xb = synth.x_bf16(qwen.shape, 10, T, T=T)
-        _check_layer(qwen, xb, qwen.forward(xb))
+@pytest.mark.parametrize("T", [1, 7, 8, 36, 37])
+def test_forward_auto_path_boundary_qwen(qwen, T):
+    """Without flags moe_forward runs the per-token GEMV path while T*k < E/2
+    (T <= 7 here), the expert-major GEMV path while T*k <= 9E/4 (T <= 36) and
+    the grouped path beyond: both sides of each switch against the oracle
+    (every 3rd token and the last above 16 tokens)."""
+    xb = synth.x_bf16(qwen.shape, 10, T, T=T)
+    sample = None if T <= 16 else sorted(set(range(0, T, 3)) | {T - 1})
+    _check_layer(qwen, xb, qwen.forward(xb), sample=sample)
 
 
 # ------------------------------------------------------------------ routing and dispatch lists
@@ -335,6 +379,8 @@ EDGE = [
     synth.Shape("h4096-e4-k2", 14, 4096, 4, 2, 512),
     synth.Shape("h2048-k3-ragged", 15, 2048, 8, 3, 768),
     synth.Shape("h2048-e256-k8", 16, 2048, 256, 8, 256),
+    synth.Shape("h8192-i256", 17, 8192, 4, 2, 256),
+    synth.Shape("h256-i2048", 18, 256, 4, 2, 2048),
 ]
 
 
@@ -347,9 +393,13 @@ def test_edge_shapes(dev, shape):
 
 
 @pytest.mark.parametrize("shape", EDGE, ids=[s.name for s in EDGE])
-def test_edge_shapes_grouped_path(dev, shape):
-    st = Setup(shape, dev, n_layers=1, max_tokens=70, flags=q.FLAG_FORCE_GROUPED)
-    for T in (2, 5, 70):          # ragged tiles: 70 tokens * k pairs over E experts
+@pytest.mark.parametrize("path", ["grouped", "expert_gemv", "gemv"])
+def test_edge_shapes_batched_paths(dev, shape, path):
+    """Each forced path on every edge shape (lane mappings of every hidden and
+    intermediate size, k = 1, k = E, many experts); 70 tokens give ragged
+    tiles and multi-chunk experts."""
+    st = Setup(shape, dev, n_layers=1, max_tokens=70, flags=dict(PATH_FLAGS)[path])
+    for T in (2, 5, 70):
         xb = synth.x_bf16(shape, 12, T, T=T)
         _check_layer(st, xb, st.forward(xb))
 
