@@ -50,12 +50,16 @@ enum moe_status {
 
 /* Routing/FFN path choice for moe_expert_ffn and moe_forward (moe_config.flags,
  * at most one of them). T = 1 always takes the per-token GEMV. Without a flag
- * the choice goes by routed pairs per expert, T*top_k/n_experts: below 1/2 the
- * per-token GEMV (each routed expert streamed once per token), up to 9/4 the
- * expert-major GEMV (each routed expert streamed once, its tokens held in
- * registers; needs inter <= 2048), beyond that the grouped MFMA GEMMs. */
+ * the choice goes by routed pairs per expert, P/E = T*top_k/n_experts: below
+ * 1/2 the per-token GEMV (each routed expert streamed once per token); up to
+ * 1 the expert-major GEMV (each routed expert streamed once, its tokens held
+ * in registers; needs inter <= 2048); beyond, the grouped MFMA GEMMs, on
+ * tiles of 16 pairs with every weight load in flight up to P/E = 12 (hidden
+ * 512, 1024 or 2048 and inter <= 1024) and on tiles of 32 or 96 pairs above.
+ * Where the 16-pair tiles do not apply, the expert-major GEMV runs up to
+ * P/E = 9/4. */
 #define MOE_FLAG_FORCE_GEMV 0x1u         /* per-token dequant-on-read GEMV for every T */
-#define MOE_FLAG_FORCE_GROUPED 0x2u      /* grouped MFMA expert GEMM for every T >= 2 */
+#define MOE_FLAG_FORCE_GROUPED 0x2u      /* grouped MFMA expert GEMMs for every T >= 2 (tile shape by P/E) */
 #define MOE_FLAG_FORCE_EXPERT_GEMV 0x4u  /* expert-major GEMV for every T >= 2; needs inter <= 2048 */
 
 typedef struct moe_config {

@@ -196,32 +196,44 @@ static const uint8_t* layer_ptr(const moe_plan* plan, const void* blob, int32_t 
 // MFMA GEMMs stream each routed expert once per batch, the former with the
 // tokens of an expert held in registers, the latter on MFMA tiles of 32 or 96
 // pairs, which pay off once experts carry many pairs.
-// The switches are in routed pairs per expert, T*k/E (measured crossovers on
-// the Qwen3-30B-A3B-shaped layer: per-token GEMV ahead up to 6 tokens, 0.375
-// pairs per expert, the expert-major GEMV from 8 tokens, 0.5, the grouped
-// GEMMs from about 36 tokens, 2.25).
-enum class Path { Gemv, ExpertGemv, Grouped };
+// The switches are in routed pairs per expert, P/E with P = T*k (measured
+// crossovers on the Qwen3-30B-A3B-shaped layer: per-token GEMV ahead up to 6
+// tokens, P/E = 0.375; expert-major GEMV from 8 tokens, 0.5, level with the
+// 16-pair MFMA tiles at 16 tokens, 1; 16-pair tiles level with 32-pair tiles
+// at 192 tokens, 12; without the 16-pair tiles the expert-major GEMV is ahead
+// of the 32-pair tiles up to about 36 tokens, 2.25).
+enum class Path { Gemv, ExpertGemv, Grouped16, Grouped };
+constexpr long long G16_MAX_PAIRS_PER_EXPERT = 12;
+// Tile shape of the grouped MFMA path: 16-pair tiles with every weight load
+// in flight while experts carry few pairs, 32- or 96-pair tiles beyond.
+static Path grouped_tiles(const Layout& d, int32_t T) {
+  if (g16_supported(d) && (long long)T * d.k <= G16_MAX_PAIRS_PER_EXPERT * d.E) return Path::Grouped16;
+  return Path::Grouped;
+}
 static Path choose_path(const moe_plan* plan, int32_t T) {
   const Layout& d = plan->d;
   if (T < 2 || (d.flags & MOE_FLAG_FORCE_GEMV)) return Path::Gemv;
-  if (d.flags & MOE_FLAG_FORCE_GROUPED) return Path::Grouped;
+  if (d.flags & MOE_FLAG_FORCE_GROUPED) return grouped_tiles(d, T);
   if (d.flags & MOE_FLAG_FORCE_EXPERT_GEMV) return Path::ExpertGemv;
-  const long long pairs4 = 4LL * T * d.k;            // 4 * T*k, against multiples of E/4
-  if (pairs4 < 2LL * d.E) return Path::Gemv;         // T*k < E/2
-  if (egemv_supported(d) && pairs4 <= 9LL * d.E) return Path::ExpertGemv;   // T*k <= 9E/4
-  return Path::Grouped;
+  const long long P = (long long)T * d.k, E = d.E;
+  if (2 * P < E) return Path::Gemv;
+  const bool g16 = g16_supported(d);
+  if (egemv_supported(d) && (P <= E || (!g16 && 4 * P <= 9 * E))) return Path::ExpertGemv;
+  return grouped_tiles(d, T);
 }
 
-// Work list of each batched path in scratch: the grouped GEMMs' tile offsets
-// or the expert-major GEMV's routed-expert records.
+// Work list of each batched path in scratch: the 32/96-pair tiles' offsets,
+// or one record per 16-pair tile, or one record per routed expert.
 struct WorkList {
   int32_t* tile_off;
   void* slots;
-  int mt;
+  int mt, max_slots;
 };
 static WorkList work_list(const Layout& d, Path p, int32_t T, uint8_t* scr, const Scratch& sc) {
-  if (p == Path::Grouped) return {reinterpret_cast<int32_t*>(scr + sc.tile_off), nullptr, grouped_mt(d, T)};
-  return {nullptr, scr + sc.slots, 1};
+  if (p == Path::Grouped) return {reinterpret_cast<int32_t*>(scr + sc.tile_off), nullptr, grouped_mt(d, T), 0};
+  if (p == Path::Grouped16) return {nullptr, scr + sc.slots, 16, g16_max_tiles(d, T)};
+  const int P = T * d.k;
+  return {nullptr, scr + sc.slots, P, 1 + (P < d.E ? P : d.E)};
 }
 
 // lists_ready: the dispatch kernel already wrote the work list into scratch.
@@ -230,13 +242,15 @@ static int batched_impl(const moe_plan* plan, Path path, const uint8_t* L, const
                         hipStream_t stream, bool lists_ready = false) {
   const Layout& d = plan->d;
   const WorkList wl = work_list(d, path, T, scr, sc);
-  if (!lists_ready && launch_work_list(d, offsets, wl.tile_off, wl.mt, wl.slots, stream) != hipSuccess)
+  if (!lists_ready &&
+      launch_work_list(d, offsets, T, wl.tile_off, wl.mt, wl.slots, wl.max_slots, stream) != hipSuccess)
     return MOE_ERR_HIP;
   _Float16* h16 = reinterpret_cast<_Float16*>(scr + sc.h16);
   float* ypair = reinterpret_cast<float*>(scr + sc.ypair);
-  const hipError_t e = path == Path::ExpertGemv
-                           ? launch_egemv_ffn(d, L, x, w, pairs, wl.slots, h16, ypair, out, T, stream)
-                           : launch_grouped_ffn(d, L, x, w, offsets, pairs, wl.tile_off, h16, ypair, out, T, stream);
+  hipError_t e;
+  if (path == Path::ExpertGemv) e = launch_egemv_ffn(d, L, x, w, pairs, wl.slots, h16, ypair, out, T, stream);
+  else if (path == Path::Grouped16) e = launch_g16_ffn(d, L, x, w, pairs, wl.slots, h16, ypair, out, T, stream);
+  else e = launch_grouped_ffn(d, L, x, w, offsets, pairs, wl.tile_off, h16, ypair, out, T, stream);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -327,7 +341,8 @@ static int forward_impl(const moe_plan* plan, const void* blob, int32_t layer, c
     int32_t* offsets = reinterpret_cast<int32_t*>(scr + sc.offsets);
     int32_t* pairs = reinterpret_cast<int32_t*>(scr + sc.pairs);
     const WorkList wl = work_list(d, path, T, scr, sc);
-    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream, wl.tile_off, wl.mt, wl.slots) != hipSuccess)
+    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream, wl.tile_off, wl.mt, wl.slots, wl.max_slots) !=
+        hipSuccess)
       return MOE_ERR_HIP;
     const int st = batched_impl(plan, path, L, x, T, w, offsets, pairs, out, scr, sc, stream, true);
     if (st) return st;

@@ -121,23 +121,34 @@ __device__ __forceinline__ float dot_codes_bf16(const u32x4& c, const u32* X) {
   return a;
 }
 
-// Load the 32 bf16 activations of one sub-block in the pair order of
-// dot_codes_bf16: X[4d+c] = (x[8d+c], x[8d+c+4]), c = 0..3. Returns sum(x),
-// taken with v_dot2_f32_bf16 against (1, 1).
-__device__ __forceinline__ float load_x_pairs(const uint16_t* xs, u32* X) {
+// The 32 bf16 activations of one sub-block: four 16-byte loads.
+__device__ __forceinline__ void load_x_raw(const uint16_t* xs, u32x4* r) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] = load16(xs + 8 * q);   // elements 8q .. 8q+7
+}
+
+// The loaded activations in the pair order of dot_codes_bf16: X[4d+c] =
+// (x[8d+c], x[8d+c+4]), c = 0..3. Returns sum(x), taken with
+// v_dot2_f32_bf16 against (1, 1).
+__device__ __forceinline__ float x_pairs(const u32x4* r, u32* X) {
   const u32 ONES = 0x3F803F80u;           // bf16 (1, 1)
   float s = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const u32x4 r = load16(xs + 8 * q);   // elements 8q .. 8q+7
-    X[4 * q + 0] = __builtin_amdgcn_perm(r.z, r.x, 0x05040100u);   // (8q, 8q+4)
-    X[4 * q + 1] = __builtin_amdgcn_perm(r.z, r.x, 0x07060302u);   // (8q+1, 8q+5)
-    X[4 * q + 2] = __builtin_amdgcn_perm(r.w, r.y, 0x05040100u);   // (8q+2, 8q+6)
-    X[4 * q + 3] = __builtin_amdgcn_perm(r.w, r.y, 0x07060302u);   // (8q+3, 8q+7)
-    s = dot2_bf16(r.x, ONES, s); s = dot2_bf16(r.y, ONES, s);
-    s = dot2_bf16(r.z, ONES, s); s = dot2_bf16(r.w, ONES, s);
+    X[4 * q + 0] = __builtin_amdgcn_perm(r[q].z, r[q].x, 0x05040100u);   // (8q, 8q+4)
+    X[4 * q + 1] = __builtin_amdgcn_perm(r[q].z, r[q].x, 0x07060302u);   // (8q+1, 8q+5)
+    X[4 * q + 2] = __builtin_amdgcn_perm(r[q].w, r[q].y, 0x05040100u);   // (8q+2, 8q+6)
+    X[4 * q + 3] = __builtin_amdgcn_perm(r[q].w, r[q].y, 0x07060302u);   // (8q+3, 8q+7)
+    s = dot2_bf16(r[q].x, ONES, s); s = dot2_bf16(r[q].y, ONES, s);
+    s = dot2_bf16(r[q].z, ONES, s); s = dot2_bf16(r[q].w, ONES, s);
   }
   return s;
+}
+
+__device__ __forceinline__ float load_x_pairs(const uint16_t* xs, u32* X) {
+  u32x4 r[4];
+  load_x_raw(xs, r);
+  return x_pairs(r, X);
 }
 
 // sum_i (1024 + q_i) * h_i over one 32-code sub-block with fp16 h, two codes

@@ -438,17 +438,19 @@ __device__ __forceinline__ void excl_scan256x2(int a, int b, int& ea, int& eb, i
 
 // Single block of 1024 threads (16 waves). counts[e] = #pairs routed to e,
 // offsets = exclusive scan (E+1 entries), pairs = pair indices p = t*k+s
-// ordered by (expert, p), and the batched paths' work list: with tile_off
-// the exclusive scan of ceil(counts[e] / mt) (E+1 entries: the grouped
-// GEMMs' tiles), with slots the routed experts' records {e, offsets[e],
-// counts[e], 0} in expert order, then zero records up to E.
+// ordered by (expert, p), and the batched paths' work list: the tiles of
+// mt pairs of each expert, either as tile_off, the exclusive scan of
+// ceil(counts[e] / mt) (E+1 entries), or as slots, one record {e, first
+// pair position, pairs} per tile in expert order, then zero records up to
+// max_slots.
 // Deterministic: ranks come from ballots, not from the order of atomics.
 constexpr int DISP_THREADS = 1024;
 constexpr int DISP_WAVES = DISP_THREADS / WAVE;
 __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
                                                                 int32_t* __restrict__ offsets, int32_t* __restrict__ pairs,
                                                                 int32_t* __restrict__ tile_off,
-                                                                int4* __restrict__ slots, int E, int P, int mt) {
+                                                                int4* __restrict__ slots, int E, int P, int mt,
+                                                                int max_slots) {
   __shared__ int cnt[DISP_WAVES][256];
   __shared__ int wsum[8];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
@@ -463,22 +465,23 @@ __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* _
   if (tid < E) {
     for (int w = 0; w < DISP_WAVES; ++w) { const int c = cnt[w][tid]; cnt[w][tid] = tot; tot += c; }
   }
-  // second scan: tiles of the grouped GEMMs, or routed experts for the slots
-  const int tiles = tid >= E ? 0 : (slots ? (tot > 0) : (tot + mt - 1) / mt);
+  const int tiles = tid < E ? (tot + mt - 1) / mt : 0;
   int ex_tot, ex_tiles, all_tot, all_tiles;
   excl_scan256x2(tid < E ? tot : 0, tiles, ex_tot, ex_tiles, all_tot, all_tiles, wsum);
   if (tid < E) {
     counts[tid] = tot;
     offsets[tid] = ex_tot;
     if (tile_off) tile_off[tid] = ex_tiles;
-    if (slots && tot > 0) slots[ex_tiles] = make_int4(tid, ex_tot, tot, 0);
-    if (slots && tid >= all_tiles) slots[tid] = make_int4(0, 0, 0, 0);
+    if (slots)
+      for (int q = 0; q < tiles; ++q) slots[ex_tiles + q] = make_int4(tid, ex_tot + q * mt, min(mt, tot - q * mt), 0);
     for (int w = 0; w < DISP_WAVES; ++w) cnt[w][tid] += ex_tot;
   }
   if (tid == 0) {
     offsets[E] = all_tot;
     if (tile_off) tile_off[E] = all_tiles;
   }
+  if (slots)
+    for (int i = all_tiles + tid; i < max_slots; i += DISP_THREADS) slots[i] = make_int4(0, 0, 0, 0);
   __syncthreads();
   // cnt[w][e] is now the first output slot of wave w's pairs for expert e
   for (int pb = p0; pb < p1; pb += WAVE) {
@@ -617,39 +620,44 @@ hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y,
 }
 
 hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* pairs, int T,
-                           hipStream_t s, int32_t* tile_off, int mt, void* slots) {
-  if ((tile_off && mt < 1) || (tile_off && slots)) return hipErrorInvalidValue;
+                           hipStream_t s, int32_t* tile_off, int mt, void* slots, int max_slots) {
+  if (mt < 1 || (tile_off && slots)) return hipErrorInvalidValue;
+  // the slot records must cover every tile: at most ceil(T*k / mt) + min(E, T*k)
+  const int P = T * d.k;
+  if (slots && max_slots < (P + mt - 1) / mt + (P < d.E ? P : d.E)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs, tile_off,
-                     static_cast<int4*>(slots), d.E, T * d.k, tile_off ? mt : 1);
+                     static_cast<int4*>(slots), d.E, P, mt, slots ? max_slots : 0);
   return hipGetLastError();
 }
 
 // The batched paths' work list from given dispatch offsets (E+1 entries),
-// as the dispatch kernel writes it: tile_off = exclusive scan of
-// ceil(count / mt) (E+1 entries), or the routed experts' slot records. One
-// block of 256 threads.
+// as the dispatch kernel writes it. One block of 256 threads.
 __global__ __launch_bounds__(BLOCK) void work_list_kernel(const int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ tile_off, int4* __restrict__ slots,
-                                                         int E, int mt) {
+                                                         int E, int mt, int max_slots) {
   __shared__ int wsum[8];
   const int tid = threadIdx.x;
   const int n = tid < E ? offsets[tid + 1] - offsets[tid] : 0;
-  const int units = tid >= E ? 0 : (slots ? (n > 0) : (n + mt - 1) / mt);
+  const int units = (n + mt - 1) / mt;
   int ex, ex2, tot, tot2;
   excl_scan256x2(units, 0, ex, ex2, tot, tot2, wsum);
   if (tid < E) {
     if (tile_off) tile_off[tid] = ex;
-    if (slots && n > 0) slots[ex] = make_int4(tid, offsets[tid], n, 0);
-    if (slots && tid >= tot) slots[tid] = make_int4(0, 0, 0, 0);
+    if (slots)
+      for (int q = 0; q < units; ++q) slots[ex + q] = make_int4(tid, offsets[tid] + q * mt, min(mt, n - q * mt), 0);
   }
   if (tid == 0 && tile_off) tile_off[E] = tot;
+  if (slots)
+    for (int i = tot + tid; i < max_slots; i += BLOCK) slots[i] = make_int4(0, 0, 0, 0);
 }
 
-hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int32_t* tile_off, int mt, void* slots,
-                            hipStream_t s) {
-  if ((!tile_off) == (!slots) || (tile_off && mt < 1)) return hipErrorInvalidValue;
+hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int T, int32_t* tile_off, int mt, void* slots,
+                            int max_slots, hipStream_t s) {
+  if ((!tile_off) == (!slots) || mt < 1) return hipErrorInvalidValue;
+  const int P = T * d.k;
+  if (slots && max_slots < (P + mt - 1) / mt + (P < d.E ? P : d.E)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(work_list_kernel, dim3(1), dim3(BLOCK), 0, s, offsets, tile_off, static_cast<int4*>(slots), d.E,
-                     mt);
+                     mt, slots ? max_slots : 0);
   return hipGetLastError();
 }
 

@@ -380,6 +380,192 @@ static hipError_t launch_wr(const Layout& d, const uint8_t* layer, const uint16_
   return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------------ 16-pair tiles, all weights in flight
+// For batches whose experts carry few pairs (a tile of 32 or 96 rows would be
+// mostly padding and its K loop would wait on one super-block at a time),
+// v_mfma_f32_16x16x32_f16 on tiles of at most 16 pairs (lane layouts checked
+// on the box: A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], D[4(l/16)+r][l%16]).
+// Lane (row r = l%16, kg = l/16) of a weight row owns the 16-byte code chunk
+// of sub-block 4m + kg for each group m of 128 K, so one group is four MFMAs
+// (one per code dword), B dequantized with dequant8 and A the matching eight
+// activations in unpack order. Every wave requests all of its weights at once
+// and takes its activations straight from L2 into registers: no LDS staging,
+// no barrier inside the K loop. Work list: one record {expert, first pair,
+// pairs} per tile, written by the dispatch.
+struct TileRec { int e, pos0, n, pad; };
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Eight bf16 activations (16 bytes) as fp16 in unpack order (0,2,4,6,1,3,5,7).
+__device__ __forceinline__ half8 bf16x8_to_unpack(const u32x4& v) {
+  auto lo = [](u32 w) { return __builtin_bit_cast(float, w << 16); };
+  auto hi = [](u32 w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); };
+  u32x4 o;
+  o.x = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_pkrtz(lo(v.x), lo(v.y)));   // (e0, e2)
+  o.y = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_pkrtz(lo(v.z), lo(v.w)));   // (e4, e6)
+  o.z = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_pkrtz(hi(v.x), hi(v.y)));   // (e1, e3)
+  o.w = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_pkrtz(hi(v.z), hi(v.w)));   // (e5, e7)
+  return __builtin_bit_cast(half8, o);
+}
+
+__device__ __forceinline__ u32 dword_of(const u32x4& c, int i) {
+  return i == 0 ? c.x : (i == 1 ? c.y : (i == 2 ? c.z : c.w));
+}
+
+// Gate/up: workgroup = one tile x 16 row pairs (intermediate rows f0 .. f0+15);
+// wave w takes K range [w*H/4, (w+1)*H/4), G = H/512 groups of 128 K. The
+// four partial products are added in wave order through LDS, then SiLU(gate)
+// * up goes to h16 at the pairs' sorted positions, in unpack order within
+// each group of 8 (as the 32/96-pair tiles write it).
+template <int G>
+__global__ __launch_bounds__(BLOCK) void gateup_g16_kernel(
+    const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles,
+    _Float16* __restrict__ h16) {
+  constexpr int NH = (G + 1) / 2;               // super-blocks per wave (a group is half of one)
+  __shared__ float red[4][2][4][WAVE];
+  const int bpt = I / 16;
+  const TileRec tr = tiles[blockIdx.x / bpt];
+  if (tr.n == 0) return;                        // past the last tile (workgroup-uniform)
+  const int f0 = (int)(blockIdx.x % bpt) * 16;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int r = lane & 15, kg = lane >> 4;
+  const int sb0 = w * 4 * G;                    // first sub-block of the wave's K range
+  // token of tile row t = l%16 first: loads complete in order, so the
+  // activation loads, which wait on it, must not queue behind the weights.
+  // Rows past the tile's pairs repeat its last row (their outputs are not
+  // stored), so every load is unconditional.
+  const int pair = pairs[tr.pos0 + min(lane & 15, tr.n - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+  // weights: row f0 + r; gate codes at 0, up codes at H/2, gate headers at H, up headers at H + H/16
+  const uint8_t* rec = gu + (size_t)tr.e * gu_expert_bytes + (size_t)(f0 + r) * rp_bytes;
+  u32x4 cg[G], cu[G], hg[NH], hu[NH];
+#pragma unroll
+  for (int m = 0; m < G; ++m) {
+    const int sbi = sb0 + 4 * m + kg;
+    cg[m] = *reinterpret_cast<const u32x4*>(rec + 16 * sbi);
+    cu[m] = *reinterpret_cast<const u32x4*>(rec + H / 2 + 16 * sbi);
+  }
+#pragma unroll
+  for (int b = 0; b < NH; ++b) {
+    const int sup = (sb0 + 8 * b) >> 3;
+    hg[b] = *reinterpret_cast<const u32x4*>(rec + H + QHDR * sup);
+    hu[b] = *reinterpret_cast<const u32x4*>(rec + H + H / 16 + QHDR * sup);
+  }
+  const int tok = pair / k;
+  u32x4 xr[G][4];
+#pragma unroll
+  for (int m = 0; m < G; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      xr[m][i] = *reinterpret_cast<const u32x4*>(x + (size_t)tok * H + 32 * (sb0 + 4 * m + kg) + 8 * i);
+  __builtin_amdgcn_sched_barrier(0);            // every load is in flight before the first use
+  half8 A[G][4];
+#pragma unroll
+  for (int m = 0; m < G; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[m][i] = bf16x8_to_unpack(xr[m][i]);
+  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < G; ++m) {
+    const int sb = (sb0 + 4 * m + kg) & 7;      // sub-block within its super-block
+    const SubScale sg = sub_scale(hg[m >> 1], sb), su = sub_scale(hu[m >> 1], sb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[m][i], dequant8(dword_of(cg[m], i), sg), accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[m][i], dequant8(dword_of(cu[m], i), su), accu, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    red[w][0][q][lane] = accg[q];
+    red[w][1][q][lane] = accu[q];
+  }
+  __syncthreads();
+  // thread -> (tile row tt, intermediate row f0 + rr); D[tt][rr] sits in lane rr + 16*(tt/4), register tt%4
+  const int tt = tid >> 4, rr = tid & 15;
+  if (tt < tr.n) {
+    const int ln = rr + 16 * (tt >> 2), q = tt & 3;
+    const float g = ((red[0][0][q][ln] + red[1][0][q][ln]) + red[2][0][q][ln]) + red[3][0][q][ln];
+    const float u = ((red[0][1][q][ln] + red[1][1][q][ln]) + red[2][1][q][ln]) + red[3][1][q][ln];
+    const int f = f0 + rr;
+    h16[(size_t)(tr.pos0 + tt) * I + (f & ~7) + nib_pos(f & 7)] = (_Float16)(g / (1.0f + expf(-g)) * u);
+  }
+}
+
+// Down: workgroup = one tile x 64 output rows, wave w rows n0 .. n0+15 over the
+// whole K = I (GD = I/128 groups); h16 holds the tile's rows in unpack order,
+// so A is a plain load. Rows go to ypair at the pair index t*k + s.
+template <int GD>
+__global__ __launch_bounds__(BLOCK) void down_g16_kernel(
+    const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I,
+    const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles, const _Float16* __restrict__ h16,
+    float* __restrict__ ypair) {
+  constexpr int NH = (GD + 1) / 2;
+  const int bpt = H / 64;
+  const TileRec tr = tiles[blockIdx.x / bpt];
+  if (tr.n == 0) return;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int n0 = (int)(blockIdx.x % bpt) * 64 + 16 * w;
+  const int r = lane & 15, kg = lane >> 4;
+  const uint8_t* row = dn + (size_t)tr.e * dn_expert_bytes + (size_t)(n0 + r) * drow_bytes;
+  u32x4 cd[GD], hd[NH];
+#pragma unroll
+  for (int m = 0; m < GD; ++m) cd[m] = *reinterpret_cast<const u32x4*>(row + 16 * (4 * m + kg));
+#pragma unroll
+  for (int b = 0; b < NH; ++b) hd[b] = *reinterpret_cast<const u32x4*>(row + I / 2 + QHDR * b);
+  // h of tile row t = l%16; rows past the tile's pairs repeat its last row
+  // (their outputs are not stored), so the loads are unconditional
+  const _Float16* hp = h16 + (size_t)(tr.pos0 + min(lane & 15, tr.n - 1)) * I;
+  half8 A[GD][4];
+#pragma unroll
+  for (int m = 0; m < GD; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[m][i] = *reinterpret_cast<const half8*>(hp + 32 * (4 * m + kg) + 8 * i);
+  // output pair indices of this lane's four accumulator rows (tile rows 4*kg .. 4*kg+3)
+  int pr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pr[q] = 4 * kg + q < tr.n ? pairs[tr.pos0 + 4 * kg + q] : -1;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < GD; ++m) {
+    const SubScale sc = sub_scale(hd[m >> 1], (4 * m + kg) & 7);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[m][i], dequant8(dword_of(cd[m], i), sc), acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (pr[q] >= 0) ypair[(size_t)pr[q] * H + n0 + r] = acc[q];
+}
+
+template <int G, int GD>
+static hipError_t launch_g16(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
+                             const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, hipStream_t s) {
+  hipLaunchKernelGGL((gateup_g16_kernel<G>), dim3(ntiles * (d.I / 16)), dim3(BLOCK), 0, s, layer + d.gu_off,
+                     d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((down_g16_kernel<GD>), dim3(ntiles * (d.H / 64)), dim3(BLOCK), 0, s, layer + d.dn_off,
+                     d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, pairs, tiles, h16, ypair);
+  return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_g16_i(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
+                               const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, hipStream_t s) {
+  switch (d.I) {
+    case 256: return launch_g16<G, 2>(d, layer, x, pairs, tiles, ntiles, h16, ypair, s);
+    case 512: return launch_g16<G, 4>(d, layer, x, pairs, tiles, ntiles, h16, ypair, s);
+    case 768: return launch_g16<G, 6>(d, layer, x, pairs, tiles, ntiles, h16, ypair, s);
+    case 1024: return launch_g16<G, 8>(d, layer, x, pairs, tiles, ntiles, h16, ypair, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace grouped
 
 int grouped_mt(const Layout& d, int T) { return (long long)T * d.k >= 64LL * d.E ? 96 : 32; }
@@ -406,6 +592,33 @@ hipError_t launch_combine(const Layout& d, const float* ypair, const float* w, f
   const int n4 = T * (d.H / 4);
   hipLaunchKernelGGL(combine_kernel, dim3((n4 + BLOCK - 1) / BLOCK), dim3(BLOCK), 0, s, ypair, w, out, d.H, d.k, T);
   return hipGetLastError();
+}
+
+bool g16_supported(const Layout& d) {
+  return (d.H == 512 || d.H == 1024 || d.H == 2048) && d.I <= 1024;
+}
+
+int g16_max_tiles(const Layout& d, int T) {
+  const int P = T * d.k;
+  return (P + 15) / 16 + (P < d.E ? P : d.E);
+}
+
+hipError_t launch_g16_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
+                          const int32_t* pairs, const void* tiles, _Float16* h16, float* ypair, float* out, int T,
+                          hipStream_t s) {
+  using namespace grouped;
+  if (!g16_supported(d)) return hipErrorInvalidValue;
+  if (T <= 0) return hipSuccess;
+  const TileRec* tr = static_cast<const TileRec*>(tiles);
+  const int nt = g16_max_tiles(d, T);
+  hipError_t e;
+  switch (d.H) {
+    case 512: e = launch_g16_i<1>(d, layer, x, pairs, tr, nt, h16, ypair, s); break;
+    case 1024: e = launch_g16_i<2>(d, layer, x, pairs, tr, nt, h16, ypair, s); break;
+    default: e = launch_g16_i<4>(d, layer, x, pairs, tr, nt, h16, ypair, s); break;
+  }
+  if (e != hipSuccess) return e;
+  return launch_combine(d, ypair, w, out, T, s);
 }
 
 }  // namespace qmoe

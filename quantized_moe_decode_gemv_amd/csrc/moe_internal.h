@@ -73,7 +73,8 @@ struct Scratch {
     offsets = take((size_t)(d.E + 1) * 4);
     pairs = take((size_t)T * d.k * 4);
     tile_off = take((size_t)(d.E + 1) * 4);
-    slots = take((size_t)d.E * 16);        // routed-expert records of the expert-major GEMV path
+    // work records {expert, first pair, pairs}: one per routed expert, or per 16-pair tile
+    slots = take((size_t)((T * d.k + 15) / 16 + d.E) * 16);
     // batched paths only (T > 1): fp16 h in expert-sorted pair order, one fp32 output row per pair
     h16 = take(T > 1 ? (size_t)T * d.k * d.I * 2 : 0);
     ypair = take(T > 1 ? (size_t)T * d.k * d.H * 4 : 0);
@@ -100,15 +101,16 @@ hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids
 hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y, uint16_t* x_next, int T,
                              hipStream_t s);
 // Batched-path work lists, written by the dispatch or, from given dispatch
-// lists, by launch_work_list: with tile_off the grouped GEMMs' tile offsets
-// (exclusive scan of ceil(counts[e] / mt), E+1 entries); with slots the
-// expert-major GEMV's records {expert, first pair, pairs} of the routed
-// experts in expert order, then {0, 0, 0} up to E records.
+// lists, by launch_work_list: the tiles of mt pairs of every expert, as
+// tile_off (exclusive scan of ceil(counts[e] / mt), E+1 entries) or as slots,
+// one record {expert, first pair position, pairs} per tile in expert order
+// followed by {0, 0, 0} records up to max_slots (at least ceil(T*k / mt) +
+// min(E, T*k)).
 hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets,
                            int32_t* pairs, int T, hipStream_t s, int32_t* tile_off = nullptr, int mt = 1,
-                           void* slots = nullptr);
-hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int32_t* tile_off, int mt, void* slots,
-                            hipStream_t s);
+                           void* slots = nullptr, int max_slots = 0);
+hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int T, int32_t* tile_off, int mt, void* slots,
+                            int max_slots, hipStream_t s);
 
 // grouped MFMA path (T > 1)
 int grouped_mt(const Layout& d, int T);          // pairs per tile of the grouped GEMMs for a T-token call
@@ -116,6 +118,13 @@ int grouped_max_tiles(const Layout& d, int T);
 hipError_t launch_grouped_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
                               const int32_t* offsets, const int32_t* pairs, const int32_t* tile_off, _Float16* h16,
                               float* ypair, float* out, int T, hipStream_t s);
+// 16-pair MFMA tiles with every weight load in flight (T > 1, a few to a
+// few dozen pairs per expert); tiles = slot records of mt = 16
+bool g16_supported(const Layout& d);
+int g16_max_tiles(const Layout& d, int T);
+hipError_t launch_g16_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
+                          const int32_t* pairs, const void* tiles, _Float16* h16, float* ypair, float* out, int T,
+                          hipStream_t s);
 // out[t] = sum_s w[t][s] * ypair[t*k + s], slot order
 hipError_t launch_combine(const Layout& d, const float* ypair, const float* w, float* out, int T, hipStream_t s);
 

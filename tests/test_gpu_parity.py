@@ -127,13 +127,14 @@ PATH_FLAGS = (("gemv", q.FLAG_FORCE_GEMV), ("expert_gemv", q.FLAG_FORCE_EXPERT_G
               ("grouped", q.FLAG_FORCE_GROUPED))
 
 
-@pytest.mark.parametrize("T", [8, 32, 128])
+@pytest.mark.parametrize("T", [8, 32, 128, 256])
 def test_small_batch_all_paths(qwen, T):
     """Small-batch decode / short prefill on the Qwen3-30B-A3B-shaped layer:
     routing from given N(0,1) logits (shared fp32 inputs -> ids must match
     exactly), expert FFN on the per-token GEMV path, the expert-major GEMV
-    path and the grouped MFMA path, each against the oracle (all tokens up to
-    32, else every 4th)."""
+    path and the grouped MFMA path (16-pair tiles up to T = 192, 32-pair
+    tiles at 256), each against the oracle (all tokens up to 32, else every
+    4th)."""
     S = qwen.shape
     d = qwen.dev
     xb = synth.x_bf16(S, 3, T, T=T)
@@ -235,12 +236,13 @@ def test_forward_batched_auto_grouped_tiny(tiny):
         check_bf16_vector(got["xn"][t], ref_next)
 
 
-@pytest.mark.parametrize("T", [1, 7, 8, 36, 37])
+@pytest.mark.parametrize("T", [1, 7, 8, 16, 17, 192, 193])
 def test_forward_auto_path_boundary_qwen(qwen, T):
     """Without flags moe_forward runs the per-token GEMV path while T*k < E/2
-    (T <= 7 here), the expert-major GEMV path while T*k <= 9E/4 (T <= 36) and
-    the grouped path beyond: both sides of each switch against the oracle
-    (every 3rd token and the last above 16 tokens)."""
+    (T <= 7 here), the expert-major GEMV path while T*k <= E (T <= 16), the
+    grouped GEMMs on 16-pair tiles while T*k <= 12E (T <= 192) and on 32-pair
+    tiles beyond: both sides of each switch against the oracle (every 3rd
+    token and the last above 16 tokens)."""
     xb = synth.x_bf16(qwen.shape, 10, T, T=T)
     sample = None if T <= 16 else sorted(set(range(0, T, 3)) | {T - 1})
     _check_layer(qwen, xb, qwen.forward(xb), sample=sample)
