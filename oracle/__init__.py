@@ -71,10 +71,16 @@ def lib():
         L.oracle_route_weights.argtypes = [vp, vp, i64, vp]
         L.oracle_silu.restype = f64
         L.oracle_silu.argtypes = [f64]
+        L.oracle_act.restype = f64
+        L.oracle_act.argtypes = [f64, f64, ctypes.c_int32]
         L.oracle_expert_ffn.restype = None
         L.oracle_expert_ffn.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp]
+        L.oracle_expert_ffn_act.restype = None
+        L.oracle_expert_ffn_act.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, ctypes.c_int32]
         L.oracle_moe_token.restype = None
         L.oracle_moe_token.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp]
+        L.oracle_moe_token_act.restype = None
+        L.oracle_moe_token_act.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, ctypes.c_int32]
         L.oracle_resid_rmsnorm.restype = None
         L.oracle_resid_rmsnorm.argtypes = [vp, vp, i64, f64, vp, vp]
         _lib = L
@@ -175,19 +181,30 @@ def silu(z):
     return lib().oracle_silu(float(z))
 
 
+# Gate activations h = act(g, u); the pages (sparkinfer CuTe-DSL README, "moe"
+# paragraph) name SiLU, ReLU2 and SwiGLU-OAI without formulas: SiLU(g) u,
+# max(g, 0)^2 u, and g' sigmoid(1.702 g') (u' + 1) with g' = min(g, 7),
+# u' = clamp(u, -7, 7).
+ACT_SILU, ACT_RELU2, ACT_SWIGLU_OAI = 0, 1, 2
+
+
+def act(g, u, kind=ACT_SILU):
+    return lib().oracle_act(float(g), float(u), int(kind))
+
+
 # ---------------------------------------------------------------- FFN
-def expert_ffn(gate, up, down, x, return_h=False):
+def expert_ffn(gate, up, down, x, return_h=False, act=ACT_SILU):
     gate, up, down = _c(gate, np.uint8), _c(up, np.uint8), _c(down, np.uint8)
     I, H = gate.shape[0], gate.shape[1] * QK
     assert up.shape == gate.shape and down.shape[0] == H and down.shape[1] * QK == I
     x = _c(x, np.float64)
     y = np.empty(H, dtype=np.float64)
     h = np.empty(I, dtype=np.float64)
-    lib().oracle_expert_ffn(_p(gate), _p(up), _p(down), H, I, _p(x), _p(y), _p(h))
+    lib().oracle_expert_ffn_act(_p(gate), _p(up), _p(down), H, I, _p(x), _p(y), _p(h), int(act))
     return (y, h) if return_h else y
 
 
-def moe_token(gates, ups, downs, w, x_bf16):
+def moe_token(gates, ups, downs, w, x_bf16, act=ACT_SILU):
     """y = sum_s w_s * FFN_s(x) for one token; gates[s] etc. are the blocks
     of the expert in slot s."""
     k = len(gates)
@@ -202,7 +219,7 @@ def moe_token(gates, ups, downs, w, x_bf16):
     w = _c(w, np.float64)
     x_bf16 = _c(x_bf16, np.uint16)
     y = np.empty(H, dtype=np.float64)
-    lib().oracle_moe_token(ga, ua, da, _p(w), k, H, I, _p(x_bf16), _p(y))
+    lib().oracle_moe_token_act(ga, ua, da, _p(w), k, H, I, _p(x_bf16), _p(y), int(act))
     return y
 
 
@@ -242,10 +259,11 @@ class ExpertSource:
         return self._synth.router(self.shape, layer)
 
 
-def moe_layer(src, layer, x_bf16, logits=None, wr=None):
+def moe_layer(src, layer, x_bf16, logits=None, wr=None, act=ACT_SILU):
     """One MoE layer for T tokens. x_bf16: [T, H] bf16 bits. ``logits`` (fp32
-    [T, E]) replaces the router GEMV when given. Returns dict with ids [T,k],
-    w [T,k], gap [T], logits [T,E] (fp64), y [T,H] (fp64)."""
+    [T, E]) replaces the router GEMV when given; ``act`` is the gate
+    activation. Returns dict with ids [T,k], w [T,k], gap [T], logits [T,E]
+    (fp64), y [T,H] (fp64)."""
     S = src.shape
     x_bf16 = np.atleast_2d(np.asarray(x_bf16, dtype=np.uint16))
     T = x_bf16.shape[0]
@@ -261,5 +279,5 @@ def moe_layer(src, layer, x_bf16, logits=None, wr=None):
     for t in range(T):
         ids[t], w[t], gap[t] = route(lg[t], S.top_k)
         bl = [src.blocks(layer, e) for e in ids[t]]
-        y[t] = moe_token([b[0] for b in bl], [b[1] for b in bl], [b[2] for b in bl], w[t], x_bf16[t])
+        y[t] = moe_token([b[0] for b in bl], [b[1] for b in bl], [b[2] for b in bl], w[t], x_bf16[t], act=act)
     return dict(ids=ids, w=w, gap=gap, logits=lg, y=y)

@@ -20,10 +20,15 @@
  *    (logit descending, expert id ascending), and the softmax restricted to
  *    the selected experts (softmax over all experts then renormalised over
  *    the top-k, which is the same number);
- *  - the expert FFN y_e = D_e (SiLU(G_e x) * (U_e x)) and the routing-weighted
+ *  - the expert FFN y_e = D_e (act(G_e x, U_e x)) and the routing-weighted
  *    sum over the selected experts (the pages' fused MoE expert FFN: sparkinfer
  *    README kernel table; sparkinfer CuTe-DSL README, "moe" paragraph, for the
- *    SiLU-gated form with top-k ids and weights as inputs);
+ *    gated form with top-k ids and weights as inputs). The same paragraph
+ *    names SiLU, ReLU2 and SwiGLU-OAI activations without formulas; read
+ *    here as act(g, u) = SiLU(g) u (the default), max(g, 0)^2 u (squared ReLU
+ *    in place of SiLU), and the clamped SwiGLU variant published with that
+ *    name: g' = min(g, 7), u' = min(max(u, -7), 7),
+ *    act = g' / (1 + exp(-1.702 g')) * (u' + 1);
  *  - the residual add and RMSNorm between stacked layers (weight 1, eps given
  *    by the caller), rounded to bf16.
  */
@@ -158,34 +163,60 @@ void oracle_route_weights(const double* logits, const int32_t* ids, int64_t k, d
 /* ---------------------------------------------------------------- FFN */
 double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* y = D (SiLU(G x) * (U x)); G, U: [I x H] blocks, D: [H x I] blocks */
-void oracle_expert_ffn(const uint8_t* gate, const uint8_t* up, const uint8_t* down,
-                       int64_t H, int64_t I, const double* x, double* y, double* h_out) {
+/* Gate activation h = act(g, u): 0 SiLU, 1 squared ReLU, 2 clamped SwiGLU
+ * (readings in the header comment). */
+double oracle_act(double g, double u, int32_t act) {
+  if (act == 1) {
+    const double r = g > 0.0 ? g : 0.0;
+    return r * r * u;
+  }
+  if (act == 2) {
+    const double gc = g < 7.0 ? g : 7.0;
+    const double uc = u < -7.0 ? -7.0 : (u > 7.0 ? 7.0 : u);
+    return gc / (1.0 + exp(-1.702 * gc)) * (uc + 1.0);
+  }
+  return oracle_silu(g) * u;
+}
+
+/* y = D act(G x, U x); G, U: [I x H] blocks, D: [H x I] blocks */
+void oracle_expert_ffn_act(const uint8_t* gate, const uint8_t* up, const uint8_t* down,
+                           int64_t H, int64_t I, const double* x, double* y, double* h_out, int32_t act) {
   double* g = (double*)malloc(sizeof(double) * (size_t)I);
   double* u = (double*)malloc(sizeof(double) * (size_t)I);
   oracle_qgemv(gate, I, H, x, g);
   oracle_qgemv(up, I, H, x, u);
-  for (int64_t i = 0; i < I; ++i) g[i] = oracle_silu(g[i]) * u[i];
+  for (int64_t i = 0; i < I; ++i) g[i] = oracle_act(g[i], u[i], act);
   if (h_out) memcpy(h_out, g, sizeof(double) * (size_t)I);
   oracle_qgemv(down, H, I, g, y);
   free(g);
   free(u);
 }
 
+void oracle_expert_ffn(const uint8_t* gate, const uint8_t* up, const uint8_t* down,
+                       int64_t H, int64_t I, const double* x, double* y, double* h_out) {
+  oracle_expert_ffn_act(gate, up, down, H, I, x, y, h_out, 0);
+}
+
 /* One token through one MoE layer given its selected experts' blocks.
  * gate/up/down: arrays of k pointers (expert of slot s); w: k routing weights. */
-void oracle_moe_token(const uint8_t* const* gate, const uint8_t* const* up, const uint8_t* const* down,
-                      const double* w, int64_t k, int64_t H, int64_t I, const uint16_t* x_bf16,
-                      double* y) {
+void oracle_moe_token_act(const uint8_t* const* gate, const uint8_t* const* up, const uint8_t* const* down,
+                          const double* w, int64_t k, int64_t H, int64_t I, const uint16_t* x_bf16,
+                          double* y, int32_t act) {
   double* x = (double*)malloc(sizeof(double) * (size_t)H);
   double* ys = (double*)malloc(sizeof(double) * (size_t)H);
   for (int64_t i = 0; i < H; ++i) { x[i] = oracle_bf16(x_bf16[i]); y[i] = 0.0; }
   for (int64_t s = 0; s < k; ++s) {
-    oracle_expert_ffn(gate[s], up[s], down[s], H, I, x, ys, NULL);
+    oracle_expert_ffn_act(gate[s], up[s], down[s], H, I, x, ys, NULL, act);
     for (int64_t i = 0; i < H; ++i) y[i] += w[s] * ys[i];
   }
   free(x);
   free(ys);
+}
+
+void oracle_moe_token(const uint8_t* const* gate, const uint8_t* const* up, const uint8_t* const* down,
+                      const double* w, int64_t k, int64_t H, int64_t I, const uint16_t* x_bf16,
+                      double* y) {
+  oracle_moe_token_act(gate, up, down, w, k, H, I, x_bf16, y, 0);
 }
 
 /* ---------------------------------------------------------------- stack */

@@ -231,11 +231,66 @@ def test_silu_closed_forms():
         assert np.isclose(oracle.silu(z), z * expit(z), rtol=1e-14, atol=1e-300)
 
 
+# ------------------------------------------------------------------ gate activations
+def test_act_silu_is_silu_times_up():
+    for g, u in [(0.0, 3.0), (1.5, -2.0), (-4.0, 0.25), (12.0, 1.0)]:
+        assert oracle.act(g, u, oracle.ACT_SILU) == oracle.silu(g) * u
+
+
+def test_act_relu2_closed_forms():
+    R = oracle.ACT_RELU2
+    for g in (-3.5, -1e-9, 0.0):                     # zero for g <= 0, any u
+        assert oracle.act(g, 7.0, R) == 0.0
+    assert oracle.act(3.0, 2.0, R) == 18.0           # exact small integers
+    assert oracle.act(0.5, 4.0, R) == 1.0
+    assert oracle.act(-2.0, -5.0, R) == 0.0
+    for c in (0.5, 2.0, 3.0):                        # degree 2 in g, degree 1 in u
+        assert np.isclose(oracle.act(c * 1.3, 0.7, R), c * c * oracle.act(1.3, 0.7, R), rtol=1e-14)
+        assert np.isclose(oracle.act(1.3, c * 0.7, R), c * oracle.act(1.3, 0.7, R), rtol=1e-14)
+
+
+def test_act_swiglu_oai_closed_forms():
+    O = oracle.ACT_SWIGLU_OAI
+    assert oracle.act(0.0, 3.0, O) == 0.0
+    for g in (-9.0, 0.3, 6.5, 20.0):                 # u' = -1 cancels the gate for any g
+        assert oracle.act(g, -1.0, O) == 0.0
+    # g' sigmoid(a g') is a swish: its odd part is g'/2, so act(g) - act(-g) = g (u' + 1)
+    for g in np.linspace(-6.9, 6.9, 47):
+        for u in (-3.0, 0.4, 6.0):
+            assert np.isclose(oracle.act(g, u, O) - oracle.act(-g, u, O), g * (u + 1.0), rtol=1e-12, atol=1e-12)
+    # clamps: the gate at 7 from above only, the up value at +-7
+    assert oracle.act(7.0, 0.5, O) == oracle.act(50.0, 0.5, O)
+    assert oracle.act(-30.0, 0.5, O) != oracle.act(-7.0, 0.5, O)
+    assert oracle.act(2.0, 7.0, O) == oracle.act(2.0, 100.0, O)
+    assert oracle.act(2.0, -7.0, O) == oracle.act(2.0, -40.0, O)
+    # sigmoid with slope 1.702 (scipy's logistic, a library routine)
+    for g, u in [(1.0, 0.0), (-2.5, 1.5), (4.0, -0.5)]:
+        assert np.isclose(oracle.act(g, u, O), g * expit(1.702 * g) * (u + 1.0), rtol=1e-14)
+    # far below zero the gate vanishes
+    assert abs(oracle.act(-40.0, 0.0, O)) < 1e-25
+
+
 # ------------------------------------------------------------------ FFN / MoE
-def _dense_ffn(src, layer, e, x):
+def _dense_ffn(src, layer, e, x, act=None):
     g, u, d = [oracle.dequant_matrix(b) for b in src.blocks(layer, e)]
-    hg = g @ x
-    return d @ (hg * expit(hg) * (u @ x))
+    hg, hu = g @ x, u @ x
+    if act is None:
+        return d @ (hg * expit(hg) * hu)
+    return d @ np.array([oracle.act(a, b, act) for a, b in zip(hg, hu)])
+
+
+@pytest.mark.parametrize("act", [1, 2])
+def test_expert_ffn_activation_matches_dense_numpy(act):
+    """FFN with each non-default gate activation against dense numpy matmuls
+    (library routines) on the dequantized matrices; x scaled up so that the
+    SwiGLU clamps act on part of the rows."""
+    src = oracle.ExpertSource(synth.TINY)
+    x = 8.0 * oracle.bf16_array(synth.x_bf16(synth.TINY, 0, 0)[0])
+    y, h = oracle.expert_ffn(*src.blocks(0, 5), x, return_h=True, act=act)
+    assert np.allclose(y, _dense_ffn(src, 0, 5, x, act), rtol=1e-11, atol=1e-12)
+    g = oracle.dequant_matrix(src.blocks(0, 5)[0]) @ x
+    if act == 2:
+        assert (g > 7.0).any() and (g < 7.0).any()
 
 
 def test_expert_ffn_matches_dense_numpy():
