@@ -274,7 +274,8 @@ def single_layer_measurements(S, blob, L, dev, stream, q, np, torch, synth):
     norm), graph-replayed: the tiny layer (hidden 256, 8 experts, top-2,
     inter 512: 442,368 expert bytes per call) and the Qwen3-30B-A3B-shaped
     layer rotating over 16 layers of the stack (21,233,664 expert bytes per
-    call, so no layer's experts are cache-resident from the previous call)."""
+    call, so no layer's experts are cache-resident from the previous call),
+    the latter also with the ReLU2 and SwiGLU-OAI gate activations."""
     res = {}
     T = synth.TINY
     tplan = q.Plan(T.hidden, T.n_experts, T.top_k, T.inter, n_layers=1, max_tokens=1)
@@ -299,6 +300,11 @@ def single_layer_measurements(S, blob, L, dev, stream, q, np, torch, synth):
     eb = S.top_k * S.expert_bytes
     res["qwen3_30b_a3b_layer"] = {"us_per_call": round(us, 2), "expert_bytes": eb,
                                  "expert_gbps": round(eb / (us * 1e-6) / 1e9, 1)}
+    # the same calls with the other gate activations (epilogue only: same bytes)
+    for name, flag in (("relu2", q.FLAG_ACT_RELU2), ("swiglu_oai", q.FLAG_ACT_SWIGLU_OAI)):
+        aplan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=L, max_tokens=1, flags=flag)
+        us = _graph_us(lambda l: aplan.forward(blob, l, x, 1, y, scratch=scr, stream=stream), n_rot, 20, stream, torch)
+        res["qwen3_30b_a3b_layer"][f"us_per_call_{name}"] = round(us, 2)
     return res
 
 

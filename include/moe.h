@@ -62,6 +62,13 @@ enum moe_status {
 #define MOE_FLAG_FORCE_GROUPED 0x2u      /* grouped MFMA expert GEMMs for every T >= 2 (tile shape by P/E) */
 #define MOE_FLAG_FORCE_EXPERT_GEMV 0x4u  /* expert-major GEMV for every T >= 2; needs inter <= 2048 */
 
+/* Gate activation h = act(g, u) of the expert FFN (at most one flag; default
+ * SiLU(g) * u). The pages name SiLU, ReLU2 and SwiGLU-OAI activations for the
+ * fused MoE (sparkinfer CuTe-DSL README, "moe" paragraph) without formulas;
+ * the readings used: */
+#define MOE_FLAG_ACT_RELU2 0x8u          /* max(g, 0)^2 * u */
+#define MOE_FLAG_ACT_SWIGLU_OAI 0x10u    /* g' * sigmoid(1.702 g') * (u' + 1), g' = min(g, 7), u' = clamp(u, -7, 7) */
+
 typedef struct moe_config {
   int32_t hidden;      /* H: multiple of 256; 256, 512, 1024 or a multiple of 2048 up to 8192 */
   int32_t n_experts;   /* E: 1..256 */

@@ -12,7 +12,8 @@ import numpy as np
 
 __all__ = [
     "MoeError", "Config", "RouteOut", "Plan", "load", "is_supported", "status_string",
-    "FLAG_FORCE_GEMV", "FLAG_FORCE_GROUPED", "FLAG_FORCE_EXPERT_GEMV", "LIB_PATH",
+    "FLAG_FORCE_GEMV", "FLAG_FORCE_GROUPED", "FLAG_FORCE_EXPERT_GEMV", "FLAG_ACT_RELU2", "FLAG_ACT_SWIGLU_OAI",
+    "LIB_PATH",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -21,6 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libqmoe.so")
 FLAG_FORCE_GEMV = 0x1
 FLAG_FORCE_GROUPED = 0x2
 FLAG_FORCE_EXPERT_GEMV = 0x4
+FLAG_ACT_RELU2 = 0x8            # gate activation max(g, 0)^2 * u
+FLAG_ACT_SWIGLU_OAI = 0x10      # clamped SwiGLU (see include/moe.h)
 
 # Every symbol include/moe.h declares.
 EXPORTS = [

@@ -27,8 +27,10 @@ static bool cfg_ok(const moe_config* c) {
   // down: k * inter/32 items per output row spread over at most 4 per lane
   if ((long long)k * (I / 32) > 256) return false;
   const uint32_t force = c->flags & (MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_EXPERT_GEMV);
-  if (c->flags & ~force) return false;
+  const uint32_t act = c->flags & (MOE_FLAG_ACT_RELU2 | MOE_FLAG_ACT_SWIGLU_OAI);
+  if (c->flags & ~(force | act)) return false;
   if (force & (force - 1)) return false;          // at most one path may be forced
+  if (act & (act - 1)) return false;              // at most one activation
   // expert-major GEMV: one 32-code sub-block of a down row per lane of a wave
   if ((force & MOE_FLAG_FORCE_EXPERT_GEMV) && I > 2048) return false;
   return true;

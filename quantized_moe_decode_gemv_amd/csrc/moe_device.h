@@ -151,6 +151,21 @@ __device__ __forceinline__ float load_x_pairs(const uint16_t* xs, u32* X) {
   return x_pairs(r, X);
 }
 
+// Gate activation h = act(g, u): 0 SiLU(g) * u, 1 max(g, 0)^2 * u, 2 the
+// clamped SwiGLU g' * sigmoid(1.702 g') * (u' + 1), g' = min(g, 7),
+// u' = clamp(u, -7, 7). act is uniform over the launch.
+__device__ __forceinline__ float gate_act(float g, float u, int act) {
+  if (act == 1) {
+    const float r = fmaxf(g, 0.f);
+    return r * r * u;
+  }
+  if (act == 2) {
+    const float gc = fminf(g, 7.0f), uc = fminf(fmaxf(u, -7.0f), 7.0f);
+    return gc / (1.0f + expf(-1.702f * gc)) * (uc + 1.0f);
+  }
+  return g / (1.0f + expf(-g)) * u;
+}
+
 // sum_i (1024 + q_i) * h_i over one 32-code sub-block with fp16 h, two codes
 // per v_dot2_f32_f16 ((1024 + q) * h is exact in fp32). X[4d+c] holds the
 // fp16 pair (h[8d+c], h[8d+c+4]).

@@ -118,7 +118,7 @@ template <int IPL, int LPR, int U, int NT>
 __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const SlotDesc* __restrict__ slots,
-    _Float16* __restrict__ h16) {
+    _Float16* __restrict__ h16, int act) {
   constexpr int LG = ilog2(LPR), RPS = WAVE / LPR, RW = RPS * U, V = 2 * U * NT;
   static_assert((1 << LG) == LPR, "LPR must be a power of two");
   const int bpe = I / (4 * RW);                 // workgroups per expert
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
     const int u = (idx >> 1) / NT, tt = (idx >> 1) % NT;
     if (tsum_owner<V, LG>(lane) && !(idx & 1) && tt < nv) {
       const int r = r0 + u * RPS + rho;
-      h16[(size_t)(pos0 + c0 + tt) * I + pos8(r)] = (_Float16)(s / (1.0f + expf(-s)) * o);
+      h16[(size_t)(pos0 + c0 + tt) * I + pos8(r)] = (_Float16)gate_act(s, o, act);
     }
   }
 }
@@ -271,7 +271,8 @@ static hipError_t gateup_go(const Layout& d, const uint8_t* layer, const uint16_
   static_assert(RW <= 64, "four waves of RW rows must divide a multiple of 256");
   const long long blocks = (long long)nslots * (d.I / (4 * RW));
   hipLaunchKernelGGL((gateup_egemv_kernel<IPL, LPR, U, NT>), dim3((unsigned)blocks), dim3(BLOCK), 0, s,
-                     layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, slots, h16);
+                     layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, slots, h16,
+                     d.act);
   return hipGetLastError();
 }
 

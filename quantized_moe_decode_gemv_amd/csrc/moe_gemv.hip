@@ -219,7 +219,9 @@ __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__
 // Wave work unit: RPS*U consecutive intermediate rows of one (token, slot);
 // RPS = 64/LPR rows per step, LPR lanes per row, IPL sub-blocks per lane.
 // h[(t*k + s)*I + r] = SiLU(G_e[r]·x_t) * (U_e[r]·x_t).
-template <int IPL, int LPR, int U>
+// ACT: the gate activation as a template argument, so the epilogue on this
+// kernel's critical path carries no branch.
+template <int IPL, int LPR, int U, int ACT>
 __global__ __launch_bounds__(BLOCK) void gateup_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int E, int k,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids_in, const float* __restrict__ logits,
@@ -292,10 +294,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
     }
     pg = group_sum<LPR>(pg);
     pu = group_sum<LPR>(pu);
-    if (lam == 0) {
-      const float silu = pg / (1.0f + expf(-pg));
-      h[(size_t)ts * I + r0 + u * RPS + rho] = silu * pu;
-    }
+    if (lam == 0) h[(size_t)ts * I + r0 + u * RPS + rho] = gate_act(pg, pu, ACT);
   }
 }
 
@@ -561,23 +560,34 @@ hipError_t launch_topk(const Layout& d, const float* logits, int32_t* ids, float
   return hipGetLastError();
 }
 
-template <int IPL, int LPR, int U>
-static void gateup_go(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids, const float* logits,
-                      int32_t* ids_out, float* w_out, float* h, int T, bool fused, hipStream_t s, hipEvent_t ev0,
-                      hipEvent_t ev1) {
+template <int IPL, int LPR, int U, int ACT>
+static void gateup_go_act(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids,
+                          const float* logits, int32_t* ids_out, float* w_out, float* h, int T, bool fused,
+                          hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr int RPS = WAVE / LPR;
   const long long units = (long long)T * d.k * d.I / (RPS * U);
   const int blocks = (int)((units + 3) / 4);
   if (ev0 || ev1) {
     // measurement launch: the events bracket this kernel's execution
-    hipExtLaunchKernelGGL((gateup_kernel<IPL, LPR, U>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s, ev0, ev1, 0,
-                          layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
+    hipExtLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s, ev0, ev1,
+                          0, layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
                           ids_out, w_out, h, T, fused ? 1 : 0);
     return;
   }
-  hipLaunchKernelGGL((gateup_kernel<IPL, LPR, U>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s,
+  hipLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s,
                      layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
                      ids_out, w_out, h, T, fused ? 1 : 0);
+}
+
+template <int IPL, int LPR, int U>
+static void gateup_go(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids, const float* logits,
+                      int32_t* ids_out, float* w_out, float* h, int T, bool fused, hipStream_t s, hipEvent_t ev0,
+                      hipEvent_t ev1) {
+  switch (d.act) {
+    case 1: gateup_go_act<IPL, LPR, U, 1>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1); break;
+    case 2: gateup_go_act<IPL, LPR, U, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1); break;
+    default: gateup_go_act<IPL, LPR, U, 0>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1); break;
+  }
 }
 
 hipError_t launch_gateup(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids,

@@ -24,7 +24,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "moe_internal.h"
+#include "moe_device.h"
 
 namespace qmoe {
 namespace grouped {
@@ -35,8 +35,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int WAVE = 64;
-constexpr int BLOCK = 256;
 constexpr int KH = 128;            // K per stage (half a super-block)
 constexpr int XS = KH + 8;         // LDS row stride (halfs): 272 B = 16 mod 128, conflict-free 16-byte reads
 constexpr int NN = 2;              // 32-feature column blocks per wave
@@ -265,7 +263,7 @@ template <int WR>
 __global__ __launch_bounds__(BLOCK, 2) void gateup_grouped_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int E, int k, int ntiles,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
-    const int32_t* __restrict__ tile_off, _Float16* __restrict__ h16) {
+    const int32_t* __restrict__ tile_off, _Float16* __restrict__ h16, int act) {
   constexpr int MT = 32 * WR;
   __shared__ Smem<WR> sm;
   int tile, fb;
@@ -296,7 +294,7 @@ __global__ __launch_bounds__(BLOCK, 2) void gateup_grouped_kernel(
       const int row = 32 * r + 8 * (q >> 2) + 4 * kg + (q & 3);
       if (row < rows) {
         const float g = acc[r][0][q], u = acc[r][1][q];
-        h16[(pos0 + row) * I + col] = (_Float16)(g / (1.0f + expf(-g)) * u);
+        h16[(pos0 + row) * I + col] = (_Float16)gate_act(g, u, act);
       }
     }
 }
@@ -372,7 +370,8 @@ static hipError_t launch_wr(const Layout& d, const uint8_t* layer, const uint16_
   const int gu_units = tiles * (d.I / FB), dn_units = tiles * (d.H / FD);
   // grids padded to a multiple of 8 (the unit dealing assumes it); extra blocks exit
   hipLaunchKernelGGL((gateup_grouped_kernel<WR>), dim3((gu_units + 7) / 8 * 8), dim3(BLOCK), 0, s, layer + d.gu_off,
-                     d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, tiles, x, offsets, pairs, tile_off, h16);
+                     d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, tiles, x, offsets, pairs, tile_off, h16,
+                     d.act);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((down_grouped_kernel<WR>), dim3((dn_units + 7) / 8 * 8), dim3(BLOCK), 0, s, layer + d.dn_off,
@@ -422,7 +421,7 @@ template <int G>
 __global__ __launch_bounds__(BLOCK) void gateup_g16_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles,
-    _Float16* __restrict__ h16) {
+    _Float16* __restrict__ h16, int act) {
   constexpr int NH = (G + 1) / 2;               // super-blocks per wave (a group is half of one)
   __shared__ float red[4][2][4][WAVE];
   const int bpt = I / 16;
@@ -491,7 +490,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16_kernel(
     const float g = ((red[0][0][q][ln] + red[1][0][q][ln]) + red[2][0][q][ln]) + red[3][0][q][ln];
     const float u = ((red[0][1][q][ln] + red[1][1][q][ln]) + red[2][1][q][ln]) + red[3][1][q][ln];
     const int f = f0 + rr;
-    h16[(size_t)(tr.pos0 + tt) * I + (f & ~7) + nib_pos(f & 7)] = (_Float16)(g / (1.0f + expf(-g)) * u);
+    h16[(size_t)(tr.pos0 + tt) * I + (f & ~7) + nib_pos(f & 7)] = (_Float16)gate_act(g, u, act);
   }
 }
 
@@ -546,7 +545,7 @@ template <int G, int GD>
 static hipError_t launch_g16(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
                              const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, hipStream_t s) {
   hipLaunchKernelGGL((gateup_g16_kernel<G>), dim3(ntiles * (d.I / 16)), dim3(BLOCK), 0, s, layer + d.gu_off,
-                     d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16);
+                     d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16, d.act);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((down_g16_kernel<GD>), dim3(ntiles * (d.H / 64)), dim3(BLOCK), 0, s, layer + d.dn_off,

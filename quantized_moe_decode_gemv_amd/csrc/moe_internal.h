@@ -27,6 +27,7 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 //   down     per expert, per output row n: [codes I/2 B][headers I/256*16 B]
 struct Layout {
   int H, E, k, I, L, maxT;
+  int act;                      // gate activation: 0 SiLU, 1 squared ReLU, 2 clamped SwiGLU
   uint32_t flags;
   float eps;
   int nbH, nbI;                 // super-blocks per gate/up row and per down row
@@ -39,6 +40,7 @@ struct Layout {
   void init(const moe_config& c) {
     H = c.hidden; E = c.n_experts; k = c.top_k; I = c.inter; L = c.n_layers; maxT = c.max_tokens;
     flags = c.flags; eps = c.rms_eps;
+    act = (c.flags & MOE_FLAG_ACT_RELU2) ? 1 : ((c.flags & MOE_FLAG_ACT_SWIGLU_OAI) ? 2 : 0);
     nbH = H / QK; nbI = I / QK;
     rp_bytes = (size_t)2 * nbH * QBYTES;
     gu_expert_bytes = (size_t)I * rp_bytes;

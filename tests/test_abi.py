@@ -47,7 +47,11 @@ def test_status_strings():
     ((256, 8, 2, 2048, 1, 1, 4, 1e-6), True),       # expert-major GEMV: inter up to 2048
     ((256, 8, 2, 2304, 1, 1, 4, 1e-6), False),      # expert-major GEMV: inter above 2048
     ((256, 8, 2, 2304, 1, 1, 0, 1e-6), True),       # same shape without the flag
-    ((2048, 128, 8, 768, 1, 1, 8, 1e-6), False),    # unknown flag
+    ((2048, 128, 8, 768, 1, 1, 0x8, 1e-6), True),   # ReLU2 gate activation
+    ((2048, 128, 8, 768, 1, 1, 0x10, 1e-6), True),  # SwiGLU-OAI gate activation
+    ((2048, 128, 8, 768, 1, 1, 0x12, 1e-6), True),  # an activation and a forced path
+    ((2048, 128, 8, 768, 1, 1, 0x18, 1e-6), False), # two activations
+    ((2048, 128, 8, 768, 1, 1, 0x20, 1e-6), False), # unknown flag
     ((300, 8, 2, 512, 1, 1, 0, 1e-6), False),       # hidden not a multiple of 256
     ((768, 8, 2, 512, 1, 1, 0, 1e-6), False),       # hidden lane mapping unsupported
     ((256, 8, 9, 512, 1, 1, 0, 1e-6), False),       # k > E

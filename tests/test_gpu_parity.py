@@ -248,6 +248,65 @@ def test_forward_auto_path_boundary_qwen(qwen, T):
     _check_layer(qwen, xb, qwen.forward(xb), sample=sample)
 
 
+# ------------------------------------------------------------------ gate activations
+ACTS = [("relu2", q.FLAG_ACT_RELU2, oracle.ACT_RELU2), ("swiglu_oai", q.FLAG_ACT_SWIGLU_OAI, oracle.ACT_SWIGLU_OAI)]
+
+
+def _scaled_bf16(xb, factor):
+    """x * factor for a power-of-two factor, exact in bf16 (bits of finite normal values)."""
+    f = (xb.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _forward_with(plan, blob, xb, S, dev):
+    T = xb.shape[0]
+    x = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).to(dev)
+    out = torch.empty(T, S.hidden, dtype=torch.float32, device=dev)
+    ids = torch.empty(T, S.top_k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, S.top_k, dtype=torch.float32, device=dev)
+    plan.forward(blob, 0, x, T, out, ids=ids, w=w, scratch=plan.new_scratch(T, device=dev))
+    torch.cuda.synchronize()
+    return dict(y=out.cpu().numpy(), ids=ids.cpu().numpy(), w=w.cpu().numpy())
+
+
+@pytest.mark.parametrize("scale", [1, 8])
+@pytest.mark.parametrize("name,flag,act", ACTS, ids=[a[0] for a in ACTS])
+def test_gate_activations_every_path_qwen(qwen, name, flag, act, scale):
+    """Each non-default gate activation on every path of the Qwen3-30B-A3B-
+    shaped layer: one token (fused per-token GEMV), 8 tokens (expert-major
+    GEMV, and the per-token GEMV forced), 32 (16-pair MFMA tiles) and 256
+    (32-pair tiles), against the oracle with the same activation. Scaling x
+    by 8 (exact in bf16) puts the gate values past the SwiGLU clamps for a
+    good share of rows."""
+    S = qwen.shape
+    for T, extra in ((1, 0), (8, 0), (8, q.FLAG_FORCE_GEMV), (32, 0), (256, 0)):
+        plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=T, flags=flag | extra)
+        xb = _scaled_bf16(synth.x_bf16(S, 13, T, T=T), scale)
+        got = _forward_with(plan, qwen.blob, xb, S, qwen.dev)
+        sample = list(range(T)) if T <= 32 else list(range(0, T, 8)) + [T - 1]
+        ref = oracle.moe_layer(qwen.src, 0, xb[sample], act=act)
+        exempt = check_routing(got["ids"][sample], got["w"][sample], ref)
+        keep = [i for i in range(len(sample)) if i not in exempt]
+        err = rel_err(got["y"][sample][keep], ref["y"][keep])
+        assert err <= REL_TOL, f"{name} x{scale} T={T} flags={extra}: {err:.3e}"
+
+
+@pytest.mark.parametrize("name,flag,act", ACTS, ids=[a[0] for a in ACTS])
+def test_gate_activations_tiny(tiny, name, flag, act):
+    """Tiny layer (hidden 256: no 16-pair tiles): T = 1, 5 (expert-major
+    GEMV) and 40 (32-pair tiles), x scaled by 8."""
+    S = tiny.shape
+    for T in (1, 5, 40):
+        plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=2, max_tokens=T, flags=flag)
+        xb = _scaled_bf16(synth.x_bf16(S, 14, T, T=T), 8)
+        got = _forward_with(plan, tiny.blob, xb, S, tiny.dev)
+        ref = oracle.moe_layer(tiny.src, 0, xb, act=act)
+        exempt = check_routing(got["ids"], got["w"], ref)
+        keep = [t for t in range(T) if t not in exempt]
+        err = rel_err(got["y"][keep], ref["y"][keep])
+        assert err <= REL_TOL, f"{name} T={T}: {err:.3e}"
+
+
 # ------------------------------------------------------------------ routing and dispatch lists
 @pytest.mark.parametrize("T,zipf", [(8, None), (128, None), (4096, 1.1)])
 def test_route_from_logits_and_dispatch_lists(qwen, T, zipf):
