@@ -176,3 +176,95 @@ def test_full_stack_chained_step_in_bench_configuration(qwen_stack):
           f"x_next flips {flips}, stopped: {why}")
     assert exact >= 1
     assert np.array_equal(out[1]["x_in"], out[0]["xs"][0])
+
+
+def _chained_forward(plan, blob, L, H, k, x0, dev):
+    """The step as L chained moe_forward calls with the RMSNorm epilogue."""
+    xs = torch.zeros(L, H, dtype=torch.int16, device=dev)
+    ys = torch.zeros(L, H, dtype=torch.float32, device=dev)
+    ids = torch.zeros(L, k, dtype=torch.int32, device=dev)
+    ws = torch.zeros(L, k, dtype=torch.float32, device=dev)
+    xs[0].copy_(x0)
+    scratch = plan.new_scratch(1, device=dev)
+    for l in range(L):
+        nxt = xs[(l + 1) % L] if l + 1 < L else torch.zeros(H, dtype=torch.int16, device=dev)
+        plan.forward(blob, l, xs[l].view(1, H), 1, ys[l].view(1, H), x_next=nxt.view(1, H), ids=ids[l].view(1, k),
+                     w=ws[l].view(1, k), scratch=scratch)
+        if l + 1 == L:
+            last = nxt
+    torch.cuda.synchronize()
+    xs[0].copy_(last)
+    return xs, ys, ids, ws
+
+
+def _stack_once(plan, blob, L, H, k, x0, dev, graph, replays=1):
+    xs = torch.zeros(L, H, dtype=torch.int16, device=dev)
+    ys = torch.zeros(L, H, dtype=torch.float32, device=dev)
+    ids = torch.zeros(L, k, dtype=torch.int32, device=dev)
+    ws = torch.zeros(L, k, dtype=torch.float32, device=dev)
+    scratch = plan.new_scratch(1, device=dev)
+    stream = torch.cuda.Stream()
+    if not graph:
+        xs[0].copy_(x0)
+        torch.cuda.synchronize()
+        plan.stack_step(blob, xs, ys, 1, ids, ws, scratch=scratch, stream=stream)
+        torch.cuda.synchronize()
+        return [(xs.clone(), ys.clone(), ids.clone(), ws.clone())]
+    g = plan.capture_step(blob, xs, ys, 1, ids, ws, scratch=scratch, stream=stream)
+    outs = []
+    for _ in range(replays):
+        xs.zero_(), ys.zero_(), ids.zero_(), ws.zero_()
+        xs[0].copy_(x0)
+        other = torch.randn(1000, device=dev).sum()   # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.launch(stream)
+        torch.cuda.synchronize()
+        assert other.isfinite()
+        outs.append((xs.clone(), ys.clone(), ids.clone(), ws.clone()))
+    return outs
+
+
+def _assert_same(a, b, what):
+    for name, u, v in zip(("xs", "ys", "ids", "w"), a, b):
+        assert torch.equal(u, v), f"{what}: {name} differs"
+
+
+@pytest.mark.parametrize("hidden,E,k,inter,L,seed", [
+    (1024, 64, 4, 256, 5, 21),
+    (4096, 32, 4, 512, 4, 22),
+    (2048, 256, 8, 256, 3, 23),    # the most experts a plan takes
+    (2048, 100, 6, 512, 3, 24),    # expert count not a multiple of 64
+    (512, 16, 2, 256, 4, 25),      # router without the norm prologue: epilogue kernel per layer
+])
+def test_stack_step_equals_chained_forward(dev, hidden, E, k, inter, L, seed):
+    """One-token stacked step (each layer's input formed inside the next
+    router launch where the kernel has that prologue): eagerly and as graph
+    replays it must reproduce, bit for bit, the chained moe_forward calls
+    with the RMSNorm epilogue; step 0 is also held against the oracle's
+    trajectory."""
+    S = synth.Shape(f"stack-h{hidden}-e{E}", seed, hidden, E, k, inter)
+    plan = q.Plan(hidden, E, k, inter, n_layers=L, max_tokens=1)
+    blob = plan.upload_blob(layer_source(S), device=dev)
+    x0 = torch.from_numpy(synth.x_bf16(S, 3, 0)[0].view(np.int16)).to(dev)
+    ref = _chained_forward(plan, blob, L, hidden, k, x0, dev)
+    _assert_same(_stack_once(plan, blob, L, hidden, k, x0, dev, graph=False)[0], ref, "eager")
+    for i, o in enumerate(_stack_once(plan, blob, L, hidden, k, x0, dev, graph=True, replays=3)):
+        _assert_same(o, ref, f"graph replay {i}")
+    got = dict(xs=ref[0].cpu().numpy().view(np.uint16), ys=ref[1].cpu().numpy(), ids=ref[2].cpu().numpy())
+    _check_step_properties(S, got)
+    compared, exact, worst, flips, why = _compare_step(S, L, oracle.ExpertSource(S), x0.cpu().numpy().view(np.uint16),
+                                                       got)
+    assert exact >= 1 and compared >= 1
+
+
+def test_full_stack_step_equals_chained_forward(dev, qwen_stack):
+    """The 48-layer stack at hidden 2048 (the benchmark's blob): the step,
+    eager and as graph replays, equals the chained moe_forward calls bit for
+    bit."""
+    S, plan, blob, _ = qwen_stack
+    H, k = S.hidden, S.top_k
+    x0 = torch.from_numpy(synth.x_bf16(S, 4, 0)[0].view(np.int16)).to(dev)
+    ref = _chained_forward(plan, blob, 48, H, k, x0, dev)
+    _assert_same(_stack_once(plan, blob, 48, H, k, x0, dev, graph=False)[0], ref, "eager")
+    for i, o in enumerate(_stack_once(plan, blob, 48, H, k, x0, dev, graph=True, replays=2)):
+        _assert_same(o, ref, f"graph replay {i}")
