@@ -11,12 +11,18 @@ README, kernel table and MoE row; sparkinfer CuTe-DSL README, "moe"
 paragraph). Expert weights come from the shared seeded generator ``synth``
 (encoded blocks only); the oracle decodes them itself.
 
+Two expert weight encodings are decoded: 144-byte 4-bit super-blocks (256
+weights) and 17-byte MXFP4 blocks (32 weights: an E8M0 scale byte and 16 bytes
+of FP4 E2M1 codes). Functions taking blocks tell them apart by the last
+dimension (144 or 17 bytes).
+
 Parity status: every function here is pinned by the CPU tests in
-``tests/test_oracle_pins.py`` (worked block example, exhaustive 6-bit field
-sweep, fp16 table, library matmul, brute-force top-k, closed forms). One thing
-stays parity unpinned: the block encoding itself is our reading of "Q4_K"
-(the pages print no bit layout), so byte compatibility with any external Q4_K
-file is not claimed.
+``tests/test_oracle_pins.py`` (worked block examples, exhaustive 6-bit field
+sweep, fp16 table, the library's E8M0 and E4M3 decoders for the MXFP4 scale
+and codes, library matmul, brute-force top-k, closed forms). One thing stays
+parity unpinned: the block encodings are our readings (the pages print no
+bit layout for either), so byte compatibility with any external file is not
+claimed.
 """
 import ctypes
 import os
@@ -30,6 +36,9 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 QK = 256
 QBLOCK_BYTES = 144
+MXK = 32
+MXBLOCK_BYTES = 17
+FMT_Q4K, FMT_MXFP4 = 0, 1
 RMS_EPS = 1e-6
 
 
@@ -63,6 +72,20 @@ def lib():
         L.oracle_dequant_matrix.argtypes = [vp, i64, i64, vp]
         L.oracle_qgemv.restype = None
         L.oracle_qgemv.argtypes = [vp, i64, i64, vp, vp]
+        L.oracle_fp4.restype = f64
+        L.oracle_fp4.argtypes = [ctypes.c_int32]
+        L.oracle_e8m0.restype = f64
+        L.oracle_e8m0.argtypes = [ctypes.c_int32]
+        L.oracle_dequant_mx_block.restype = None
+        L.oracle_dequant_mx_block.argtypes = [vp, vp]
+        L.oracle_dequant_mx_matrix.restype = None
+        L.oracle_dequant_mx_matrix.argtypes = [vp, i64, i64, vp]
+        L.oracle_qgemv_fmt.restype = None
+        L.oracle_qgemv_fmt.argtypes = [vp, i64, i64, vp, vp, ctypes.c_int32]
+        L.oracle_expert_ffn_fmt.restype = None
+        L.oracle_expert_ffn_fmt.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, ctypes.c_int32, ctypes.c_int32]
+        L.oracle_moe_token_fmt.restype = None
+        L.oracle_moe_token_fmt.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, ctypes.c_int32, ctypes.c_int32]
         L.oracle_router_logits.restype = None
         L.oracle_router_logits.argtypes = [vp, i64, i64, vp, vp]
         L.oracle_topk.restype = None
@@ -115,6 +138,33 @@ def round_bf16(v):
 
 
 # ---------------------------------------------------------------- dequant / GEMV
+def block_format(blocks):
+    """(fmt, weights per block) from the block byte count (144 or 17)."""
+    nbytes = np.shape(blocks)[-1]
+    if nbytes == QBLOCK_BYTES:
+        return FMT_Q4K, QK
+    if nbytes == MXBLOCK_BYTES:
+        return FMT_MXFP4, MXK
+    raise ValueError(f"no block encoding of {nbytes} bytes")
+
+
+def fp4(code):
+    """FP4 E2M1 code -> value."""
+    return lib().oracle_fp4(int(code))
+
+
+def e8m0(e):
+    """E8M0 scale code -> 2^(e-127) (NaN for 255)."""
+    return lib().oracle_e8m0(int(e))
+
+
+def dequant_mx_block(blk):
+    blk = _c(blk, np.uint8).reshape(MXBLOCK_BYTES)
+    w = np.empty(MXK, dtype=np.float64)
+    lib().oracle_dequant_mx_block(_p(blk), _p(w))
+    return w
+
+
 def dequant_block(blk):
     blk = _c(blk, np.uint8).reshape(QBLOCK_BYTES)
     w = np.empty(QK, dtype=np.float64)
@@ -123,21 +173,24 @@ def dequant_block(blk):
 
 
 def dequant_matrix(blocks):
-    """[rows, cols/256, 144] uint8 -> fp64 [rows, cols]."""
+    """[rows, cols/K, bytes] uint8 (either encoding) -> fp64 [rows, cols]."""
     blocks = _c(blocks, np.uint8)
+    fmt, K = block_format(blocks)
     rows, nb = blocks.shape[0], blocks.shape[1]
-    w = np.empty((rows, nb * QK), dtype=np.float64)
-    lib().oracle_dequant_matrix(_p(blocks), rows, nb * QK, _p(w))
+    w = np.empty((rows, nb * K), dtype=np.float64)
+    fn = lib().oracle_dequant_mx_matrix if fmt == FMT_MXFP4 else lib().oracle_dequant_matrix
+    fn(_p(blocks), rows, nb * K, _p(w))
     return w
 
 
 def qgemv(blocks, x):
     blocks = _c(blocks, np.uint8)
+    fmt, K = block_format(blocks)
     rows, nb = blocks.shape[0], blocks.shape[1]
     x = _c(x, np.float64)
-    assert x.shape == (nb * QK,)
+    assert x.shape == (nb * K,)
     y = np.empty(rows, dtype=np.float64)
-    lib().oracle_qgemv(_p(blocks), rows, nb * QK, _p(x), _p(y))
+    lib().oracle_qgemv_fmt(_p(blocks), rows, nb * K, _p(x), _p(y), fmt)
     return y
 
 
@@ -195,12 +248,14 @@ def act(g, u, kind=ACT_SILU):
 # ---------------------------------------------------------------- FFN
 def expert_ffn(gate, up, down, x, return_h=False, act=ACT_SILU):
     gate, up, down = _c(gate, np.uint8), _c(up, np.uint8), _c(down, np.uint8)
-    I, H = gate.shape[0], gate.shape[1] * QK
-    assert up.shape == gate.shape and down.shape[0] == H and down.shape[1] * QK == I
+    fmt, K = block_format(gate)
+    I, H = gate.shape[0], gate.shape[1] * K
+    assert up.shape == gate.shape and down.shape[0] == H and down.shape[1] * K == I
+    assert block_format(down)[0] == fmt
     x = _c(x, np.float64)
     y = np.empty(H, dtype=np.float64)
     h = np.empty(I, dtype=np.float64)
-    lib().oracle_expert_ffn_act(_p(gate), _p(up), _p(down), H, I, _p(x), _p(y), _p(h), int(act))
+    lib().oracle_expert_ffn_fmt(_p(gate), _p(up), _p(down), H, I, _p(x), _p(y), _p(h), int(act), fmt)
     return (y, h) if return_h else y
 
 
@@ -211,7 +266,8 @@ def moe_token(gates, ups, downs, w, x_bf16, act=ACT_SILU):
     gates = [_c(g, np.uint8) for g in gates]
     ups = [_c(u, np.uint8) for u in ups]
     downs = [_c(d, np.uint8) for d in downs]
-    I, H = gates[0].shape[0], gates[0].shape[1] * QK
+    fmt, K = block_format(gates[0])
+    I, H = gates[0].shape[0], gates[0].shape[1] * K
     PA = ctypes.c_void_p * k
     ga = PA(*[g.ctypes.data for g in gates])
     ua = PA(*[u.ctypes.data for u in ups])
@@ -219,7 +275,7 @@ def moe_token(gates, ups, downs, w, x_bf16, act=ACT_SILU):
     w = _c(w, np.float64)
     x_bf16 = _c(x_bf16, np.uint16)
     y = np.empty(H, dtype=np.float64)
-    lib().oracle_moe_token_act(ga, ua, da, _p(w), k, H, I, _p(x_bf16), _p(y), int(act))
+    lib().oracle_moe_token_fmt(ga, ua, da, _p(w), k, H, I, _p(x_bf16), _p(y), int(act), fmt)
     return y
 
 

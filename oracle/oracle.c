@@ -15,7 +15,17 @@
  *    then sub-block mins m_0..m_7), then 128 bytes of 4-bit codes with
  *    sub-block j in bytes 16+16j..31+16j and element 2i of a sub-block in the
  *    low nibble of byte i. Weight = d*sc_j*q - dmin*m_j, exact in fp64;
- *  - the quantized GEMV y = Deq(W) x with fp64 accumulation;
+ *  - dequantization of a 17-byte MXFP4 block (the pages' FP4 expert
+ *    weights with bf16 activations and inline dequant: sparkinfer CuTe-DSL
+ *    README, "moe" paragraph; the 32-value E8M0 scale blocks: the same README,
+ *    compressed-collective table and the paragraph after it). The canonical
+ *    block read here: one E8M0 scale byte e (2^(e-127); 255 is NaN), then 16
+ *    bytes of FP4 E2M1 codes, element 2i in the low nibble of byte 1+i. An
+ *    E2M1 code is sign (bit 3), 2-bit exponent (bits 2-1, bias 1) and one
+ *    mantissa bit (bit 0); exponent 0 is subnormal (0 or 1/2). Weight =
+ *    E2M1(q) * 2^(e-127), exact in fp64;
+ *  - the quantized GEMV y = Deq(W) x with fp64 accumulation, over either
+ *    format (fmt 0: 4-bit super-blocks, fmt 1: MXFP4 blocks);
  *  - the router: logits = W_r x, exact top-k by a full stable sort on
  *    (logit descending, expert id ascending), and the softmax restricted to
  *    the selected experts (softmax over all experts then renormalised over
@@ -39,6 +49,8 @@
 
 #define QK 256
 #define QBLOCK_BYTES 144
+#define MXK 32
+#define MXBLOCK_BYTES 17
 
 /* ---------------------------------------------------------------- numbers */
 double oracle_f16(uint16_t h) {
@@ -102,6 +114,25 @@ void oracle_dequant_block(const uint8_t* blk, double* w) {
   }
 }
 
+/* FP4 E2M1 code (low 4 bits) -> value */
+double oracle_fp4(int32_t code) {
+  const int sign = (code >> 3) & 1, ex = (code >> 1) & 3, man = code & 1;
+  const double mag = ex == 0 ? 0.5 * man : ldexp(1.0 + 0.5 * man, ex - 1);
+  return sign ? -mag : mag;
+}
+
+/* E8M0 scale code -> 2^(e-127); 255 is NaN */
+double oracle_e8m0(int32_t e) { return e == 255 ? NAN : ldexp(1.0, (e & 255) - 127); }
+
+/* one MXFP4 block -> 32 weights */
+void oracle_dequant_mx_block(const uint8_t* blk, double* w) {
+  const double scale = oracle_e8m0(blk[0]);
+  for (int i = 0; i < MXK; ++i) {
+    const uint8_t byte = blk[1 + i / 2];
+    w[i] = oracle_fp4((i & 1) ? (byte >> 4) : (byte & 15)) * scale;
+  }
+}
+
 void oracle_dequant_matrix(const uint8_t* blocks, int64_t rows, int64_t cols, double* w) {
   int64_t nb = cols / QK;
   for (int64_t r = 0; r < rows; ++r)
@@ -109,18 +140,34 @@ void oracle_dequant_matrix(const uint8_t* blocks, int64_t rows, int64_t cols, do
       oracle_dequant_block(blocks + (r * nb + b) * QBLOCK_BYTES, w + r * cols + b * QK);
 }
 
-/* y[r] = sum_c Deq(W)[r][c] * x[c], fp64 */
-void oracle_qgemv(const uint8_t* blocks, int64_t rows, int64_t cols, const double* x, double* y) {
-  int64_t nb = cols / QK;
+void oracle_dequant_mx_matrix(const uint8_t* blocks, int64_t rows, int64_t cols, double* w) {
+  int64_t nb = cols / MXK;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b)
+      oracle_dequant_mx_block(blocks + (r * nb + b) * MXBLOCK_BYTES, w + r * cols + b * MXK);
+}
+
+/* y[r] = sum_c Deq(W)[r][c] * x[c], fp64; blocks [rows][cols/K][bytes] of
+ * format fmt (0: 4-bit super-blocks of 256, 1: MXFP4 blocks of 32) */
+void oracle_qgemv_fmt(const uint8_t* blocks, int64_t rows, int64_t cols, const double* x, double* y, int32_t fmt) {
+  const int K = fmt == 1 ? MXK : QK;
+  const int bytes = fmt == 1 ? MXBLOCK_BYTES : QBLOCK_BYTES;
+  int64_t nb = cols / K;
   double w[QK];
   for (int64_t r = 0; r < rows; ++r) {
     double acc = 0.0;
     for (int64_t b = 0; b < nb; ++b) {
-      oracle_dequant_block(blocks + (r * nb + b) * QBLOCK_BYTES, w);
-      for (int i = 0; i < QK; ++i) acc += w[i] * x[b * QK + i];
+      const uint8_t* blk = blocks + (r * nb + b) * bytes;
+      if (fmt == 1) oracle_dequant_mx_block(blk, w);
+      else oracle_dequant_block(blk, w);
+      for (int i = 0; i < K; ++i) acc += w[i] * x[b * K + i];
     }
     y[r] = acc;
   }
+}
+
+void oracle_qgemv(const uint8_t* blocks, int64_t rows, int64_t cols, const double* x, double* y) {
+  oracle_qgemv_fmt(blocks, rows, cols, x, y, 0);
 }
 
 /* ---------------------------------------------------------------- router */
@@ -178,18 +225,24 @@ double oracle_act(double g, double u, int32_t act) {
   return oracle_silu(g) * u;
 }
 
-/* y = D act(G x, U x); G, U: [I x H] blocks, D: [H x I] blocks */
-void oracle_expert_ffn_act(const uint8_t* gate, const uint8_t* up, const uint8_t* down,
-                           int64_t H, int64_t I, const double* x, double* y, double* h_out, int32_t act) {
+/* y = D act(G x, U x); G, U: [I x H] blocks, D: [H x I] blocks of format fmt */
+void oracle_expert_ffn_fmt(const uint8_t* gate, const uint8_t* up, const uint8_t* down,
+                           int64_t H, int64_t I, const double* x, double* y, double* h_out, int32_t act,
+                           int32_t fmt) {
   double* g = (double*)malloc(sizeof(double) * (size_t)I);
   double* u = (double*)malloc(sizeof(double) * (size_t)I);
-  oracle_qgemv(gate, I, H, x, g);
-  oracle_qgemv(up, I, H, x, u);
+  oracle_qgemv_fmt(gate, I, H, x, g, fmt);
+  oracle_qgemv_fmt(up, I, H, x, u, fmt);
   for (int64_t i = 0; i < I; ++i) g[i] = oracle_act(g[i], u[i], act);
   if (h_out) memcpy(h_out, g, sizeof(double) * (size_t)I);
-  oracle_qgemv(down, H, I, g, y);
+  oracle_qgemv_fmt(down, H, I, g, y, fmt);
   free(g);
   free(u);
+}
+
+void oracle_expert_ffn_act(const uint8_t* gate, const uint8_t* up, const uint8_t* down,
+                           int64_t H, int64_t I, const double* x, double* y, double* h_out, int32_t act) {
+  oracle_expert_ffn_fmt(gate, up, down, H, I, x, y, h_out, act, 0);
 }
 
 void oracle_expert_ffn(const uint8_t* gate, const uint8_t* up, const uint8_t* down,
@@ -199,18 +252,24 @@ void oracle_expert_ffn(const uint8_t* gate, const uint8_t* up, const uint8_t* do
 
 /* One token through one MoE layer given its selected experts' blocks.
  * gate/up/down: arrays of k pointers (expert of slot s); w: k routing weights. */
-void oracle_moe_token_act(const uint8_t* const* gate, const uint8_t* const* up, const uint8_t* const* down,
+void oracle_moe_token_fmt(const uint8_t* const* gate, const uint8_t* const* up, const uint8_t* const* down,
                           const double* w, int64_t k, int64_t H, int64_t I, const uint16_t* x_bf16,
-                          double* y, int32_t act) {
+                          double* y, int32_t act, int32_t fmt) {
   double* x = (double*)malloc(sizeof(double) * (size_t)H);
   double* ys = (double*)malloc(sizeof(double) * (size_t)H);
   for (int64_t i = 0; i < H; ++i) { x[i] = oracle_bf16(x_bf16[i]); y[i] = 0.0; }
   for (int64_t s = 0; s < k; ++s) {
-    oracle_expert_ffn_act(gate[s], up[s], down[s], H, I, x, ys, NULL, act);
+    oracle_expert_ffn_fmt(gate[s], up[s], down[s], H, I, x, ys, NULL, act, fmt);
     for (int64_t i = 0; i < H; ++i) y[i] += w[s] * ys[i];
   }
   free(x);
   free(ys);
+}
+
+void oracle_moe_token_act(const uint8_t* const* gate, const uint8_t* const* up, const uint8_t* const* down,
+                          const double* w, int64_t k, int64_t H, int64_t I, const uint16_t* x_bf16,
+                          double* y, int32_t act) {
+  oracle_moe_token_fmt(gate, up, down, w, k, H, I, x_bf16, y, act, 0);
 }
 
 void oracle_moe_token(const uint8_t* const* gate, const uint8_t* const* up, const uint8_t* const* down,

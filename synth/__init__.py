@@ -3,8 +3,9 @@
 The only module both the GPU library's callers and the CPU oracle draw inputs
 from. It holds no step of the MoE computation: it makes Gaussian weights,
 activations and logits from counter-based streams and encodes expert weights
-into canonical 144-byte 4-bit super-blocks (see ``synth.c`` for the layout and
-the quantizer). Both sides decode those blocks with their own code.
+into canonical 144-byte 4-bit super-blocks or 17-byte MXFP4 blocks (see
+``synth.c`` for the layouts and the quantizers; a shape's ``fmt`` picks one).
+Both sides decode those blocks with their own code.
 
 Shapes follow the pages' model: a Qwen3-30B-A3B-shaped MoE layer (hidden 2048,
 128 experts, top-8, expert intermediate 768) kept quantized-resident, and a
@@ -26,7 +27,12 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 
 QK = 256
 QBLOCK_BYTES = 144
+MXK = 32
+MXBLOCK_BYTES = 17
 WEIGHT_SIGMA = 0.02
+
+# expert weight encodings
+FMT_Q4K, FMT_MXFP4 = 0, 1
 
 # stream kinds (second key component)
 _K_EXPERT, _K_ROUTER, _K_X, _K_LOGITS, _K_PERM = 0, 1, 2, 3, 4
@@ -70,6 +76,12 @@ def lib():
         L.synth_q4k_matrix.argtypes = [u64, i64, i64, f32, vp, ctypes.c_int]
         L.synth_q4k_matrices.restype = None
         L.synth_q4k_matrices.argtypes = [vp, i64, i64, i64, f32, vp, ctypes.c_int]
+        L.synth_quantize_mx_block.restype = None
+        L.synth_quantize_mx_block.argtypes = [vp, vp]
+        L.synth_quantize_mx_rows.restype = None
+        L.synth_quantize_mx_rows.argtypes = [vp, i64, i64, vp]
+        L.synth_mx_matrices.restype = None
+        L.synth_mx_matrices.argtypes = [vp, i64, i64, i64, f32, vp, ctypes.c_int]
         L.synth_philox4x32_10.restype = None
         L.synth_philox4x32_10.argtypes = [vp, vp, vp]
         _lib = L
@@ -82,22 +94,32 @@ def _ptr(a):
 
 @dataclass(frozen=True)
 class Shape:
-    """One MoE layer shape. ``model`` seeds the weight streams."""
+    """One MoE layer shape. ``model`` seeds the weight streams; ``fmt``
+    picks the expert weight encoding (the same Gaussian weights either way)."""
     name: str
     model: int
     hidden: int
     n_experts: int
     top_k: int
     inter: int
+    fmt: int = FMT_Q4K
+
+    @property
+    def block(self):
+        """(weights per block, bytes per block) of the encoding."""
+        return (MXK, MXBLOCK_BYTES) if self.fmt == FMT_MXFP4 else (QK, QBLOCK_BYTES)
 
     @property
     def expert_bytes(self):
         """Bytes of one expert's three encoded matrices (gate, up, down)."""
-        return 3 * self.inter * self.hidden // QK * QBLOCK_BYTES
+        K, B = self.block
+        return 3 * self.inter * self.hidden // K * B
 
 
 TINY = Shape("tiny", 1, 256, 8, 2, 512)
 QWEN3_30B_A3B = Shape("qwen3-30b-a3b-moe", 2, 2048, 128, 8, 768)
+# the same layer (same Gaussian weights) with MXFP4 expert weights
+QWEN3_30B_A3B_MXFP4 = Shape("qwen3-30b-a3b-moe-mxfp4", 2, 2048, 128, 8, 768, FMT_MXFP4)
 
 
 # ---------------------------------------------------------------- primitives
@@ -124,11 +146,16 @@ def bf16_bits_to_f32(b):
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def quantize_rows(w):
-    """Encode float32 [rows, cols] (cols % 256 == 0) into canonical blocks
-    [rows, cols/256, 144] uint8."""
+def quantize_rows(w, fmt=FMT_Q4K):
+    """Encode float32 [rows, cols] into canonical blocks: [rows, cols/256, 144]
+    uint8 super-blocks, or [rows, cols/32, 17] MXFP4 blocks."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     rows, cols = w.shape
+    if fmt == FMT_MXFP4:
+        assert cols % MXK == 0
+        out = np.empty((rows, cols // MXK, MXBLOCK_BYTES), dtype=np.uint8)
+        lib().synth_quantize_mx_rows(_ptr(w), rows, cols, _ptr(out))
+        return out
     assert cols % QK == 0
     out = np.empty((rows, cols // QK, QBLOCK_BYTES), dtype=np.uint8)
     lib().synth_quantize_rows(_ptr(w), rows, cols, _ptr(out))
@@ -141,7 +168,10 @@ def expert_matrix_shape(shape, mat):
 
 
 def expert_matrix(shape, layer, expert, mat, nthreads=0):
-    """Canonical blocks of one expert matrix: [rows, cols/256, 144] uint8."""
+    """Canonical blocks of one expert matrix: [rows, cols/K, bytes] uint8 in
+    the shape's encoding."""
+    if shape.fmt == FMT_MXFP4:
+        return layer_experts(shape, layer, mat, [expert], nthreads)[0]
     rows, cols = expert_matrix_shape(shape, mat)
     out = np.empty((rows, cols // QK, QBLOCK_BYTES), dtype=np.uint8)
     k = key(shape.model, _K_EXPERT, layer, expert, mat)
@@ -158,15 +188,17 @@ def expert_matrix_f32(shape, layer, expert, mat):
 
 def layer_experts(shape, layer, mat, experts=None, nthreads=0):
     """Canonical blocks of one matrix kind for many experts of a layer:
-    [n, rows, cols/256, 144] uint8 (all experts when ``experts`` is None)."""
+    [n, rows, cols/K, bytes] uint8 (all experts when ``experts`` is None)."""
     if experts is None:
         experts = range(shape.n_experts)
     experts = list(experts)
     rows, cols = expert_matrix_shape(shape, mat)
+    K, B = shape.block
     keys = np.array([key(shape.model, _K_EXPERT, layer, e, mat) for e in experts], dtype=np.uint64)
-    out = np.empty((len(experts), rows, cols // QK, QBLOCK_BYTES), dtype=np.uint8)
+    out = np.empty((len(experts), rows, cols // K, B), dtype=np.uint8)
     if len(experts):
-        lib().synth_q4k_matrices(_ptr(keys), len(experts), rows, cols, WEIGHT_SIGMA, _ptr(out), nthreads)
+        gen = lib().synth_mx_matrices if shape.fmt == FMT_MXFP4 else lib().synth_q4k_matrices
+        gen(_ptr(keys), len(experts), rows, cols, WEIGHT_SIGMA, _ptr(out), nthreads)
     return out
 
 

@@ -22,6 +22,15 @@
  * 16+16j..31+16j, element 2i of the sub-block in the low nibble of byte i and
  * element 2i+1 in the high nibble. A weight decodes as d*sc_j*q - dmin*m_j.
  * The quantizer is plain round-to-nearest per sub-block (no search).
+ *
+ * MXFP4 encoding (the pages' FP4 expert weights with 32-value E8M0 scale
+ * blocks): 17 bytes per 32 weights, one E8M0 scale byte e (2^(e-127)) then
+ * 16 bytes of FP4 E2M1 codes, element 2i in the low nibble of byte 1+i. The
+ * quantizer takes the shared exponent floor(log2(max|x|)) - 2 (2 is the
+ * largest E2M1 exponent), kept to e in [2, 254] (so every nonzero weight is a
+ * normal bf16 and fp32 number), and rounds x / 2^(e-127) to the nearest E2M1
+ * value, ties to the even code, saturating at +-6. An all-zero block gets
+ * e = 127 and zero codes.
  */
 #include <stdint.h>
 #include <string.h>
@@ -30,6 +39,8 @@
 
 #define QK 256
 #define QBLOCK_BYTES 144
+#define MXK 32
+#define MXBLOCK_BYTES 17
 
 /* ---------------- Philox4x32-10 ---------------- */
 static inline void philox_round(uint32_t c[4], const uint32_t k[2]) {
@@ -206,6 +217,67 @@ void synth_quantize_block(const float* x, uint8_t* blk) {
       int q = step > 0 ? clampi(rint((x[32 * j + i] + off) / step), 0, 15) : 0;
       uint8_t* p = &blk[16 + 16 * j + i / 2];
       *p |= (uint8_t)((i & 1) ? (q << 4) : q);
+    }
+  }
+}
+
+/* ---------------- round-to-nearest MXFP4 block quantizer ---------------- */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* encode one block of 32 weights into 17 bytes */
+void synth_quantize_mx_block(const float* x, uint8_t* blk) {
+  double amax = 0.0;
+  for (int i = 0; i < MXK; ++i) {
+    const double a = fabs((double)x[i]);
+    if (a > amax) amax = a;
+  }
+  int e = 127;
+  if (amax > 0.0) {
+    e = (int)floor(log2(amax)) - 2 + 127;
+    if (e < 2) e = 2;
+    if (e > 254) e = 254;
+  }
+  const double scale = ldexp(1.0, e - 127);
+  memset(blk, 0, MXBLOCK_BYTES);
+  blk[0] = (uint8_t)e;
+  for (int i = 0; i < MXK; ++i) {
+    const double v = (double)x[i] / scale;
+    const double a = fabs(v);
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+      const double dc = fabs(a - E2M1_MAG[c]), db = fabs(a - E2M1_MAG[best]);
+      if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    }
+    const int code = best | ((v < 0.0 && best != 0) ? 8 : 0);
+    blk[1 + i / 2] |= (uint8_t)((i & 1) ? (code << 4) : code);
+  }
+}
+
+/* rows x cols float weights (cols % 32 == 0) -> rows x cols/32 MXFP4 blocks */
+void synth_quantize_mx_rows(const float* w, int64_t rows, int64_t cols, uint8_t* out) {
+  int64_t nb = cols / MXK;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b)
+      synth_quantize_mx_block(w + r * cols + b * MXK, out + (r * nb + b) * MXBLOCK_BYTES);
+}
+
+/* Many matrices, as synth_q4k_matrices, encoded as MXFP4 blocks (the same
+ * N(0, sigma) elements: element index r*cols + c of each stream). */
+void synth_mx_matrices(const uint64_t* keys, int64_t nmat, int64_t rows, int64_t cols, float sigma,
+                       uint8_t* out, int nthreads) {
+  int64_t nb = cols / MXK;
+  int64_t per = rows * nb * MXBLOCK_BYTES;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+  {
+    float buf[MXK];
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < nmat * rows; ++t) {
+      int64_t mi = t / rows, r = t % rows;
+      for (int64_t b = 0; b < nb; ++b) {
+        synth_normal_f32(keys[mi], (uint64_t)(r * cols + b * MXK), MXK, sigma, buf);
+        synth_quantize_mx_block(buf, out + mi * per + (r * nb + b) * MXBLOCK_BYTES);
+      }
     }
   }
 }

@@ -358,3 +358,128 @@ def test_rmsnorm_unit_rms_and_scale_invariance():
     ms = np.mean((v * 1e-3) ** 2)
     assert np.isclose(np.sqrt(np.mean(r3 * r3)), np.sqrt(ms / (ms + 1e-6)), rtol=1e-12)
     assert all(rb[i] == oracle.round_bf16(r[i]) for i in range(0, 2048, 97))
+
+
+# ------------------------------------------------------------------ MXFP4 codec
+MXB = oracle.MXBLOCK_BYTES
+
+
+def _load_mx_worked_example(golden_dir):
+    blk = w = None
+    with open(os.path.join(golden_dir, "mxfp4_worked_example.txt")) as f:
+        for line in f:
+            if line.startswith("block_hex "):
+                blk = np.frombuffer(bytes.fromhex(line.split()[1]), dtype=np.uint8)
+            elif line.startswith("weights_eighths "):
+                w = np.array([float(v) for v in line.split()[1:]], dtype=np.float64) / 8.0
+    return blk, w
+
+
+def _mx_block(e, codes):
+    """Independent encoder for test blocks: scale byte, then code pairs."""
+    blk = bytearray(MXB)
+    blk[0] = int(e)
+    for i, c in enumerate(codes):
+        blk[1 + i // 2] |= (int(c) << 4) if (i & 1) else int(c)
+    return np.frombuffer(bytes(blk), dtype=np.uint8)
+
+
+def test_mx_worked_example_block(golden_dir):
+    blk, w = _load_mx_worked_example(golden_dir)
+    assert blk.size == MXB and w.size == 32
+    got = oracle.dequant_mx_block(blk)
+    assert np.array_equal(got, w)
+    assert got[7] == 0.75 and got[9] == -1 / 16 and got[31] == -0.75
+
+
+def test_e8m0_every_code_matches_library_decode():
+    """All 256 scale codes against torch's float8_e8m0fnu conversion."""
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    lib_vals = codes.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    mine = np.array([oracle.e8m0(e) for e in range(256)])
+    assert np.isnan(mine[255]) and np.isnan(lib_vals[255])
+    assert np.array_equal(mine[:255], lib_vals[:255])
+
+
+def test_fp4_every_code_matches_library_e4m3_decode():
+    """Each E2M1 code re-encoded as the float8 E4M3 number of the same sign,
+    unbiased exponent and mantissa (E2M1 exponent bias 1, one mantissa bit;
+    E4M3 bias 7, three mantissa bits; the E2M1 subnormal 1/2 is the normal
+    2^-1), decoded by torch's float8_e4m3fn conversion; plus the format's
+    invariants: sign symmetry, strictly increasing magnitudes, largest 6."""
+    import torch
+    bits = []
+    for c in range(16):
+        s, ex, m = c >> 3, (c >> 1) & 3, c & 1
+        if ex == 0 and m == 0:
+            e4 = 0                                    # zero
+        elif ex == 0:
+            e4 = (s << 7) | ((-1 + 7) << 3)           # 2^-1
+        else:
+            e4 = (s << 7) | ((ex - 1 + 7) << 3) | (m << 2)
+        bits.append(e4)
+    lib_vals = torch.tensor(bits, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    mine = np.array([oracle.fp4(c) for c in range(16)])
+    assert np.array_equal(np.abs(mine), np.abs(lib_vals.numpy()))
+    assert np.array_equal(np.sign(mine[9:]), -np.ones(7)) and np.array_equal(mine[8:], -mine[:8])
+    assert np.all(np.diff(mine[:8]) > 0) and mine[7] == 6.0 and mine[1] == 0.5
+
+
+def test_mx_every_nibble_position_and_scale():
+    """A single nonzero code at every element position (the nibble order) and
+    every usable scale code 1..254 (the power of two applied)."""
+    for i in range(32):
+        codes = np.zeros(32, np.int64)
+        codes[i] = 5                                   # 3.0
+        got = oracle.dequant_mx_block(_mx_block(127, codes))
+        ref = np.zeros(32)
+        ref[i] = 3.0
+        assert np.array_equal(got, ref), i
+    for e in range(1, 255):
+        got = oracle.dequant_mx_block(_mx_block(e, [2] * 32))   # 1.0 each
+        assert np.all(got == 2.0 ** (e - 127)), e
+
+
+@pytest.mark.parametrize("mat", [synth.GATE, synth.DOWN])
+def test_mx_qgemv_matches_library_matmul(mat):
+    S = synth.Shape("tiny-mx", 1, 256, 8, 2, 512, synth.FMT_MXFP4)
+    blocks = synth.expert_matrix(S, 0, 1, mat)
+    assert blocks.shape[-1] == MXB
+    W = oracle.dequant_matrix(blocks)
+    # the matrix decoder is the block decoder applied block by block
+    assert np.array_equal(W[3, 64:96], oracle.dequant_mx_block(blocks[3, 2]))
+    x = np.random.default_rng(2).standard_normal(W.shape[1])
+    y = oracle.qgemv(blocks, x)
+    assert np.allclose(y, W @ x, rtol=1e-12, atol=1e-12 * np.abs(W).sum(1).max())
+
+
+def test_mx_quantizer_bound_and_idempotence():
+    """The shared generator's MXFP4 encoder and the oracle's decoder agree:
+    each decoded weight is within half a grid step of its Gaussian value
+    (values beyond 6 * scale saturate to 6 * scale), and re-encoding the
+    decoded weights gives the same blocks."""
+    S = synth.Shape("tiny-mx", 1, 256, 8, 2, 512, synth.FMT_MXFP4)
+    w = synth.expert_matrix_f32(S, 0, 3, synth.UP).astype(np.float64)
+    blocks = synth.expert_matrix(S, 0, 3, synth.UP)
+    deq = oracle.dequant_matrix(blocks)
+    scale = np.array([[oracle.e8m0(e) for e in row] for row in blocks[:, :, 0]])
+    sc = np.repeat(scale, 32, axis=1)
+    a = np.abs(w) / sc
+    half_step = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0)) * sc
+    sat = a > 6
+    assert np.all(np.abs(deq - w)[~sat] <= half_step[~sat] * (1 + 1e-12))
+    assert np.all(np.abs(deq[sat]) == 6 * sc[sat])
+    assert np.array_equal(synth.quantize_rows(deq.astype(np.float32), synth.FMT_MXFP4), blocks)
+
+
+def test_mx_expert_ffn_matches_dense_numpy():
+    S = synth.Shape("tiny-mx", 1, 256, 8, 2, 512, synth.FMT_MXFP4)
+    src = oracle.ExpertSource(S)
+    x = oracle.bf16_array(synth.x_bf16(S, 0, 0)[0])
+    y = oracle.expert_ffn(*src.blocks(0, 5), x)
+    assert np.allclose(y, _dense_ffn(src, 0, 5, x), rtol=1e-11, atol=1e-12)
+    res = oracle.moe_layer(src, 0, synth.x_bf16(S, 0, 0))
+    ids, w = res["ids"][0], res["w"][0]
+    ref = sum(w[s] * _dense_ffn(src, 0, ids[s], x) for s in range(S.top_k))
+    assert np.allclose(res["y"][0], ref, rtol=1e-11, atol=1e-13)
