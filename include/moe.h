@@ -69,6 +69,15 @@ enum moe_status {
 #define MOE_FLAG_ACT_RELU2 0x8u          /* max(g, 0)^2 * u */
 #define MOE_FLAG_ACT_SWIGLU_OAI 0x10u    /* g' * sigmoid(1.702 g') * (u' + 1), g' = min(g, 7), u' = clamp(u, -7, 7) */
 
+/* Expert weight encoding (default: 144-byte 4-bit super-blocks of 256
+ * weights). MXFP4: the pages' FP4 experts with bf16 activations and inline
+ * dequant (sparkinfer CuTe-DSL README, "moe" paragraph), in 17-byte blocks of
+ * 32 weights: one E8M0 scale byte e (2^(e-127)), then 16 bytes of FP4 E2M1
+ * codes, element 2i in the low nibble of byte 1+i. Scale codes 0 and 255
+ * are rejected by the packer. Runs on the per-token GEMV path for every T;
+ * a forced batched path is unsupported with it. */
+#define MOE_FLAG_WEIGHTS_MXFP4 0x20u
+
 typedef struct moe_config {
   int32_t hidden;      /* H: multiple of 256; 256, 512, 1024 or a multiple of 2048 up to 8192 */
   int32_t n_experts;   /* E: 1..256 */
@@ -99,11 +108,13 @@ size_t moe_scratch_bytes(const moe_plan* plan, int32_t T);     /* device scratch
 
 /* ---------------------------------------------------------------- packing
  * Canonical input: for one layer, gate_host and up_host are
- * [E][inter][hidden/256] blocks of 144 bytes, down_host is
- * [E][hidden][inter/256] blocks, router_host is fp32 [E][hidden]; all
- * row-major, host memory, read only. The device layout written to
- * dst_host (moe_layer_bytes, host memory owned by the caller) is private to
- * the library; the caller copies it to blob + moe_layer_offset(layer).
+ * [E][inter][hidden/K] blocks, down_host is [E][hidden][inter/K] blocks
+ * (K = 256 and 144-byte blocks, or with MOE_FLAG_WEIGHTS_MXFP4 K = 32 and
+ * 17-byte blocks), router_host is fp32 [E][hidden]; all row-major, host
+ * memory, read only. The device layout written to dst_host (moe_layer_bytes,
+ * host memory owned by the caller) is private to the library; the caller
+ * copies it to blob + moe_layer_offset(layer). moe_pack_layer returns
+ * MOE_ERR_INVALID_ARGUMENT for an MXFP4 scale code of 0 or 255.
  */
 int moe_pack_header(const moe_plan* plan, void* dst_host);
 int moe_pack_layer(const moe_plan* plan, const uint8_t* gate_host, const uint8_t* up_host,

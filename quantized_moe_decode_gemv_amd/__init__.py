@@ -13,6 +13,7 @@ import numpy as np
 __all__ = [
     "MoeError", "Config", "RouteOut", "Plan", "load", "is_supported", "status_string",
     "FLAG_FORCE_GEMV", "FLAG_FORCE_GROUPED", "FLAG_FORCE_EXPERT_GEMV", "FLAG_ACT_RELU2", "FLAG_ACT_SWIGLU_OAI",
+    "FLAG_WEIGHTS_MXFP4",
     "LIB_PATH",
 ]
 
@@ -24,6 +25,7 @@ FLAG_FORCE_GROUPED = 0x2
 FLAG_FORCE_EXPERT_GEMV = 0x4
 FLAG_ACT_RELU2 = 0x8            # gate activation max(g, 0)^2 * u
 FLAG_ACT_SWIGLU_OAI = 0x10      # clamped SwiGLU (see include/moe.h)
+FLAG_WEIGHTS_MXFP4 = 0x20       # MXFP4 expert blocks (17 bytes per 32 weights) instead of 4-bit super-blocks
 
 # Every symbol include/moe.h declares.
 EXPORTS = [
@@ -157,6 +159,8 @@ class Plan:
         self._h = h
         self.hidden, self.n_experts, self.top_k, self.inter = hidden, n_experts, top_k, inter
         self.n_layers, self.max_tokens = n_layers, max_tokens
+        # canonical block of the expert weights: (weights, bytes)
+        self.block = (32, 17) if flags & FLAG_WEIGHTS_MXFP4 else (256, 144)
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -196,7 +200,8 @@ class Plan:
         up = np.ascontiguousarray(up, dtype=np.uint8)
         down = np.ascontiguousarray(down, dtype=np.uint8)
         router = np.ascontiguousarray(router, dtype=np.float32)
-        assert gate.size == E * I * H // 256 * 144 and up.size == gate.size and down.size == gate.size
+        K, B = self.block
+        assert gate.size == E * I * H // K * B and up.size == gate.size and down.size == gate.size
         assert router.shape == (E, H)
         if out is None:
             out = np.empty(self.layer_bytes(), dtype=np.uint8)
@@ -208,9 +213,10 @@ class Plan:
     def unpack_layer(self, packed):
         E, H, I = self.n_experts, self.hidden, self.inter
         packed = np.ascontiguousarray(packed, dtype=np.uint8)
-        gate = np.empty((E, I, H // 256, 144), dtype=np.uint8)
+        K, B = self.block
+        gate = np.empty((E, I, H // K, B), dtype=np.uint8)
         up = np.empty_like(gate)
-        down = np.empty((E, H, I // 256, 144), dtype=np.uint8)
+        down = np.empty((E, H, I // K, B), dtype=np.uint8)
         router = np.empty((E, H), dtype=np.float32)
         _check(load().moe_unpack_layer(self._h, _np_ptr(packed), _np_ptr(gate), _np_ptr(up), _np_ptr(down),
                                        _np_ptr(router)), "moe_unpack_layer")

@@ -28,7 +28,10 @@ static bool cfg_ok(const moe_config* c) {
   if ((long long)k * (I / 32) > 256) return false;
   const uint32_t force = c->flags & (MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_EXPERT_GEMV);
   const uint32_t act = c->flags & (MOE_FLAG_ACT_RELU2 | MOE_FLAG_ACT_SWIGLU_OAI);
-  if (c->flags & ~(force | act)) return false;
+  const uint32_t fmt = c->flags & MOE_FLAG_WEIGHTS_MXFP4;
+  if (c->flags & ~(force | act | fmt)) return false;
+  // MXFP4 weights run on the per-token GEMV path only
+  if (fmt && (force & (MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_EXPERT_GEMV))) return false;
   if (force & (force - 1)) return false;          // at most one path may be forced
   if (act & (act - 1)) return false;              // at most one activation
   // expert-major GEMV: one 32-code sub-block of a down row per lane of a wave
@@ -83,6 +86,7 @@ extern "C" int moe_pack_header(const moe_plan* plan, void* dst_host) {
   h.n_layers = plan->d.L;
   h.layer_bytes = plan->d.layer_bytes;
   h.header_bytes = HEADER_BYTES;
+  h.weight_format = plan->d.fmt;
   memcpy(dst_host, &h, sizeof(h));
   return MOE_OK;
 }
@@ -93,7 +97,8 @@ extern "C" int moe_blob_check(const moe_plan* plan, const void* header_host) {
   memcpy(&h, header_host, sizeof(h));
   const Layout& d = plan->d;
   if (h.magic != BLOB_MAGIC || h.version != BLOB_VERSION || h.hidden != d.H || h.n_experts != d.E ||
-      h.inter != d.I || h.n_layers != d.L || h.layer_bytes != d.layer_bytes || h.header_bytes != HEADER_BYTES)
+      h.inter != d.I || h.n_layers != d.L || h.layer_bytes != d.layer_bytes || h.header_bytes != HEADER_BYTES ||
+      h.weight_format != d.fmt)
     return MOE_ERR_BLOB_MISMATCH;
   return MOE_OK;
 }
@@ -108,6 +113,65 @@ static inline void join_block(const uint8_t* hdr, const uint8_t* codes, uint8_t*
   memcpy(blk + QHDR, codes, QCODES);
 }
 
+// MXFP4 rows: canonical [scale][16 code bytes] blocks <-> [codes][scales]
+static bool mx_scale_ok(uint8_t e) { return e != 0 && e != 255; }
+
+static int pack_mx_layer(const Layout& d, const uint8_t* gate, const uint8_t* up, const uint8_t* down,
+                         uint8_t* dst) {
+  const int nbH = d.H / MXK, nbI = d.I / MXK;
+  for (int e = 0; e < d.E; ++e) {
+    for (int r = 0; r < d.I; ++r) {
+      uint8_t* rp = dst + d.gu_off + (size_t)e * d.gu_expert_bytes + (size_t)r * d.rp_bytes;
+      for (int m = 0; m < 2; ++m) {          // gate, up
+        const uint8_t* src = (m ? up : gate) + ((size_t)e * d.I + r) * nbH * MXBYTES;
+        uint8_t* codes = rp + (size_t)m * d.H / 2;
+        uint8_t* scales = rp + d.H + (size_t)m * nbH;
+        for (int b = 0; b < nbH; ++b) {
+          if (!mx_scale_ok(src[(size_t)b * MXBYTES])) return MOE_ERR_INVALID_ARGUMENT;
+          scales[b] = src[(size_t)b * MXBYTES];
+          memcpy(codes + (size_t)b * 16, src + (size_t)b * MXBYTES + 1, 16);
+        }
+      }
+    }
+    for (int n = 0; n < d.H; ++n) {
+      const uint8_t* src = down + ((size_t)e * d.H + n) * nbI * MXBYTES;
+      uint8_t* row = dst + d.dn_off + (size_t)e * d.dn_expert_bytes + (size_t)n * d.drow_bytes;
+      for (int b = 0; b < nbI; ++b) {
+        if (!mx_scale_ok(src[(size_t)b * MXBYTES])) return MOE_ERR_INVALID_ARGUMENT;
+        row[d.I / 2 + b] = src[(size_t)b * MXBYTES];
+        memcpy(row + (size_t)b * 16, src + (size_t)b * MXBYTES + 1, 16);
+      }
+    }
+  }
+  return MOE_OK;
+}
+
+static void unpack_mx_layer(const Layout& d, const uint8_t* src, uint8_t* gate, uint8_t* up, uint8_t* down) {
+  const int nbH = d.H / MXK, nbI = d.I / MXK;
+  for (int e = 0; e < d.E; ++e) {
+    for (int r = 0; r < d.I; ++r) {
+      const uint8_t* rp = src + d.gu_off + (size_t)e * d.gu_expert_bytes + (size_t)r * d.rp_bytes;
+      for (int m = 0; m < 2; ++m) {
+        uint8_t* out = (m ? up : gate) + ((size_t)e * d.I + r) * nbH * MXBYTES;
+        const uint8_t* codes = rp + (size_t)m * d.H / 2;
+        const uint8_t* scales = rp + d.H + (size_t)m * nbH;
+        for (int b = 0; b < nbH; ++b) {
+          out[(size_t)b * MXBYTES] = scales[b];
+          memcpy(out + (size_t)b * MXBYTES + 1, codes + (size_t)b * 16, 16);
+        }
+      }
+    }
+    for (int n = 0; n < d.H; ++n) {
+      uint8_t* out = down + ((size_t)e * d.H + n) * nbI * MXBYTES;
+      const uint8_t* row = src + d.dn_off + (size_t)e * d.dn_expert_bytes + (size_t)n * d.drow_bytes;
+      for (int b = 0; b < nbI; ++b) {
+        out[(size_t)b * MXBYTES] = row[d.I / 2 + b];
+        memcpy(out + (size_t)b * MXBYTES + 1, row + (size_t)b * 16, 16);
+      }
+    }
+  }
+}
+
 extern "C" int moe_pack_layer(const moe_plan* plan, const uint8_t* gate, const uint8_t* up, const uint8_t* down,
                               const float* router, void* dst_host) {
   if (!plan || !gate || !up || !down || !router || !dst_host) return MOE_ERR_INVALID_ARGUMENT;
@@ -115,6 +179,7 @@ extern "C" int moe_pack_layer(const moe_plan* plan, const uint8_t* gate, const u
   uint8_t* dst = static_cast<uint8_t*>(dst_host);
   memset(dst, 0, d.layer_bytes);
   memcpy(dst + d.router_off, router, (size_t)d.E * d.H * 4);
+  if (d.fmt == FMT_MXFP4) return pack_mx_layer(d, gate, up, down, dst);
   const size_t grow = (size_t)d.nbH * QBYTES;   // canonical bytes of one gate/up row
   const size_t drow = (size_t)d.nbI * QBYTES;   // canonical bytes of one down row
   for (int e = 0; e < d.E; ++e) {
@@ -147,6 +212,10 @@ extern "C" int moe_unpack_layer(const moe_plan* plan, const void* src_host, uint
   const Layout& d = plan->d;
   const uint8_t* src = static_cast<const uint8_t*>(src_host);
   memcpy(router, src + d.router_off, (size_t)d.E * d.H * 4);
+  if (d.fmt == FMT_MXFP4) {
+    unpack_mx_layer(d, src, gate, up, down);
+    return MOE_OK;
+  }
   const size_t grow = (size_t)d.nbH * QBYTES;
   const size_t drow = (size_t)d.nbI * QBYTES;
   for (int e = 0; e < d.E; ++e) {
@@ -214,7 +283,7 @@ static Path grouped_tiles(const Layout& d, int32_t T) {
 }
 static Path choose_path(const moe_plan* plan, int32_t T) {
   const Layout& d = plan->d;
-  if (T < 2 || (d.flags & MOE_FLAG_FORCE_GEMV)) return Path::Gemv;
+  if (T < 2 || (d.flags & MOE_FLAG_FORCE_GEMV) || d.fmt == FMT_MXFP4) return Path::Gemv;
   if (d.flags & MOE_FLAG_FORCE_GROUPED) return grouped_tiles(d, T);
   if (d.flags & MOE_FLAG_FORCE_EXPERT_GEMV) return Path::ExpertGemv;
   const long long P = (long long)T * d.k, E = d.E;

@@ -182,4 +182,55 @@ __device__ __forceinline__ float dot_codes_f16(const u32x4& c, const u32* X) {
   return a;
 }
 
+// ---------------------------------------------------------------- MXFP4
+// gfx950 converts one byte of FP4 E2M1 codes (low nibble first) to a bf16 or
+// fp16 pair, times a power of two taken from the exponent of an fp32
+// operand; with 1.0 the pair holds the exact E2M1 values.
+__device__ __forceinline__ void fp4_pairs_bf16(u32 v, u32* P) {
+  P[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0));
+  P[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1));
+  P[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2));
+  P[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3));
+}
+__device__ __forceinline__ void fp4_pairs_f16(u32 v, u32* P) {
+  P[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0));
+  P[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1));
+  P[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2));
+  P[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3));
+}
+
+// sum_i E2M1(q_i) * x_i over one 32-code block; X[i] holds the bf16 pair
+// (x[2i], x[2i+1]) (the natural order of bf16 words). Products are exact in
+// fp32 (2 + 8 significant bits).
+__device__ __forceinline__ float dot_fp4_bf16(const u32x4& c, const u32* X) {
+  const u32 w[4] = {c.x, c.y, c.z, c.w};
+  float a = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    u32 P[4];
+    fp4_pairs_bf16(w[d], P);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a = dot2_bf16(P[q], X[4 * d + q], a);
+  }
+  return a;
+}
+
+// The same with fp16 pairs (h[2i], h[2i+1]).
+__device__ __forceinline__ float dot_fp4_f16(const u32x4& c, const u32* X) {
+  const u32 w[4] = {c.x, c.y, c.z, c.w};
+  float a = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    u32 P[4];
+    fp4_pairs_f16(w[d], P);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a = dot2_f16(P[q], X[4 * d + q], a);
+  }
+  return a;
+}
+
+// E8M0 scale code e in [1, 254] -> 2^(e-127) as fp32 (exact; the packer
+// rejects 0 and 255).
+__device__ __forceinline__ float e8m0_scale(u32 e) { return __builtin_bit_cast(float, e << 23); }
+
 }  // namespace qmoe

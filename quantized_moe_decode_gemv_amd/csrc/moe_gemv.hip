@@ -220,8 +220,9 @@ __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__
 // RPS = 64/LPR rows per step, LPR lanes per row, IPL sub-blocks per lane.
 // h[(t*k + s)*I + r] = SiLU(G_e[r]·x_t) * (U_e[r]·x_t).
 // ACT: the gate activation as a template argument, so the epilogue on this
-// kernel's critical path carries no branch.
-template <int IPL, int LPR, int U, int ACT>
+// kernel's critical path carries no branch. FMT: the weight encoding; with
+// MXFP4 a lane's sub-block is one 32-code block with its E8M0 scale byte.
+template <int IPL, int LPR, int U, int ACT, int FMT>
 __global__ __launch_bounds__(BLOCK) void gateup_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int E, int k,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids_in, const float* __restrict__ logits,
@@ -246,7 +247,17 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
 #pragma unroll
   for (int q = 0; q < IPL; ++q) {
     const int j = lam + LPR * q;
-    S[q] = load_x_pairs(x + (size_t)t * H + 32 * j, X[q]);
+    if constexpr (FMT == FMT_MXFP4) {
+      u32x4 r[4];
+      load_x_raw(x + (size_t)t * H + 32 * j, r);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        X[q][4 * m] = r[m].x; X[q][4 * m + 1] = r[m].y; X[q][4 * m + 2] = r[m].z; X[q][4 * m + 3] = r[m].w;
+      }
+      S[q] = 0.f;
+    } else {
+      S[q] = load_x_pairs(x + (size_t)t * H + 32 * j, X[q]);
+    }
   }
   if (fused_topk) {
     // T == 1: wave 0 of every block derives the same routing from the logits;
@@ -265,6 +276,36 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
   const uint8_t* base = gu + (size_t)e * gu_expert_bytes;
   const int half = H / 2;                 // code bytes per matrix row
   const int hdr = H / 2 * 2;              // headers start after both code areas
+  if constexpr (FMT == FMT_MXFP4) {
+    // scale bytes: gate's H/32, then up's
+    u32x4 cg[U][IPL], cu[U][IPL];
+    u32 sg[U][IPL], su[U][IPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint8_t* rp = base + (size_t)(r0 + u * RPS + rho) * rp_bytes;
+#pragma unroll
+      for (int q = 0; q < IPL; ++q) {
+        const int j = lam + LPR * q;
+        cg[u][q] = load_nt(rp + 16 * j);
+        cu[u][q] = load_nt(rp + half + 16 * j);
+        sg[u][q] = __builtin_nontemporal_load(rp + hdr + j);
+        su[u][q] = __builtin_nontemporal_load(rp + hdr + H / MXK + j);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float pg = 0.f, pu = 0.f;
+#pragma unroll
+      for (int q = 0; q < IPL; ++q) {
+        pg = fmaf(e8m0_scale(sg[u][q]), dot_fp4_bf16(cg[u][q], X[q]), pg);
+        pu = fmaf(e8m0_scale(su[u][q]), dot_fp4_bf16(cu[u][q], X[q]), pu);
+      }
+      pg = group_sum<LPR>(pg);
+      pu = group_sum<LPR>(pu);
+      if (lam == 0) h[(size_t)ts * I + r0 + u * RPS + rho] = gate_act(pg, pu, ACT);
+    }
+    return;
+  }
   const int nb = H / QK;
   u32x4 cg[U][IPL], cu[U][IPL], hg[U][IPL], hu[U][IPL];
 #pragma unroll
@@ -308,8 +349,10 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
 // leave as soon as the expert ids arrive. The four wave partials of a row are
 // added in wave order. h is rounded to fp16 for v_dot2_f32_f16 (relative
 // rounding 2^-11 per value); products and sums are fp32.
-// y[t*H + n] = sum_s w_s * D_{e_s}[n]·h_{t,s}.
-template <int R>
+// y[t*H + n] = sum_s w_s * D_{e_s}[n]·h_{t,s}. With MXFP4 weights an item's
+// 32 codes share one E8M0 scale byte and the fp16 pairs of h are in natural
+// order.
+template <int R, int FMT>
 __global__ __launch_bounds__(BLOCK) void down_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I, int k,
     const int32_t* __restrict__ ids, const float* __restrict__ wts, const float* __restrict__ h,
@@ -334,38 +377,61 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
 #pragma unroll
   for (int c = 0; c < 8; ++c) hr[c] = valid ? load16(hp + 4 * c) : u32x4{0u, 0u, 0u, 0u};
   const uint8_t* row0 = dn + (size_t)e * dn_expert_bytes + (size_t)n0 * drow_bytes;
-  const int hdr = I / 2 + QHDR * (j >> 3);
-  u32x4 cd[R], hd[R];
+  float p[R];
+  if constexpr (FMT == FMT_MXFP4) {
+    u32x4 cd[R];
+    u32 sd[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint8_t* row = row0 + (size_t)r * drow_bytes;
-    cd[r] = valid ? load_nt(row + 16 * j) : u32x4{0u, 0u, 0u, 0u};
-    hd[r] = valid ? load_nt(row + hdr) : u32x4{0u, 0u, 0u, 0u};
-  }
-  // h -> fp16 pairs in nibble order; S is the sum of the rounded values
-  u32 X[16];
-  float S = 0.f;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const u32 v[8] = {hr[2 * d].x, hr[2 * d].y, hr[2 * d].z, hr[2 * d].w,
-                      hr[2 * d + 1].x, hr[2 * d + 1].y, hr[2 * d + 1].z, hr[2 * d + 1].w};
-    _Float16 hh[8];
+    for (int r = 0; r < R; ++r) {
+      const uint8_t* row = row0 + (size_t)r * drow_bytes;
+      cd[r] = valid ? load_nt(row + 16 * j) : u32x4{0u, 0u, 0u, 0u};
+      sd[r] = valid ? (u32)__builtin_nontemporal_load(row + I / 2 + j) : 0u;
+    }
+    u32 X[16];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      hh[c] = (_Float16)as_f32(v[c]);
-      S += (float)hh[c];
+      const u32 v[4] = {hr[c].x, hr[c].y, hr[c].z, hr[c].w};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const _Float16 lo = (_Float16)as_f32(v[2 * m]), hi = (_Float16)as_f32(v[2 * m + 1]);
+        X[2 * c + m] = (u32)__builtin_bit_cast(unsigned short, lo) | ((u32)__builtin_bit_cast(unsigned short, hi) << 16);
+      }
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      X[4 * d + c] = (u32)__builtin_bit_cast(unsigned short, hh[c]) |
-                     ((u32)__builtin_bit_cast(unsigned short, hh[c + 4]) << 16);
-  }
-  float p[R];
+    for (int r = 0; r < R; ++r) p[r] = group_sum<WAVE>(ws * (e8m0_scale(sd[r]) * dot_fp4_f16(cd[r], X)));
+  } else {
+    const int hdr = I / 2 + QHDR * (j >> 3);
+    u32x4 cd[R], hd[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const Affine a = header_affine(hd[r], j & 7);
-    const float dq = dot_codes_f16(cd[r], X);
-    p[r] = group_sum<WAVE>(ws * (a.a * dq - (1024.f * a.a + a.b) * S));
+    for (int r = 0; r < R; ++r) {
+      const uint8_t* row = row0 + (size_t)r * drow_bytes;
+      cd[r] = valid ? load_nt(row + 16 * j) : u32x4{0u, 0u, 0u, 0u};
+      hd[r] = valid ? load_nt(row + hdr) : u32x4{0u, 0u, 0u, 0u};
+    }
+    // h -> fp16 pairs in nibble order; S is the sum of the rounded values
+    u32 X[16];
+    float S = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const u32 v[8] = {hr[2 * d].x, hr[2 * d].y, hr[2 * d].z, hr[2 * d].w,
+                        hr[2 * d + 1].x, hr[2 * d + 1].y, hr[2 * d + 1].z, hr[2 * d + 1].w};
+      _Float16 hh[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        hh[c] = (_Float16)as_f32(v[c]);
+        S += (float)hh[c];
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        X[4 * d + c] = (u32)__builtin_bit_cast(unsigned short, hh[c]) |
+                       ((u32)__builtin_bit_cast(unsigned short, hh[c + 4]) << 16);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const Affine a = header_affine(hd[r], j & 7);
+      const float dq = dot_codes_f16(cd[r], X);
+      p[r] = group_sum<WAVE>(ws * (a.a * dq - (1024.f * a.a + a.b) * S));
+    }
   }
   if (lane == 0) {
 #pragma unroll
@@ -560,7 +626,7 @@ hipError_t launch_topk(const Layout& d, const float* logits, int32_t* ids, float
   return hipGetLastError();
 }
 
-template <int IPL, int LPR, int U, int ACT>
+template <int IPL, int LPR, int U, int ACT, int FMT>
 static void gateup_go_act(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids,
                           const float* logits, int32_t* ids_out, float* w_out, float* h, int T, bool fused,
                           hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
@@ -569,12 +635,12 @@ static void gateup_go_act(const Layout& d, const uint8_t* layer, const uint16_t*
   const int blocks = (int)((units + 3) / 4);
   if (ev0 || ev1) {
     // measurement launch: the events bracket this kernel's execution
-    hipExtLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s, ev0, ev1,
+    hipExtLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s, ev0, ev1,
                           0, layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
                           ids_out, w_out, h, T, fused ? 1 : 0);
     return;
   }
-  hipLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s,
+  hipLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s,
                      layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
                      ids_out, w_out, h, T, fused ? 1 : 0);
 }
@@ -583,10 +649,18 @@ template <int IPL, int LPR, int U>
 static void gateup_go(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids, const float* logits,
                       int32_t* ids_out, float* w_out, float* h, int T, bool fused, hipStream_t s, hipEvent_t ev0,
                       hipEvent_t ev1) {
+  if (d.fmt == FMT_MXFP4) {
+    switch (d.act) {
+      case 1: gateup_go_act<IPL, LPR, U, 1, FMT_MXFP4>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1); break;
+      case 2: gateup_go_act<IPL, LPR, U, 2, FMT_MXFP4>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1); break;
+      default: gateup_go_act<IPL, LPR, U, 0, FMT_MXFP4>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1); break;
+    }
+    return;
+  }
   switch (d.act) {
-    case 1: gateup_go_act<IPL, LPR, U, 1>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1); break;
-    case 2: gateup_go_act<IPL, LPR, U, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1); break;
-    default: gateup_go_act<IPL, LPR, U, 0>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1); break;
+    case 1: gateup_go_act<IPL, LPR, U, 1, FMT_Q4K>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1); break;
+    case 2: gateup_go_act<IPL, LPR, U, 2, FMT_Q4K>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1); break;
+    default: gateup_go_act<IPL, LPR, U, 0, FMT_Q4K>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1); break;
   }
 }
 
@@ -619,8 +693,12 @@ hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids
   constexpr int R = 8;                       // divides every supported H
   if (d.k * (d.I / 32) > 4 * WAVE || d.H % R) return hipErrorInvalidValue;
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL((down_kernel<R>), dim3(T * (d.H / R)), dim3(BLOCK), 0, s, layer + d.dn_off,
-                     d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
+  if (d.fmt == FMT_MXFP4)
+    hipLaunchKernelGGL((down_kernel<R, FMT_MXFP4>), dim3(T * (d.H / R)), dim3(BLOCK), 0, s, layer + d.dn_off,
+                       d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
+  else
+    hipLaunchKernelGGL((down_kernel<R, FMT_Q4K>), dim3(T * (d.H / R)), dim3(BLOCK), 0, s, layer + d.dn_off,
+                       d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
   return hipGetLastError();
 }
 

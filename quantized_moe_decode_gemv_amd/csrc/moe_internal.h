@@ -13,6 +13,9 @@ constexpr int QK = 256;            // weights per super-block
 constexpr int QBYTES = 144;        // bytes per super-block
 constexpr int QHDR = 16;           // header bytes (d, dmin, 12 bytes of 6-bit fields)
 constexpr int QCODES = 128;        // code bytes
+constexpr int MXK = 32;            // weights per MXFP4 block
+constexpr int MXBYTES = 17;        // bytes per MXFP4 block (E8M0 scale, 16 code bytes)
+constexpr int FMT_Q4K = 0, FMT_MXFP4 = 1;
 constexpr size_t HEADER_BYTES = 4096;
 constexpr uint64_t BLOB_MAGIC = 0x31424F4C42454F4DULL;  // "MOEBLOB1" little-endian
 constexpr uint32_t BLOB_VERSION = 1;
@@ -25,9 +28,13 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 //            [gate codes H/2 B][up codes H/2 B][gate headers H/256*16 B][up headers H/256*16 B]
 //            (codes of super-block b, sub-block j' at byte 128*b + 16*j'; canonical nibble order)
 //   down     per expert, per output row n: [codes I/2 B][headers I/256*16 B]
+// With MXFP4 weights the headers are the E8M0 scale bytes, one per 32-weight
+// block (block b's 16 code bytes at 16*b, its scale at scales + b), and each
+// record is padded to a multiple of 16 bytes.
 struct Layout {
   int H, E, k, I, L, maxT;
   int act;                      // gate activation: 0 SiLU, 1 squared ReLU, 2 clamped SwiGLU
+  int fmt;                      // FMT_Q4K or FMT_MXFP4
   uint32_t flags;
   float eps;
   int nbH, nbI;                 // super-blocks per gate/up row and per down row
@@ -41,10 +48,16 @@ struct Layout {
     H = c.hidden; E = c.n_experts; k = c.top_k; I = c.inter; L = c.n_layers; maxT = c.max_tokens;
     flags = c.flags; eps = c.rms_eps;
     act = (c.flags & MOE_FLAG_ACT_RELU2) ? 1 : ((c.flags & MOE_FLAG_ACT_SWIGLU_OAI) ? 2 : 0);
+    fmt = (c.flags & MOE_FLAG_WEIGHTS_MXFP4) ? FMT_MXFP4 : FMT_Q4K;
     nbH = H / QK; nbI = I / QK;
-    rp_bytes = (size_t)2 * nbH * QBYTES;
+    if (fmt == FMT_MXFP4) {
+      rp_bytes = align_up((size_t)H + H / MXK * 2, 16);
+      drow_bytes = align_up((size_t)I / 2 + I / MXK, 16);
+    } else {
+      rp_bytes = (size_t)2 * nbH * QBYTES;
+      drow_bytes = (size_t)nbI * QBYTES;
+    }
     gu_expert_bytes = (size_t)I * rp_bytes;
-    drow_bytes = (size_t)nbI * QBYTES;
     dn_expert_bytes = (size_t)H * drow_bytes;
     router_off = 0;
     gu_off = align_up((size_t)E * H * 4, 256);
@@ -59,6 +72,7 @@ struct BlobHeader {
   int32_t hidden, n_experts, top_k, inter, n_layers;
   uint64_t layer_bytes;
   uint64_t header_bytes;
+  int32_t weight_format;        // FMT_Q4K or FMT_MXFP4
 };
 
 // Scratch carve-up for T tokens (offsets 256-aligned).

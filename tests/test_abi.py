@@ -51,7 +51,11 @@ def test_status_strings():
     ((2048, 128, 8, 768, 1, 1, 0x10, 1e-6), True),  # SwiGLU-OAI gate activation
     ((2048, 128, 8, 768, 1, 1, 0x12, 1e-6), True),  # an activation and a forced path
     ((2048, 128, 8, 768, 1, 1, 0x18, 1e-6), False), # two activations
-    ((2048, 128, 8, 768, 1, 1, 0x20, 1e-6), False), # unknown flag
+    ((2048, 128, 8, 768, 1, 1, 0x20, 1e-6), True),  # MXFP4 expert weights
+    ((2048, 128, 8, 768, 1, 1, 0x29, 1e-6), True),  # MXFP4 with an activation and the per-token path forced
+    ((2048, 128, 8, 768, 1, 1, 0x22, 1e-6), False), # MXFP4 with the grouped path forced
+    ((2048, 128, 8, 768, 1, 1, 0x24, 1e-6), False), # MXFP4 with the expert-major GEMV forced
+    ((2048, 128, 8, 768, 1, 1, 0x40, 1e-6), False), # unknown flag
     ((300, 8, 2, 512, 1, 1, 0, 1e-6), False),       # hidden not a multiple of 256
     ((768, 8, 2, 512, 1, 1, 0, 1e-6), False),       # hidden lane mapping unsupported
     ((256, 8, 9, 512, 1, 1, 0, 1e-6), False),       # k > E
@@ -100,6 +104,41 @@ def test_pack_unpack_identity():
     assert not np.array_equal(packed[p.layer_bytes() - d.size:], d.reshape(-1))
 
 
+def test_sizes_qwen_mxfp4():
+    """MXFP4 records: codes plus one scale byte per 32 weights, padded to 16
+    bytes (gate/up row pair 2048 + 128 = 2176 B, down row 384 + 24 -> 416 B)."""
+    S = synth.QWEN3_30B_A3B_MXFP4
+    p = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, flags=q.FLAG_WEIGHTS_MXFP4)
+    assert p.block == (32, 17)
+    per_expert = 768 * 2176 + 2048 * 416
+    assert p.layer_bytes() == 128 * per_expert + 128 * 2048 * 4
+    # algorithmic bytes of one expert: 3 matrices x 1,572,864 weights x 4.25 bits
+    assert S.expert_bytes == 3 * 768 * 2048 // 32 * 17 == 2_506_752
+
+
+def test_pack_unpack_identity_mxfp4():
+    S = synth.Shape("pack-mx", 20, 512, 4, 2, 256, synth.FMT_MXFP4)
+    p = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, flags=q.FLAG_WEIGHTS_MXFP4)
+    g = synth.layer_experts(S, 0, synth.GATE)
+    u = synth.layer_experts(S, 0, synth.UP)
+    d = synth.layer_experts(S, 0, synth.DOWN)
+    r = synth.router(S, 0)
+    assert g.shape == (4, 256, 16, 17) and d.shape == (4, 512, 8, 17)
+    packed = p.pack_layer(g, u, d, r)
+    g2, u2, d2, r2 = p.unpack_layer(packed)
+    assert np.array_equal(g2, g) and np.array_equal(u2, u) and np.array_equal(d2, d) and np.array_equal(r2, r)
+    # the scale codes the format leaves out (2^-127 and NaN) are refused
+    for bad in (0, 255):
+        d_bad = d.copy()
+        d_bad[1, 7, 3, 0] = bad
+        with pytest.raises(q.MoeError):
+            p.pack_layer(g, u, d_bad, r)
+        g_bad = g.copy()
+        g_bad[2, 5, 0, 0] = bad
+        with pytest.raises(q.MoeError):
+            p.pack_layer(g_bad, u, d, r)
+
+
 def test_blob_header_check():
     p = q.Plan(256, 8, 2, 512, n_layers=3)
     hdr = p.pack_header()
@@ -109,6 +148,10 @@ def test_blob_header_check():
     assert p.blob_check(bad) == -3
     other = q.Plan(256, 8, 2, 512, n_layers=2)
     assert other.blob_check(hdr) == -3
+    # a blob of the other weight encoding does not match
+    mx = q.Plan(256, 8, 2, 512, n_layers=3, flags=q.FLAG_WEIGHTS_MXFP4)
+    assert mx.blob_check(mx.pack_header()) == 0
+    assert mx.blob_check(hdr) == -3 and p.blob_check(mx.pack_header()) == -3
 
 
 def test_argument_errors_before_launch():

@@ -229,21 +229,23 @@ def _assert_same(a, b, what):
         assert torch.equal(u, v), f"{what}: {name} differs"
 
 
-@pytest.mark.parametrize("hidden,E,k,inter,L,seed", [
-    (1024, 64, 4, 256, 5, 21),
-    (4096, 32, 4, 512, 4, 22),
-    (2048, 256, 8, 256, 3, 23),    # the most experts a plan takes
-    (2048, 100, 6, 512, 3, 24),    # expert count not a multiple of 64
-    (512, 16, 2, 256, 4, 25),      # router without the norm prologue: epilogue kernel per layer
+@pytest.mark.parametrize("hidden,E,k,inter,L,seed,fmt", [
+    (1024, 64, 4, 256, 5, 21, "q4k"),
+    (4096, 32, 4, 512, 4, 22, "q4k"),
+    (2048, 256, 8, 256, 3, 23, "q4k"),     # the most experts a plan takes
+    (2048, 100, 6, 512, 3, 24, "q4k"),     # expert count not a multiple of 64
+    (512, 16, 2, 256, 4, 25, "q4k"),       # router without the norm prologue: epilogue kernel per layer
+    (2048, 128, 8, 768, 4, 26, "mxfp4"),   # MXFP4 expert weights
 ])
-def test_stack_step_equals_chained_forward(dev, hidden, E, k, inter, L, seed):
+def test_stack_step_equals_chained_forward(dev, hidden, E, k, inter, L, seed, fmt):
     """One-token stacked step (each layer's input formed inside the next
     router launch where the kernel has that prologue): eagerly and as graph
     replays it must reproduce, bit for bit, the chained moe_forward calls
     with the RMSNorm epilogue; step 0 is also held against the oracle's
     trajectory."""
-    S = synth.Shape(f"stack-h{hidden}-e{E}", seed, hidden, E, k, inter)
-    plan = q.Plan(hidden, E, k, inter, n_layers=L, max_tokens=1)
+    mx = fmt == "mxfp4"
+    S = synth.Shape(f"stack-h{hidden}-e{E}", seed, hidden, E, k, inter, synth.FMT_MXFP4 if mx else synth.FMT_Q4K)
+    plan = q.Plan(hidden, E, k, inter, n_layers=L, max_tokens=1, flags=q.FLAG_WEIGHTS_MXFP4 if mx else 0)
     blob = plan.upload_blob(layer_source(S), device=dev)
     x0 = torch.from_numpy(synth.x_bf16(S, 3, 0)[0].view(np.int16)).to(dev)
     ref = _chained_forward(plan, blob, L, hidden, k, x0, dev)
