@@ -174,6 +174,11 @@ def main():
         single = single_layer_measurements(S, blob, L, dev, stream, q, np, torch, synth)
         log(f"single layer calls: {json.dumps(single)}")
 
+    mxfp4 = None
+    if not args.no_extras:
+        mxfp4 = mxfp4_decode(L, dev, stream, args, q, np, torch, synth)
+        log(f"mxfp4 decode: {json.dumps(mxfp4)}")
+
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "gateup_kernel_traffic.json")
     if os.path.exists(tpath):
@@ -235,6 +240,7 @@ def main():
         },
         "step_time": step_pct,
         "single_layer": single,
+        "mxfp4": mxfp4,
         "cpu_baseline": cpu,
         "batched": batched,
         "parity_step0": parity,
@@ -244,6 +250,68 @@ def main():
 
 
 MFMA_FP16_PEAK_TFLOPS = 2500.0
+
+
+def mxfp4_decode(L, dev, stream, args, q, np, torch, synth):
+    """The same decode step with MXFP4 expert weights: the L layers'
+    Gaussian weights encoded as FP4 E2M1 codes with an E8M0 scale per 32
+    (4.25 bits per weight), a blob of their own, the step captured as one
+    graph and timed like the main leg; plus the gate/up kernel alone."""
+    S = synth.QWEN3_30B_A3B_MXFP4
+    plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=L, max_tokens=1, flags=q.FLAG_WEIGHTS_MXFP4)
+    t0 = time.time()
+    blob = torch.empty(plan.blob_bytes(), dtype=torch.uint8, device=dev)
+    blob[: plan.header_bytes()].copy_(torch.from_numpy(plan.pack_header()))
+    staging = torch.empty(plan.layer_bytes(), dtype=torch.uint8, pin_memory=True)
+    host = staging.numpy()
+    for layer in range(L):
+        plan.pack_layer(synth.layer_experts(S, layer, synth.GATE), synth.layer_experts(S, layer, synth.UP),
+                        synth.layer_experts(S, layer, synth.DOWN), synth.router(S, layer), out=host)
+        off = plan.layer_offset(layer)
+        blob[off:off + plan.layer_bytes()].copy_(staging)
+        if layer % 16 == 15 or layer == L - 1:
+            log(f"mxfp4 weights: {layer + 1}/{L} layers generated and uploaded ({time.time() - t0:.0f}s)")
+    H, k = S.hidden, S.top_k
+    xs = torch.zeros(L, H, dtype=torch.int16, device=dev)
+    ys = torch.zeros(L, H, dtype=torch.float32, device=dev)
+    ids = torch.zeros(L, k, dtype=torch.int32, device=dev)
+    ws = torch.zeros(L, k, dtype=torch.float32, device=dev)
+    scratch = plan.new_scratch(1, device=dev)
+    xs[0].copy_(torch.from_numpy(synth.x_bf16(S, 3, 0)[0].view(np.int16)))
+    torch.cuda.synchronize()
+    graph = plan.capture_step(blob, xs, ys, 1, ids, ws, scratch=scratch, stream=stream)
+    for _ in range(args.warmup):
+        graph.launch(stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        graph.launch(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    finite = bool(torch.isfinite(ys).all().item())
+    expert_bytes = L * S.top_k * S.expert_bytes
+    # gate/up kernel alone, rotating over the layers
+    gu_bytes = S.top_k * S.inter * 2 * S.hidden // 32 * 17
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    times = []
+    for rep in range(args.kernel_reps):
+        for l in range(L):
+            plan.profile_gate_up(blob, l, xs[l], 1, evs[l][0], evs[l][1], scratch=scratch, stream=stream)
+        torch.cuda.synchronize()
+        times += [a.elapsed_time(b) for a, b in evs]
+    gu_us = float(np.mean(times)) * 1e3
+    del graph, blob, staging
+    torch.cuda.synchronize()
+    return {"us_per_step": round(us, 1), "tok_s": round(1e6 / us, 1), "expert_bytes_per_token": expert_bytes,
+            "expert_gbps": round(expert_bytes / us * 1e-3, 1), "gateup_us": round(gu_us, 3),
+            "gateup_bytes_per_launch": gu_bytes, "gateup_gbps": round(gu_bytes / gu_us * 1e-3, 1),
+            "outputs_finite": finite}
 
 
 def _graph_us(calls, n_rot, reps, stream, torch):

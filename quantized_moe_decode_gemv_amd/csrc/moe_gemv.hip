@@ -352,7 +352,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
 // y[t*H + n] = sum_s w_s * D_{e_s}[n]·h_{t,s}. With MXFP4 weights an item's
 // 32 codes share one E8M0 scale byte and the fp16 pairs of h are in natural
 // order.
-template <int R, int FMT>
+template <int R, int FMT, int PH>
 __global__ __launch_bounds__(BLOCK) void down_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I, int k,
     const int32_t* __restrict__ ids, const float* __restrict__ wts, const float* __restrict__ h,
@@ -379,14 +379,18 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
   const uint8_t* row0 = dn + (size_t)e * dn_expert_bytes + (size_t)n0 * drow_bytes;
   float p[R];
   if constexpr (FMT == FMT_MXFP4) {
+    // unconditional loads (in both encodings): an idle lane reads expert 0's
+    // first block (in bounds) and contributes ws = 0 times a zero h
     u32x4 cd[R];
     u32 sd[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint8_t* row = row0 + (size_t)r * drow_bytes;
-      cd[r] = valid ? load_nt(row + 16 * j) : u32x4{0u, 0u, 0u, 0u};
-      sd[r] = valid ? (u32)__builtin_nontemporal_load(row + I / 2 + j) : 0u;
+      cd[r] = load_nt(row + 16 * j);
+      sd[r] = __builtin_nontemporal_load(row + I / 2 + j);
     }
+    // every weight load in flight before the h conversion waits for h
+    __builtin_amdgcn_sched_barrier(0);
     u32 X[16];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -400,37 +404,46 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
 #pragma unroll
     for (int r = 0; r < R; ++r) p[r] = group_sum<WAVE>(ws * (e8m0_scale(sd[r]) * dot_fp4_f16(cd[r], X)));
   } else {
+    // the rows in PH phases: a phase's loads are issued once the previous
+    // phase's rows are summed (measured faster than all 2R loads at once)
     const int hdr = I / 2 + QHDR * (j >> 3);
     u32x4 cd[R], hd[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint8_t* row = row0 + (size_t)r * drow_bytes;
-      cd[r] = valid ? load_nt(row + 16 * j) : u32x4{0u, 0u, 0u, 0u};
-      hd[r] = valid ? load_nt(row + hdr) : u32x4{0u, 0u, 0u, 0u};
-    }
-    // h -> fp16 pairs in nibble order; S is the sum of the rounded values
     u32 X[16];
     float S = 0.f;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const u32 v[8] = {hr[2 * d].x, hr[2 * d].y, hr[2 * d].z, hr[2 * d].w,
-                        hr[2 * d + 1].x, hr[2 * d + 1].y, hr[2 * d + 1].z, hr[2 * d + 1].w};
-      _Float16 hh[8];
+    for (int ph = 0; ph < PH; ++ph) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        hh[c] = (_Float16)as_f32(v[c]);
-        S += (float)hh[c];
+      for (int r = ph * (R / PH); r < (ph + 1) * (R / PH); ++r) {
+        const uint8_t* row = row0 + (size_t)r * drow_bytes;
+        cd[r] = load_nt(row + 16 * j);
+        hd[r] = load_nt(row + hdr);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (ph == 0) {
+        // h -> fp16 pairs in nibble order; S is the sum of the rounded values
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const u32 v[8] = {hr[2 * d].x, hr[2 * d].y, hr[2 * d].z, hr[2 * d].w,
+                            hr[2 * d + 1].x, hr[2 * d + 1].y, hr[2 * d + 1].z, hr[2 * d + 1].w};
+          _Float16 hh[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            hh[c] = (_Float16)as_f32(v[c]);
+            S += (float)hh[c];
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            X[4 * d + c] = (u32)__builtin_bit_cast(unsigned short, hh[c]) |
+                           ((u32)__builtin_bit_cast(unsigned short, hh[c + 4]) << 16);
+        }
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        X[4 * d + c] = (u32)__builtin_bit_cast(unsigned short, hh[c]) |
-                       ((u32)__builtin_bit_cast(unsigned short, hh[c + 4]) << 16);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const Affine a = header_affine(hd[r], j & 7);
-      const float dq = dot_codes_f16(cd[r], X);
-      p[r] = group_sum<WAVE>(ws * (a.a * dq - (1024.f * a.a + a.b) * S));
+      for (int r = ph * (R / PH); r < (ph + 1) * (R / PH); ++r) {
+        const Affine a = header_affine(hd[r], j & 7);
+        const float dq = dot_codes_f16(cd[r], X);
+        p[r] = group_sum<WAVE>(ws * (a.a * dq - (1024.f * a.a + a.b) * S));
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (lane == 0) {
@@ -691,13 +704,14 @@ hipError_t launch_gateup(const Layout& d, const uint8_t* layer, const uint16_t* 
 hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids, const float* w, const float* h,
                        float* y, int T, hipStream_t s) {
   constexpr int R = 8;                       // divides every supported H
+  constexpr int DOWN_PHASES = 2;
   if (d.k * (d.I / 32) > 4 * WAVE || d.H % R) return hipErrorInvalidValue;
   if (T <= 0) return hipSuccess;
   if (d.fmt == FMT_MXFP4)
-    hipLaunchKernelGGL((down_kernel<R, FMT_MXFP4>), dim3(T * (d.H / R)), dim3(BLOCK), 0, s, layer + d.dn_off,
+    hipLaunchKernelGGL((down_kernel<R, FMT_MXFP4, 1>), dim3(T * (d.H / R)), dim3(BLOCK), 0, s, layer + d.dn_off,
                        d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
   else
-    hipLaunchKernelGGL((down_kernel<R, FMT_Q4K>), dim3(T * (d.H / R)), dim3(BLOCK), 0, s, layer + d.dn_off,
+    hipLaunchKernelGGL((down_kernel<R, FMT_Q4K, DOWN_PHASES>), dim3(T * (d.H / R)), dim3(BLOCK), 0, s, layer + d.dn_off,
                        d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
   return hipGetLastError();
 }
