@@ -368,9 +368,12 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
   const int IW = (G + 3) / 4;
   const int i = wid * IW + lane;
   const bool valid = lane < IW && i < G;
-  const int s = valid ? i / nsb : 0;
-  const int j = valid ? i % nsb : 0;
-  const int e = valid ? ids[(size_t)t * k + s] : 0;
+  // an idle lane takes the item of the wave's last busy lane: its loads hit
+  // lines already fetched, and ws = 0 and a zero h make its share zero
+  const int ic = min(wid * IW + min(lane, IW - 1), G - 1);
+  const int s = ic / nsb;
+  const int j = ic % nsb;
+  const int e = ids[(size_t)t * k + s];
   const float ws = valid ? wts[(size_t)t * k + s] : 0.f;
   u32x4 hr[8];
   const float* hp = h + ((size_t)t * k + s) * I + 32 * j;
@@ -379,8 +382,6 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
   const uint8_t* row0 = dn + (size_t)e * dn_expert_bytes + (size_t)n0 * drow_bytes;
   float p[R];
   if constexpr (FMT == FMT_MXFP4) {
-    // unconditional loads (in both encodings): an idle lane reads expert 0's
-    // first block (in bounds) and contributes ws = 0 times a zero h
     u32x4 cd[R];
     u32 sd[R];
 #pragma unroll
