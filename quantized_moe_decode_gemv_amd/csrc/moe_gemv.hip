@@ -158,10 +158,11 @@ __device__ __forceinline__ float block_sum4(float v, float* part) {
 // One block per expert row; the 256 threads split the hidden dimension
 // (4 consecutive fp32 weights each per chunk). Tokens loop inside with the
 // weight slice held in registers. Block reduction in a fixed order.
-// With y_prev != nullptr the block first forms its input as
-// x = bf16(RMSNorm(x_in + y_prev)) (the stacked-layer epilogue of the
-// previous layer, recomputed by every block) and block 0 stores it to x_out.
-template <int CH>  // chunks of 4 weights per thread: H = CH * 1024
+// With NORM the block first forms its input as x = bf16(RMSNorm(x_in +
+// y_prev)) (the stacked-layer epilogue of the previous layer, recomputed by
+// every block) and block 0 stores it to x_out. A token's x and y loads are
+// issued together, before either is waited for.
+template <int CH, bool NORM>  // chunks of 4 weights per thread: H = CH * 1024
 __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__ wr, const uint16_t* __restrict__ x,
                                                        const float* __restrict__ y_prev, uint16_t* __restrict__ x_out,
                                                        float eps, float* __restrict__ logits, int E, int H, int T) {
@@ -175,18 +176,26 @@ __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__
     w[c][0] = as_f32(v.x); w[c][1] = as_f32(v.y); w[c][2] = as_f32(v.z); w[c][3] = as_f32(v.w);
   }
   for (int t = 0; t < T; ++t) {
+    uint2 xq[CH];
+    u32x4 yq[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      xq[c] = *reinterpret_cast<const uint2*>(x + (size_t)t * H + 4 * (tid + BLOCK * c));
+      if constexpr (NORM) yq[c] = load16(y_prev + (size_t)t * H + 4 * (tid + BLOCK * c));
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float xv[CH][4];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const uint2 q = *reinterpret_cast<const uint2*>(x + (size_t)t * H + 4 * (tid + BLOCK * c));
+      const uint2 q = xq[c];
       xv[c][0] = bf16_bits_to_float(q.x & 0xFFFFu); xv[c][1] = bf16_bits_to_float(q.x >> 16);
       xv[c][2] = bf16_bits_to_float(q.y & 0xFFFFu); xv[c][3] = bf16_bits_to_float(q.y >> 16);
     }
-    if (y_prev) {
+    if constexpr (NORM) {
       float ss = 0.f;
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        const u32x4 q = load16(y_prev + (size_t)t * H + 4 * (tid + BLOCK * c));
+        const u32x4 q = yq[c];
         xv[c][0] += as_f32(q.x); xv[c][1] += as_f32(q.y); xv[c][2] += as_f32(q.z); xv[c][3] += as_f32(q.w);
 #pragma unroll
         for (int i = 0; i < 4; ++i) ss = fmaf(xv[c][i], xv[c][i], ss);
@@ -591,7 +600,11 @@ static hipError_t launch_router_big(const Layout& d, const float* wr, const uint
                                     uint16_t* x_out, float* logits, int T, hipStream_t s) {
   const int CH = d.H / 1024;
   dim3 grid(d.E), block(BLOCK);
-#define QMOE_ROUTER(C) hipLaunchKernelGGL(router_kernel<C>, grid, block, 0, s, wr, x, y_prev, x_out, d.eps, logits, d.E, d.H, T)
+#define QMOE_ROUTER(C)                                                                                        \
+  if (y_prev)                                                                                                 \
+    hipLaunchKernelGGL((router_kernel<C, true>), grid, block, 0, s, wr, x, y_prev, x_out, d.eps, logits, d.E, d.H, T); \
+  else                                                                                                        \
+    hipLaunchKernelGGL((router_kernel<C, false>), grid, block, 0, s, wr, x, y_prev, x_out, d.eps, logits, d.E, d.H, T)
   switch (CH) {
     case 1: QMOE_ROUTER(1); break;
     case 2: QMOE_ROUTER(2); break;
