@@ -220,6 +220,15 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
   const bool has = j < I / 32;
   const uint8_t* base = dn + (size_t)sd.e * dn_expert_bytes;
   const int hdr = I / 2 + QHDR * (j >> 3);
+  // the first chunk's h before the weights: a wait for a later load would
+  // also wait for the weights
+  const int jh = has ? j : 0;             // lanes past the row read its first block (in bounds)
+  u32x4 hq[NT][4];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
+    if (tt < n)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) hq[tt][g] = load16(h16 + (size_t)(pos0 + tt) * I + 32 * jh + 8 * g);
   u32x4 cd[U], hd[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -227,6 +236,7 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
     cd[u] = has ? load_nt(row + 16 * j) : u32x4{0u, 0u, 0u, 0u};
     hd[u] = has ? load_nt(row + hdr) : u32x4{0u, 0u, 0u, 0u};
   }
+  __builtin_amdgcn_sched_barrier(0);
   const u32 ONES = 0x3C003C00u;           // fp16 (1, 1)
   for (int c0 = 0; c0 < n; c0 += NT) {
     const int nv = min(NT, n - c0);
@@ -235,11 +245,11 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       if (tt < nv) {
-        const _Float16* hp = h16 + (size_t)(pos0 + c0 + tt) * I + 32 * j;
+        const _Float16* hp = h16 + (size_t)(pos0 + c0 + tt) * I + 32 * jh;
         float s = 0.f;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const u32x4 r = has ? load16(hp + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+          const u32x4 r = c0 == 0 ? hq[tt][g] : load16(hp + 8 * g);
           X[tt][4 * g + 0] = r.x; X[tt][4 * g + 1] = r.y; X[tt][4 * g + 2] = r.z; X[tt][4 * g + 3] = r.w;
           s = dot2_f16(r.x, ONES, s); s = dot2_f16(r.y, ONES, s);
           s = dot2_f16(r.z, ONES, s); s = dot2_f16(r.w, ONES, s);
