@@ -74,8 +74,10 @@ enum moe_status {
  * dequant (sparkinfer CuTe-DSL README, "moe" paragraph), in 17-byte blocks of
  * 32 weights: one E8M0 scale byte e (2^(e-127)), then 16 bytes of FP4 E2M1
  * codes, element 2i in the low nibble of byte 1+i. Scale codes 0 and 255
- * are rejected by the packer. Runs on the per-token GEMV path for every T;
- * a forced batched path is unsupported with it. */
+ * are rejected by the packer. Runs on the per-token GEMV path while
+ * T*k < E/2 and on the expert-major GEMV above (MOE_FLAG_FORCE_EXPERT_GEMV
+ * and MOE_FLAG_FORCE_GEMV apply); forcing the grouped MFMA path is
+ * unsupported with it. */
 #define MOE_FLAG_WEIGHTS_MXFP4 0x20u
 
 typedef struct moe_config {

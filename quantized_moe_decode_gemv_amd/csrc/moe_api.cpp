@@ -30,8 +30,8 @@ static bool cfg_ok(const moe_config* c) {
   const uint32_t act = c->flags & (MOE_FLAG_ACT_RELU2 | MOE_FLAG_ACT_SWIGLU_OAI);
   const uint32_t fmt = c->flags & MOE_FLAG_WEIGHTS_MXFP4;
   if (c->flags & ~(force | act | fmt)) return false;
-  // MXFP4 weights run on the per-token GEMV path only
-  if (fmt && (force & (MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_EXPERT_GEMV))) return false;
+  // MXFP4 weights run on the per-token and expert-major GEMV paths
+  if (fmt && (force & MOE_FLAG_FORCE_GROUPED)) return false;
   if (force & (force - 1)) return false;          // at most one path may be forced
   if (act & (act - 1)) return false;              // at most one activation
   // expert-major GEMV: one 32-code sub-block of a down row per lane of a wave
@@ -283,11 +283,14 @@ static Path grouped_tiles(const Layout& d, int32_t T) {
 }
 static Path choose_path(const moe_plan* plan, int32_t T) {
   const Layout& d = plan->d;
-  if (T < 2 || (d.flags & MOE_FLAG_FORCE_GEMV) || d.fmt == FMT_MXFP4) return Path::Gemv;
+  if (T < 2 || (d.flags & MOE_FLAG_FORCE_GEMV)) return Path::Gemv;
   if (d.flags & MOE_FLAG_FORCE_GROUPED) return grouped_tiles(d, T);
   if (d.flags & MOE_FLAG_FORCE_EXPERT_GEMV) return Path::ExpertGemv;
   const long long P = (long long)T * d.k, E = d.E;
   if (2 * P < E) return Path::Gemv;
+  // MXFP4: no MFMA tiles; the expert-major GEMV streams each routed expert
+  // once for any larger batch
+  if (d.fmt == FMT_MXFP4) return egemv_supported(d) ? Path::ExpertGemv : Path::Gemv;
   const bool g16 = g16_supported(d);
   if (egemv_supported(d) && (P <= E || (!g16 && 4 * P <= 9 * E))) return Path::ExpertGemv;
   return grouped_tiles(d, T);

@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_device.h"
 
 namespace qmoe {
@@ -114,7 +116,7 @@ struct SlotDesc { int e, pos0, n, pad; };
 // Workgroup: 4 waves on rows [r0, r0 + 4*RW) of the expert in slot a, all of
 // its routed pairs, NT at a time; h16[pos * I + pos8(r)] = SiLU(G_e[r]·x_t) *
 // (U_e[r]·x_t) for the pair at expert-sorted position pos, t its token.
-template <int IPL, int LPR, int U, int NT>
+template <int IPL, int LPR, int U, int NT, int FMT>
 __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const SlotDesc* __restrict__ slots,
@@ -136,9 +138,12 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
   for (int tt = 0; tt < NT; ++tt) t0[tt] = tt < n ? pairs[pos0 + tt] / k : 0;
   const uint8_t* base = gu + (size_t)sd.e * gu_expert_bytes;
   const int half = H / 2;                 // code bytes per matrix row
-  const int hdr = H;                      // headers start after both code areas
+  const int hdr = H;                      // headers (MXFP4: scale bytes) start after both code areas
   const int nb = H / QK;
-  u32x4 cg[U][IPL], cu[U][IPL], hg[U][IPL], hu[U][IPL];
+  // per lane and row: the sub-block's 16-byte header, or its E8M0 scale byte
+  using Hdr = std::conditional_t<FMT == FMT_MXFP4, u32, u32x4>;
+  u32x4 cg[U][IPL], cu[U][IPL];
+  Hdr hg[U][IPL], hu[U][IPL];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint8_t* rp = base + (size_t)(r0 + u * RPS + rho) * rp_bytes;
@@ -147,8 +152,13 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
       const int j = lam + LPR * q;
       cg[u][q] = load_nt(rp + 16 * j);
       cu[u][q] = load_nt(rp + half + 16 * j);
-      hg[u][q] = load_nt(rp + hdr + QHDR * (j >> 3));
-      hu[u][q] = load_nt(rp + hdr + QHDR * nb + QHDR * (j >> 3));
+      if constexpr (FMT == FMT_MXFP4) {
+        hg[u][q] = __builtin_nontemporal_load(rp + hdr + j);
+        hu[u][q] = __builtin_nontemporal_load(rp + hdr + H / MXK + j);
+      } else {
+        hg[u][q] = load_nt(rp + hdr + QHDR * (j >> 3));
+        hu[u][q] = load_nt(rp + hdr + QHDR * nb + QHDR * (j >> 3));
+      }
     }
   }
   for (int c0 = 0; c0 < n; c0 += NT) {
@@ -160,7 +170,22 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
       if (tt < nv) {
         const int t = c0 == 0 ? t0[tt] : pairs[pos0 + c0 + tt] / k;
 #pragma unroll
-        for (int q = 0; q < IPL; ++q) S[tt][q] = load_x_pairs(x + (size_t)t * H + 32 * (lam + LPR * q), X[tt][q]);
+        for (int q = 0; q < IPL; ++q) {
+          const uint16_t* xp = x + (size_t)t * H + 32 * (lam + LPR * q);
+          if constexpr (FMT == FMT_MXFP4) {
+            // natural pair order, no sums needed
+            u32x4 r[4];
+            load_x_raw(xp, r);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              X[tt][q][4 * m] = r[m].x; X[tt][q][4 * m + 1] = r[m].y;
+              X[tt][q][4 * m + 2] = r[m].z; X[tt][q][4 * m + 3] = r[m].w;
+            }
+            S[tt][q] = 0.f;
+          } else {
+            S[tt][q] = load_x_pairs(xp, X[tt][q]);
+          }
+        }
       }
     }
     float v[V];
@@ -170,16 +195,27 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int q = 0; q < IPL; ++q) {
-        const int jj = (lam + LPR * q) & 7;
-        const Affine ag = header_affine(hg[u][q], jj);
-        const Affine au = header_affine(hu[u][q], jj);
+        if constexpr (FMT == FMT_MXFP4) {
+          const float sg = e8m0_scale(hg[u][q]), su = e8m0_scale(hu[u][q]);
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          if (tt < nv) {
-            const float Ag = dot_codes_bf16(cg[u][q], X[tt][q]);
-            const float Au = dot_codes_bf16(cu[u][q], X[tt][q]);
-            v[2 * (u * NT + tt)] += ag.a * Ag - (128.f * ag.a + ag.b) * S[tt][q];
-            v[2 * (u * NT + tt) + 1] += au.a * Au - (128.f * au.a + au.b) * S[tt][q];
+          for (int tt = 0; tt < NT; ++tt) {
+            if (tt < nv) {
+              v[2 * (u * NT + tt)] = fmaf(sg, dot_fp4_bf16(cg[u][q], X[tt][q]), v[2 * (u * NT + tt)]);
+              v[2 * (u * NT + tt) + 1] = fmaf(su, dot_fp4_bf16(cu[u][q], X[tt][q]), v[2 * (u * NT + tt) + 1]);
+            }
+          }
+        } else {
+          const int jj = (lam + LPR * q) & 7;
+          const Affine ag = header_affine(hg[u][q], jj);
+          const Affine au = header_affine(hu[u][q], jj);
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) {
+            if (tt < nv) {
+              const float Ag = dot_codes_bf16(cg[u][q], X[tt][q]);
+              const float Au = dot_codes_bf16(cu[u][q], X[tt][q]);
+              v[2 * (u * NT + tt)] += ag.a * Ag - (128.f * ag.a + ag.b) * S[tt][q];
+              v[2 * (u * NT + tt) + 1] += au.a * Au - (128.f * au.a + au.b) * S[tt][q];
+            }
           }
         }
       }
@@ -192,7 +228,8 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
     const int u = (idx >> 1) / NT, tt = (idx >> 1) % NT;
     if (tsum_owner<V, LG>(lane) && !(idx & 1) && tt < nv) {
       const int r = r0 + u * RPS + rho;
-      h16[(size_t)(pos0 + c0 + tt) * I + pos8(r)] = (_Float16)gate_act(s, o, act);
+      // super-blocks: stored as the down kernel's dot2 operand pairs; MXFP4: natural order
+      h16[(size_t)(pos0 + c0 + tt) * I + (FMT == FMT_MXFP4 ? r : pos8(r))] = (_Float16)gate_act(s, o, act);
     }
   }
 }
@@ -202,7 +239,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
 // slot a; one 32-code sub-block of the row per lane (lanes with j >= I/32
 // hold nothing); ypair[p * H + f] = D_e[f]·h_p for each of the expert's pairs
 // p = t*k + s.
-template <int LPR, int U, int NT>
+template <int LPR, int U, int NT, int FMT>
 __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I,
     const int32_t* __restrict__ pairs, const SlotDesc* __restrict__ slots, const _Float16* __restrict__ h16,
@@ -229,12 +266,15 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
     if (tt < n)
 #pragma unroll
       for (int g = 0; g < 4; ++g) hq[tt][g] = load16(h16 + (size_t)(pos0 + tt) * I + 32 * jh + 8 * g);
-  u32x4 cd[U], hd[U];
+  using Hdr = std::conditional_t<FMT == FMT_MXFP4, u32, u32x4>;
+  u32x4 cd[U];
+  Hdr hd[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint8_t* row = base + (size_t)(n0 + u * RPS + rho) * drow_bytes;
     cd[u] = has ? load_nt(row + 16 * j) : u32x4{0u, 0u, 0u, 0u};
-    hd[u] = has ? load_nt(row + hdr) : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (FMT == FMT_MXFP4) hd[u] = has ? (u32)__builtin_nontemporal_load(row + I / 2 + j) : 0u;
+    else hd[u] = has ? load_nt(row + hdr) : u32x4{0u, 0u, 0u, 0u};
   }
   __builtin_amdgcn_sched_barrier(0);
   const u32 ONES = 0x3C003C00u;           // fp16 (1, 1)
@@ -251,8 +291,10 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
         for (int g = 0; g < 4; ++g) {
           const u32x4 r = c0 == 0 ? hq[tt][g] : load16(hp + 8 * g);
           X[tt][4 * g + 0] = r.x; X[tt][4 * g + 1] = r.y; X[tt][4 * g + 2] = r.z; X[tt][4 * g + 3] = r.w;
-          s = dot2_f16(r.x, ONES, s); s = dot2_f16(r.y, ONES, s);
-          s = dot2_f16(r.z, ONES, s); s = dot2_f16(r.w, ONES, s);
+          if constexpr (FMT != FMT_MXFP4) {    // the super-block min term needs sum(h)
+            s = dot2_f16(r.x, ONES, s); s = dot2_f16(r.y, ONES, s);
+            s = dot2_f16(r.z, ONES, s); s = dot2_f16(r.w, ONES, s);
+          }
         }
         S[tt] = s;
       }
@@ -262,10 +304,18 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
     for (int i = 0; i < V; ++i) v[i] = 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const Affine af = header_affine(hd[u], j & 7);
+      if constexpr (FMT == FMT_MXFP4) {
+        // a lane past the row has scale code 0 (factor 0) and zero codes
+        const float sc = e8m0_scale(hd[u]);
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
-        if (tt < nv) v[u * NT + tt] = af.a * dot_codes_f16(cd[u], X[tt]) - (1024.f * af.a + af.b) * S[tt];
+        for (int tt = 0; tt < NT; ++tt)
+          if (tt < nv) v[u * NT + tt] = sc * dot_fp4_f16(cd[u], X[tt]);
+      } else {
+        const Affine af = header_affine(hd[u], j & 7);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          if (tt < nv) v[u * NT + tt] = af.a * dot_codes_f16(cd[u], X[tt]) - (1024.f * af.a + af.b) * S[tt];
+      }
     }
     const float s = tsum<V, LG>(v);
     const int idx = tsum_index<V>(lane);
@@ -274,53 +324,53 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
   }
 }
 
-template <int IPL, int LPR, int U, int NT>
+template <int IPL, int LPR, int U, int NT, int FMT>
 static hipError_t gateup_go(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
                             const SlotDesc* slots, _Float16* h16, int nslots, hipStream_t s) {
   constexpr int RW = (WAVE / LPR) * U;
   static_assert(RW <= 64, "four waves of RW rows must divide a multiple of 256");
   const long long blocks = (long long)nslots * (d.I / (4 * RW));
-  hipLaunchKernelGGL((gateup_egemv_kernel<IPL, LPR, U, NT>), dim3((unsigned)blocks), dim3(BLOCK), 0, s,
+  hipLaunchKernelGGL((gateup_egemv_kernel<IPL, LPR, U, NT, FMT>), dim3((unsigned)blocks), dim3(BLOCK), 0, s,
                      layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, slots, h16,
                      d.act);
   return hipGetLastError();
 }
 
-template <int LPR, int U, int NT>
+template <int LPR, int U, int NT, int FMT>
 static hipError_t down_go(const Layout& d, const uint8_t* layer, const int32_t* pairs, const SlotDesc* slots,
                           const _Float16* h16, float* ypair, int nslots, hipStream_t s) {
   constexpr int RW = (WAVE / LPR) * U;
   static_assert(RW <= 64, "four waves of RW rows must divide a multiple of 256");
   const long long blocks = (long long)nslots * (d.H / (4 * RW));
-  hipLaunchKernelGGL((down_egemv_kernel<LPR, U, NT>), dim3((unsigned)blocks), dim3(BLOCK), 0, s, layer + d.dn_off,
+  hipLaunchKernelGGL((down_egemv_kernel<LPR, U, NT, FMT>), dim3((unsigned)blocks), dim3(BLOCK), 0, s, layer + d.dn_off,
                      d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, pairs, slots, h16, ypair);
   return hipGetLastError();
 }
 
 // Token chunk NT of both kernels: 2 while the routed experts average at most
 // 2 pairs (fewer registers, more waves in flight), else 4.
-template <int NT>
+template <int NT, int FMT>
 static hipError_t egemv_go(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
                            const SlotDesc* slots, _Float16* h16, float* ypair, int nslots, hipStream_t s) {
   hipError_t e;
   // gate/up: the per-token kernel's lane mapping of a hidden-size row
   switch (d.H) {
-    case 256: e = gateup_go<1, 8, 2, 2>(d, layer, x, pairs, slots, h16, nslots, s); break;
-    case 512: e = gateup_go<1, 16, 2, NT>(d, layer, x, pairs, slots, h16, nslots, s); break;
-    case 1024: e = gateup_go<1, 32, 4, NT>(d, layer, x, pairs, slots, h16, nslots, s); break;
-    case 2048: e = gateup_go<1, 64, 4, NT>(d, layer, x, pairs, slots, h16, nslots, s); break;
-    case 4096: e = gateup_go<2, 64, 2, 2>(d, layer, x, pairs, slots, h16, nslots, s); break;
-    case 6144: e = gateup_go<3, 64, 1, 1>(d, layer, x, pairs, slots, h16, nslots, s); break;
-    case 8192: e = gateup_go<4, 64, 1, 1>(d, layer, x, pairs, slots, h16, nslots, s); break;
+    case 256: e = gateup_go<1, 8, 2, 2, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
+    case 512: e = gateup_go<1, 16, 2, NT, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
+    case 1024: e = gateup_go<1, 32, 4, NT, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
+    case 2048: e = gateup_go<1, 64, 4, NT, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
+    case 4096: e = gateup_go<2, 64, 2, 2, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
+    case 6144: e = gateup_go<3, 64, 1, 1, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
+    case 8192: e = gateup_go<4, 64, 1, 1, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
   // down: a power-of-two lane group covering the I/32 sub-blocks of a row
   const int nsb = d.I / 32;
-  if (nsb <= 8) return down_go<8, 2, NT>(d, layer, pairs, slots, h16, ypair, nslots, s);
-  if (nsb <= 16) return down_go<16, 4, NT>(d, layer, pairs, slots, h16, ypair, nslots, s);
-  if (nsb <= 32) return down_go<32, 4, NT>(d, layer, pairs, slots, h16, ypair, nslots, s);
-  return down_go<64, 4, NT>(d, layer, pairs, slots, h16, ypair, nslots, s);
+  if (nsb <= 8) return down_go<8, 2, NT, FMT>(d, layer, pairs, slots, h16, ypair, nslots, s);
+  if (nsb <= 16) return down_go<16, 4, NT, FMT>(d, layer, pairs, slots, h16, ypair, nslots, s);
+  if (nsb <= 32) return down_go<32, 4, NT, FMT>(d, layer, pairs, slots, h16, ypair, nslots, s);
+  return down_go<64, 4, NT, FMT>(d, layer, pairs, slots, h16, ypair, nslots, s);
 }
 
 }  // namespace egemv
@@ -336,8 +386,13 @@ hipError_t launch_egemv_ffn(const Layout& d, const uint8_t* layer, const uint16_
   const int P = T * d.k;
   const int nslots = P < d.E ? P : d.E;     // routed experts, at most
   const SlotDesc* slots = static_cast<const SlotDesc*>(slot_desc);
-  const hipError_t e = P <= 2 * d.E ? egemv_go<2>(d, layer, x, pairs, slots, h16, ypair, nslots, s)
-                                    : egemv_go<4>(d, layer, x, pairs, slots, h16, ypair, nslots, s);
+  hipError_t e;
+  if (d.fmt == FMT_MXFP4)
+    e = P <= 2 * d.E ? egemv_go<2, FMT_MXFP4>(d, layer, x, pairs, slots, h16, ypair, nslots, s)
+                     : egemv_go<4, FMT_MXFP4>(d, layer, x, pairs, slots, h16, ypair, nslots, s);
+  else
+    e = P <= 2 * d.E ? egemv_go<2, FMT_Q4K>(d, layer, x, pairs, slots, h16, ypair, nslots, s)
+                     : egemv_go<4, FMT_Q4K>(d, layer, x, pairs, slots, h16, ypair, nslots, s);
   if (e != hipSuccess) return e;
   return launch_combine(d, ypair, w, out, T, s);
 }

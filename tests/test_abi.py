@@ -54,7 +54,8 @@ def test_status_strings():
     ((2048, 128, 8, 768, 1, 1, 0x20, 1e-6), True),  # MXFP4 expert weights
     ((2048, 128, 8, 768, 1, 1, 0x29, 1e-6), True),  # MXFP4 with an activation and the per-token path forced
     ((2048, 128, 8, 768, 1, 1, 0x22, 1e-6), False), # MXFP4 with the grouped path forced
-    ((2048, 128, 8, 768, 1, 1, 0x24, 1e-6), False), # MXFP4 with the expert-major GEMV forced
+    ((2048, 128, 8, 768, 1, 1, 0x24, 1e-6), True),  # MXFP4 with the expert-major GEMV forced
+    ((256, 8, 2, 2304, 1, 1, 0x24, 1e-6), False),   # ... which needs inter <= 2048
     ((2048, 128, 8, 768, 1, 1, 0x40, 1e-6), False), # unknown flag
     ((300, 8, 2, 512, 1, 1, 0, 1e-6), False),       # hidden not a multiple of 256
     ((768, 8, 2, 512, 1, 1, 0, 1e-6), False),       # hidden lane mapping unsupported

@@ -484,11 +484,11 @@ def test_mx_qwen_forward_single_tokens(mx_qwen):
     print(f"MXFP4 decode, 6 tokens: worst max|err|/max|ref| = {worst:.3e}")
 
 
-@pytest.mark.parametrize("T", [7, 64])
+@pytest.mark.parametrize("T", [7, 8, 16, 64])
 def test_mx_qwen_batched_tokens(mx_qwen, T):
-    """Batches run the per-token GEMV path with MXFP4 weights; 64 tokens are
-    checked on a sample, routing and outputs of every token are checked for
-    properties."""
+    """Batches with MXFP4 weights: 7 tokens run the per-token GEMV path, 8 and
+    more the expert-major GEMV (2 and 4 token chunks); 64 tokens are checked
+    on a sample, routing and outputs of every token for properties."""
     xb = synth.x_bf16(mx_qwen.shape, 41, T, T=T)
     got = mx_qwen.forward(xb)
     sample = None if T <= 8 else [0, 1, T // 2, T - 2, T - 1]
@@ -499,6 +499,16 @@ def test_mx_qwen_batched_tokens(mx_qwen, T):
 
 MX_EDGE = [synth.Shape(s.name + "-mx", s.model, s.hidden, s.n_experts, s.top_k, s.inter, synth.FMT_MXFP4)
            for s in EDGE]
+
+
+@pytest.mark.parametrize("shape", MX_EDGE, ids=[s.name for s in MX_EDGE])
+def test_mx_edge_shapes_expert_gemv(dev, shape):
+    """The expert-major GEMV forced with MXFP4 weights on every edge shape;
+    70 tokens give multi-chunk experts."""
+    st = Setup(shape, dev, n_layers=1, max_tokens=70, flags=MX | q.FLAG_FORCE_EXPERT_GEMV)
+    for T in (2, 5, 70):
+        xb = synth.x_bf16(shape, 12, T, T=T)
+        _check_layer(st, xb, st.forward(xb))
 
 
 @pytest.mark.parametrize("shape", MX_EDGE, ids=[s.name for s in MX_EDGE])
@@ -515,8 +525,8 @@ def test_mx_edge_shapes(dev, shape):
                                            ("swiglu_oai", q.FLAG_ACT_SWIGLU_OAI, oracle.ACT_SWIGLU_OAI)])
 def test_mx_gate_activations(dev, name, flag, act):
     S = synth.Shape("h1024-mx-act", 13, 1024, 16, 4, 256, synth.FMT_MXFP4)
-    st = Setup(S, dev, n_layers=1, max_tokens=4, flags=MX | flag)
-    for T in (1, 4):
+    st = Setup(S, dev, n_layers=1, max_tokens=16, flags=MX | flag)
+    for T in (1, 4, 16):
         xb = synth.x_bf16(S, 9, T, T=T)
         got = st.forward(xb)
         ref = oracle.moe_layer(st.src, 0, xb, act=act)
