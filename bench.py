@@ -306,12 +306,17 @@ def mxfp4_decode(L, dev, stream, args, q, np, torch, synth):
         torch.cuda.synchronize()
         times += [a.elapsed_time(b) for a, b in evs]
     gu_us = float(np.mean(times)) * 1e3
+    batched = None
+    if not args.no_batched:
+        batched = batched_measurements(S, blob, L, dev, stream, q, np, torch, synth, base_flags=q.FLAG_WEIGHTS_MXFP4,
+                                       paths={8: ("gemv", "expert_gemv"), 32: ("gemv", "expert_gemv"),
+                                              128: ("expert_gemv",)}, with_zipf=False)
     del graph, blob, staging
     torch.cuda.synchronize()
     return {"us_per_step": round(us, 1), "tok_s": round(1e6 / us, 1), "expert_bytes_per_token": expert_bytes,
             "expert_gbps": round(expert_bytes / us * 1e-3, 1), "gateup_us": round(gu_us, 3),
             "gateup_bytes_per_launch": gu_bytes, "gateup_gbps": round(gu_bytes / gu_us * 1e-3, 1),
-            "outputs_finite": finite}
+            "outputs_finite": finite, "batched": batched}
 
 
 def _graph_us(calls, n_rot, reps, stream, torch):
@@ -376,19 +381,21 @@ def single_layer_measurements(S, blob, L, dev, stream, q, np, torch, synth):
     return res
 
 
-def batched_measurements(S, blob, L, dev, stream, q, np, torch, synth):
+def batched_measurements(S, blob, L, dev, stream, q, np, torch, synth, base_flags=0, paths=None, with_zipf=True):
     """Small-batch decode / short prefill (T = 2 ... 256; N(0,1) logits) on
     the per-token GEMV path, the expert-major GEMV path and the grouped MFMA
     path, and the Zipf-skewed 4096-token chunk on the grouped path. Routing from given logits, expert
     FFN only, each call on a different layer of the stack in turn (so a
     layer's experts are not cache-resident from the previous call); captured
     in a graph, timed with HIP events. Unique expert bytes = experts with at
-    least one routed pair x 2,654,208 B."""
+    least one routed pair x the shape's expert bytes (2,654,208 B; MXFP4
+    2,506,752 B). base_flags / paths / with_zipf select the weight encoding
+    and the cases."""
     res = {}
     n_rot = min(L, 16)
 
     def run_case(T, zipf, flag, case):
-        plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=L, max_tokens=T, flags=flag)
+        plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=L, max_tokens=T, flags=flag | base_flags)
         scratch = plan.new_scratch(T, device=dev)
         xb = synth.x_bf16(S, case, T, T=T)
         x = torch.from_numpy(xb.view(np.int16)).to(dev)
@@ -437,13 +444,15 @@ def batched_measurements(S, blob, L, dev, stream, q, np, torch, synth):
         return r
 
     flags = {"gemv": q.FLAG_FORCE_GEMV, "expert_gemv": q.FLAG_FORCE_EXPERT_GEMV, "grouped": q.FLAG_FORCE_GROUPED}
-    paths = {2: ("gemv", "expert_gemv"), 8: tuple(flags), 32: tuple(flags), 128: tuple(flags),
-             256: ("expert_gemv", "grouped")}
+    if paths is None:
+        paths = {2: ("gemv", "expert_gemv"), 8: tuple(flags), 32: tuple(flags), 128: tuple(flags),
+                 256: ("expert_gemv", "grouped")}
     for T, names in paths.items():
         res[f"T{T}"] = {name: run_case(T, None, flags[name], 3) for name in names}
-    z = run_case(4096, 1.1, q.FLAG_FORCE_GROUPED, 4)
-    z["mfma_util"] = round(z["tflops"] / MFMA_FP16_PEAK_TFLOPS, 4)
-    res["T4096_zipf"] = z
+    if with_zipf:
+        z = run_case(4096, 1.1, q.FLAG_FORCE_GROUPED, 4)
+        z["mfma_util"] = round(z["tflops"] / MFMA_FP16_PEAK_TFLOPS, 4)
+        res["T4096_zipf"] = z
     res["note"] = "route (given logits) + expert FFN per call; us per call averaged over rotating layers"
     return res
 
