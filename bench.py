@@ -256,7 +256,9 @@ def mxfp4_decode(L, dev, stream, args, q, np, torch, synth):
     """The same decode step with MXFP4 expert weights: the L layers'
     Gaussian weights encoded as FP4 E2M1 codes with an E8M0 scale per 32
     (4.25 bits per weight), a blob of their own, the step captured as one
-    graph and timed like the main leg; plus the gate/up kernel alone."""
+    graph and timed like the main leg; plus the gate/up kernel alone and the
+    batched legs on the MXFP4 paths (the grouped path is its 16-pair MFMA
+    tiles at every size)."""
     S = synth.QWEN3_30B_A3B_MXFP4
     plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=L, max_tokens=1, flags=q.FLAG_WEIGHTS_MXFP4)
     t0 = time.time()
@@ -309,8 +311,8 @@ def mxfp4_decode(L, dev, stream, args, q, np, torch, synth):
     batched = None
     if not args.no_batched:
         batched = batched_measurements(S, blob, L, dev, stream, q, np, torch, synth, base_flags=q.FLAG_WEIGHTS_MXFP4,
-                                       paths={8: ("gemv", "expert_gemv"), 32: ("gemv", "expert_gemv"),
-                                              128: ("expert_gemv",)}, with_zipf=False)
+                                       paths={8: ("gemv", "expert_gemv"), 32: ("expert_gemv", "grouped"),
+                                              128: ("expert_gemv", "grouped"), 256: ("grouped",)}, with_zipf=True)
     del graph, blob, staging
     torch.cuda.synchronize()
     return {"us_per_step": round(us, 1), "tok_s": round(1e6 / us, 1), "expert_bytes_per_token": expert_bytes,

@@ -73,11 +73,11 @@ enum moe_status {
  * weights). MXFP4: the pages' FP4 experts with bf16 activations and inline
  * dequant (sparkinfer CuTe-DSL README, "moe" paragraph), in 17-byte blocks of
  * 32 weights: one E8M0 scale byte e (2^(e-127)), then 16 bytes of FP4 E2M1
- * codes, element 2i in the low nibble of byte 1+i. Scale codes 0 and 255
- * are rejected by the packer. Runs on the per-token GEMV path while
- * T*k < E/2 and on the expert-major GEMV above (MOE_FLAG_FORCE_EXPERT_GEMV
- * and MOE_FLAG_FORCE_GEMV apply); forcing the grouped MFMA path is
- * unsupported with it. */
+ * codes, element 2i in the low nibble of byte 1+i. The packer accepts scale
+ * codes 2..252 (2^-125 .. 2^125). Paths: per-token GEMV while T*k < E/2,
+ * expert-major GEMV up to T*k = 2.5 E, then MFMA tiles of 16 pairs (hidden 512,
+ * 1024 or 2048 and inter <= 1024; otherwise the expert-major GEMV). The
+ * force flags apply, MOE_FLAG_FORCE_GROUPED only where the 16-pair tiles do. */
 #define MOE_FLAG_WEIGHTS_MXFP4 0x20u
 
 typedef struct moe_config {
@@ -116,7 +116,7 @@ size_t moe_scratch_bytes(const moe_plan* plan, int32_t T);     /* device scratch
  * memory, read only. The device layout written to dst_host (moe_layer_bytes,
  * host memory owned by the caller) is private to the library; the caller
  * copies it to blob + moe_layer_offset(layer). moe_pack_layer returns
- * MOE_ERR_INVALID_ARGUMENT for an MXFP4 scale code of 0 or 255.
+ * MOE_ERR_INVALID_ARGUMENT for an MXFP4 scale code outside 2..252.
  */
 int moe_pack_header(const moe_plan* plan, void* dst_host);
 int moe_pack_layer(const moe_plan* plan, const uint8_t* gate_host, const uint8_t* up_host,

@@ -30,8 +30,8 @@ static bool cfg_ok(const moe_config* c) {
   const uint32_t act = c->flags & (MOE_FLAG_ACT_RELU2 | MOE_FLAG_ACT_SWIGLU_OAI);
   const uint32_t fmt = c->flags & MOE_FLAG_WEIGHTS_MXFP4;
   if (c->flags & ~(force | act | fmt)) return false;
-  // MXFP4 weights run on the per-token and expert-major GEMV paths
-  if (fmt && (force & MOE_FLAG_FORCE_GROUPED)) return false;
+  // MXFP4 on MFMA: the 16-pair tiles only (hidden 512, 1024 or 2048, inter <= 1024)
+  if (fmt && (force & MOE_FLAG_FORCE_GROUPED) && !((H == 512 || H == 1024 || H == 2048) && I <= 1024)) return false;
   if (force & (force - 1)) return false;          // at most one path may be forced
   if (act & (act - 1)) return false;              // at most one activation
   // expert-major GEMV: one 32-code sub-block of a down row per lane of a wave
@@ -114,7 +114,9 @@ static inline void join_block(const uint8_t* hdr, const uint8_t* codes, uint8_t*
 }
 
 // MXFP4 rows: canonical [scale][16 code bytes] blocks <-> [codes][scales]
-static bool mx_scale_ok(uint8_t e) { return e != 0 && e != 255; }
+// scale codes 2..252: every weight, and every scaled pair the MFMA tiles
+// convert, is then a normal bf16 (or zero)
+static bool mx_scale_ok(uint8_t e) { return e >= 2 && e <= 252; }
 
 static int pack_mx_layer(const Layout& d, const uint8_t* gate, const uint8_t* up, const uint8_t* down,
                          uint8_t* dst) {
@@ -278,6 +280,7 @@ constexpr long long G16_MAX_PAIRS_PER_EXPERT = 12;
 // Tile shape of the grouped MFMA path: 16-pair tiles with every weight load
 // in flight while experts carry few pairs, 32- or 96-pair tiles beyond.
 static Path grouped_tiles(const Layout& d, int32_t T) {
+  if (d.fmt == FMT_MXFP4) return Path::Grouped16;   // its only MFMA tiles
   if (g16_supported(d) && (long long)T * d.k <= G16_MAX_PAIRS_PER_EXPERT * d.E) return Path::Grouped16;
   return Path::Grouped;
 }
@@ -288,9 +291,13 @@ static Path choose_path(const moe_plan* plan, int32_t T) {
   if (d.flags & MOE_FLAG_FORCE_EXPERT_GEMV) return Path::ExpertGemv;
   const long long P = (long long)T * d.k, E = d.E;
   if (2 * P < E) return Path::Gemv;
-  // MXFP4: no MFMA tiles; the expert-major GEMV streams each routed expert
-  // once for any larger batch
-  if (d.fmt == FMT_MXFP4) return egemv_supported(d) ? Path::ExpertGemv : Path::Gemv;
+  // MXFP4: the expert-major GEMV up to 2.5 pairs per expert, the 16-pair
+  // MFMA tiles beyond where the shape has them (measured on the
+  // Qwen3-30B-A3B-shaped layer: level between 32 and 48 tokens)
+  if (d.fmt == FMT_MXFP4) {
+    if (g16_supported(d) && (2 * P > 5 * E || !egemv_supported(d))) return Path::Grouped16;
+    return egemv_supported(d) ? Path::ExpertGemv : Path::Gemv;
+  }
   const bool g16 = g16_supported(d);
   if (egemv_supported(d) && (P <= E || (!g16 && 4 * P <= 9 * E))) return Path::ExpertGemv;
   return grouped_tiles(d, T);
@@ -305,7 +312,7 @@ struct WorkList {
 };
 static WorkList work_list(const Layout& d, Path p, int32_t T, uint8_t* scr, const Scratch& sc) {
   if (p == Path::Grouped) return {reinterpret_cast<int32_t*>(scr + sc.tile_off), nullptr, grouped_mt(d, T), 0};
-  if (p == Path::Grouped16) return {nullptr, scr + sc.slots, 16, g16_max_tiles(d, T)};
+  if (p == Path::Grouped16) return {nullptr, scr + sc.slots, g16_mt(d, T), g16_max_tiles(d, T)};
   const int P = T * d.k;
   return {nullptr, scr + sc.slots, P, 1 + (P < d.E ? P : d.E)};
 }

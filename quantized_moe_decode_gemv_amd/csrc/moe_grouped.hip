@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_device.h"
 
 namespace qmoe {
@@ -412,17 +414,39 @@ __device__ __forceinline__ u32 dword_of(const u32x4& c, int i) {
   return i == 0 ? c.x : (i == 1 ? c.y : (i == 2 ? c.z : c.w));
 }
 
-// Gate/up: workgroup = one tile x 16 row pairs (intermediate rows f0 .. f0+15);
+// MXFP4 on the 16-pair tiles: the block's E8M0 scale goes into the FP4
+// conversion, which yields the exact weights as bf16 (scale codes 2..252 keep
+// every value a normal bf16), so v_mfma_f32_16x16x32_bf16 runs on exact
+// operands in natural K order: A is the bf16 activations as loaded, B the
+// eight weights of one code dword.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 fp4x8_bf16(u32 v, float scale) {
+  u32x4 o;
+  o.x = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 0));
+  o.y = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 1));
+  o.z = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2));
+  o.w = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3));
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+// Gate/up: workgroup = one tile x 16 row pairs (intermediate rows f0 .. f0+15),
+// the tile's pairs 16 at a time (a tile holds 16 pairs, or for MXFP4 at
+// large batches 64 or 128, which then reuse the weights in registers);
 // wave w takes K range [w*H/4, (w+1)*H/4), G = H/512 groups of 128 K. The
 // four partial products are added in wave order through LDS, then SiLU(gate)
 // * up goes to h16 at the pairs' sorted positions, in unpack order within
 // each group of 8 (as the 32/96-pair tiles write it).
-template <int G>
+// MXFP4 (FMT): h is written as bf16 hi and lo parts, h = hi + lo to about
+// 2^-17, natural order, the lo plane hlo elements after the hi plane.
+template <int G, int FMT, bool MULTI>
 __global__ __launch_bounds__(BLOCK) void gateup_g16_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles,
-    _Float16* __restrict__ h16, int act) {
-  constexpr int NH = (G + 1) / 2;               // super-blocks per wave (a group is half of one)
+    _Float16* __restrict__ h16, int act, size_t hlo) {
+  constexpr bool MX = FMT == FMT_MXFP4;
+  // super-blocks per wave (a group is half of one); MXFP4: one scale byte per group
+  constexpr int NH = MX ? G : (G + 1) / 2;
+  using Hdr = std::conditional_t<MX, u32, u32x4>;
   __shared__ float red[4][2][4][WAVE];
   const int bpt = I / 16;
   const TileRec tr = tiles[blockIdx.x / bpt];
@@ -440,7 +464,8 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16_kernel(
   __builtin_amdgcn_sched_barrier(0);
   // weights: row f0 + r; gate codes at 0, up codes at H/2, gate headers at H, up headers at H + H/16
   const uint8_t* rec = gu + (size_t)tr.e * gu_expert_bytes + (size_t)(f0 + r) * rp_bytes;
-  u32x4 cg[G], cu[G], hg[NH], hu[NH];
+  u32x4 cg[G], cu[G];
+  Hdr hg[NH], hu[NH];
 #pragma unroll
   for (int m = 0; m < G; ++m) {
     const int sbi = sb0 + 4 * m + kg;
@@ -449,60 +474,97 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16_kernel(
   }
 #pragma unroll
   for (int b = 0; b < NH; ++b) {
-    const int sup = (sb0 + 8 * b) >> 3;
-    hg[b] = *reinterpret_cast<const u32x4*>(rec + H + QHDR * sup);
-    hu[b] = *reinterpret_cast<const u32x4*>(rec + H + H / 16 + QHDR * sup);
-  }
-  const int tok = pair / k;
-  u32x4 xr[G][4];
-#pragma unroll
-  for (int m = 0; m < G; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      xr[m][i] = *reinterpret_cast<const u32x4*>(x + (size_t)tok * H + 32 * (sb0 + 4 * m + kg) + 8 * i);
-  __builtin_amdgcn_sched_barrier(0);            // every load is in flight before the first use
-  half8 A[G][4];
-#pragma unroll
-  for (int m = 0; m < G; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) A[m][i] = bf16x8_to_unpack(xr[m][i]);
-  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int m = 0; m < G; ++m) {
-    const int sb = (sb0 + 4 * m + kg) & 7;      // sub-block within its super-block
-    const SubScale sg = sub_scale(hg[m >> 1], sb), su = sub_scale(hu[m >> 1], sb);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[m][i], dequant8(dword_of(cg[m], i), sg), accg, 0, 0, 0);
-      accu = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[m][i], dequant8(dword_of(cu[m], i), su), accu, 0, 0, 0);
+    if constexpr (MX) {
+      const int sbi = sb0 + 4 * b + kg;          // the scale of this lane's block of group b
+      hg[b] = rec[H + sbi];
+      hu[b] = rec[H + H / MXK + sbi];
+    } else {
+      const int sup = (sb0 + 8 * b) >> 3;
+      hg[b] = *reinterpret_cast<const u32x4*>(rec + H + QHDR * sup);
+      hu[b] = *reinterpret_cast<const u32x4*>(rec + H + H / 16 + QHDR * sup);
     }
   }
+  // the tile's pairs 16 at a time (tiles of more than 16 pairs, MULTI, reuse
+  // the weights held in registers; a 16-pair tile is one pass, compiled as such)
+  for (int b0 = 0; b0 < (MULTI ? tr.n : 1); b0 += 16) {
+    const int nb = min(16, tr.n - b0);
+    const int tok = (b0 == 0 ? pair : pairs[tr.pos0 + b0 + min(lane & 15, nb - 1)]) / k;
+    u32x4 xr[G][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    red[w][0][q][lane] = accg[q];
-    red[w][1][q][lane] = accu[q];
-  }
-  __syncthreads();
-  // thread -> (tile row tt, intermediate row f0 + rr); D[tt][rr] sits in lane rr + 16*(tt/4), register tt%4
-  const int tt = tid >> 4, rr = tid & 15;
-  if (tt < tr.n) {
-    const int ln = rr + 16 * (tt >> 2), q = tt & 3;
-    const float g = ((red[0][0][q][ln] + red[1][0][q][ln]) + red[2][0][q][ln]) + red[3][0][q][ln];
-    const float u = ((red[0][1][q][ln] + red[1][1][q][ln]) + red[2][1][q][ln]) + red[3][1][q][ln];
-    const int f = f0 + rr;
-    h16[(size_t)(tr.pos0 + tt) * I + (f & ~7) + nib_pos(f & 7)] = (_Float16)gate_act(g, u, act);
+    for (int m = 0; m < G; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xr[m][i] = *reinterpret_cast<const u32x4*>(x + (size_t)tok * H + 32 * (sb0 + 4 * m + kg) + 8 * i);
+    __builtin_amdgcn_sched_barrier(0);            // every load is in flight before the first use
+    f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (MX) {
+#pragma unroll
+      for (int m = 0; m < G; ++m) {
+        const float sg = e8m0_scale(hg[m]), su = e8m0_scale(hu[m]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, xr[m][i]);
+          accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_bf16(dword_of(cg[m], i), sg), accg, 0, 0, 0);
+          accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_bf16(dword_of(cu[m], i), su), accu, 0, 0, 0);
+        }
+      }
+    } else {
+      half8 A[G][4];
+#pragma unroll
+      for (int m = 0; m < G; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A[m][i] = bf16x8_to_unpack(xr[m][i]);
+#pragma unroll
+      for (int m = 0; m < G; ++m) {
+        const int sb = (sb0 + 4 * m + kg) & 7;    // sub-block within its super-block
+        const SubScale sg = sub_scale(hg[m >> 1], sb), su = sub_scale(hu[m >> 1], sb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[m][i], dequant8(dword_of(cg[m], i), sg), accg, 0, 0, 0);
+          accu = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[m][i], dequant8(dword_of(cu[m], i), su), accu, 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      red[w][0][q][lane] = accg[q];
+      red[w][1][q][lane] = accu[q];
+    }
+    __syncthreads();
+    // thread -> (tile row tt, intermediate row f0 + rr); D[tt][rr] sits in lane rr + 16*(tt/4), register tt%4
+    const int tt = tid >> 4, rr = tid & 15;
+    if (tt < nb) {
+      const int ln = rr + 16 * (tt >> 2), q = tt & 3;
+      const float g = ((red[0][0][q][ln] + red[1][0][q][ln]) + red[2][0][q][ln]) + red[3][0][q][ln];
+      const float u = ((red[0][1][q][ln] + red[1][1][q][ln]) + red[2][1][q][ln]) + red[3][1][q][ln];
+      const int f = f0 + rr;
+      const float hv = gate_act(g, u, act);
+      if constexpr (MX) {
+        uint16_t* hb = reinterpret_cast<uint16_t*>(h16) + (size_t)(tr.pos0 + b0 + tt) * I + f;
+        const uint16_t hi = float_to_bf16_rne(hv);
+        hb[0] = hi;
+        hb[hlo] = float_to_bf16_rne(hv - bf16_bits_to_float(hi));
+      } else {
+        h16[(size_t)(tr.pos0 + b0 + tt) * I + (f & ~7) + nib_pos(f & 7)] = (_Float16)hv;
+      }
+    }
+    if constexpr (MULTI)
+      if (b0 + 16 < tr.n) __syncthreads();      // red is rewritten by the next block
   }
 }
 
 // Down: workgroup = one tile x 64 output rows, wave w rows n0 .. n0+15 over the
 // whole K = I (GD = I/128 groups); h16 holds the tile's rows in unpack order,
 // so A is a plain load. Rows go to ypair at the pair index t*k + s.
-template <int GD>
+// MXFP4 (FMT): h as its bf16 hi and lo planes, two bf16 MFMAs per slice.
+template <int GD, int FMT, bool MULTI>
 __global__ __launch_bounds__(BLOCK) void down_g16_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I,
     const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles, const _Float16* __restrict__ h16,
-    float* __restrict__ ypair) {
-  constexpr int NH = (GD + 1) / 2;
+    float* __restrict__ ypair, size_t hlo) {
+  constexpr bool MX = FMT == FMT_MXFP4;
+  constexpr int NH = MX ? GD : (GD + 1) / 2;
+  using Hdr = std::conditional_t<MX, u32, u32x4>;
   const int bpt = H / 64;
   const TileRec tr = tiles[blockIdx.x / bpt];
   if (tr.n == 0) return;
@@ -511,56 +573,95 @@ __global__ __launch_bounds__(BLOCK) void down_g16_kernel(
   const int n0 = (int)(blockIdx.x % bpt) * 64 + 16 * w;
   const int r = lane & 15, kg = lane >> 4;
   const uint8_t* row = dn + (size_t)tr.e * dn_expert_bytes + (size_t)(n0 + r) * drow_bytes;
-  u32x4 cd[GD], hd[NH];
+  u32x4 cd[GD];
+  Hdr hd[NH];
 #pragma unroll
   for (int m = 0; m < GD; ++m) cd[m] = *reinterpret_cast<const u32x4*>(row + 16 * (4 * m + kg));
 #pragma unroll
-  for (int b = 0; b < NH; ++b) hd[b] = *reinterpret_cast<const u32x4*>(row + I / 2 + QHDR * b);
-  // h of tile row t = l%16; rows past the tile's pairs repeat its last row
-  // (their outputs are not stored), so the loads are unconditional
-  const _Float16* hp = h16 + (size_t)(tr.pos0 + min(lane & 15, tr.n - 1)) * I;
-  half8 A[GD][4];
-#pragma unroll
-  for (int m = 0; m < GD; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) A[m][i] = *reinterpret_cast<const half8*>(hp + 32 * (4 * m + kg) + 8 * i);
-  // output pair indices of this lane's four accumulator rows (tile rows 4*kg .. 4*kg+3)
-  int pr[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) pr[q] = 4 * kg + q < tr.n ? pairs[tr.pos0 + 4 * kg + q] : -1;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int m = 0; m < GD; ++m) {
-    const SubScale sc = sub_scale(hd[m >> 1], (4 * m + kg) & 7);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[m][i], dequant8(dword_of(cd[m], i), sc), acc, 0, 0, 0);
+  for (int b = 0; b < NH; ++b) {
+    if constexpr (MX) hd[b] = row[I / 2 + 4 * b + kg];
+    else hd[b] = *reinterpret_cast<const u32x4*>(row + I / 2 + QHDR * b);
   }
+  // the tile's pairs 16 at a time, the weights held in registers
+  for (int b0 = 0; b0 < (MULTI ? tr.n : 1); b0 += 16) {
+    const int nb = min(16, tr.n - b0);
+    // h of tile row t = l%16; rows past the tile's pairs repeat its last row
+    // (their outputs are not stored), so the loads are unconditional
+    const _Float16* hp = h16 + (size_t)(tr.pos0 + b0 + min(lane & 15, nb - 1)) * I;
+    half8 A[MX ? 1 : GD][4];
+    if constexpr (!MX) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (pr[q] >= 0) ypair[(size_t)pr[q] * H + n0 + r] = acc[q];
+      for (int m = 0; m < GD; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A[m][i] = *reinterpret_cast<const half8*>(hp + 32 * (4 * m + kg) + 8 * i);
+    }
+    // output pair indices of this lane's four accumulator rows (tile rows 4*kg .. 4*kg+3)
+    int pr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pr[q] = 4 * kg + q < nb ? pairs[tr.pos0 + b0 + 4 * kg + q] : -1;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (MX) {
+      const uint16_t* hb = reinterpret_cast<const uint16_t*>(hp);
+#pragma unroll
+      for (int m = 0; m < GD; ++m) {
+        const float sc = e8m0_scale(hd[m]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint16_t* a = hb + 32 * (4 * m + kg) + 8 * i;
+          const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(a), alo = *reinterpret_cast<const bf16x8*>(a + hlo);
+          const bf16x8 b = fp4x8_bf16(dword_of(cd[m], i), sc);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc, 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < GD; ++m) {
+        const SubScale sc = sub_scale(hd[m >> 1], (4 * m + kg) & 7);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[m][i], dequant8(dword_of(cd[m], i), sc), acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (pr[q] >= 0) ypair[(size_t)pr[q] * H + n0 + r] = acc[q];
+  }
 }
 
-template <int G, int GD>
-static hipError_t launch_g16(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
-                             const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, hipStream_t s) {
-  hipLaunchKernelGGL((gateup_g16_kernel<G>), dim3(ntiles * (d.I / 16)), dim3(BLOCK), 0, s, layer + d.gu_off,
-                     d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16, d.act);
+template <int G, int GD, int FMT, bool MULTI>
+static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
+                               const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo,
+                               hipStream_t s) {
+  hipLaunchKernelGGL((gateup_g16_kernel<G, FMT, MULTI>), dim3(ntiles * (d.I / 16)), dim3(BLOCK), 0, s,
+                     layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
+                     d.act, hlo);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((down_g16_kernel<GD>), dim3(ntiles * (d.H / 64)), dim3(BLOCK), 0, s, layer + d.dn_off,
-                     d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, pairs, tiles, h16, ypair);
+  hipLaunchKernelGGL((down_g16_kernel<GD, FMT, MULTI>), dim3(ntiles * (d.H / 64)), dim3(BLOCK), 0, s,
+                     layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, pairs, tiles, h16, ypair, hlo);
   return hipGetLastError();
+}
+
+// hlo: elements from the hi plane of h to its lo plane (MXFP4 only)
+template <int G, int GD>
+static hipError_t launch_g16(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
+                             const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo, bool multi,
+                             hipStream_t s) {
+  if (d.fmt != FMT_MXFP4) return launch_g16_f<G, GD, FMT_Q4K, false>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, s);
+  if (multi) return launch_g16_f<G, GD, FMT_MXFP4, true>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, s);
+  return launch_g16_f<G, GD, FMT_MXFP4, false>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, s);
 }
 
 template <int G>
 static hipError_t launch_g16_i(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
-                               const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, hipStream_t s) {
+                               const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo,
+                               bool multi, hipStream_t s) {
   switch (d.I) {
-    case 256: return launch_g16<G, 2>(d, layer, x, pairs, tiles, ntiles, h16, ypair, s);
-    case 512: return launch_g16<G, 4>(d, layer, x, pairs, tiles, ntiles, h16, ypair, s);
-    case 768: return launch_g16<G, 6>(d, layer, x, pairs, tiles, ntiles, h16, ypair, s);
-    case 1024: return launch_g16<G, 8>(d, layer, x, pairs, tiles, ntiles, h16, ypair, s);
+    case 256: return launch_g16<G, 2>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, s);
+    case 512: return launch_g16<G, 4>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, s);
+    case 768: return launch_g16<G, 6>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, s);
+    case 1024: return launch_g16<G, 8>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -597,9 +698,17 @@ bool g16_supported(const Layout& d) {
   return (d.H == 512 || d.H == 1024 || d.H == 2048) && d.I <= 1024;
 }
 
+// Pairs per tile: 16; MXFP4 (whose only MFMA path this is) takes 64 or 128
+// at larger batches, so a workgroup's weights serve more pairs.
+int g16_mt(const Layout& d, int T) {
+  if (d.fmt != FMT_MXFP4) return 16;
+  const long long P = (long long)T * d.k;
+  return P <= 8LL * d.E ? 16 : (P <= 32LL * d.E ? 64 : 128);
+}
+
 int g16_max_tiles(const Layout& d, int T) {
-  const int P = T * d.k;
-  return (P + 15) / 16 + (P < d.E ? P : d.E);
+  const int P = T * d.k, mt = g16_mt(d, T);
+  return (P + mt - 1) / mt + (P < d.E ? P : d.E);
 }
 
 hipError_t launch_g16_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
@@ -610,11 +719,14 @@ hipError_t launch_g16_ffn(const Layout& d, const uint8_t* layer, const uint16_t*
   if (T <= 0) return hipSuccess;
   const TileRec* tr = static_cast<const TileRec*>(tiles);
   const int nt = g16_max_tiles(d, T);
+  // MXFP4: h's bf16 lo plane follows the hi plane (scratch holds 4 bytes per value)
+  const size_t hlo = (size_t)T * d.k * d.I;
+  const bool multi = g16_mt(d, T) > 16;
   hipError_t e;
   switch (d.H) {
-    case 512: e = launch_g16_i<1>(d, layer, x, pairs, tr, nt, h16, ypair, s); break;
-    case 1024: e = launch_g16_i<2>(d, layer, x, pairs, tr, nt, h16, ypair, s); break;
-    default: e = launch_g16_i<4>(d, layer, x, pairs, tr, nt, h16, ypair, s); break;
+    case 512: e = launch_g16_i<1>(d, layer, x, pairs, tr, nt, h16, ypair, hlo, multi, s); break;
+    case 1024: e = launch_g16_i<2>(d, layer, x, pairs, tr, nt, h16, ypair, hlo, multi, s); break;
+    default: e = launch_g16_i<4>(d, layer, x, pairs, tr, nt, h16, ypair, hlo, multi, s); break;
   }
   if (e != hipSuccess) return e;
   return launch_combine(d, ypair, w, out, T, s);

@@ -91,8 +91,9 @@ struct Scratch {
     tile_off = take((size_t)(d.E + 1) * 4);
     // work records {expert, first pair, pairs}: one per routed expert, or per 16-pair tile
     slots = take((size_t)((T * d.k + 15) / 16 + d.E) * 16);
-    // batched paths only (T > 1): fp16 h in expert-sorted pair order, one fp32 output row per pair
-    h16 = take(T > 1 ? (size_t)T * d.k * d.I * 2 : 0);
+    // batched paths only (T > 1): fp16 h in expert-sorted pair order (MXFP4 on
+    // the 16-pair tiles: bf16 hi and lo planes), one fp32 output row per pair
+    h16 = take(T > 1 ? (size_t)T * d.k * d.I * (d.fmt == FMT_MXFP4 ? 4 : 2) : 0);
     ypair = take(T > 1 ? (size_t)T * d.k * d.H * 4 : 0);
     total = o;
   }
@@ -137,6 +138,7 @@ hipError_t launch_grouped_ffn(const Layout& d, const uint8_t* layer, const uint1
 // 16-pair MFMA tiles with every weight load in flight (T > 1, a few to a
 // few dozen pairs per expert); tiles = slot records of mt = 16
 bool g16_supported(const Layout& d);
+int g16_mt(const Layout& d, int T);
 int g16_max_tiles(const Layout& d, int T);
 hipError_t launch_g16_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
                           const int32_t* pairs, const void* tiles, _Float16* h16, float* ypair, float* out, int T,

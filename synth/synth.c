@@ -27,7 +27,7 @@
  * blocks): 17 bytes per 32 weights, one E8M0 scale byte e (2^(e-127)) then
  * 16 bytes of FP4 E2M1 codes, element 2i in the low nibble of byte 1+i. The
  * quantizer takes the shared exponent floor(log2(max|x|)) - 2 (2 is the
- * largest E2M1 exponent), kept to e in [2, 254] (so every nonzero weight is a
+ * largest E2M1 exponent), kept to e in [2, 252] (so every nonzero weight is a
  * normal bf16 and fp32 number), and rounds x / 2^(e-127) to the nearest E2M1
  * value, ties to the even code, saturating at +-6. An all-zero block gets
  * e = 127 and zero codes.
@@ -235,7 +235,7 @@ void synth_quantize_mx_block(const float* x, uint8_t* blk) {
   if (amax > 0.0) {
     e = (int)floor(log2(amax)) - 2 + 127;
     if (e < 2) e = 2;
-    if (e > 254) e = 254;
+    if (e > 252) e = 252;
   }
   const double scale = ldexp(1.0, e - 127);
   memset(blk, 0, MXBLOCK_BYTES);

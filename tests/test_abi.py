@@ -53,7 +53,8 @@ def test_status_strings():
     ((2048, 128, 8, 768, 1, 1, 0x18, 1e-6), False), # two activations
     ((2048, 128, 8, 768, 1, 1, 0x20, 1e-6), True),  # MXFP4 expert weights
     ((2048, 128, 8, 768, 1, 1, 0x29, 1e-6), True),  # MXFP4 with an activation and the per-token path forced
-    ((2048, 128, 8, 768, 1, 1, 0x22, 1e-6), False), # MXFP4 with the grouped path forced
+    ((2048, 128, 8, 768, 1, 1, 0x22, 1e-6), True),  # MXFP4 with the 16-pair MFMA tiles forced
+    ((4096, 32, 4, 512, 1, 1, 0x22, 1e-6), False),  # ... which hidden 4096 does not have
     ((2048, 128, 8, 768, 1, 1, 0x24, 1e-6), True),  # MXFP4 with the expert-major GEMV forced
     ((256, 8, 2, 2304, 1, 1, 0x24, 1e-6), False),   # ... which needs inter <= 2048
     ((2048, 128, 8, 768, 1, 1, 0x40, 1e-6), False), # unknown flag
@@ -128,8 +129,9 @@ def test_pack_unpack_identity_mxfp4():
     packed = p.pack_layer(g, u, d, r)
     g2, u2, d2, r2 = p.unpack_layer(packed)
     assert np.array_equal(g2, g) and np.array_equal(u2, u) and np.array_equal(d2, d) and np.array_equal(r2, r)
-    # the scale codes the format leaves out (2^-127 and NaN) are refused
-    for bad in (0, 255):
+    # scale codes outside 2..252 are refused (2^-127 and 2^-126 would make
+    # subnormal or flushed products, 2^126 and up overflow bf16, 255 is NaN)
+    for bad in (0, 1, 253, 254, 255):
         d_bad = d.copy()
         d_bad[1, 7, 3, 0] = bad
         with pytest.raises(q.MoeError):

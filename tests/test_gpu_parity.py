@@ -484,11 +484,11 @@ def test_mx_qwen_forward_single_tokens(mx_qwen):
     print(f"MXFP4 decode, 6 tokens: worst max|err|/max|ref| = {worst:.3e}")
 
 
-@pytest.mark.parametrize("T", [7, 8, 16, 64])
+@pytest.mark.parametrize("T", [7, 8, 16, 40, 41, 64])
 def test_mx_qwen_batched_tokens(mx_qwen, T):
-    """Batches with MXFP4 weights: 7 tokens run the per-token GEMV path, 8 and
-    more the expert-major GEMV (2 and 4 token chunks); 64 tokens are checked
-    on a sample, routing and outputs of every token for properties."""
+    """Batches with MXFP4 weights: 7 tokens run the per-token GEMV path, 8 to
+    40 the expert-major GEMV, 41 and 64 the 16-pair MFMA tiles; 64 tokens are
+    checked on a sample, routing and outputs of every token for properties."""
     xb = synth.x_bf16(mx_qwen.shape, 41, T, T=T)
     got = mx_qwen.forward(xb)
     sample = None if T <= 8 else [0, 1, T // 2, T - 2, T - 1]
@@ -499,6 +499,63 @@ def test_mx_qwen_batched_tokens(mx_qwen, T):
 
 MX_EDGE = [synth.Shape(s.name + "-mx", s.model, s.hidden, s.n_experts, s.top_k, s.inter, synth.FMT_MXFP4)
            for s in EDGE]
+MX_G16 = [s for s in MX_EDGE if s.hidden in (512, 1024, 2048) and s.inter <= 1024]
+
+
+@pytest.mark.parametrize("shape", MX_G16, ids=[s.name for s in MX_G16])
+def test_mx_edge_shapes_mfma_tiles(dev, shape):
+    """The 16-pair MFMA tiles forced with MXFP4 weights on every edge shape
+    that has them (bf16 MFMA on exactly converted weights, h as bf16 hi + lo);
+    2, 5 and 70 tokens give single, partial and multi-tile experts."""
+    st = Setup(shape, dev, n_layers=1, max_tokens=70, flags=MX | q.FLAG_FORCE_GROUPED)
+    for T in (2, 5, 70):
+        xb = synth.x_bf16(shape, 12, T, T=T)
+        _check_layer(st, xb, st.forward(xb))
+
+
+@pytest.mark.parametrize("T", [256, 1024])
+def test_mx_qwen_mfma_tiles_large_batch(dev, T):
+    """256 and 1024 tokens of the Qwen3-30B-A3B-shaped layer with MXFP4
+    weights on the MFMA tiles (64- and 128-pair tiles walked 16 pairs at a
+    time), sampled tokens against the oracle."""
+    S = synth.QWEN3_30B_A3B_MXFP4
+    st = Setup(S, dev, n_layers=1, max_tokens=T, flags=MX)
+    xb = synth.x_bf16(S, 42, T, T=T)
+    got = st.forward(xb)
+    _check_layer(st, xb, got, sample=[0, 1, 77, T // 2, T - 2, T - 1])
+    assert np.isfinite(got["y"]).all()
+
+
+def test_mx_zipf_skewed_4096_tokens(dev):
+    """The Zipf-skewed 4096-token chunk (hot experts with thousands of pairs)
+    with MXFP4 weights: routing from the shared fp32 logits must match the
+    oracle exactly; outputs of sampled tokens, including tokens routed to the
+    hottest expert, within the tolerance."""
+    S = synth.QWEN3_30B_A3B_MXFP4
+    T = 4096
+    st = Setup(S, dev, n_layers=1, max_tokens=T, flags=MX)
+    xb = synth.x_bf16(S, 43, T, T=T)
+    lg = synth.logits_f32(S, 4, T, zipf_s=1.1)
+    k = S.top_k
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    counts = torch.empty(S.n_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(S.n_experts + 1, dtype=torch.int32, device=dev)
+    pairs = torch.empty(T * k, dtype=torch.int32, device=dev)
+    out = torch.empty(T, S.hidden, dtype=torch.float32, device=dev)
+    x = st.xdev(xb)
+    lgd = torch.from_numpy(lg).to(dev)
+    st.plan.route(st.blob, 0, None, lgd, T, ids, w, counts, offsets, pairs, scratch=st.scratch)
+    st.plan.expert_ffn(st.blob, 0, x, T, ids, w, out, counts, offsets, pairs, scratch=st.scratch)
+    torch.cuda.synchronize()
+    got_ids, y = ids.cpu().numpy(), out.cpu().numpy()
+    hot = int(np.argmax(counts.cpu().numpy()))
+    hot_tok = int(np.nonzero((got_ids == hot).any(1))[0][0])
+    sample = sorted({0, 1, hot_tok, 2048, T - 1})
+    ref = oracle.moe_layer(st.src, 0, xb[sample], logits=lg[sample])
+    assert np.array_equal(np.sort(got_ids[sample], 1), np.sort(ref["ids"], 1))
+    assert rel_err(y[sample], ref["y"]) <= REL_TOL
+    assert np.isfinite(y).all()
 
 
 @pytest.mark.parametrize("shape", MX_EDGE, ids=[s.name for s in MX_EDGE])
