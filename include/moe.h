@@ -75,7 +75,7 @@ enum moe_status {
  * 32 weights: one E8M0 scale byte e (2^(e-127)), then 16 bytes of FP4 E2M1
  * codes, element 2i in the low nibble of byte 1+i. The packer accepts scale
  * codes 2..252 (2^-125 .. 2^125). Paths: per-token GEMV while T*k < E/2,
- * expert-major GEMV up to T*k = 2.5 E, then MFMA tiles of 16 pairs (hidden 512,
+ * expert-major GEMV up to T*k = 1.75 E, then MFMA tiles (hidden 512,
  * 1024 or 2048 and inter <= 1024; otherwise the expert-major GEMV). The
  * force flags apply, MOE_FLAG_FORCE_GROUPED only where the 16-pair tiles do. */
 #define MOE_FLAG_WEIGHTS_MXFP4 0x20u

@@ -291,11 +291,11 @@ static Path choose_path(const moe_plan* plan, int32_t T) {
   if (d.flags & MOE_FLAG_FORCE_EXPERT_GEMV) return Path::ExpertGemv;
   const long long P = (long long)T * d.k, E = d.E;
   if (2 * P < E) return Path::Gemv;
-  // MXFP4: the expert-major GEMV up to 2.5 pairs per expert, the 16-pair
-  // MFMA tiles beyond where the shape has them (measured on the
-  // Qwen3-30B-A3B-shaped layer: level between 32 and 48 tokens)
+  // MXFP4: the expert-major GEMV up to 1.75 pairs per expert, the MFMA
+  // tiles beyond where the shape has them (measured on the
+  // Qwen3-30B-A3B-shaped layer: 88 / 94 us at 24 tokens, 106 / 103 at 32)
   if (d.fmt == FMT_MXFP4) {
-    if (g16_supported(d) && (2 * P > 5 * E || !egemv_supported(d))) return Path::Grouped16;
+    if (g16_supported(d) && (4 * P > 7 * E || !egemv_supported(d))) return Path::Grouped16;
     return egemv_supported(d) ? Path::ExpertGemv : Path::Gemv;
   }
   const bool g16 = g16_supported(d);

@@ -488,6 +488,12 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16_kernel(
   // the weights held in registers; a 16-pair tile is one pass, compiled as such)
   for (int b0 = 0; b0 < (MULTI ? tr.n : 1); b0 += 16) {
     const int nb = min(16, tr.n - b0);
+    if constexpr (MULTI) {
+      // the codes stay the live state across blocks (32 registers), not
+      // their bf16 conversions (128): convert again per block
+#pragma unroll
+      for (int m = 0; m < G; ++m) asm volatile("" : "+v"(cg[m]), "+v"(cu[m]));
+    }
     const int tok = (b0 == 0 ? pair : pairs[tr.pos0 + b0 + min(lane & 15, nb - 1)]) / k;
     u32x4 xr[G][4];
 #pragma unroll
@@ -629,15 +635,188 @@ __global__ __launch_bounds__(BLOCK) void down_g16_kernel(
   }
 }
 
+// MXFP4 gate/up on tiles of more than 16 pairs: workgroup = one tile x
+// 16*NW row pairs (f0 .. f0 + 16 NW), wave w the K range [w H/4, (w+1) H/4)
+// for all NW row blocks; the tile's pairs 16 at a time, each activation slice
+// loaded once and used for the NW blocks' gate and up MFMAs, so the
+// activations are read I/(16 NW) times per tile instead of I/16. The four
+// partial products are added in wave order through LDS, as in the 16-pair
+// kernel; h goes to the bf16 hi and lo planes.
+template <int G, int NW>
+__global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
+    const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles,
+    _Float16* __restrict__ h16, int act, size_t hlo) {
+  __shared__ float red[4][2][NW][4][WAVE];
+  const int bpt = I / (16 * NW);
+  const TileRec tr = tiles[blockIdx.x / bpt];
+  if (tr.n == 0) return;
+  const int f0 = (int)(blockIdx.x % bpt) * 16 * NW;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int r = lane & 15, kg = lane >> 4;
+  const int sb0 = w * 4 * G;                    // first 32-block of the wave's K range
+  u32x4 cg[NW][G], cu[NW][G];
+  u32 sg[NW][G], su[NW][G];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const uint8_t* rec = gu + (size_t)tr.e * gu_expert_bytes + (size_t)(f0 + 16 * j + r) * rp_bytes;
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+      const int sbi = sb0 + 4 * m + kg;
+      cg[j][m] = *reinterpret_cast<const u32x4*>(rec + 16 * sbi);
+      cu[j][m] = *reinterpret_cast<const u32x4*>(rec + H / 2 + 16 * sbi);
+      sg[j][m] = rec[H + sbi];
+      su[j][m] = rec[H + H / MXK + sbi];
+    }
+  }
+  for (int b0 = 0; b0 < tr.n; b0 += 16) {
+    const int nb = min(16, tr.n - b0);
+    // the codes stay the live state across blocks, converted again per block
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+#pragma unroll
+      for (int m = 0; m < G; ++m) asm volatile("" : "+v"(cg[j][m]), "+v"(cu[j][m]));
+    const int tok = pairs[tr.pos0 + b0 + min(lane & 15, nb - 1)] / k;
+    u32x4 xr[G][4];
+#pragma unroll
+    for (int m = 0; m < G; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xr[m][i] = *reinterpret_cast<const u32x4*>(x + (size_t)tok * H + 32 * (sb0 + 4 * m + kg) + 8 * i);
+    f32x4 accg[NW], accu[NW];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) accg[j] = accu[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, xr[m][i]);
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+          accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_bf16(dword_of(cg[j][m], i), e8m0_scale(sg[j][m])),
+                                                            accg[j], 0, 0, 0);
+          accu[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_bf16(dword_of(cu[j][m], i), e8m0_scale(su[j][m])),
+                                                            accu[j], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        red[w][0][j][q][lane] = accg[j][q];
+        red[w][1][j][q][lane] = accu[j][q];
+      }
+    __syncthreads();
+    // thread -> (tile row tt, row rr of each block); D[tt][rr] sits in lane rr + 16*(tt/4), register tt%4
+    const int tt = tid >> 4, rr = tid & 15;
+    if (tt < nb) {
+      const int ln = rr + 16 * (tt >> 2), q = tt & 3;
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        const float g = ((red[0][0][j][q][ln] + red[1][0][j][q][ln]) + red[2][0][j][q][ln]) + red[3][0][j][q][ln];
+        const float u = ((red[0][1][j][q][ln] + red[1][1][j][q][ln]) + red[2][1][j][q][ln]) + red[3][1][j][q][ln];
+        const float hv = gate_act(g, u, act);
+        uint16_t* hb = reinterpret_cast<uint16_t*>(h16) + (size_t)(tr.pos0 + b0 + tt) * I + f0 + 16 * j + rr;
+        const uint16_t hi = float_to_bf16_rne(hv);
+        hb[0] = hi;
+        hb[hlo] = float_to_bf16_rne(hv - bf16_bits_to_float(hi));
+      }
+    }
+    if (b0 + 16 < tr.n) __syncthreads();        // red is rewritten by the next block
+  }
+}
+
+// MXFP4 down on tiles of more than 16 pairs: workgroup = one tile x
+// 4*NW*16 output rows, wave w the NW blocks of 16 rows from
+// n0 = (256*NW/4)*fb + 16*NW*w over the whole K = I; the tile's pairs 16 at a
+// time, each slice of h (hi and lo planes) loaded once and used for all NW
+// row blocks, so h is read H/(64 NW) times per tile instead of H/16.
+template <int GD, int NW>
+__global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
+    const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I,
+    const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles, const _Float16* __restrict__ h16,
+    float* __restrict__ ypair, size_t hlo) {
+  const int bpt = H / (64 * NW);
+  const TileRec tr = tiles[blockIdx.x / bpt];
+  if (tr.n == 0) return;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int n0 = (int)(blockIdx.x % bpt) * 64 * NW + 16 * NW * w;
+  const int r = lane & 15, kg = lane >> 4;
+  const uint8_t* base = dn + (size_t)tr.e * dn_expert_bytes;
+  u32x4 cd[NW][GD];
+  u32 sc[NW][GD];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const uint8_t* row = base + (size_t)(n0 + 16 * j + r) * drow_bytes;
+#pragma unroll
+    for (int m = 0; m < GD; ++m) {
+      cd[j][m] = *reinterpret_cast<const u32x4*>(row + 16 * (4 * m + kg));
+      sc[j][m] = row[I / 2 + 4 * m + kg];
+    }
+  }
+  for (int b0 = 0; b0 < tr.n; b0 += 16) {
+    const int nb = min(16, tr.n - b0);
+    // the codes stay the live state across blocks, converted again per block
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+#pragma unroll
+      for (int m = 0; m < GD; ++m) asm volatile("" : "+v"(cd[j][m]));
+    const uint16_t* hb = reinterpret_cast<const uint16_t*>(h16) + (size_t)(tr.pos0 + b0 + min(lane & 15, nb - 1)) * I;
+    int pr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pr[q] = 4 * kg + q < nb ? pairs[tr.pos0 + b0 + 4 * kg + q] : -1;
+    f32x4 acc[NW];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < GD; ++m) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t* a = hb + 32 * (4 * m + kg) + 8 * i;
+        const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(a), alo = *reinterpret_cast<const bf16x8*>(a + hlo);
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+          const bf16x8 b = fp4x8_bf16(dword_of(cd[j][m], i), e8m0_scale(sc[j][m]));
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc[j], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (pr[q] >= 0) ypair[(size_t)pr[q] * H + n0 + 16 * j + r] = acc[j][q];
+  }
+}
+
 template <int G, int GD, int FMT, bool MULTI>
 static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
                                const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo,
                                hipStream_t s) {
-  hipLaunchKernelGGL((gateup_g16_kernel<G, FMT, MULTI>), dim3(ntiles * (d.I / 16)), dim3(BLOCK), 0, s,
-                     layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
-                     d.act, hlo);
+  constexpr int NWG = 2;                         // row blocks per wave of the multi-block MXFP4 gate/up
+  if constexpr (FMT == FMT_MXFP4 && MULTI)
+    hipLaunchKernelGGL((gateup_g16m_kernel<G, NWG>), dim3(ntiles * (d.I / (16 * NWG))), dim3(BLOCK), 0, s,
+                       layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
+                       d.act, hlo);
+  else
+    hipLaunchKernelGGL((gateup_g16_kernel<G, FMT, MULTI>), dim3(ntiles * (d.I / 16)), dim3(BLOCK), 0, s,
+                       layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
+                       d.act, hlo);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  constexpr int NW = 4;                          // row blocks per wave of the multi-block MXFP4 down
+  if constexpr (FMT == FMT_MXFP4 && MULTI) {
+    if (d.H % (64 * NW) == 0) {
+      hipLaunchKernelGGL((down_g16m_kernel<GD, NW>), dim3(ntiles * (d.H / (64 * NW))), dim3(BLOCK), 0, s,
+                         layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, pairs, tiles, h16, ypair,
+                         hlo);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((down_g16_kernel<GD, FMT, MULTI>), dim3(ntiles * (d.H / 64)), dim3(BLOCK), 0, s,
                      layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, pairs, tiles, h16, ypair, hlo);
   return hipGetLastError();
@@ -698,12 +877,14 @@ bool g16_supported(const Layout& d) {
   return (d.H == 512 || d.H == 1024 || d.H == 2048) && d.I <= 1024;
 }
 
-// Pairs per tile: 16; MXFP4 (whose only MFMA path this is) takes 64 or 128
-// at larger batches, so a workgroup's weights serve more pairs.
+// Pairs per tile: 16; MXFP4 (whose only MFMA path this is) takes 64 above
+// one pair per expert and 128 above 16, walked by the multi-block kernels
+// (measured on the Qwen3-30B-A3B-shaped layer: at 41 / 96 / 128 tokens
+// 108 / 122 / 126 us against 123 / 151 / 166 us on 16-pair tiles).
 int g16_mt(const Layout& d, int T) {
   if (d.fmt != FMT_MXFP4) return 16;
   const long long P = (long long)T * d.k;
-  return P <= 8LL * d.E ? 16 : (P <= 32LL * d.E ? 64 : 128);
+  return P <= d.E ? 16 : (P <= 16LL * d.E ? 64 : 128);
 }
 
 int g16_max_tiles(const Layout& d, int T) {

@@ -484,11 +484,12 @@ def test_mx_qwen_forward_single_tokens(mx_qwen):
     print(f"MXFP4 decode, 6 tokens: worst max|err|/max|ref| = {worst:.3e}")
 
 
-@pytest.mark.parametrize("T", [7, 8, 16, 40, 41, 64])
+@pytest.mark.parametrize("T", [7, 8, 16, 28, 29, 64])
 def test_mx_qwen_batched_tokens(mx_qwen, T):
     """Batches with MXFP4 weights: 7 tokens run the per-token GEMV path, 8 to
-    40 the expert-major GEMV, 41 and 64 the 16-pair MFMA tiles; 64 tokens are
-    checked on a sample, routing and outputs of every token for properties."""
+    28 the expert-major GEMV, 29 and 64 the MFMA tiles (64-pair tiles walked
+    16 pairs at a time); 64 tokens are checked on a sample, routing and
+    outputs of every token for properties."""
     xb = synth.x_bf16(mx_qwen.shape, 41, T, T=T)
     got = mx_qwen.forward(xb)
     sample = None if T <= 8 else [0, 1, T // 2, T - 2, T - 1]
