@@ -642,11 +642,14 @@ __global__ __launch_bounds__(BLOCK) void down_g16_kernel(
 // activations are read I/(16 NW) times per tile instead of I/16. The four
 // partial products are added in wave order through LDS, as in the 16-pair
 // kernel; h goes to the bf16 hi and lo planes.
-template <int G, int NW>
+template <int G, int NW, int FMT>
 __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles,
     _Float16* __restrict__ h16, int act, size_t hlo) {
+  constexpr bool MX = FMT == FMT_MXFP4;
+  constexpr int NH = MX ? G : (G + 1) / 2;     // scale bytes, or super-block headers, per row
+  using Hdr = std::conditional_t<MX, u32, u32x4>;
   __shared__ float red[4][2][NW][4][WAVE];
   const int bpt = I / (16 * NW);
   const TileRec tr = tiles[blockIdx.x / bpt];
@@ -657,7 +660,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
   const int r = lane & 15, kg = lane >> 4;
   const int sb0 = w * 4 * G;                    // first 32-block of the wave's K range
   u32x4 cg[NW][G], cu[NW][G];
-  u32 sg[NW][G], su[NW][G];
+  Hdr sg[NW][NH], su[NW][NH];
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
     const uint8_t* rec = gu + (size_t)tr.e * gu_expert_bytes + (size_t)(f0 + 16 * j + r) * rp_bytes;
@@ -666,8 +669,17 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
       const int sbi = sb0 + 4 * m + kg;
       cg[j][m] = *reinterpret_cast<const u32x4*>(rec + 16 * sbi);
       cu[j][m] = *reinterpret_cast<const u32x4*>(rec + H / 2 + 16 * sbi);
-      sg[j][m] = rec[H + sbi];
-      su[j][m] = rec[H + H / MXK + sbi];
+    }
+#pragma unroll
+    for (int b = 0; b < NH; ++b) {
+      if constexpr (MX) {
+        sg[j][b] = rec[H + sb0 + 4 * b + kg];
+        su[j][b] = rec[H + H / MXK + sb0 + 4 * b + kg];
+      } else {
+        const int sup = (sb0 + 8 * b) >> 3;
+        sg[j][b] = *reinterpret_cast<const u32x4*>(rec + H + QHDR * sup);
+        su[j][b] = *reinterpret_cast<const u32x4*>(rec + H + H / 16 + QHDR * sup);
+      }
     }
   }
   for (int b0 = 0; b0 < tr.n; b0 += 16) {
@@ -691,13 +703,25 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
     for (int m = 0; m < G; ++m) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, xr[m][i]);
+        if constexpr (MX) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, xr[m][i]);
 #pragma unroll
-        for (int j = 0; j < NW; ++j) {
-          accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_bf16(dword_of(cg[j][m], i), e8m0_scale(sg[j][m])),
-                                                            accg[j], 0, 0, 0);
-          accu[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_bf16(dword_of(cu[j][m], i), e8m0_scale(su[j][m])),
-                                                            accu[j], 0, 0, 0);
+          for (int j = 0; j < NW; ++j) {
+            accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, fp4x8_bf16(dword_of(cg[j][m], i), e8m0_scale(sg[j][m])), accg[j], 0, 0, 0);
+            accu[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, fp4x8_bf16(dword_of(cu[j][m], i), e8m0_scale(su[j][m])), accu[j], 0, 0, 0);
+          }
+        } else {
+          const half8 a = bf16x8_to_unpack(xr[m][i]);
+          const int sb = (sb0 + 4 * m + kg) & 7;
+#pragma unroll
+          for (int j = 0; j < NW; ++j) {
+            accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                a, dequant8(dword_of(cg[j][m], i), sub_scale(sg[j][m >> 1], sb)), accg[j], 0, 0, 0);
+            accu[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                a, dequant8(dword_of(cu[j][m], i), sub_scale(su[j][m >> 1], sb)), accu[j], 0, 0, 0);
+          }
         }
       }
     }
@@ -718,10 +742,15 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
         const float g = ((red[0][0][j][q][ln] + red[1][0][j][q][ln]) + red[2][0][j][q][ln]) + red[3][0][j][q][ln];
         const float u = ((red[0][1][j][q][ln] + red[1][1][j][q][ln]) + red[2][1][j][q][ln]) + red[3][1][j][q][ln];
         const float hv = gate_act(g, u, act);
-        uint16_t* hb = reinterpret_cast<uint16_t*>(h16) + (size_t)(tr.pos0 + b0 + tt) * I + f0 + 16 * j + rr;
-        const uint16_t hi = float_to_bf16_rne(hv);
-        hb[0] = hi;
-        hb[hlo] = float_to_bf16_rne(hv - bf16_bits_to_float(hi));
+        const int f = f0 + 16 * j + rr;
+        if constexpr (MX) {
+          uint16_t* hb = reinterpret_cast<uint16_t*>(h16) + (size_t)(tr.pos0 + b0 + tt) * I + f;
+          const uint16_t hi = float_to_bf16_rne(hv);
+          hb[0] = hi;
+          hb[hlo] = float_to_bf16_rne(hv - bf16_bits_to_float(hi));
+        } else {
+          h16[(size_t)(tr.pos0 + b0 + tt) * I + (f & ~7) + nib_pos(f & 7)] = (_Float16)hv;
+        }
       }
     }
     if (b0 + 16 < tr.n) __syncthreads();        // red is rewritten by the next block
@@ -733,11 +762,14 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
 // n0 = (256*NW/4)*fb + 16*NW*w over the whole K = I; the tile's pairs 16 at a
 // time, each slice of h (hi and lo planes) loaded once and used for all NW
 // row blocks, so h is read H/(64 NW) times per tile instead of H/16.
-template <int GD, int NW>
+template <int GD, int NW, int FMT>
 __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I,
     const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles, const _Float16* __restrict__ h16,
     float* __restrict__ ypair, size_t hlo) {
+  constexpr bool MX = FMT == FMT_MXFP4;
+  constexpr int NH = MX ? GD : (GD + 1) / 2;
+  using Hdr = std::conditional_t<MX, u32, u32x4>;
   const int bpt = H / (64 * NW);
   const TileRec tr = tiles[blockIdx.x / bpt];
   if (tr.n == 0) return;
@@ -747,14 +779,16 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
   const int r = lane & 15, kg = lane >> 4;
   const uint8_t* base = dn + (size_t)tr.e * dn_expert_bytes;
   u32x4 cd[NW][GD];
-  u32 sc[NW][GD];
+  Hdr sc[NW][NH];
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
     const uint8_t* row = base + (size_t)(n0 + 16 * j + r) * drow_bytes;
 #pragma unroll
-    for (int m = 0; m < GD; ++m) {
-      cd[j][m] = *reinterpret_cast<const u32x4*>(row + 16 * (4 * m + kg));
-      sc[j][m] = row[I / 2 + 4 * m + kg];
+    for (int m = 0; m < GD; ++m) cd[j][m] = *reinterpret_cast<const u32x4*>(row + 16 * (4 * m + kg));
+#pragma unroll
+    for (int b = 0; b < NH; ++b) {
+      if constexpr (MX) sc[j][b] = row[I / 2 + 4 * b + kg];
+      else sc[j][b] = *reinterpret_cast<const u32x4*>(row + I / 2 + QHDR * b);
     }
   }
   for (int b0 = 0; b0 < tr.n; b0 += 16) {
@@ -776,12 +810,22 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint16_t* a = hb + 32 * (4 * m + kg) + 8 * i;
-        const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(a), alo = *reinterpret_cast<const bf16x8*>(a + hlo);
+        if constexpr (MX) {
+          const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(a), alo = *reinterpret_cast<const bf16x8*>(a + hlo);
 #pragma unroll
-        for (int j = 0; j < NW; ++j) {
-          const bf16x8 b = fp4x8_bf16(dword_of(cd[j][m], i), e8m0_scale(sc[j][m]));
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc[j], 0, 0, 0);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc[j], 0, 0, 0);
+          for (int j = 0; j < NW; ++j) {
+            const bf16x8 b = fp4x8_bf16(dword_of(cd[j][m], i), e8m0_scale(sc[j][m]));
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc[j], 0, 0, 0);
+          }
+        } else {
+          // h16 holds fp16 h in unpack order
+          const half8 ah = *reinterpret_cast<const half8*>(a);
+          const int sb = (4 * m + kg) & 7;
+#pragma unroll
+          for (int j = 0; j < NW; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, dequant8(dword_of(cd[j][m], i), sub_scale(sc[j][m >> 1], sb)),
+                                                           acc[j], 0, 0, 0);
         }
       }
     }
@@ -793,13 +837,18 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
   }
 }
 
+// rows: the multi-row kernels (2 / 4 blocks of 16 rows per wave), which read
+// a tile's activations and h fewer times but run fewer workgroups: always
+// for tiles of more than 16 pairs, and for 16-pair tiles above 6 pairs per
+// expert (super-block weights, Qwen3-30B-A3B shape, same box: at 64 tokens
+// 109 / 112 us without / with, at 128 and 192 tokens 123 / 119 and 146 / 133).
 template <int G, int GD, int FMT, bool MULTI>
 static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
                                const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo,
-                               hipStream_t s) {
-  constexpr int NWG = 2;                         // row blocks per wave of the multi-block MXFP4 gate/up
-  if constexpr (FMT == FMT_MXFP4 && MULTI)
-    hipLaunchKernelGGL((gateup_g16m_kernel<G, NWG>), dim3(ntiles * (d.I / (16 * NWG))), dim3(BLOCK), 0, s,
+                               bool rows, hipStream_t s) {
+  constexpr int NWG = 2;                         // row blocks per wave of the multi-row gate/up
+  if (MULTI || rows)
+    hipLaunchKernelGGL((gateup_g16m_kernel<G, NWG, FMT>), dim3(ntiles * (d.I / (16 * NWG))), dim3(BLOCK), 0, s,
                        layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
                        d.act, hlo);
   else
@@ -808,10 +857,10 @@ static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint
                        d.act, hlo);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int NW = 4;                          // row blocks per wave of the multi-block MXFP4 down
-  if constexpr (FMT == FMT_MXFP4 && MULTI) {
+  constexpr int NW = 4;                          // row blocks per wave of the multi-row down
+  if (MULTI || rows) {
     if (d.H % (64 * NW) == 0) {
-      hipLaunchKernelGGL((down_g16m_kernel<GD, NW>), dim3(ntiles * (d.H / (64 * NW))), dim3(BLOCK), 0, s,
+      hipLaunchKernelGGL((down_g16m_kernel<GD, NW, FMT>), dim3(ntiles * (d.H / (64 * NW))), dim3(BLOCK), 0, s,
                          layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, pairs, tiles, h16, ypair,
                          hlo);
       return hipGetLastError();
@@ -826,21 +875,22 @@ static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint
 template <int G, int GD>
 static hipError_t launch_g16(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
                              const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo, bool multi,
-                             hipStream_t s) {
-  if (d.fmt != FMT_MXFP4) return launch_g16_f<G, GD, FMT_Q4K, false>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, s);
-  if (multi) return launch_g16_f<G, GD, FMT_MXFP4, true>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, s);
-  return launch_g16_f<G, GD, FMT_MXFP4, false>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, s);
+                             bool rows, hipStream_t s) {
+  if (d.fmt != FMT_MXFP4)
+    return launch_g16_f<G, GD, FMT_Q4K, false>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, rows, s);
+  if (multi) return launch_g16_f<G, GD, FMT_MXFP4, true>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, rows, s);
+  return launch_g16_f<G, GD, FMT_MXFP4, false>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, rows, s);
 }
 
 template <int G>
 static hipError_t launch_g16_i(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
                                const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo,
-                               bool multi, hipStream_t s) {
+                               bool multi, bool rows, hipStream_t s) {
   switch (d.I) {
-    case 256: return launch_g16<G, 2>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, s);
-    case 512: return launch_g16<G, 4>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, s);
-    case 768: return launch_g16<G, 6>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, s);
-    case 1024: return launch_g16<G, 8>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, s);
+    case 256: return launch_g16<G, 2>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, rows, s);
+    case 512: return launch_g16<G, 4>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, rows, s);
+    case 768: return launch_g16<G, 6>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, rows, s);
+    case 1024: return launch_g16<G, 8>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, rows, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -903,11 +953,12 @@ hipError_t launch_g16_ffn(const Layout& d, const uint8_t* layer, const uint16_t*
   // MXFP4: h's bf16 lo plane follows the hi plane (scratch holds 4 bytes per value)
   const size_t hlo = (size_t)T * d.k * d.I;
   const bool multi = g16_mt(d, T) > 16;
+  const bool rows = multi || (long long)T * d.k > 6LL * d.E;
   hipError_t e;
   switch (d.H) {
-    case 512: e = launch_g16_i<1>(d, layer, x, pairs, tr, nt, h16, ypair, hlo, multi, s); break;
-    case 1024: e = launch_g16_i<2>(d, layer, x, pairs, tr, nt, h16, ypair, hlo, multi, s); break;
-    default: e = launch_g16_i<4>(d, layer, x, pairs, tr, nt, h16, ypair, hlo, multi, s); break;
+    case 512: e = launch_g16_i<1>(d, layer, x, pairs, tr, nt, h16, ypair, hlo, multi, rows, s); break;
+    case 1024: e = launch_g16_i<2>(d, layer, x, pairs, tr, nt, h16, ypair, hlo, multi, rows, s); break;
+    default: e = launch_g16_i<4>(d, layer, x, pairs, tr, nt, h16, ypair, hlo, multi, rows, s); break;
   }
   if (e != hipSuccess) return e;
   return launch_combine(d, ypair, w, out, T, s);
