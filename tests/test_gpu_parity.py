@@ -384,18 +384,22 @@ def test_graph_replay_matches_eager_bitwise(qwen):
         assert torch.equal(xn, eager_xn), rep
 
 
-@pytest.mark.parametrize("T", [12, 64, 1024])
-def test_batched_graph_replay_matches_eager_bitwise(qwen, T):
+@pytest.mark.parametrize("T,mx", [(12, False), (64, False), (1024, False), (64, True), (1024, True)])
+def test_batched_graph_replay_matches_eager_bitwise(qwen, mx_qwen, T, mx):
     """Batched forward captured in a graph: per-token GEMV path (12 tokens),
-    grouped path with 32-pair tiles (64) and with 96-pair tiles (1024), each
-    including the on-device top-k and dispatch. Every replay (with unrelated
-    eager work in between) must reproduce the eager result bit for bit, and
-    two eager runs must agree."""
-    S = qwen.shape
-    d = qwen.dev
-    plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=T)
+    16-pair tiles (64) and 96-pair tiles (1024), and with MXFP4 weights the
+    64- and 128-pair tiles walked 16 pairs at a time; each including the
+    on-device top-k and dispatch. Every replay (with unrelated eager work in
+    between) must reproduce the eager result bit for bit, and two eager runs
+    must agree."""
+    st = mx_qwen if mx else qwen
+    S = st.shape
+    d = st.dev
+    plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=T,
+                  flags=q.FLAG_WEIGHTS_MXFP4 if mx else 0)
     scratch = plan.new_scratch(T, device=d)
-    x = qwen.xdev(synth.x_bf16(S, 13, T, T=T))
+    x = st.xdev(synth.x_bf16(S, 13, T, T=T))
+    qwen = st
     out = torch.zeros(T, S.hidden, dtype=torch.float32, device=d)
     ids = torch.zeros(T, S.top_k, dtype=torch.int32, device=d)
     w = torch.zeros(T, S.top_k, dtype=torch.float32, device=d)
