@@ -53,7 +53,7 @@ def main():
                     help="first run one plain 256 MiB device copy (reference kernel for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
 
