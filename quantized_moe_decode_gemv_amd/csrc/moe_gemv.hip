@@ -532,8 +532,12 @@ __device__ __forceinline__ void excl_scan256x2(int a, int b, int& ea, int& eb, i
 // pair position, pairs} per tile in expert order, then zero records up to
 // max_slots.
 // Deterministic: ranks come from ballots, not from the order of atomics.
+// NPL: a wave's ids are read NPL per lane at a time, all loads in flight
+// before the first use (32 for large P; 1, the plain loop, for small P,
+// where the unrolled form cost ~2 us).
 constexpr int DISP_THREADS = 1024;
 constexpr int DISP_WAVES = DISP_THREADS / WAVE;
+template <int NPL>
 __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
                                                                 int32_t* __restrict__ offsets, int32_t* __restrict__ pairs,
                                                                 int32_t* __restrict__ tile_off,
@@ -546,7 +550,21 @@ __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* _
   __syncthreads();
   const int chunk = (P + DISP_WAVES - 1) / DISP_WAVES;
   const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
-  for (int p = p0 + lane; p < p1; p += WAVE) atomicAdd(&cnt[wid][ids[p]], 1);
+  if constexpr (NPL == 1) {
+    for (int p = p0 + lane; p < p1; p += WAVE) atomicAdd(&cnt[wid][ids[p]], 1);
+  } else {
+    for (int sb = p0; sb < p1; sb += WAVE * NPL) {
+      int ev[NPL];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const int p = sb + WAVE * j + lane;
+        ev[j] = p < p1 ? ids[p] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (ev[j] >= 0) atomicAdd(&cnt[wid][ev[j]], 1);
+    }
+  }
   __syncthreads();
   // thread e: its expert's column over the waves (exclusive within the expert)
   int tot = 0;
@@ -571,11 +589,9 @@ __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* _
   if (slots)
     for (int i = all_tiles + tid; i < max_slots; i += DISP_THREADS) slots[i] = make_int4(0, 0, 0, 0);
   __syncthreads();
-  // cnt[w][e] is now the first output slot of wave w's pairs for expert e
-  for (int pb = p0; pb < p1; pb += WAVE) {
-    const int p = pb + lane;
-    const bool act = p < p1;
-    const int e = act ? ids[p] : -1;
+  // cnt[w][e] is now the first output slot of wave w's pairs for expert e;
+  // pairs in increasing p (groups of 64 in order, lanes in order)
+  auto place = [&](int p, bool act, int e) {
     unsigned long long same = __ballot(act);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -591,6 +607,28 @@ __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* _
     if (act) pairs[base + rank] = p;
     if (act && rank == n - 1) cnt[wid][e] = base + n;
     __builtin_amdgcn_wave_barrier();
+  };
+  if constexpr (NPL == 1) {
+    for (int pb = p0; pb < p1; pb += WAVE) {
+      const int p = pb + lane;
+      const bool act = p < p1;
+      place(p, act, act ? ids[p] : -1);
+    }
+  } else {
+    for (int sb = p0; sb < p1; sb += WAVE * NPL) {
+      int ev[NPL];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const int p = sb + WAVE * j + lane;
+        ev[j] = p < p1 ? ids[p] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        if (sb + WAVE * j >= p1) break;               // wave-uniform
+        const int p = sb + WAVE * j + lane;
+        place(p, p < p1, ev[j]);
+      }
+    }
   }
 }
 
@@ -743,8 +781,12 @@ hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts,
   // the slot records must cover every tile: at most ceil(T*k / mt) + min(E, T*k)
   const int P = T * d.k;
   if (slots && max_slots < (P + mt - 1) / mt + (P < d.E ? P : d.E)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs, tile_off,
-                     static_cast<int4*>(slots), d.E, P, mt, slots ? max_slots : 0);
+  if (P > 4 * DISP_THREADS)
+    hipLaunchKernelGGL((dispatch_kernel<32>), dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs, tile_off,
+                       static_cast<int4*>(slots), d.E, P, mt, slots ? max_slots : 0);
+  else
+    hipLaunchKernelGGL((dispatch_kernel<1>), dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs, tile_off,
+                       static_cast<int4*>(slots), d.E, P, mt, slots ? max_slots : 0);
   return hipGetLastError();
 }
 
