@@ -629,3 +629,59 @@ def test_host_side_errors(tiny):
     with pytest.raises(q.MoeError) as e:
         tiny.plan.forward(tiny.blob, 0, x, 65, out, scratch=tiny.scratch)
     assert e.value.status == -1
+
+
+class _RescaledSource(oracle.ExpertSource):
+    """MXFP4 blocks of a shape with every scale byte replaced by a seeded
+    draw from [lo, hi]: the kernels' scale decoding across many codes
+    (values stay where fp16 h, used by the GEMV down paths, cannot
+    overflow)."""
+
+    def __init__(self, shape, lo, hi, seed):
+        super().__init__(shape)
+        self.lo, self.hi, self.seed = lo, hi, seed
+
+    def blocks(self, layer, expert):
+        key = (layer, int(expert))
+        if key not in self._cache:
+            mats = []
+            for m in (synth.GATE, synth.UP, synth.DOWN):
+                b = synth.expert_matrix(self.shape, layer, int(expert), m).copy()
+                rng = np.random.default_rng([self.seed, layer, int(expert), m])
+                b[..., 0] = rng.integers(self.lo, self.hi + 1, size=b.shape[:-1], dtype=np.uint8)
+                mats.append(b)
+            self._cache[key] = tuple(mats)
+        return self._cache[key]
+
+
+@pytest.mark.parametrize("flags,Ts", [(0, (1, 3)), (q.FLAG_FORCE_EXPERT_GEMV, (5, 40)),
+                                      (q.FLAG_FORCE_GROUPED, (5, 70))],
+                         ids=["gemv", "expert_gemv", "mfma_tiles"])
+def test_mx_scale_codes_across_range(dev, flags, Ts):
+    """MXFP4 blocks whose scale bytes are drawn from 100..124 (2^-27 .. 2^-3,
+    24 distinct powers of two within every row) on each path, against the
+    oracle on the same blocks."""
+    S = synth.Shape("h512-mx-scales", 31, 512, 8, 2, 256, synth.FMT_MXFP4)
+    src = _RescaledSource(S, 100, 124, 5)
+    plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=max(Ts), flags=MX | flags)
+
+    def layer(l):
+        bl = [src.blocks(l, e) for e in range(S.n_experts)]
+        return (np.stack([b[0] for b in bl]), np.stack([b[1] for b in bl]), np.stack([b[2] for b in bl]),
+                synth.router(S, l))
+
+    blob = plan.upload_blob(layer, device=dev)
+    scratch = plan.new_scratch(max(Ts), device=dev)
+    for T in Ts:
+        xb = synth.x_bf16(S, 14, T, T=T)
+        x = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).to(dev)
+        out = torch.empty(T, S.hidden, dtype=torch.float32, device=dev)
+        ids = torch.empty(T, S.top_k, dtype=torch.int32, device=dev)
+        w = torch.empty(T, S.top_k, dtype=torch.float32, device=dev)
+        plan.forward(blob, 0, x, T, out, ids=ids, w=w, scratch=scratch)
+        torch.cuda.synchronize()
+        ref = oracle.moe_layer(src, 0, xb)
+        got_ids, y = ids.cpu().numpy(), out.cpu().numpy()
+        exempt = check_routing(got_ids, w.cpu().numpy(), ref)
+        keep = [t for t in range(T) if t not in exempt]
+        assert rel_err(y[keep], ref["y"][keep]) <= REL_TOL, (T, rel_err(y[keep], ref["y"][keep]))
