@@ -757,6 +757,8 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
   }
 }
 
+constexpr bool H16_STAGE = true;
+
 // MXFP4 down on tiles of more than 16 pairs: workgroup = one tile x
 // 4*NW*16 output rows, wave w the NW blocks of 16 rows from
 // n0 = (256*NW/4)*fb + 16*NW*w over the whole K = I; the tile's pairs 16 at a
@@ -770,6 +772,10 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
   constexpr bool MX = FMT == FMT_MXFP4;
   constexpr int NH = MX ? GD : (GD + 1) / 2;
   using Hdr = std::conditional_t<MX, u32, u32x4>;
+  // a block's 16 rows of h (MXFP4: hi and lo planes) staged in LDS once for
+  // the four waves; rows padded by 16 bytes against bank conflicts
+  constexpr int PL = MX ? 2 : 1, IK = 128 * GD, LS = IK + 8, CPR = IK / 8;
+  __shared__ __align__(16) uint16_t hs[H16_STAGE ? PL : 1][H16_STAGE ? 16 : 1][H16_STAGE ? LS : 8];
   const int bpt = H / (64 * NW);
   const TileRec tr = tiles[blockIdx.x / bpt];
   if (tr.n == 0) return;
@@ -799,6 +805,21 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
 #pragma unroll
       for (int m = 0; m < GD; ++m) asm volatile("" : "+v"(cd[j][m]));
     const uint16_t* hb = reinterpret_cast<const uint16_t*>(h16) + (size_t)(tr.pos0 + b0 + min(lane & 15, nb - 1)) * I;
+    if constexpr (H16_STAGE) {
+      u32x4 st[PL * 16 * CPR / BLOCK];
+#pragma unroll
+      for (int q = 0; q < PL * 16 * CPR / BLOCK; ++q) {
+        const int c = tid + BLOCK * q, pl = c / (16 * CPR), rem = c % (16 * CPR), row = rem / CPR, c8 = rem % CPR;
+        st[q] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(h16) + (pl ? hlo : 0) +
+                                                (size_t)(tr.pos0 + b0 + min(row, nb - 1)) * I + 8 * c8);
+      }
+#pragma unroll
+      for (int q = 0; q < PL * 16 * CPR / BLOCK; ++q) {
+        const int c = tid + BLOCK * q, pl = c / (16 * CPR), rem = c % (16 * CPR), row = rem / CPR, c8 = rem % CPR;
+        *reinterpret_cast<u32x4*>(&hs[pl][row][8 * c8]) = st[q];
+      }
+      __syncthreads();
+    }
     int pr[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) pr[q] = 4 * kg + q < nb ? pairs[tr.pos0 + b0 + 4 * kg + q] : -1;
@@ -809,9 +830,10 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
     for (int m = 0; m < GD; ++m) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint16_t* a = hb + 32 * (4 * m + kg) + 8 * i;
+        const uint16_t* a = H16_STAGE ? &hs[0][lane & 15][32 * (4 * m + kg) + 8 * i] : hb + 32 * (4 * m + kg) + 8 * i;
         if constexpr (MX) {
-          const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(a), alo = *reinterpret_cast<const bf16x8*>(a + hlo);
+          const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(a);
+          const bf16x8 alo = *reinterpret_cast<const bf16x8*>(H16_STAGE ? a + (PL > 1 ? 16 * LS : 0) : a + hlo);
 #pragma unroll
           for (int j = 0; j < NW; ++j) {
             const bf16x8 b = fp4x8_bf16(dword_of(cd[j][m], i), e8m0_scale(sc[j][m]));
@@ -834,6 +856,8 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (pr[q] >= 0) ypair[(size_t)pr[q] * H + n0 + 16 * j + r] = acc[j][q];
+    if constexpr (H16_STAGE)
+      if (b0 + 16 < tr.n) __syncthreads();        // hs is rewritten by the next block
   }
 }
 
