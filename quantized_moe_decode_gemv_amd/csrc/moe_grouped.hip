@@ -758,6 +758,87 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
 }
 
 constexpr bool H16_STAGE = true;
+constexpr bool GATEUP_ROW_SPLIT = true;
+
+// MXFP4 gate/up on tiles of more than 16 pairs, rows split over the waves:
+// workgroup = one tile x 64 row pairs, wave w rows f0 + 16w .. + 15 (gate and
+// up) over the whole K = H with its codes held in registers; each 16-pair
+// block of activations is staged in LDS once for the four waves (rows padded
+// by 16 bytes), so a tile's activations are read I/64 times and no partial
+// sums cross waves.
+template <int GK>   // GK = H/128 groups of 128 K
+__global__ __launch_bounds__(BLOCK, 2) void gateup_g16r_kernel(
+    const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles,
+    _Float16* __restrict__ h16, int act, size_t hlo) {
+  constexpr int HK = 128 * GK, LS = HK + 8, CPR = HK / 8;
+  __shared__ __align__(16) uint16_t xs[16][LS];
+  __shared__ int tok_s[16];
+  const int bpt = I / 64;
+  const TileRec tr = tiles[blockIdx.x / bpt];
+  if (tr.n == 0) return;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int f0 = (int)(blockIdx.x % bpt) * 64 + 16 * w;
+  const int r = lane & 15, kg = lane >> 4;
+  const uint8_t* rec = gu + (size_t)tr.e * gu_expert_bytes + (size_t)(f0 + r) * rp_bytes;
+  u32x4 cg[GK], cu[GK];
+  u32 sg[GK], su[GK];
+#pragma unroll
+  for (int m = 0; m < GK; ++m) {
+    const int sbi = 4 * m + kg;
+    cg[m] = *reinterpret_cast<const u32x4*>(rec + 16 * sbi);
+    cu[m] = *reinterpret_cast<const u32x4*>(rec + H / 2 + 16 * sbi);
+    sg[m] = rec[H + sbi];
+    su[m] = rec[H + H / MXK + sbi];
+  }
+  for (int b0 = 0; b0 < tr.n; b0 += 16) {
+    const int nb = min(16, tr.n - b0);
+#pragma unroll
+    for (int m = 0; m < GK; ++m) asm volatile("" : "+v"(cg[m]), "+v"(cu[m]));
+    if (tid < 16) tok_s[tid] = pairs[tr.pos0 + b0 + min(tid, nb - 1)] / k;
+    __syncthreads();
+    {
+      u32x4 st[16 * CPR / BLOCK];
+#pragma unroll
+      for (int q = 0; q < 16 * CPR / BLOCK; ++q) {
+        const int c = tid + BLOCK * q, row = c / CPR, c8 = c % CPR;
+        st[q] = *reinterpret_cast<const u32x4*>(x + (size_t)tok_s[row] * H + 8 * c8);
+      }
+#pragma unroll
+      for (int q = 0; q < 16 * CPR / BLOCK; ++q) {
+        const int c = tid + BLOCK * q, row = c / CPR, c8 = c % CPR;
+        *reinterpret_cast<u32x4*>(&xs[row][8 * c8]) = st[q];
+      }
+    }
+    __syncthreads();
+    f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < GK; ++m) {
+      const float scg = e8m0_scale(sg[m]), scu = e8m0_scale(su[m]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&xs[lane & 15][32 * (4 * m + kg) + 8 * i]);
+        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_bf16(dword_of(cg[m], i), scg), accg, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_bf16(dword_of(cu[m], i), scu), accu, 0, 0, 0);
+      }
+    }
+    // D[tt][rr]: tile row tt = 4 kg + q, row rr = lane % 16
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int tt = 4 * kg + q;
+      if (tt < nb) {
+        const float hv = gate_act(accg[q], accu[q], act);
+        uint16_t* hb = reinterpret_cast<uint16_t*>(h16) + (size_t)(tr.pos0 + b0 + tt) * I + f0 + r;
+        const uint16_t hi = float_to_bf16_rne(hv);
+        hb[0] = hi;
+        hb[hlo] = float_to_bf16_rne(hv - bf16_bits_to_float(hi));
+      }
+    }
+    if (b0 + 16 < tr.n) __syncthreads();          // xs and tok_s are rewritten by the next block
+  }
+}
+
 
 // MXFP4 down on tiles of more than 16 pairs: workgroup = one tile x
 // 4*NW*16 output rows, wave w the NW blocks of 16 rows from
@@ -871,7 +952,11 @@ static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint
                                const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo,
                                bool rows, hipStream_t s) {
   constexpr int NWG = 2;                         // row blocks per wave of the multi-row gate/up
-  if (MULTI || rows)
+  if (FMT == FMT_MXFP4 && MULTI && GATEUP_ROW_SPLIT && d.I % 64 == 0)
+    hipLaunchKernelGGL((gateup_g16r_kernel<4 * G>), dim3(ntiles * (d.I / 64)), dim3(BLOCK), 0, s,
+                       layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
+                       d.act, hlo);
+  else if (MULTI || rows)
     hipLaunchKernelGGL((gateup_g16m_kernel<G, NWG, FMT>), dim3(ntiles * (d.I / (16 * NWG))), dim3(BLOCK), 0, s,
                        layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
                        d.act, hlo);
