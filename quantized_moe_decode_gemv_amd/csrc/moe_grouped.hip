@@ -950,9 +950,9 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
 template <int G, int GD, int FMT, bool MULTI>
 static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
                                const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo,
-                               bool rows, hipStream_t s) {
+                               int rows, hipStream_t s) {
   constexpr int NWG = 2;                         // row blocks per wave of the multi-row gate/up
-  if (FMT == FMT_MXFP4 && MULTI && GATEUP_ROW_SPLIT && d.I % 64 == 0)
+  if (FMT == FMT_MXFP4 && MULTI && rows == 2 && GATEUP_ROW_SPLIT && d.I % 64 == 0)
     hipLaunchKernelGGL((gateup_g16r_kernel<4 * G>), dim3(ntiles * (d.I / 64)), dim3(BLOCK), 0, s,
                        layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
                        d.act, hlo);
@@ -984,7 +984,7 @@ static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint
 template <int G, int GD>
 static hipError_t launch_g16(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
                              const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo, bool multi,
-                             bool rows, hipStream_t s) {
+                             int rows, hipStream_t s) {
   if (d.fmt != FMT_MXFP4)
     return launch_g16_f<G, GD, FMT_Q4K, false>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, rows, s);
   if (multi) return launch_g16_f<G, GD, FMT_MXFP4, true>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, rows, s);
@@ -994,7 +994,7 @@ static hipError_t launch_g16(const Layout& d, const uint8_t* layer, const uint16
 template <int G>
 static hipError_t launch_g16_i(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
                                const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo,
-                               bool multi, bool rows, hipStream_t s) {
+                               bool multi, int rows, hipStream_t s) {
   switch (d.I) {
     case 256: return launch_g16<G, 2>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, rows, s);
     case 512: return launch_g16<G, 4>(d, layer, x, pairs, tiles, ntiles, h16, ypair, hlo, multi, rows, s);
@@ -1062,7 +1062,10 @@ hipError_t launch_g16_ffn(const Layout& d, const uint8_t* layer, const uint16_t*
   // MXFP4: h's bf16 lo plane follows the hi plane (scratch holds 4 bytes per value)
   const size_t hlo = (size_t)T * d.k * d.I;
   const bool multi = g16_mt(d, T) > 16;
-  const bool rows = multi || (long long)T * d.k > 6LL * d.E;
+  // 0: one row block per wave; 1: multi-row kernels; 2: above 6 pairs per
+  // expert, where the MXFP4 gate/up splits rows over the waves (fewer
+  // workgroups per tile: a loss below that, measured at 32-64 tokens here)
+  const int rows = (long long)T * d.k > 6LL * d.E ? 2 : (multi ? 1 : 0);
   hipError_t e;
   switch (d.H) {
     case 512: e = launch_g16_i<1>(d, layer, x, pairs, tr, nt, h16, ypair, hlo, multi, rows, s); break;
