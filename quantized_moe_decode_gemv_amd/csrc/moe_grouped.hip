@@ -75,6 +75,27 @@ __device__ __forceinline__ void unit_of_block(int ntiles, int* tile, int* fb) {
   *fb = u / ntiles;
 }
 
+// Work unit of a multi-row 16-pair-tile workgroup: tiles are dealt to the
+// XCDs round-robin (tile t to XCD t % 8, so empty tiles spread evenly) and
+// the bpt row blocks of one tile follow each other on that XCD, so the
+// tile's activations (or h) are fetched into one L2 and re-read from there.
+// The grid is 8 * bpt * ceil(ntiles / 8); units past the last tile return.
+constexpr bool XCD_TILES = true;
+__device__ __forceinline__ bool tile_unit(int ntiles, int bpt, int* tile, int* rb) {
+  if (!XCD_TILES) {
+    *tile = (int)blockIdx.x / bpt;
+    *rb = (int)blockIdx.x % bpt;
+    return true;
+  }
+  const int su = (int)(blockIdx.x >> 3);
+  *tile = (su / bpt) * 8 + (int)(blockIdx.x & 7);
+  *rb = su % bpt;
+  return *tile < ntiles;
+}
+__host__ __forceinline__ unsigned tile_unit_grid(int ntiles, int bpt) {
+  return XCD_TILES ? 8u * (unsigned)bpt * (unsigned)((ntiles + 7) / 8) : (unsigned)(ntiles * bpt);
+}
+
 // Per-sub-block dequantization constants (a, -b) as fp16 pairs:
 // weight = a*q - b with a = d*sc, b = dmin*m (products exact in fp32, then
 // rounded to fp16). The 6-bit fields sit at bit 6*sb (scales) and 48 + 6*sb
@@ -646,15 +667,17 @@ template <int G, int NW, int FMT>
 __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles,
-    _Float16* __restrict__ h16, int act, size_t hlo) {
+    _Float16* __restrict__ h16, int act, size_t hlo, int ntiles) {
   constexpr bool MX = FMT == FMT_MXFP4;
   constexpr int NH = MX ? G : (G + 1) / 2;     // scale bytes, or super-block headers, per row
   using Hdr = std::conditional_t<MX, u32, u32x4>;
   __shared__ float red[4][2][NW][4][WAVE];
   const int bpt = I / (16 * NW);
-  const TileRec tr = tiles[blockIdx.x / bpt];
+  int ti, rb;
+  if (!tile_unit(ntiles, bpt, &ti, &rb)) return;
+  const TileRec tr = tiles[ti];
   if (tr.n == 0) return;
-  const int f0 = (int)(blockIdx.x % bpt) * 16 * NW;
+  const int f0 = rb * 16 * NW;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int r = lane & 15, kg = lane >> 4;
@@ -770,16 +793,18 @@ template <int GK>   // GK = H/128 groups of 128 K
 __global__ __launch_bounds__(BLOCK, 2) void gateup_g16r_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles,
-    _Float16* __restrict__ h16, int act, size_t hlo) {
+    _Float16* __restrict__ h16, int act, size_t hlo, int ntiles) {
   constexpr int HK = 128 * GK, LS = HK + 8, CPR = HK / 8;
   __shared__ __align__(16) uint16_t xs[16][LS];
   __shared__ int tok_s[16];
   const int bpt = I / 64;
-  const TileRec tr = tiles[blockIdx.x / bpt];
+  int ti, rb;
+  if (!tile_unit(ntiles, bpt, &ti, &rb)) return;
+  const TileRec tr = tiles[ti];
   if (tr.n == 0) return;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
-  const int f0 = (int)(blockIdx.x % bpt) * 64 + 16 * w;
+  const int f0 = rb * 64 + 16 * w;
   const int r = lane & 15, kg = lane >> 4;
   const uint8_t* rec = gu + (size_t)tr.e * gu_expert_bytes + (size_t)(f0 + r) * rp_bytes;
   u32x4 cg[GK], cu[GK];
@@ -849,7 +874,7 @@ template <int GD, int NW, int FMT>
 __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I,
     const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles, const _Float16* __restrict__ h16,
-    float* __restrict__ ypair, size_t hlo) {
+    float* __restrict__ ypair, size_t hlo, int ntiles) {
   constexpr bool MX = FMT == FMT_MXFP4;
   constexpr int NH = MX ? GD : (GD + 1) / 2;
   using Hdr = std::conditional_t<MX, u32, u32x4>;
@@ -858,11 +883,13 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
   constexpr int PL = MX ? 2 : 1, IK = 128 * GD, LS = IK + 8, CPR = IK / 8;
   __shared__ __align__(16) uint16_t hs[H16_STAGE ? PL : 1][H16_STAGE ? 16 : 1][H16_STAGE ? LS : 8];
   const int bpt = H / (64 * NW);
-  const TileRec tr = tiles[blockIdx.x / bpt];
+  int ti, rb;
+  if (!tile_unit(ntiles, bpt, &ti, &rb)) return;
+  const TileRec tr = tiles[ti];
   if (tr.n == 0) return;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
-  const int n0 = (int)(blockIdx.x % bpt) * 64 * NW + 16 * NW * w;
+  const int n0 = rb * 64 * NW + 16 * NW * w;
   const int r = lane & 15, kg = lane >> 4;
   const uint8_t* base = dn + (size_t)tr.e * dn_expert_bytes;
   u32x4 cd[NW][GD];
@@ -953,13 +980,13 @@ static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint
                                int rows, hipStream_t s) {
   constexpr int NWG = 2;                         // row blocks per wave of the multi-row gate/up
   if (FMT == FMT_MXFP4 && MULTI && rows == 2 && GATEUP_ROW_SPLIT && d.I % 64 == 0)
-    hipLaunchKernelGGL((gateup_g16r_kernel<4 * G>), dim3(ntiles * (d.I / 64)), dim3(BLOCK), 0, s,
+    hipLaunchKernelGGL((gateup_g16r_kernel<4 * G>), dim3(tile_unit_grid(ntiles, d.I / 64)), dim3(BLOCK), 0, s,
                        layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
-                       d.act, hlo);
+                       d.act, hlo, ntiles);
   else if (MULTI || rows)
-    hipLaunchKernelGGL((gateup_g16m_kernel<G, NWG, FMT>), dim3(ntiles * (d.I / (16 * NWG))), dim3(BLOCK), 0, s,
-                       layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
-                       d.act, hlo);
+    hipLaunchKernelGGL((gateup_g16m_kernel<G, NWG, FMT>), dim3(tile_unit_grid(ntiles, d.I / (16 * NWG))), dim3(BLOCK),
+                       0, s, layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
+                       d.act, hlo, ntiles);
   else
     hipLaunchKernelGGL((gateup_g16_kernel<G, FMT, MULTI>), dim3(ntiles * (d.I / 16)), dim3(BLOCK), 0, s,
                        layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
@@ -969,9 +996,9 @@ static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint
   constexpr int NW = 4;                          // row blocks per wave of the multi-row down
   if (MULTI || rows) {
     if (d.H % (64 * NW) == 0) {
-      hipLaunchKernelGGL((down_g16m_kernel<GD, NW, FMT>), dim3(ntiles * (d.H / (64 * NW))), dim3(BLOCK), 0, s,
-                         layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, pairs, tiles, h16, ypair,
-                         hlo);
+      hipLaunchKernelGGL((down_g16m_kernel<GD, NW, FMT>), dim3(tile_unit_grid(ntiles, d.H / (64 * NW))), dim3(BLOCK),
+                         0, s, layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, pairs, tiles, h16,
+                         ypair, hlo, ntiles);
       return hipGetLastError();
     }
   }
