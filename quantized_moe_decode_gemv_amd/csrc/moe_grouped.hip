@@ -782,6 +782,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
 
 constexpr bool H16_STAGE = true;
 constexpr bool GATEUP_ROW_SPLIT = true;
+constexpr bool GATEUP_KCHUNK = true;
 
 // MXFP4 gate/up on tiles of more than 16 pairs, rows split over the waves:
 // workgroup = one tile x 64 row pairs, wave w rows f0 + 16w .. + 15 (gate and
@@ -870,6 +871,126 @@ __global__ __launch_bounds__(BLOCK, 2) void gateup_g16r_kernel(
 // n0 = (256*NW/4)*fb + 16*NW*w over the whole K = I; the tile's pairs 16 at a
 // time, each slice of h (hi and lo planes) loaded once and used for all NW
 // row blocks, so h is read H/(64 NW) times per tile instead of H/16.
+// MXFP4 gate/up on tiles of up to 128 pairs, K outermost: workgroup = one
+// tile x 64 row pairs (wave w: rows f0 + 16w .. + 15, gate and up). K runs
+// in chunks of 128: the tile's activations for the chunk are staged in LDS
+// (rows padded by 16 bytes) while the next chunk is loaded into registers,
+// and each wave converts its 32-wide code slices once per chunk and feeds
+// every 16-pair block of the tile from that one conversion, with one
+// accumulator pair per block. The K order of the sums is the same as in the
+// row-split kernel (ascending 32-blocks).
+constexpr int KCH = 128, KCM = KCH / 128;
+template <int NBR, int MT>   // NBR = 16-pair blocks this tile fills (the MFMAs run unconditionally)
+__device__ __forceinline__ void g16k_body(const uint8_t* __restrict__ rec, int H, int I, const uint16_t* __restrict__ x,
+                                          const TileRec& tr, _Float16* __restrict__ h16, int act, size_t hlo,
+                                          int f0, uint16_t (*xs)[KCH + 8], const int* tok_s) {
+  constexpr int CPR = KCH / 8, NST = 16 * NBR * CPR / BLOCK;
+  static_assert(NST * BLOCK == 16 * NBR * CPR || NBR < 2, "staging split");
+  constexpr int NSTX = NST > 0 ? NST : 1;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int r = lane & 15, kg = lane >> 4;
+  // staging unit c = tid + BLOCK q: row c / CPR, 16-byte column c % CPR
+  u32x4 st[NSTX];
+  auto load_x = [&](int c0) {
+#pragma unroll
+    for (int q = 0; q < NSTX; ++q) {
+      const int c = tid + BLOCK * q, row = c / CPR;
+      if (row < 16 * NBR)
+        st[q] = *reinterpret_cast<const u32x4*>(x + (size_t)tok_s[row] * H + c0 + 8 * (c % CPR));
+    }
+  };
+  u32x4 cg[KCM], cu[KCM];
+  u32 sg[KCM], su[KCM];
+  auto load_codes = [&](int c0) {
+#pragma unroll
+    for (int m = 0; m < KCM; ++m) {
+      const int sbi = c0 / MXK + 4 * m + kg;
+      cg[m] = *reinterpret_cast<const u32x4*>(rec + 16 * sbi);
+      cu[m] = *reinterpret_cast<const u32x4*>(rec + H / 2 + 16 * sbi);
+      sg[m] = rec[H + sbi];
+      su[m] = rec[H + H / MXK + sbi];
+    }
+  };
+  f32x4 accg[NBR], accu[NBR];
+#pragma unroll
+  for (int b = 0; b < NBR; ++b) accg[b] = accu[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load_x(0);
+  load_codes(0);
+  for (int c0 = 0; c0 < H; c0 += KCH) {
+    if (c0) __syncthreads();                        // the previous chunk's reads of xs are done
+#pragma unroll
+    for (int q = 0; q < NSTX; ++q) {
+      const int c = tid + BLOCK * q, row = c / CPR;
+      if (row < 16 * NBR) *reinterpret_cast<u32x4*>(&xs[row][8 * (c % CPR)]) = st[q];
+    }
+    __syncthreads();
+    u32x4 ncg[KCM], ncu[KCM];
+    u32 nsg[KCM], nsu[KCM];
+#pragma unroll
+    for (int m = 0; m < KCM; ++m) { ncg[m] = cg[m]; ncu[m] = cu[m]; nsg[m] = sg[m]; nsu[m] = su[m]; }
+    if (c0 + KCH < H) {
+      load_x(c0 + KCH);
+      load_codes(c0 + KCH);
+    }
+#pragma unroll
+    for (int m = 0; m < KCM; ++m) {
+      const float scg = e8m0_scale(nsg[m]), scu = e8m0_scale(nsu[m]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 bg = fp4x8_bf16(dword_of(ncg[m], i), scg);
+        const bf16x8 bu = fp4x8_bf16(dword_of(ncu[m], i), scu);
+#pragma unroll
+        for (int b = 0; b < NBR; ++b) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&xs[16 * b + r][128 * m + 32 * kg + 8 * i]);
+          accg[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bg, accg[b], 0, 0, 0);
+          accu[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bu, accu[b], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // D[tt][rr] of block b: pair 16 b + tt, tt = 4 kg + q; row rr = lane % 16
+#pragma unroll
+  for (int b = 0; b < NBR; ++b) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int p = 16 * b + 4 * kg + q;
+      const float hv = gate_act(accg[b][q], accu[b][q], act);
+      if (p < tr.n) {
+        uint16_t* hb = reinterpret_cast<uint16_t*>(h16) + (size_t)(tr.pos0 + p) * I + f0 + r;
+        const uint16_t hi = float_to_bf16_rne(hv);
+        hb[0] = hi;
+        hb[hlo] = float_to_bf16_rne(hv - bf16_bits_to_float(hi));
+      }
+    }
+  }
+}
+
+template <int NB>   // up to 16 NB pairs per tile
+__global__ __launch_bounds__(BLOCK, 2) void gateup_g16k_kernel(
+    const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles,
+    _Float16* __restrict__ h16, int act, size_t hlo, int ntiles) {
+  constexpr int MT = 16 * NB;
+  __shared__ __align__(16) uint16_t xs[MT][KCH + 8];
+  __shared__ int tok_s[MT];
+  const int bpt = I / 64;
+  int ti, rb;
+  if (!tile_unit(ntiles, bpt, &ti, &rb)) return;
+  const TileRec tr = tiles[ti];
+  if (tr.n == 0) return;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int f0 = rb * 64 + 16 * w;
+  const uint8_t* rec = gu + (size_t)tr.e * gu_expert_bytes + (size_t)(f0 + (tid & 15)) * rp_bytes;
+  if (tid < MT) tok_s[tid] = pairs[tr.pos0 + min(tid, tr.n - 1)] / k;
+  __syncthreads();
+  const int nblk = (tr.n + 15) >> 4;               // uniform over the workgroup
+  if (NB >= 8 && nblk > 4) g16k_body<8, MT>(rec, H, I, x, tr, h16, act, hlo, f0, xs, tok_s);
+  else if (nblk > 2) g16k_body<4, MT>(rec, H, I, x, tr, h16, act, hlo, f0, xs, tok_s);
+  else if (nblk > 1) g16k_body<2, MT>(rec, H, I, x, tr, h16, act, hlo, f0, xs, tok_s);
+  else g16k_body<1, MT>(rec, H, I, x, tr, h16, act, hlo, f0, xs, tok_s);
+}
+
 template <int GD, int NW, int FMT>
 __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I,
@@ -979,7 +1100,11 @@ static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint
                                const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo,
                                int rows, hipStream_t s) {
   constexpr int NWG = 2;                         // row blocks per wave of the multi-row gate/up
-  if (FMT == FMT_MXFP4 && MULTI && rows == 2 && GATEUP_ROW_SPLIT && d.I % 64 == 0)
+  if (FMT == FMT_MXFP4 && MULTI && rows == 3 && GATEUP_KCHUNK && d.I % 64 == 0)
+    hipLaunchKernelGGL((gateup_g16k_kernel<8>), dim3(tile_unit_grid(ntiles, d.I / 64)), dim3(BLOCK), 0, s,
+                       layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
+                       d.act, hlo, ntiles);
+  else if (FMT == FMT_MXFP4 && MULTI && rows >= 2 && GATEUP_ROW_SPLIT && d.I % 64 == 0)
     hipLaunchKernelGGL((gateup_g16r_kernel<4 * G>), dim3(tile_unit_grid(ntiles, d.I / 64)), dim3(BLOCK), 0, s,
                        layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
                        d.act, hlo, ntiles);
@@ -1091,8 +1216,12 @@ hipError_t launch_g16_ffn(const Layout& d, const uint8_t* layer, const uint16_t*
   const bool multi = g16_mt(d, T) > 16;
   // 0: one row block per wave; 1: multi-row kernels; 2: above 6 pairs per
   // expert, where the MXFP4 gate/up splits rows over the waves (fewer
-  // workgroups per tile: a loss below that, measured at 32-64 tokens here)
-  const int rows = (long long)T * d.k > 6LL * d.E ? 2 : (multi ? 1 : 0);
+  // workgroups per tile: a loss below that, measured at 32-64 tokens); 3:
+  // above 12 pairs per expert, where it runs K outermost and reuses each
+  // converted code slice for all of a tile's blocks (tiles of one block,
+  // common below that, gain nothing and pay a barrier pair per 128 K)
+  const long long P = (long long)T * d.k;
+  const int rows = P > 12LL * d.E ? 3 : (P > 6LL * d.E ? 2 : (multi ? 1 : 0));
   hipError_t e;
   switch (d.H) {
     case 512: e = launch_g16_i<1>(d, layer, x, pairs, tr, nt, h16, ypair, hlo, multi, rows, s); break;
