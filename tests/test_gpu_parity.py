@@ -563,6 +563,68 @@ def test_mx_zipf_skewed_4096_tokens(dev):
     assert np.isfinite(y).all()
 
 
+TILE_EDGES = (1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 255, 256, 257)
+
+
+def _logits_with_counts(E, k, T, edges):
+    """fp32 router logits under which expert i (i < len(edges) kept) receives
+    exactly edges[i] of the T*k routed pairs, the last 3 experts none and the
+    rest an even share. Expert slots are laid out as one sequence (each
+    expert's pairs consecutive) and slot j goes to token j % T, so no token
+    gets an expert twice while every count is at most T; the k experts of a
+    token get logits 8 - pos/8 (distinct, exact), all others -4."""
+    P = T * k
+    cnt = [c for c in edges if c <= T]
+    rest = P - sum(cnt)
+    others = E - len(cnt) - 3
+    base, extra = divmod(rest, others)
+    cnt += [base + (1 if i < extra else 0) for i in range(others)] + [0, 0, 0]
+    assert sum(cnt) == P and max(cnt) <= T
+    seq = np.repeat(np.arange(E), cnt)
+    lg = np.full((T, E), -4.0, dtype=np.float32)
+    first, last = {}, {}
+    for j, e in enumerate(seq):
+        t, pos = j % T, j // T
+        lg[t, e] = 8.0 - pos / 8.0
+        first.setdefault(int(e), t)
+        last[int(e)] = t
+    return lg, cnt, first, last
+
+
+@pytest.mark.parametrize("mx,T", [(False, 64), (False, 160), (False, 512), (False, 1280),
+                                  (True, 64), (True, 160), (True, 512), (True, 1280)],
+                         ids=lambda v: str(v))
+def test_tile_boundary_expert_counts(dev, mx, T):
+    """Experts holding exactly 1, 15-17, 31-33, ... 255-257 pairs (full tiles,
+    one pair over, one short, for every tile size the automatic path uses at
+    4, 10, 32 and 80 pairs per expert), three empty experts: routing exact
+    and, for the first and last token of each such expert (its first and its
+    ragged last tile), the output within the tolerance."""
+    S = synth.QWEN3_30B_A3B_MXFP4 if mx else synth.QWEN3_30B_A3B
+    st = Setup(S, dev, n_layers=1, max_tokens=T, flags=MX if mx else 0)
+    lg, cnt, first, last = _logits_with_counts(S.n_experts, S.top_k, T, TILE_EDGES)
+    xb = synth.x_bf16(S, 51, T, T=T)
+    k = S.top_k
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    counts = torch.empty(S.n_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(S.n_experts + 1, dtype=torch.int32, device=dev)
+    pairs = torch.empty(T * k, dtype=torch.int32, device=dev)
+    out = torch.empty(T, S.hidden, dtype=torch.float32, device=dev)
+    st.plan.route(st.blob, 0, None, torch.from_numpy(lg).to(dev), T, ids, w, counts, offsets, pairs,
+                  scratch=st.scratch)
+    st.plan.expert_ffn(st.blob, 0, st.xdev(xb), T, ids, w, out, counts, offsets, pairs, scratch=st.scratch)
+    torch.cuda.synchronize()
+    assert counts.cpu().numpy().tolist() == cnt
+    got_ids, y = ids.cpu().numpy(), out.cpu().numpy()
+    edge_experts = [e for e, c in enumerate(cnt[:len(TILE_EDGES)]) if c in TILE_EDGES]
+    sample = sorted({first[e] for e in edge_experts} | {last[e] for e in edge_experts} | {0, T - 1})
+    ref = oracle.moe_layer(st.src, 0, xb[sample], logits=lg[sample])
+    assert np.array_equal(np.sort(got_ids[sample], 1), np.sort(ref["ids"], 1))
+    assert rel_err(y[sample], ref["y"]) <= REL_TOL
+    assert np.isfinite(y).all()
+
+
 @pytest.mark.parametrize("shape", MX_EDGE, ids=[s.name for s in MX_EDGE])
 def test_mx_edge_shapes_expert_gemv(dev, shape):
     """The expert-major GEMV forced with MXFP4 weights on every edge shape;
