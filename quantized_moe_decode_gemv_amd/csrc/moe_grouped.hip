@@ -656,7 +656,9 @@ __global__ __launch_bounds__(BLOCK) void down_g16_kernel(
   }
 }
 
-// MXFP4 gate/up on tiles of more than 16 pairs: workgroup = one tile x
+// Multi-row gate/up (both encodings: super-block 16-pair tiles above 6
+// pairs per expert, MXFP4 tiles of more than 16 pairs up to 6 pairs per
+// expert, and wherever I is not a multiple of 64): workgroup = one tile x
 // 16*NW row pairs (f0 .. f0 + 16 NW), wave w the K range [w H/4, (w+1) H/4)
 // for all NW row blocks; the tile's pairs 16 at a time, each activation slice
 // loaded once and used for the NW blocks' gate and up MFMAs, so the
@@ -784,8 +786,8 @@ constexpr bool H16_STAGE = true;
 constexpr bool GATEUP_ROW_SPLIT = true;
 constexpr bool GATEUP_KCHUNK = true;
 
-// MXFP4 gate/up on tiles of more than 16 pairs, rows split over the waves:
-// workgroup = one tile x 64 row pairs, wave w rows f0 + 16w .. + 15 (gate and
+// MXFP4 gate/up on tiles of more than 16 pairs between 6 and 12 pairs per
+// expert, rows split over the waves: workgroup = one tile x 64 row pairs, wave w rows f0 + 16w .. + 15 (gate and
 // up) over the whole K = H with its codes held in registers; each 16-pair
 // block of activations is staged in LDS once for the four waves (rows padded
 // by 16 bytes), so a tile's activations are read I/64 times and no partial
@@ -871,7 +873,8 @@ __global__ __launch_bounds__(BLOCK, 2) void gateup_g16r_kernel(
 // n0 = (256*NW/4)*fb + 16*NW*w over the whole K = I; the tile's pairs 16 at a
 // time, each slice of h (hi and lo planes) loaded once and used for all NW
 // row blocks, so h is read H/(64 NW) times per tile instead of H/16.
-// MXFP4 gate/up on tiles of up to 128 pairs, K outermost: workgroup = one
+// MXFP4 gate/up above 12 pairs per expert (tiles of up to 128 pairs), K
+// outermost: workgroup = one
 // tile x 64 row pairs (wave w: rows f0 + 16w .. + 15, gate and up). K runs
 // in chunks of 128: the tile's activations for the chunk are staged in LDS
 // (rows padded by 16 bytes) while the next chunk is loaded into registers,
