@@ -1038,18 +1038,18 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
       for (int m = 0; m < GD; ++m) asm volatile("" : "+v"(cd[j][m]));
     const uint16_t* hb = reinterpret_cast<const uint16_t*>(h16) + (size_t)(tr.pos0 + b0 + min(lane & 15, nb - 1)) * I;
     if constexpr (H16_STAGE) {
-      u32x4 st[PL * 16 * CPR / BLOCK];
+      // thread -> one (plane, row) and every TPR-th 16-byte column of it:
+      // one address per thread, the rest immediate offsets
+      constexpr int TPR = BLOCK / (PL * 16), NQ = CPR / TPR;
+      static_assert(CPR % TPR == 0, "h staging split");
+      const int prw = tid / TPR, pl = prw / 16, row = prw % 16, col0 = tid % TPR;
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(h16) + (pl ? hlo : 0) +
+                            (size_t)(tr.pos0 + b0 + min(row, nb - 1)) * I + 8 * col0;
+      u32x4 st[NQ];
 #pragma unroll
-      for (int q = 0; q < PL * 16 * CPR / BLOCK; ++q) {
-        const int c = tid + BLOCK * q, pl = c / (16 * CPR), rem = c % (16 * CPR), row = rem / CPR, c8 = rem % CPR;
-        st[q] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(h16) + (pl ? hlo : 0) +
-                                                (size_t)(tr.pos0 + b0 + min(row, nb - 1)) * I + 8 * c8);
-      }
+      for (int q = 0; q < NQ; ++q) st[q] = *reinterpret_cast<const u32x4*>(src + 8 * TPR * q);
 #pragma unroll
-      for (int q = 0; q < PL * 16 * CPR / BLOCK; ++q) {
-        const int c = tid + BLOCK * q, pl = c / (16 * CPR), rem = c % (16 * CPR), row = rem / CPR, c8 = rem % CPR;
-        *reinterpret_cast<u32x4*>(&hs[pl][row][8 * c8]) = st[q];
-      }
+      for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4*>(&hs[pl][row][8 * col0 + 8 * TPR * q]) = st[q];
       __syncthreads();
     }
     int pr[4];
