@@ -80,20 +80,14 @@ __device__ __forceinline__ void unit_of_block(int ntiles, int* tile, int* fb) {
 // the bpt row blocks of one tile follow each other on that XCD, so the
 // tile's activations (or h) are fetched into one L2 and re-read from there.
 // The grid is 8 * bpt * ceil(ntiles / 8); units past the last tile return.
-constexpr bool XCD_TILES = true;
 __device__ __forceinline__ bool tile_unit(int ntiles, int bpt, int* tile, int* rb) {
-  if (!XCD_TILES) {
-    *tile = (int)blockIdx.x / bpt;
-    *rb = (int)blockIdx.x % bpt;
-    return true;
-  }
   const int su = (int)(blockIdx.x >> 3);
   *tile = (su / bpt) * 8 + (int)(blockIdx.x & 7);
   *rb = su % bpt;
   return *tile < ntiles;
 }
 __host__ __forceinline__ unsigned tile_unit_grid(int ntiles, int bpt) {
-  return XCD_TILES ? 8u * (unsigned)bpt * (unsigned)((ntiles + 7) / 8) : (unsigned)(ntiles * bpt);
+  return 8u * (unsigned)bpt * (unsigned)((ntiles + 7) / 8);
 }
 
 // Per-sub-block dequantization constants (a, -b) as fp16 pairs:
@@ -782,9 +776,6 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
   }
 }
 
-constexpr bool H16_STAGE = true;
-constexpr bool GATEUP_ROW_SPLIT = true;
-constexpr bool GATEUP_KCHUNK = true;
 
 // MXFP4 gate/up on tiles of more than 16 pairs between 6 and 12 pairs per
 // expert, rows split over the waves: workgroup = one tile x 64 row pairs, wave w rows f0 + 16w .. + 15 (gate and
@@ -1005,7 +996,7 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
   // a block's 16 rows of h (MXFP4: hi and lo planes) staged in LDS once for
   // the four waves; rows padded by 16 bytes against bank conflicts
   constexpr int PL = MX ? 2 : 1, IK = 128 * GD, LS = IK + 8, CPR = IK / 8;
-  __shared__ __align__(16) uint16_t hs[H16_STAGE ? PL : 1][H16_STAGE ? 16 : 1][H16_STAGE ? LS : 8];
+  __shared__ __align__(16) uint16_t hs[PL][16][LS];
   const int bpt = H / (64 * NW);
   int ti, rb;
   if (!tile_unit(ntiles, bpt, &ti, &rb)) return;
@@ -1036,8 +1027,7 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
     for (int j = 0; j < NW; ++j)
 #pragma unroll
       for (int m = 0; m < GD; ++m) asm volatile("" : "+v"(cd[j][m]));
-    const uint16_t* hb = reinterpret_cast<const uint16_t*>(h16) + (size_t)(tr.pos0 + b0 + min(lane & 15, nb - 1)) * I;
-    if constexpr (H16_STAGE) {
+    {
       // thread -> one (plane, row) and every TPR-th 16-byte column of it:
       // one address per thread, the rest immediate offsets
       constexpr int TPR = BLOCK / (PL * 16), NQ = CPR / TPR;
@@ -1062,10 +1052,10 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
     for (int m = 0; m < GD; ++m) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint16_t* a = H16_STAGE ? &hs[0][lane & 15][32 * (4 * m + kg) + 8 * i] : hb + 32 * (4 * m + kg) + 8 * i;
+        const uint16_t* a = &hs[0][lane & 15][32 * (4 * m + kg) + 8 * i];
         if constexpr (MX) {
           const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(a);
-          const bf16x8 alo = *reinterpret_cast<const bf16x8*>(H16_STAGE ? a + (PL > 1 ? 16 * LS : 0) : a + hlo);
+          const bf16x8 alo = *reinterpret_cast<const bf16x8*>(a + 16 * LS);   // the lo plane
 #pragma unroll
           for (int j = 0; j < NW; ++j) {
             const bf16x8 b = fp4x8_bf16(dword_of(cd[j][m], i), e8m0_scale(sc[j][m]));
@@ -1088,8 +1078,7 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (pr[q] >= 0) ypair[(size_t)pr[q] * H + n0 + 16 * j + r] = acc[j][q];
-    if constexpr (H16_STAGE)
-      if (b0 + 16 < tr.n) __syncthreads();        // hs is rewritten by the next block
+    if (b0 + 16 < tr.n) __syncthreads();          // hs is rewritten by the next block
   }
 }
 
@@ -1103,11 +1092,11 @@ static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint
                                const TileRec* tiles, int ntiles, _Float16* h16, float* ypair, size_t hlo,
                                int rows, hipStream_t s) {
   constexpr int NWG = 2;                         // row blocks per wave of the multi-row gate/up
-  if (FMT == FMT_MXFP4 && MULTI && rows == 3 && GATEUP_KCHUNK && d.I % 64 == 0)
+  if (FMT == FMT_MXFP4 && MULTI && rows == 3 && d.I % 64 == 0)
     hipLaunchKernelGGL((gateup_g16k_kernel<8>), dim3(tile_unit_grid(ntiles, d.I / 64)), dim3(BLOCK), 0, s,
                        layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
                        d.act, hlo, ntiles);
-  else if (FMT == FMT_MXFP4 && MULTI && rows >= 2 && GATEUP_ROW_SPLIT && d.I % 64 == 0)
+  else if (FMT == FMT_MXFP4 && MULTI && rows >= 2 && d.I % 64 == 0)
     hipLaunchKernelGGL((gateup_g16r_kernel<4 * G>), dim3(tile_unit_grid(ntiles, d.I / 64)), dim3(BLOCK), 0, s,
                        layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, h16,
                        d.act, hlo, ntiles);
