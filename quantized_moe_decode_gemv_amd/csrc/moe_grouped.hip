@@ -883,7 +883,11 @@ __device__ __forceinline__ void g16k_body(const uint8_t* __restrict__ rec, int H
   constexpr int NSTX = NST > 0 ? NST : 1;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int r = lane & 15, kg = lane >> 4;
-  // staging unit c = tid + BLOCK q: row c / CPR, 16-byte column c % CPR
+  // staging unit c = tid + BLOCK q: row c / CPR, 16-byte column c % CPR.
+  // The row guards below always hold (the units cover exactly 16 NBR rows);
+  // they stay because without them the compiler schedules the staging so
+  // that the kernel needs 174 registers instead of 163, two waves per SIMD
+  // instead of three.
   u32x4 st[NSTX];
   auto load_x = [&](int c0) {
 #pragma unroll
