@@ -76,7 +76,8 @@ enum moe_status {
  * codes, element 2i in the low nibble of byte 1+i. The packer accepts scale
  * codes 2..252 (2^-125 .. 2^125). Paths: per-token GEMV while T*k < E/2,
  * expert-major GEMV up to T*k = 1.75 E, then MFMA tiles (hidden 512,
- * 1024 or 2048 and inter <= 1024; otherwise the expert-major GEMV). The
+ * 1024 or 2048 and inter <= 1024; otherwise the expert-major GEMV) of 16
+ * pairs up to P/E = 1, 64 pairs up to 16 and 128 pairs beyond. The
  * force flags apply, MOE_FLAG_FORCE_GROUPED only where the 16-pair tiles do. */
 #define MOE_FLAG_WEIGHTS_MXFP4 0x20u
 
