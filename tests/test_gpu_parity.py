@@ -511,11 +511,14 @@ MX_G16 = [s for s in MX_EDGE if s.hidden in (512, 1024, 2048) and s.inter <= 102
 def test_mx_edge_shapes_mfma_tiles(dev, shape):
     """The 16-pair MFMA tiles forced with MXFP4 weights on every edge shape
     that has them (bf16 MFMA on exactly converted weights, h as bf16 hi + lo);
-    2, 5 and 70 tokens give single, partial and multi-tile experts."""
-    st = Setup(shape, dev, n_layers=1, max_tokens=70, flags=MX | q.FLAG_FORCE_GROUPED)
-    for T in (2, 5, 70):
+    2, 5 and 70 tokens give single, partial and multi-tile experts, and 140
+    tokens (every 7th token and the last checked) puts the 512-wide shape
+    above 12 pairs per expert, on the K-outermost gate/up."""
+    st = Setup(shape, dev, n_layers=1, max_tokens=140, flags=MX | q.FLAG_FORCE_GROUPED)
+    for T in (2, 5, 70, 140):
         xb = synth.x_bf16(shape, 12, T, T=T)
-        _check_layer(st, xb, st.forward(xb))
+        sample = sorted(set(range(0, T, 7)) | {T - 1}) if T > 70 else None
+        _check_layer(st, xb, st.forward(xb), sample=sample)
 
 
 @pytest.mark.parametrize("T", [256, 1024])
