@@ -462,11 +462,14 @@ def test_edge_shapes(dev, shape):
 def test_edge_shapes_batched_paths(dev, shape, path):
     """Each forced path on every edge shape (lane mappings of every hidden and
     intermediate size, k = 1, k = E, many experts); 70 tokens give ragged
-    tiles and multi-chunk experts."""
-    st = Setup(shape, dev, n_layers=1, max_tokens=70, flags=dict(PATH_FLAGS)[path])
-    for T in (2, 5, 70):
+    tiles and multi-chunk experts; on the grouped path 140 more tokens (every
+    7th and the last checked) put most shapes on the 32- or 96-pair tiles."""
+    Ts = (2, 5, 70, 140) if path == "grouped" else (2, 5, 70)
+    st = Setup(shape, dev, n_layers=1, max_tokens=max(Ts), flags=dict(PATH_FLAGS)[path])
+    for T in Ts:
         xb = synth.x_bf16(shape, 12, T, T=T)
-        _check_layer(st, xb, st.forward(xb))
+        sample = sorted(set(range(0, T, 7)) | {T - 1}) if T > 70 else None
+        _check_layer(st, xb, st.forward(xb), sample=sample)
 
 
 # ------------------------------------------------------------------ MXFP4 expert weights
