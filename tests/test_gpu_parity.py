@@ -384,11 +384,14 @@ def test_graph_replay_matches_eager_bitwise(qwen):
         assert torch.equal(xn, eager_xn), rep
 
 
-@pytest.mark.parametrize("T,mx", [(12, False), (64, False), (1024, False), (64, True), (1024, True)])
+@pytest.mark.parametrize("T,mx", [(12, False), (64, False), (128, False), (256, False), (1024, False),
+                                  (64, True), (128, True), (1024, True)])
 def test_batched_graph_replay_matches_eager_bitwise(qwen, mx_qwen, T, mx):
     """Batched forward captured in a graph: per-token GEMV path (12 tokens),
-    16-pair tiles (64) and 96-pair tiles (1024), and with MXFP4 weights the
-    64- and 128-pair tiles walked 16 pairs at a time; each including the
+    16-pair tiles (64; 128 on the multi-row kernels), 32-pair (256) and
+    96-pair tiles (1024), and with MXFP4 weights the 64-pair tiles (64: two
+    row blocks per wave; 128: rows split over the waves) and the 128-pair
+    tiles with the K-outermost gate/up (1024); each including the
     on-device top-k and dispatch. Every replay (with unrelated eager work in
     between) must reproduce the eager result bit for bit, and two eager runs
     must agree."""
