@@ -106,6 +106,11 @@ def lib():
         L.oracle_moe_token_act.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, ctypes.c_int32]
         L.oracle_resid_rmsnorm.restype = None
         L.oracle_resid_rmsnorm.argtypes = [vp, vp, i64, f64, vp, vp]
+        for fn in (L.oracle_emul_bf16, L.oracle_emul_fp16, L.oracle_emul_fp16_rtz):
+            fn.restype = f64
+            fn.argtypes = [f64]
+        L.oracle_emul_moe_token.restype = None
+        L.oracle_emul_moe_token.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp] + [ctypes.c_int32] * 5
         _lib = L
     return _lib
 
@@ -220,14 +225,21 @@ def route_weights(logits, ids):
     return w
 
 
+def selection_margin(logits, k):
+    """Margin of the top-k selection: the k-th largest logit minus the
+    (k+1)-th largest (0 when they are equal, so that the selection depends on
+    the tie rule; inf when k equals the number of experts, where every
+    selection is the same set)."""
+    srt = np.sort(np.asarray(logits, dtype=np.float64))[::-1]
+    return srt[k - 1] - srt[k] if k < srt.size else np.inf
+
+
 def route(logits, k):
     """(ids, weights, gap) for one token. ``gap`` = l_(k) - l_(k+1), the
     margin of the selection (inf when k == E)."""
     ids = topk(logits, k)
     w = route_weights(logits, ids)
-    srt = np.sort(np.asarray(logits, dtype=np.float64))[::-1]
-    gap = srt[k - 1] - srt[k] if k < srt.size else np.inf
-    return ids, w, gap
+    return ids, w, selection_margin(logits, k)
 
 
 def silu(z):
@@ -337,3 +349,57 @@ def moe_layer(src, layer, x_bf16, logits=None, wr=None, act=ACT_SILU):
         bl = [src.blocks(layer, e) for e in ids[t]]
         y[t] = moe_token([b[0] for b in bl], [b[1] for b in bl], [b[2] for b in bl], w[t], x_bf16[t], act=act)
     return dict(ids=ids, w=w, gap=gap, logits=lg, y=y)
+
+
+# ---------------------------------------------------------------- recipe emulation
+# Weight, h and activation modes of the recipe emulation (see oracle.c): it
+# predicts a GPU arithmetic recipe's error; parity checks never use it.
+W_EXACT_CODES, W_BF16, W_FP16, W_BF16_HILO = 0, 1, 2, 3
+H_FP32, H_BF16, H_FP16, H_BF16_HILO = 0, 1, 2, 3
+X_BF16, X_FP16_RTZ = 0, 1
+
+
+def emul_bf16(v):
+    return lib().oracle_emul_bf16(float(v))
+
+
+def emul_fp16(v):
+    return lib().oracle_emul_fp16(float(v))
+
+
+def emul_fp16_rtz(v):
+    return lib().oracle_emul_fp16_rtz(float(v))
+
+
+def emulate_moe_token(gates, ups, downs, w, x_bf16, wmode, hmode, xmode=X_BF16, act=ACT_SILU):
+    """One token through its selected experts with a recipe's roundings (fp32
+    result as fp64)."""
+    k = len(gates)
+    gates = [_c(g, np.uint8) for g in gates]
+    ups = [_c(u, np.uint8) for u in ups]
+    downs = [_c(d, np.uint8) for d in downs]
+    fmt, K = block_format(gates[0])
+    I, H = gates[0].shape[0], gates[0].shape[1] * K
+    PA = ctypes.c_void_p * k
+    ga = PA(*[g.ctypes.data for g in gates])
+    ua = PA(*[u.ctypes.data for u in ups])
+    da = PA(*[d.ctypes.data for d in downs])
+    w = _c(w, np.float64)
+    x_bf16 = _c(x_bf16, np.uint16)
+    y = np.empty(H, dtype=np.float64)
+    lib().oracle_emul_moe_token(ga, ua, da, _p(w), k, H, I, _p(x_bf16), _p(y), int(act), fmt, int(wmode), int(hmode),
+                                int(xmode))
+    return y
+
+
+def emulate_moe_layer(src, layer, x_bf16, wmode, hmode, xmode=X_BF16, logits=None, act=ACT_SILU):
+    """moe_layer with the expert FFNs under a recipe; routing is the exact
+    oracle's. Returns (emulated y [T, H], exact oracle result dict)."""
+    ref = moe_layer(src, layer, x_bf16, logits=logits, act=act)
+    x_bf16 = np.atleast_2d(np.asarray(x_bf16, dtype=np.uint16))
+    y = np.zeros_like(ref["y"])
+    for t in range(x_bf16.shape[0]):
+        bl = [src.blocks(layer, e) for e in ref["ids"][t]]
+        y[t] = emulate_moe_token([b[0] for b in bl], [b[1] for b in bl], [b[2] for b in bl], ref["w"][t],
+                                 x_bf16[t], wmode, hmode, xmode, act)
+    return y, ref

@@ -40,7 +40,14 @@
  *    name: g' = min(g, 7), u' = min(max(u, -7), 7),
  *    act = g' / (1 + exp(-1.702 g')) * (u' + 1);
  *  - the residual add and RMSNorm between stacked layers (weight 1, eps given
- *    by the caller), rounded to bf16.
+ *    by the caller), rounded to bf16;
+ *  - a recipe emulation of the expert FFN: the same FFN with the roundings of
+ *    a GPU arithmetic recipe (fp32 accumulation; weights as exact codes with
+ *    an fp32 sub-block affine, or rounded to bf16 / fp16 / bf16 hi + lo; the
+ *    intermediate h stored as fp32 / bf16 / fp16 / bf16 hi + lo; activations
+ *    as given or converted to fp16 toward zero), which predicts a recipe's
+ *    error before its kernel exists. It is not the reference: every parity
+ *    check compares against the fp64 functions above.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -100,18 +107,26 @@ static int field6(const uint8_t* blk, int f) {
   return v;
 }
 
-/* one super-block -> 256 weights */
-void oracle_dequant_block(const uint8_t* blk, double* w) {
-  double d = oracle_f16((uint16_t)(blk[0] | (blk[1] << 8)));
-  double dmin = oracle_f16((uint16_t)(blk[2] | (blk[3] << 8)));
+/* the fields of one super-block: d, dmin, sub-block scales and mins, codes */
+static void q4k_fields(const uint8_t* blk, double* d, double* dmin, int* sc, int* m, int* q) {
+  *d = oracle_f16((uint16_t)(blk[0] | (blk[1] << 8)));
+  *dmin = oracle_f16((uint16_t)(blk[2] | (blk[3] << 8)));
   for (int j = 0; j < 8; ++j) {
-    int sc = field6(blk, j), m = field6(blk, 8 + j);
+    sc[j] = field6(blk, j);
+    m[j] = field6(blk, 8 + j);
     for (int i = 0; i < 32; ++i) {
       uint8_t byte = blk[16 + 16 * j + i / 2];
-      int q = (i & 1) ? (byte >> 4) : (byte & 15);
-      w[32 * j + i] = d * sc * q - dmin * m;
+      q[32 * j + i] = (i & 1) ? (byte >> 4) : (byte & 15);
     }
   }
+}
+
+/* one super-block -> 256 weights */
+void oracle_dequant_block(const uint8_t* blk, double* w) {
+  double d, dmin;
+  int sc[8], m[8], q[QK];
+  q4k_fields(blk, &d, &dmin, sc, m, q);
+  for (int i = 0; i < QK; ++i) w[i] = d * sc[i / 32] * q[i] - dmin * m[i / 32];
 }
 
 /* FP4 E2M1 code (low 4 bits) -> value */
@@ -292,4 +307,145 @@ void oracle_resid_rmsnorm(const uint16_t* x_bf16, const double* y, int64_t n, do
     if (r_bf16) r_bf16[i] = oracle_round_bf16(ri);
   }
   free(v);
+}
+
+/* ---------------------------------------------------------------- recipe emulation
+ * The expert FFN and the routing-weighted sum again, with the roundings of a
+ * GPU arithmetic recipe, so that a recipe's error can be predicted before its
+ * kernel is written. Every sum is an fp32 sum in the order of the formula
+ * (the GPU's order differs; the size of the error is what is predicted), and
+ * every product-add is one fused fp32 operation, as on the GPU.
+ *   wmode  0: exact codes with an fp32 sub-block affine: for 4-bit
+ *             super-blocks, per 32-weight sub-block P = sum q*x and
+ *             S = sum x, then acc += a*P - b*S (a = d*sc, b = dmin*m, both
+ *             exact in fp32); MXFP4 weights are exact in fp32 and enter as
+ *             they are;
+ *          1: each weight rounded to bf16 (nearest even);
+ *          2: each weight rounded to fp16 (nearest even);
+ *          3: each weight as bf16 hi + lo (hi = bf16(w), lo = bf16(w - hi)).
+ *   hmode  0: h stored in fp32; 1: bf16; 2: fp16 (nearest even, overflow to
+ *          infinity); 3: bf16 hi + lo.
+ *   xmode  0: the bf16 activations as they are; 1: converted to fp16 toward
+ *          zero (saturating at 65504), as a round-toward-zero conversion does.
+ */
+/* nearest value (ties to even), or toward zero, with p significant bits and
+ * smallest normal exponent emin (below it the spacing stays 2^(emin-p+1)) */
+static double round_sig(double v, int p, int emin, int toward_zero) {
+  if (v == 0.0 || !isfinite(v)) return v;
+  double a = fabs(v);
+  int e;
+  frexp(a, &e);
+  int E = e - 1;                                  /* a in [2^E, 2^(E+1)) */
+  if (E < emin) E = emin;
+  double unit = ldexp(1.0, E - (p - 1));
+  double qv = a / unit;
+  double r = floor(qv);
+  if (!toward_zero) {
+    double frac = qv - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  }
+  double out = r * unit;
+  return v < 0 ? -out : out;
+}
+
+double oracle_emul_bf16(double v) { return round_sig(v, 8, -126, 0); }
+
+double oracle_emul_fp16(double v) {
+  double r = round_sig(v, 11, -14, 0);
+  return fabs(r) > 65504.0 ? copysign(INFINITY, v) : r;
+}
+
+double oracle_emul_fp16_rtz(double v) {
+  double r = round_sig(v, 11, -14, 1);
+  return fabs(r) > 65504.0 ? copysign(65504.0, v) : r;
+}
+
+/* y = Deq(W) x under weight mode wmode, fp32 accumulation; x already in the
+ * form the recipe feeds (fp32 values) */
+static void emul_qgemv(const uint8_t* blocks, int64_t rows, int64_t cols, const float* x, float* y, int32_t fmt,
+                       int32_t wmode) {
+  const int K = fmt == 1 ? MXK : QK;
+  const int bytes = fmt == 1 ? MXBLOCK_BYTES : QBLOCK_BYTES;
+  const int64_t nb = cols / K;
+  double w[QK], d, dmin;
+  int sc[8], m[8], q[QK];
+  for (int64_t r = 0; r < rows; ++r) {
+    float acc = 0.0f;
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t* blk = blocks + (r * nb + b) * bytes;
+      const float* xb = x + b * K;
+      if (wmode == 0 && fmt == 0) {
+        q4k_fields(blk, &d, &dmin, sc, m, q);
+        for (int j = 0; j < 8; ++j) {
+          float P = 0.0f, S = 0.0f;
+          for (int i = 0; i < 32; ++i) {
+            P = fmaf((float)q[32 * j + i], xb[32 * j + i], P);
+            S += xb[32 * j + i];
+          }
+          const float a = (float)(d * sc[j]), bb = (float)(dmin * m[j]);
+          acc = fmaf(a, P, acc);
+          acc = fmaf(-bb, S, acc);
+        }
+        continue;
+      }
+      if (fmt == 1) oracle_dequant_mx_block(blk, w);
+      else oracle_dequant_block(blk, w);
+      for (int i = 0; i < K; ++i) {
+        if (wmode == 0) {
+          acc = fmaf((float)w[i], xb[i], acc);                  /* MXFP4: exact in fp32 */
+        } else if (wmode == 1) {
+          acc = fmaf((float)oracle_emul_bf16(w[i]), xb[i], acc);
+        } else if (wmode == 2) {
+          acc = fmaf((float)oracle_emul_fp16(w[i]), xb[i], acc);
+        } else {
+          const double hi = oracle_emul_bf16(w[i]);
+          const double lo = oracle_emul_bf16(w[i] - hi);
+          acc = fmaf((float)hi, xb[i], acc);
+          acc = fmaf((float)lo, xb[i], acc);
+        }
+      }
+    }
+    y[r] = acc;
+  }
+}
+
+/* stored form of one h value under hmode (hi + lo is exact in fp32) */
+static float emul_store_h(float h, int32_t hmode) {
+  if (hmode == 1) return (float)oracle_emul_bf16(h);
+  if (hmode == 2) return (float)oracle_emul_fp16(h);
+  if (hmode == 3) {
+    const double hi = oracle_emul_bf16(h);
+    return (float)(hi + oracle_emul_bf16((double)h - hi));
+  }
+  return h;
+}
+
+/* One token through its k selected experts under the recipe; y (fp64 out)
+ * holds the fp32 result. w: the k routing weights (used as fp32). */
+void oracle_emul_moe_token(const uint8_t* const* gate, const uint8_t* const* up, const uint8_t* const* down,
+                           const double* w, int64_t k, int64_t H, int64_t I, const uint16_t* x_bf16, double* y,
+                           int32_t act, int32_t fmt, int32_t wmode, int32_t hmode, int32_t xmode) {
+  float* x = (float*)malloc(sizeof(float) * (size_t)H);
+  float* g = (float*)malloc(sizeof(float) * (size_t)I);
+  float* u = (float*)malloc(sizeof(float) * (size_t)I);
+  float* ye = (float*)malloc(sizeof(float) * (size_t)H);
+  float* acc = (float*)malloc(sizeof(float) * (size_t)H);
+  for (int64_t i = 0; i < H; ++i) {
+    const double xv = oracle_bf16(x_bf16[i]);
+    x[i] = (float)(xmode == 1 ? oracle_emul_fp16_rtz(xv) : xv);
+    acc[i] = 0.0f;
+  }
+  for (int64_t s = 0; s < k; ++s) {
+    emul_qgemv(gate[s], I, H, x, g, fmt, wmode);
+    emul_qgemv(up[s], I, H, x, u, fmt, wmode);
+    for (int64_t i = 0; i < I; ++i) g[i] = emul_store_h((float)oracle_act(g[i], u[i], act), hmode);
+    emul_qgemv(down[s], H, I, g, ye, fmt, wmode);
+    for (int64_t i = 0; i < H; ++i) acc[i] = fmaf((float)w[s], ye[i], acc[i]);
+  }
+  for (int64_t i = 0; i < H; ++i) y[i] = acc[i];
+  free(x);
+  free(g);
+  free(u);
+  free(ye);
+  free(acc);
 }

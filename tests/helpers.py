@@ -2,6 +2,7 @@
 device upload through the C ABI's packer, and the comparison rules."""
 import numpy as np
 
+import oracle
 import synth
 
 # Tolerance stated for the method's outputs: max|y - ref| <= 2e-3 * max|ref|.
@@ -31,28 +32,78 @@ def rel_err(y, ref):
     return np.abs(y - ref).max() / (m if m > 0 else 1.0)
 
 
-def check_routing(ids_gpu, w_gpu, ref, exact=False, tau=TAU):
+def check_routing(ids_gpu, w_gpu, ref, exact=False, tau=TAU, max_exempt=None, label=""):
     """Compare GPU routing with the oracle's per token: the selected set must
     match (graded as a set; weights matched per id) unless the oracle's
-    selection margin is below tau (then any valid selection passes). With
-    exact=True (shared fp32 logits) every token must match. Returns the list
-    of tokens exempted as near-ties."""
+    selection margin is at most tau. A token is exempted only when the two
+    selections differ solely by experts whose oracle logits lie within tau of
+    the oracle's k-th largest logit (either selection is then correct); its
+    GPU weights must still be the oracle's softmax over the GPU's selection.
+    With exact=True (shared fp32 logits) every token must match. The number
+    of exempted tokens is printed and bounded by max_exempt (default
+    1 + T // 64). Returns the list of exempted tokens."""
     ids_gpu = np.asarray(ids_gpu)
     w_gpu = np.asarray(w_gpu, dtype=np.float64)
+    T = ids_gpu.shape[0]
     exempt = []
-    for t in range(ids_gpu.shape[0]):
+    near = 0
+    for t in range(T):
         gs, rs = ids_gpu[t].tolist(), ref["ids"][t].tolist()
         assert len(set(gs)) == len(gs), f"token {t}: duplicate ids {gs}"
         assert abs(w_gpu[t].sum() - 1.0) <= 1e-5 * len(gs), f"token {t}: weights sum {w_gpu[t].sum()}"
+        near += int(ref["gap"][t] <= tau)
         if set(gs) != set(rs):
-            if not exact and ref["gap"][t] <= tau:
-                exempt.append(t)
-                continue
-            raise AssertionError(f"token {t}: ids {gs} vs oracle {rs} (gap {ref['gap'][t]:.3e})")
+            if exact or ref["gap"][t] > tau:
+                raise AssertionError(f"token {t}: ids {gs} vs oracle {rs} (gap {ref['gap'][t]:.3e})")
+            lg = np.asarray(ref["logits"][t], dtype=np.float64)
+            kth = np.sort(lg)[::-1][len(rs) - 1]
+            for e in set(gs) ^ set(rs):
+                assert abs(lg[e] - kth) <= tau, f"token {t}: expert {e} is {lg[e] - kth:.3e} from the k-th logit"
+            rw = oracle.route_weights(lg, np.asarray(gs, dtype=np.int32))
+            assert np.abs(w_gpu[t] - rw).max() <= W_TOL, f"token {t}: weights of the GPU's selection"
+            exempt.append(t)
+            continue
         wr = dict(zip(rs, ref["w"][t]))
         for i, e in enumerate(gs):
             assert abs(w_gpu[t, i] - wr[e]) <= W_TOL, f"token {t}: weight of expert {e}: {w_gpu[t, i]} vs {wr[e]}"
+    bound = 1 + T // 64 if max_exempt is None else max_exempt
+    if near or exempt:
+        print(f"routing{(' ' + label) if label else ''}: {near} of {T} tokens within the near-tie margin, "
+              f"{len(exempt)} selected differently")
+    assert len(exempt) <= bound, f"{len(exempt)} near-tie exemptions among {T} tokens (bound {bound})"
     return exempt
+
+
+def reference_outputs(src, layer, xb, ref, ids_gpu, exempt, act=oracle.ACT_SILU):
+    """The oracle's outputs, with each exempted token recomputed under the
+    GPU's selection (weights: the oracle's softmax over those experts), so
+    that every token's output is compared."""
+    y = np.array(ref["y"], dtype=np.float64, copy=True)
+    xb = np.atleast_2d(xb)
+    for t in exempt:
+        ids = np.asarray(ids_gpu[t], dtype=np.int32)
+        w = oracle.route_weights(ref["logits"][t], ids)
+        bl = [src.blocks(layer, e) for e in ids]
+        y[t] = oracle.moe_token([b[0] for b in bl], [b[1] for b in bl], [b[2] for b in bl], w, xb[t], act=act)
+    return y
+
+
+def token_ratios(y, ref):
+    """Per-token max|err| / max|ref| (the per-token view of the tolerance)."""
+    y = np.atleast_2d(np.asarray(y, dtype=np.float64))
+    ref = np.atleast_2d(np.asarray(ref, dtype=np.float64))
+    m = np.abs(ref).max(1)
+    return np.abs(y - ref).max(1) / np.where(m > 0, m, 1.0)
+
+
+def check_outputs(y, ref, tol=REL_TOL, label=""):
+    """max|y - ref| <= tol * max|ref| over the whole tensor; prints the
+    whole-tensor ratio and the worst per-token ratio. Returns the ratio."""
+    err = rel_err(y, ref)
+    worst_tok = float(token_ratios(y, ref).max()) if np.size(ref) else 0.0
+    print(f"{label or 'outputs'}: max|err|/max|ref| = {err:.3e}, worst per-token ratio {worst_tok:.3e}")
+    assert err <= tol, f"{label}: max|err|/max|ref| = {err:.3e}"
+    return err
 
 
 def bf16_step(bits):

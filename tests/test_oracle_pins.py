@@ -483,3 +483,151 @@ def test_mx_expert_ffn_matches_dense_numpy():
     ids, w = res["ids"][0], res["w"][0]
     ref = sum(w[s] * _dense_ffn(src, 0, ids[s], x) for s in range(S.top_k))
     assert np.allclose(res["y"][0], ref, rtol=1e-11, atol=1e-13)
+
+
+# ------------------------------------------------------------------ selection margin
+def _kth_largest_by_counting(lg, k):
+    """The k-th largest value by counting (no sort): v with #{l > v} < k <= #{l >= v}."""
+    for v in lg:
+        if np.count_nonzero(lg > v) < k <= np.count_nonzero(lg >= v):
+            return v
+    raise AssertionError("no k-th value")
+
+
+def test_selection_margin_against_brute_force():
+    """route()'s margin l_(k) - l_(k+1) against k-th values found by counting,
+    on random logits, on sorted and reversed logits, with constructed ties
+    (margin 0 exactly where the tie rule decides) and with k = E (every
+    selection is the same set: infinite margin)."""
+    rng = np.random.default_rng(21)
+    for trial in range(300):
+        E = int(rng.integers(2, 40))
+        k = int(rng.integers(1, E + 1))
+        lg = rng.standard_normal(E)
+        if trial % 5 == 1:
+            lg = np.sort(lg)
+        elif trial % 5 == 2:
+            lg = np.sort(lg)[::-1].copy()
+        elif trial % 5 == 3:
+            lg = np.round(lg * 2) / 2               # many exact ties
+        ids, w, gap = oracle.route(lg, k)
+        if k == E:
+            assert gap == np.inf
+            continue
+        ref = _kth_largest_by_counting(lg, k) - _kth_largest_by_counting(lg, k + 1)
+        assert gap == ref and gap >= 0
+        # the margin separates the selection from the rest, and is attained
+        sel = set(ids.tolist())
+        rest = [e for e in range(E) if e not in sel]
+        assert min(lg[list(sel)]) - max(lg[rest]) == gap
+    lg = np.array([3.0, 1.0, 2.0, 2.0, 0.5])
+    assert oracle.route(lg, 2)[2] == 0.0          # experts 2 and 3 tie for the 2nd place
+    assert oracle.route(lg, 3)[2] == 1.0
+    assert oracle.route(lg, 1)[2] == 1.0
+    assert oracle.route(np.array([1.0, -1.0]), 2)[2] == np.inf
+
+
+def test_check_routing_rejects_far_swaps_and_bounds_exemptions():
+    """The parity tests' routing rule (host logic): a selection that differs
+    from the oracle's only by an expert tied with the k-th logit within tau
+    is exempted; one that differs by an expert far from it, or too many
+    exemptions, fail."""
+    from helpers import TAU, check_routing
+    lg = np.array([[4.0, 1.0, 1.0 + 0.5 * TAU, -2.0, 0.0]])
+    ref = dict(ids=np.array([[0, 2]]), w=oracle.route_weights(lg[0], np.array([0, 2], np.int32))[None],
+               gap=np.array([0.5 * TAU]), logits=lg)
+    w_alt = oracle.route_weights(lg[0], np.array([0, 1], np.int32))[None]
+    assert check_routing(np.array([[0, 1]]), w_alt, ref) == [0]
+    with pytest.raises(AssertionError):
+        check_routing(np.array([[0, 1]]), w_alt, ref, exact=True)
+    with pytest.raises(AssertionError):            # expert 4 is far from the k-th logit
+        check_routing(np.array([[0, 4]]), oracle.route_weights(lg[0], np.array([0, 4], np.int32))[None], ref)
+    with pytest.raises(AssertionError):
+        check_routing(np.array([[0, 1]]), w_alt, ref, max_exempt=0)
+
+
+# ------------------------------------------------------------------ recipe emulation
+def test_emulation_roundings_match_library_conversions():
+    """The emulation's fp16 (nearest even, overflow to inf) and bf16 roundings
+    against numpy's float16 and torch's bfloat16 conversions, over normals,
+    subnormals, exact midpoints and overflow; the toward-zero fp16 rounding
+    never increases the magnitude, stays within one fp16 step and saturates
+    at 65504."""
+    import torch
+    rng = np.random.default_rng(22)
+    vals = rng.standard_normal(4000) * np.exp(rng.uniform(-25, 12, 4000))
+    mids = (np.arange(1, 2000, dtype=np.float64) + 0.5) * 2.0 ** -24       # fp16 subnormal midpoints
+    vals = np.concatenate([vals, mids, -mids, [65504.0, 65519.0, 65520.0, 1e6, -7e4, 2.0 ** -25, 3 * 2.0 ** -26]])
+    with np.errstate(over="ignore"):
+        ref16 = vals.astype(np.float16).astype(np.float64)
+    got16 = np.array([oracle.emul_fp16(v) for v in vals])
+    assert np.array_equal(got16, ref16)
+    v32 = vals.astype(np.float32)                   # bf16 rounds the fp32 value the GPU holds
+    refb = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+    gotb = np.array([oracle.emul_bf16(float(v)) for v in v32])
+    assert np.array_equal(gotb, refb)
+    for v in vals:
+        r = oracle.emul_fp16_rtz(v)
+        assert abs(r) <= abs(v) and np.sign(r) in (0, np.sign(v))
+        if abs(v) <= 65504:
+            with np.errstate(over="ignore"):
+                up = np.nextafter(np.float16(abs(r)), np.float16(np.inf)).astype(np.float64)
+            assert abs(v) < up
+        else:
+            assert abs(r) == 65504.0
+
+
+def test_recipe_emulation_at_full_precision_is_the_oracle():
+    """Exact codes with an fp32 sub-block affine and fp32 h differ from the
+    fp64 oracle only by fp32 rounding (both encodings)."""
+    for S in (synth.TINY, synth.Shape("tiny-mx", 1, 256, 8, 2, 512, synth.FMT_MXFP4)):
+        src = oracle.ExpertSource(S)
+        xb = synth.x_bf16(S, 61, 0, T=3)
+        y, ref = oracle.emulate_moe_layer(src, 0, xb, oracle.W_EXACT_CODES, oracle.H_FP32)
+        err = np.abs(y - ref["y"]).max() / np.abs(ref["y"]).max()
+        assert 0 < err < 2e-6, err
+
+
+def test_recipe_emulation_reproduces_precision_table():
+    """P13: on the Qwen3-30B-A3B-shaped layer the emulation reproduces the
+    recipe-error table worked out when the survey planned the MFMA recipe
+    (max|err|/max|ref| of plain bf16 weights with bf16 h about 3.9e-3, bf16
+    weights with fp32 h 3.5e-3, exact codes with bf16 h 2.08e-3, exact codes
+    with h as bf16 hi + lo 2.7e-6, weights and h both hi + lo 4.6e-6, exact
+    codes with fp16 h 2.1e-4), each within a factor of 2.5 on four tokens,
+    and in the same order."""
+    S = synth.QWEN3_30B_A3B
+    src = oracle.ExpertSource(S)
+    xb = synth.x_bf16(S, 60, 0, T=4)
+    table = [(oracle.W_BF16, oracle.H_BF16, 3.9e-3), (oracle.W_BF16, oracle.H_FP32, 3.5e-3),
+             (oracle.W_EXACT_CODES, oracle.H_BF16, 2.08e-3), (oracle.W_EXACT_CODES, oracle.H_BF16_HILO, 2.7e-6),
+             (oracle.W_BF16_HILO, oracle.H_BF16_HILO, 4.6e-6), (oracle.W_EXACT_CODES, oracle.H_FP16, 2.1e-4)]
+    ref = oracle.moe_layer(src, 0, xb)
+    m = np.abs(ref["y"]).max()
+    errs = []
+    for wm, hm, expected in table:
+        y, _ = oracle.emulate_moe_layer(src, 0, xb, wm, hm)
+        e = np.abs(y - ref["y"]).max() / m
+        errs.append(e)
+        assert expected / 2.5 <= e <= expected * 2.5, (wm, hm, e, expected)
+    order = np.argsort([t[2] for t in table])
+    assert list(np.argsort(errs)) == list(order)
+
+
+def test_recipe_emulation_predicts_fp16_range_failure():
+    """With the squared-ReLU gate and inputs scaled by 2^8 (exact in bf16),
+    h exceeds the fp16 range on the tiny layer: the fp16-h recipe (and fp16
+    activations toward zero) breaks down while fp32 h and bf16 hi + lo h stay
+    at fp32-level error."""
+    S = synth.TINY
+    src = oracle.ExpertSource(S)
+    xb = synth.x_bf16(S, 62, 0, T=2)
+    xs = ((xb.astype(np.uint32) + (8 << 7)) & 0xFFFF).astype(np.uint16)   # exponent + 8: x * 256
+    assert np.array_equal(oracle.bf16_array(xs), 256.0 * oracle.bf16_array(xb))
+    R = oracle.ACT_RELU2
+    y16, ref = oracle.emulate_moe_layer(src, 0, xs, oracle.W_EXACT_CODES, oracle.H_FP16, act=R)
+    m = np.abs(ref["y"]).max()
+    assert not np.isfinite(y16).all() or np.abs(y16 - ref["y"]).max() / m > 1e-2
+    for hm in (oracle.H_FP32, oracle.H_BF16_HILO):
+        y, _ = oracle.emulate_moe_layer(src, 0, xs, oracle.W_EXACT_CODES, hm, act=R)
+        assert np.abs(y - ref["y"]).max() / m < 2e-5, hm
