@@ -52,14 +52,15 @@ enum moe_status {
  * at most one of them). T = 1 always takes the per-token GEMV. Without a flag
  * the choice goes by routed pairs per expert, P/E = T*top_k/n_experts: below
  * 1/2 the per-token GEMV (each routed expert streamed once per token); up to
- * 1 the expert-major GEMV (each routed expert streamed once, its tokens held
- * in registers; needs inter <= 2048); beyond, the grouped MFMA GEMMs, on
- * tiles of 16 pairs with every weight load in flight up to P/E = 12 (hidden
- * 512, 1024 or 2048 and inter <= 1024) and on tiles of 32 or 96 pairs above.
- * Where the 16-pair tiles do not apply, the expert-major GEMV runs up to
- * P/E = 9/4. */
+ * 1 (MXFP4 weights: 1.75) the expert-major GEMV (each routed expert streamed
+ * once, its tokens held in registers; needs inter <= 2048); beyond, the MFMA
+ * tiles (grouped GEMMs on tiles of 16, 64 or 128 routed pairs of one expert;
+ * hidden 512, 1024 or 2048 and inter <= 1024). Shapes without the tiles keep
+ * the expert-major GEMV. Every path computes with exact operands and fp32
+ * accumulation (h in fp32, or as bf16 hi + lo planes on the tiles), so the
+ * results agree to fp32-level rounding over the whole input range. */
 #define MOE_FLAG_FORCE_GEMV 0x1u         /* per-token dequant-on-read GEMV for every T */
-#define MOE_FLAG_FORCE_GROUPED 0x2u      /* grouped MFMA expert GEMMs for every T >= 2 (tile shape by P/E) */
+#define MOE_FLAG_FORCE_GROUPED 0x2u      /* MFMA tiles for every T >= 2 (tile size by P/E); shapes with the tiles only */
 #define MOE_FLAG_FORCE_EXPERT_GEMV 0x4u  /* expert-major GEMV for every T >= 2; needs inter <= 2048 */
 
 /* Gate activation h = act(g, u) of the expert FFN (at most one flag; default
@@ -74,35 +75,41 @@ enum moe_status {
  * dequant (sparkinfer CuTe-DSL README, "moe" paragraph), in 17-byte blocks of
  * 32 weights: one E8M0 scale byte e (2^(e-127)), then 16 bytes of FP4 E2M1
  * codes, element 2i in the low nibble of byte 1+i. The packer accepts scale
- * codes 2..252 (2^-125 .. 2^125). Paths: per-token GEMV while T*k < E/2,
- * expert-major GEMV up to T*k = 1.75 E, then MFMA tiles (hidden 512,
- * 1024 or 2048 and inter <= 1024; otherwise the expert-major GEMV) of 16
- * pairs up to P/E = 1, 64 pairs up to 16 and 128 pairs beyond. The
- * force flags apply, MOE_FLAG_FORCE_GROUPED only where the 16-pair tiles do. */
+ * codes 2..252 (2^-125 .. 2^125). The paths and force flags are those
+ * above. */
 #define MOE_FLAG_WEIGHTS_MXFP4 0x20u
 
 typedef struct moe_config {
-  int32_t hidden;      /* H: multiple of 256; 256, 512, 1024 or a multiple of 2048 up to 8192 */
+  int32_t hidden;      /* H: 256, 512, 1024 or a multiple of 2048 up to 8192 */
   int32_t n_experts;   /* E: 1..256 */
   int32_t top_k;       /* k: 1..min(E, 16) */
   int32_t inter;       /* I: expert intermediate size, multiple of 256, up to 4096 */
   int32_t n_layers;    /* layers held in one blob, >= 1 */
-  int32_t max_tokens;  /* largest T any call will pass, >= 1 */
+  int32_t max_tokens;  /* largest T any call will pass, >= 1, with max_tokens*top_k*max(hidden, inter) < 2^31 */
   uint32_t flags;      /* MOE_FLAG_* */
   float rms_eps;       /* RMSNorm epsilon of the stacked-layer epilogue, >= 0 */
 } moe_config;
 
 typedef struct moe_plan moe_plan;
 
-/* 1 if the configuration is supported, else 0. No side effects. */
+/* 1 if the configuration is supported, else 0. No side effects. (Every op
+ * of the pages' kernel library exports such a query: sparkinfer (formerly
+ * b12x) README, the paragraph after "Using it".) */
 int moe_is_supported(const moe_config* cfg);
 
 /* Host-only. Validates cfg and builds an immutable plan (host allocation).
- * *out is set to NULL on error. Thread-safe to use concurrently once made. */
+ * *out is set to NULL on error (MOE_ERR_UNSUPPORTED for a configuration
+ * moe_is_supported refuses). Thread-safe to use concurrently once made.
+ * The plan step of the pages' plan / bind / run split: the plan is host-side
+ * and may allocate, the device calls below never do (sparkinfer (formerly
+ * b12x) README, "Using it" and the paragraph after it). */
 int moe_plan_create(const moe_config* cfg, moe_plan** out);
 void moe_plan_destroy(moe_plan* plan);
 
-/* Pure size queries (0 on a NULL plan or T out of range). */
+/* Pure size queries (0 on a NULL plan or T out of range). moe_scratch_bytes
+ * sizes the one device workspace a call needs for T tokens, as the pages'
+ * plans report their scratch (sparkinfer (formerly b12x) README, "Using it":
+ * scratch_specs). */
 size_t moe_blob_bytes(const moe_plan* plan);          /* header + n_layers * layer bytes */
 size_t moe_header_bytes(const moe_plan* plan);        /* blob header (4096) */
 size_t moe_layer_bytes(const moe_plan* plan);         /* one packed layer */
@@ -110,6 +117,11 @@ size_t moe_layer_offset(const moe_plan* plan, int32_t layer);  /* byte offset of
 size_t moe_scratch_bytes(const moe_plan* plan, int32_t T);     /* device scratch for T tokens */
 
 /* ---------------------------------------------------------------- packing
+ * The weights are prepared once per model, as the pages' fused MoE prepares
+ * its experts (sparkinfer (formerly b12x) README, "Using it": plan_weights /
+ * prepare_weights), and stay resident in the 4-bit encoding that is
+ * dequantized on read (sparkinfer README, "Deeper MoE-bandwidth
+ * specialization" bullet).
  * Canonical input: for one layer, gate_host and up_host are
  * [E][inter][hidden/K] blocks, down_host is [E][hidden][inter/K] blocks
  * (K = 256 and 144-byte blocks, or with MOE_FLAG_WEIGHTS_MXFP4 K = 32 and
@@ -144,31 +156,50 @@ typedef struct moe_route_out {
   int32_t* pairs;
 } moe_route_out;
 
-/* Router for T tokens of layer `layer`. If logits is NULL the logits are the
- * router GEMV of x_bf16 ([T][hidden] bf16) with the layer's fp32 router
- * weights; otherwise logits (fp32 [T][E], device) are used and x_bf16 is
- * ignored (may be NULL). */
+/* Router for T tokens of layer `layer`: the pages' sync-free MoE router and
+ * expert dispatch, with the expert counts computed on the device and no host
+ * readback, so it can be captured in a graph (sparkinfer README, repository
+ * layout table, moe/ row). If logits is NULL the logits are the router GEMV
+ * of x_bf16 ([T][hidden] bf16) with the layer's fp32 router weights;
+ * otherwise logits (fp32 [T][E], device) are used and x_bf16 is ignored (may
+ * be NULL). out->topk_ids/topk_w receive the top_k experts (descending logit,
+ * equal logits to the lower id) and their softmax restricted to the
+ * selection; with the three list pointers set, also counts, offsets and
+ * pairs. Errors: MOE_ERR_INVALID_ARGUMENT for a NULL or misaligned buffer,
+ * a partial set of list pointers, a layer or T out of range;
+ * MOE_ERR_SCRATCH_TOO_SMALL. */
 int moe_route(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16,
               const float* logits, int32_t T, const moe_route_out* out, void* scratch,
               size_t scratch_bytes, hipStream_t stream);
 
-/* Expert FFN and weighted sum for T tokens given routing results r. The
- * batched paths read the dispatch lists (r->offsets, r->pairs); without them
- * the per-token GEMV path runs, unless a batched path is forced, which is
- * then an invalid argument. out: fp32 [T][hidden]. */
+/* Expert FFN and weighted sum for T tokens given routing results r: the
+ * pages' fused MoE consumes top-k ids and weights computed outside it
+ * (sparkinfer (formerly b12x) README, "Using it": fused_moe bound with
+ * topk_weights and topk_ids; the kernel table's fused quantized MoE expert
+ * FFN in the sparkinfer README's layout table). x_bf16: [T][hidden] bf16;
+ * r->topk_ids, r->topk_w: [T][k]; out: fp32 [T][hidden], written in full.
+ * The batched paths read the dispatch lists (r->offsets, r->pairs, as
+ * moe_route writes them); without them the per-token GEMV path runs, unless
+ * a batched path is forced, which is then MOE_ERR_INVALID_ARGUMENT. */
 int moe_expert_ffn(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16,
                    int32_t T, const moe_route_out* r, float* out, void* scratch, size_t scratch_bytes,
                    hipStream_t stream);
 
-/* Router + expert FFN for T tokens: out = y (fp32 [T][hidden]). If x_next is
+/* Router + expert FFN for T tokens, the whole MoE block of one layer as the
+ * pages' decode runs it (sparkinfer README, opening paragraph and layout
+ * table: router, dispatch and fused quantized expert FFN): out = y (fp32
+ * [T][hidden]). If x_next is
  * not NULL it also writes x_next = bf16(RMSNorm(x + y)) ([T][hidden] bf16),
- * the input of the next stacked layer. route_out may be NULL; if given, the
- * routing results are written there too. Routing comes from the router GEMV. */
+ * the input of the next stacked layer; x_next may be x itself. route_out may
+ * be NULL; if given, topk_ids and topk_w receive the routing, and its
+ * dispatch lists (counts, offsets, pairs: all three, or none) the on-device
+ * lists, whichever path runs. Routing comes from the router GEMV. */
 int moe_forward(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16,
                 int32_t T, float* out, uint16_t* x_next, const moe_route_out* route_out,
                 void* scratch, size_t scratch_bytes, hipStream_t stream);
 
-/* One decode step of the whole stack for T tokens: for l = 0..n_layers-1,
+/* One decode step of the whole stack for T tokens (the greedy bs=1 decode
+ * the pages time: sparkinfer README, opening paragraph): for l = 0..n_layers-1,
  * moe_forward(layer l, x = xs[l], out = ys[l], x_next = xs[(l+1) % n_layers]),
  * so the last layer's normalised output becomes the next step's layer-0
  * input. xs: bf16 [n_layers][T][hidden]; ys: fp32 [n_layers][T][hidden];
@@ -177,7 +208,9 @@ int moe_forward(const moe_plan* plan, const void* blob, int32_t layer, const uin
 int moe_stack_step(const moe_plan* plan, const void* blob, uint16_t* xs, float* ys, int32_t* ids, float* w,
                    int32_t T, void* scratch, size_t scratch_bytes, hipStream_t stream);
 
-/* A decode step captured once as a hipGraph and replayed per token. Capture
+/* A decode step captured once as a hipGraph and replayed per token (the
+ * pages' CUDA-graph decode: sparkinfer README, repository layout table,
+ * runtime/ row). Capture
  * is a set-up call (like plan creation: it may allocate runtime resources)
  * and needs a non-default `stream`; it records moe_stack_step with exactly
  * these buffers, which must stay alive and in place for the graph's life.

@@ -241,10 +241,11 @@ class Plan:
         _check(load().moe_expert_ffn(self._h, _dptr(blob), layer, _dptr(x), T, ctypes.byref(ro), _dptr(out),
                                      _dptr(scratch), sb, _stream(stream)), "moe_expert_ffn")
 
-    def forward(self, blob, layer, x, T, out, x_next=None, ids=None, w=None, scratch=None, stream=None):
+    def forward(self, blob, layer, x, T, out, x_next=None, ids=None, w=None, scratch=None, stream=None,
+                counts=None, offsets=None, pairs=None):
         ro = None
         if ids is not None or w is not None:
-            ro = ctypes.byref(RouteOut(_dptr(ids), _dptr(w), None, None, None))
+            ro = ctypes.byref(RouteOut(_dptr(ids), _dptr(w), _dptr(counts), _dptr(offsets), _dptr(pairs)))
         sb = scratch.numel() * scratch.element_size() if scratch is not None else 0
         _check(load().moe_forward(self._h, _dptr(blob), layer, _dptr(x), T, _dptr(out), _dptr(x_next), ro,
                                   _dptr(scratch), sb, _stream(stream)), "moe_forward")

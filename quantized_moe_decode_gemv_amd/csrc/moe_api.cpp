@@ -20,6 +20,8 @@ static bool cfg_ok(const moe_config* c) {
   const int H = c->hidden, E = c->n_experts, k = c->top_k, I = c->inter;
   if (H <= 0 || H % QK || E < 1 || E > 256 || k < 1 || k > 16 || k > E || I <= 0 || I % QK) return false;
   if (c->n_layers < 1 || c->max_tokens < 1 || !(c->rms_eps >= 0.0f)) return false;
+  // device index arithmetic over (token, slot, row) runs in 32 bits
+  if ((long long)c->max_tokens * k * (H > I ? H : I) >= (1LL << 31)) return false;
   // gate/up lane mapping: hidden/32 sub-blocks per row either fill a
   // power-of-two lane group (256, 512, 1024) or whole waves (2048 * {1..4})
   const bool h_ok = H == 256 || H == 512 || H == 1024 || (H % 2048 == 0 && H / 2048 <= 4);
@@ -30,8 +32,8 @@ static bool cfg_ok(const moe_config* c) {
   const uint32_t act = c->flags & (MOE_FLAG_ACT_RELU2 | MOE_FLAG_ACT_SWIGLU_OAI);
   const uint32_t fmt = c->flags & MOE_FLAG_WEIGHTS_MXFP4;
   if (c->flags & ~(force | act | fmt)) return false;
-  // MXFP4 on MFMA: the 16-pair tiles only (hidden 512, 1024 or 2048, inter <= 1024)
-  if (fmt && (force & MOE_FLAG_FORCE_GROUPED) && !((H == 512 || H == 1024 || H == 2048) && I <= 1024)) return false;
+  // the MFMA tiles: hidden 512, 1024 or 2048, inter <= 1024
+  if ((force & MOE_FLAG_FORCE_GROUPED) && !((H == 512 || H == 1024 || H == 2048) && I <= 1024)) return false;
   if (force & (force - 1)) return false;          // at most one path may be forced
   if (act & (act - 1)) return false;              // at most one activation
   // expert-major GEMV: one 32-code sub-block of a down row per lane of a wave
@@ -265,56 +267,39 @@ static const uint8_t* layer_ptr(const moe_plan* plan, const void* blob, int32_t 
 }
 
 // Path choice by the host-known token count T. The per-token GEMV streams
-// every routed expert once per token; the expert-major GEMV and the grouped
-// MFMA GEMMs stream each routed expert once per batch, the former with the
-// tokens of an expert held in registers, the latter on MFMA tiles of 32 or 96
-// pairs, which pay off once experts carry many pairs.
-// The switches are in routed pairs per expert, P/E with P = T*k (measured
-// crossovers on the Qwen3-30B-A3B-shaped layer: per-token GEMV ahead up to 6
-// tokens, P/E = 0.375; expert-major GEMV from 8 tokens, 0.5, level with the
-// 16-pair MFMA tiles at 16 tokens, 1; 16-pair tiles level with 32-pair tiles
-// at 192 tokens, 12; without the 16-pair tiles the expert-major GEMV is ahead
-// of the 32-pair tiles up to about 36 tokens, 2.25).
-enum class Path { Gemv, ExpertGemv, Grouped16, Grouped };
-constexpr long long G16_MAX_PAIRS_PER_EXPERT = 12;
-// Tile shape of the grouped MFMA path: 16-pair tiles with every weight load
-// in flight while experts carry few pairs, 32- or 96-pair tiles beyond.
-static Path grouped_tiles(const Layout& d, int32_t T) {
-  if (d.fmt == FMT_MXFP4) return Path::Grouped16;   // its only MFMA tiles
-  if (g16_supported(d) && (long long)T * d.k <= G16_MAX_PAIRS_PER_EXPERT * d.E) return Path::Grouped16;
-  return Path::Grouped;
-}
+// every routed expert once per token; the expert-major GEMV and the MFMA
+// tiles stream each routed expert once per batch, the former with the tokens
+// of an expert held in registers, the latter as GEMMs on tiles of 16, 64 or
+// 128 pairs, which pay off once experts carry several pairs. The switches
+// are in routed pairs per expert, P/E with P = T*k (measured on the
+// Qwen3-30B-A3B-shaped layer: the per-token GEMV ahead up to 6 tokens,
+// P/E = 0.375; the expert-major GEMV from 8 tokens, 0.5, up to P/E = 1 with
+// super-block weights and 1.75 with MXFP4 weights). Shapes without the MFMA
+// tiles keep the expert-major GEMV (or the per-token GEMV where that does
+// not apply either).
+enum class Path { Gemv, ExpertGemv, Tiles };
 static Path choose_path(const moe_plan* plan, int32_t T) {
   const Layout& d = plan->d;
   if (T < 2 || (d.flags & MOE_FLAG_FORCE_GEMV)) return Path::Gemv;
-  if (d.flags & MOE_FLAG_FORCE_GROUPED) return grouped_tiles(d, T);
+  if (d.flags & MOE_FLAG_FORCE_GROUPED) return Path::Tiles;       // cfg_ok: the shape has the tiles
   if (d.flags & MOE_FLAG_FORCE_EXPERT_GEMV) return Path::ExpertGemv;
   const long long P = (long long)T * d.k, E = d.E;
   if (2 * P < E) return Path::Gemv;
-  // MXFP4: the expert-major GEMV up to 1.75 pairs per expert, the MFMA
-  // tiles beyond where the shape has them (measured on the
-  // Qwen3-30B-A3B-shaped layer: 88 / 94 us at 24 tokens, 106 / 103 at 32)
-  if (d.fmt == FMT_MXFP4) {
-    if (g16_supported(d) && (4 * P > 7 * E || !egemv_supported(d))) return Path::Grouped16;
-    return egemv_supported(d) ? Path::ExpertGemv : Path::Gemv;
-  }
-  const bool g16 = g16_supported(d);
-  if (egemv_supported(d) && (P <= E || (!g16 && 4 * P <= 9 * E))) return Path::ExpertGemv;
-  return grouped_tiles(d, T);
+  const bool past_egemv = d.fmt == FMT_MXFP4 ? 4 * P > 7 * E : P > E;
+  if (g16_supported(d) && (past_egemv || !egemv_supported(d))) return Path::Tiles;
+  return egemv_supported(d) ? Path::ExpertGemv : Path::Gemv;
 }
 
-// Work list of each batched path in scratch: the 32/96-pair tiles' offsets,
-// or one record per 16-pair tile, or one record per routed expert.
+// Work list of each batched path in scratch: one record per MFMA tile, or
+// one record per routed expert.
 struct WorkList {
-  int32_t* tile_off;
   void* slots;
   int mt, max_slots;
 };
 static WorkList work_list(const Layout& d, Path p, int32_t T, uint8_t* scr, const Scratch& sc) {
-  if (p == Path::Grouped) return {reinterpret_cast<int32_t*>(scr + sc.tile_off), nullptr, grouped_mt(d, T), 0};
-  if (p == Path::Grouped16) return {nullptr, scr + sc.slots, g16_mt(d, T), g16_max_tiles(d, T)};
+  if (p == Path::Tiles) return {scr + sc.slots, g16_mt(d, T), g16_max_tiles(d, T)};
   const int P = T * d.k;
-  return {nullptr, scr + sc.slots, P, 1 + (P < d.E ? P : d.E)};
+  return {scr + sc.slots, P, 1 + (P < d.E ? P : d.E)};
 }
 
 // lists_ready: the dispatch kernel already wrote the work list into scratch.
@@ -323,15 +308,14 @@ static int batched_impl(const moe_plan* plan, Path path, const uint8_t* L, const
                         hipStream_t stream, bool lists_ready = false) {
   const Layout& d = plan->d;
   const WorkList wl = work_list(d, path, T, scr, sc);
-  if (!lists_ready &&
-      launch_work_list(d, offsets, T, wl.tile_off, wl.mt, wl.slots, wl.max_slots, stream) != hipSuccess)
+  if (!lists_ready && launch_work_list(d, offsets, T, wl.mt, wl.slots, wl.max_slots, stream) != hipSuccess)
     return MOE_ERR_HIP;
-  _Float16* h16 = reinterpret_cast<_Float16*>(scr + sc.h16);
   float* ypair = reinterpret_cast<float*>(scr + sc.ypair);
   hipError_t e;
-  if (path == Path::ExpertGemv) e = launch_egemv_ffn(d, L, x, w, pairs, wl.slots, h16, ypair, out, T, stream);
-  else if (path == Path::Grouped16) e = launch_g16_ffn(d, L, x, w, pairs, wl.slots, h16, ypair, out, T, stream);
-  else e = launch_grouped_ffn(d, L, x, w, offsets, pairs, wl.tile_off, h16, ypair, out, T, stream);
+  if (path == Path::ExpertGemv)
+    e = launch_egemv_ffn(d, L, x, w, pairs, wl.slots, reinterpret_cast<float*>(scr + sc.hbuf), ypair, out, T, stream);
+  else
+    e = launch_g16_ffn(d, L, x, w, pairs, wl.slots, reinterpret_cast<uint16_t*>(scr + sc.hbuf), ypair, out, T, stream);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -398,10 +382,12 @@ extern "C" int moe_expert_ffn(const moe_plan* plan, const void* blob, int32_t la
 
 // Router + expert FFN for one layer. With y_prev the layer input is formed
 // inside the router kernel as bf16(RMSNorm(x_in + y_prev)) and stored to
-// x_formed; otherwise x_in is the layer input.
+// x_formed; otherwise x_in is the layer input. lists: the caller's dispatch
+// lists (counts, offsets, pairs) to fill, or nullptr for scratch.
 static int forward_impl(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_in,
                         const float* y_prev, uint16_t* x_formed, int32_t T, float* out, uint16_t* x_next,
-                        int32_t* ids, float* w, uint8_t* scr, const Scratch& sc, hipStream_t stream) {
+                        int32_t* ids, float* w, uint8_t* scr, const Scratch& sc, hipStream_t stream,
+                        const moe_route_out* lists = nullptr) {
   const Layout& d = plan->d;
   const uint8_t* L = layer_ptr(plan, blob, layer);
   float* lg = reinterpret_cast<float*>(scr + sc.logits);
@@ -417,19 +403,20 @@ static int forward_impl(const moe_plan* plan, const void* blob, int32_t layer, c
   const bool fused = (T == 1);
   if (!fused && launch_topk(d, lg, ids, w, T, stream) != hipSuccess) return MOE_ERR_HIP;
   const Path path = choose_path(plan, T);
+  int32_t* counts = lists ? lists->counts : reinterpret_cast<int32_t*>(scr + sc.counts);
+  int32_t* offsets = lists ? lists->offsets : reinterpret_cast<int32_t*>(scr + sc.offsets);
+  int32_t* pairs = lists ? lists->pairs : reinterpret_cast<int32_t*>(scr + sc.pairs);
   if (path != Path::Gemv) {
-    int32_t* counts = reinterpret_cast<int32_t*>(scr + sc.counts);
-    int32_t* offsets = reinterpret_cast<int32_t*>(scr + sc.offsets);
-    int32_t* pairs = reinterpret_cast<int32_t*>(scr + sc.pairs);
     const WorkList wl = work_list(d, path, T, scr, sc);
-    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream, wl.tile_off, wl.mt, wl.slots, wl.max_slots) !=
-        hipSuccess)
+    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream, wl.mt, wl.slots, wl.max_slots) != hipSuccess)
       return MOE_ERR_HIP;
     const int st = batched_impl(plan, path, L, x, T, w, offsets, pairs, out, scr, sc, stream, true);
     if (st) return st;
   } else {
     if (launch_gateup(d, L, x, ids, lg, ids, w, h, T, fused, stream) != hipSuccess) return MOE_ERR_HIP;
     if (launch_down(d, L, ids, w, h, out, T, stream) != hipSuccess) return MOE_ERR_HIP;
+    // the per-token path needs no dispatch lists; build them when asked for
+    if (lists && launch_dispatch(d, ids, counts, offsets, pairs, T, stream) != hipSuccess) return MOE_ERR_HIP;
   }
   if (x_next && launch_resid_norm(d, x, out, x_next, T, stream) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
@@ -444,11 +431,14 @@ extern "C" int moe_forward(const moe_plan* plan, const void* blob, int32_t layer
   if (!x_bf16 || !aligned(x_bf16, 16) || !out || !aligned(out, 16)) return MOE_ERR_INVALID_ARGUMENT;
   if (x_next && !aligned(x_next, 16)) return MOE_ERR_INVALID_ARGUMENT;
   if (route_out && (!route_out->topk_ids || !route_out->topk_w)) return MOE_ERR_INVALID_ARGUMENT;
+  const bool lists = route_out && (route_out->counts || route_out->offsets || route_out->pairs);
+  if (lists && !(route_out->counts && route_out->offsets && route_out->pairs)) return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
   uint8_t* scr = static_cast<uint8_t*>(scratch);
   int32_t* ids = route_out ? route_out->topk_ids : reinterpret_cast<int32_t*>(scr + sc.ids);
   float* w = route_out ? route_out->topk_w : reinterpret_cast<float*>(scr + sc.w);
-  return forward_impl(plan, blob, layer, x_bf16, nullptr, nullptr, T, out, x_next, ids, w, scr, sc, stream);
+  return forward_impl(plan, blob, layer, x_bf16, nullptr, nullptr, T, out, x_next, ids, w, scr, sc, stream,
+                      lists ? route_out : nullptr);
 }
 
 // ---------------------------------------------------------------- stacked decode step

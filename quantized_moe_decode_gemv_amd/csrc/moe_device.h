@@ -166,37 +166,44 @@ __device__ __forceinline__ float gate_act(float g, float u, int act) {
   return g / (1.0f + expf(-g)) * u;
 }
 
-// sum_i (1024 + q_i) * h_i over one 32-code sub-block with fp16 h, two codes
-// per v_dot2_f32_f16 ((1024 + q) * h is exact in fp32). X[4d+c] holds the
-// fp16 pair (h[8d+c], h[8d+c+4]).
-__device__ __forceinline__ float dot_codes_f16(const u32x4& c, const u32* X) {
+// Exact conversion of 4-bit codes: a byte 0x0q read as an FP8 E4M3 number is
+// q * 2^-9 (a subnormal m 2^-9 for q = m < 8, (8 + m) 2^-9 for q = 8 + m), so
+// gfx950's scaled FP8 conversion with scale 2^9 yields q exactly (checked on
+// the device for all 16 codes). One instruction turns two codes (one 16-bit
+// word of masked nibbles) into two fp32 or bf16 values.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <bool HIGH_WORD>
+__device__ __forceinline__ f32x2 codes2_f32(u32 nibble_bytes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(nibble_bytes, 512.0f, HIGH_WORD);
+}
+
+// sum_i q_i * h_i over one 32-code sub-block with fp32 h (h[i] = element i
+// of the sub-block): the codes are converted exactly, products and sums are
+// fused fp32 operations; two accumulators halve the dependent chain.
+__device__ __forceinline__ float dot_codes_f32(const u32x4& c, const float* h) {
   const u32 w[4] = {c.x, c.y, c.z, c.w};
-  float a = 0.f;
+  float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    u32 P[4];
-    code_pairs(w[d], 0x64646464u, P);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) a = dot2_f16(P[q], X[4 * d + q], a);
+    const u32 lo = w[d] & 0x0F0F0F0Fu, hi = (w[d] >> 4) & 0x0F0F0F0Fu;   // elements 8d + (0,2,4,6) / (1,3,5,7)
+    const f32x2 q02 = codes2_f32<false>(lo), q46 = codes2_f32<true>(lo);
+    const f32x2 q13 = codes2_f32<false>(hi), q57 = codes2_f32<true>(hi);
+    const float* hd = h + 8 * d;
+    a0 = fmaf(q02.x, hd[0], a0); a0 = fmaf(q02.y, hd[2], a0); a0 = fmaf(q46.x, hd[4], a0); a0 = fmaf(q46.y, hd[6], a0);
+    a1 = fmaf(q13.x, hd[1], a1); a1 = fmaf(q13.y, hd[3], a1); a1 = fmaf(q57.x, hd[5], a1); a1 = fmaf(q57.y, hd[7], a1);
   }
-  return a;
+  return a0 + a1;
 }
 
 // ---------------------------------------------------------------- MXFP4
-// gfx950 converts one byte of FP4 E2M1 codes (low nibble first) to a bf16 or
-// fp16 pair, times a power of two taken from the exponent of an fp32
+// gfx950 converts one byte of FP4 E2M1 codes (low nibble first) to a bf16
+// (or fp32) pair, times a power of two taken from the exponent of an fp32
 // operand; with 1.0 the pair holds the exact E2M1 values.
 __device__ __forceinline__ void fp4_pairs_bf16(u32 v, u32* P) {
   P[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0));
   P[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1));
   P[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2));
   P[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3));
-}
-__device__ __forceinline__ void fp4_pairs_f16(u32 v, u32* P) {
-  P[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0));
-  P[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1));
-  P[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2));
-  P[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3));
 }
 
 // sum_i E2M1(q_i) * x_i over one 32-code block; X[i] holds the bf16 pair
@@ -215,18 +222,25 @@ __device__ __forceinline__ float dot_fp4_bf16(const u32x4& c, const u32* X) {
   return a;
 }
 
-// The same with fp16 pairs (h[2i], h[2i+1]).
-__device__ __forceinline__ float dot_fp4_f16(const u32x4& c, const u32* X) {
+// sum_i E2M1(q_i) * h_i over one 32-code block with fp32 h: each byte of
+// codes becomes two exact fp32 values (v_cvt_scalef32_pk_f32_fp4, low nibble
+// first, scale 1), then fused fp32 products and sums.
+__device__ __forceinline__ float dot_fp4_f32(const u32x4& c, const float* h) {
   const u32 w[4] = {c.x, c.y, c.z, c.w};
-  float a = 0.f;
+  float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    u32 P[4];
-    fp4_pairs_f16(w[d], P);
+    const f32x2 v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 0),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 1),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 2),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 3)};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) a = dot2_f16(P[q], X[4 * d + q], a);
+    for (int b = 0; b < 4; ++b) {
+      a0 = fmaf(v[b].x, h[8 * d + 2 * b], a0);
+      a1 = fmaf(v[b].y, h[8 * d + 2 * b + 1], a1);
+    }
   }
-  return a;
+  return a0 + a1;
 }
 
 // E8M0 scale code e in [1, 254] -> 2^(e-127) as fp32 (exact; the packer

@@ -15,7 +15,8 @@
 // the tokens' activations (NT tokens at a time) stay in registers for all
 // its rows. The arithmetic is that of the per-token kernels: gate/up take
 // bf16 activations against codes made exact bf16 values 128 + q, down takes
-// h rounded to fp16 against 1024 + q; products and sums are fp32. The 2*U*NT
+// fp32 h against the exactly converted codes; products and sums are fp32, so
+// h keeps its full range and precision. The 2*U*NT
 // (gate/up) or U*NT (down) partial sums of a lane are reduced over the LPR
 // lanes of its row by a transposed butterfly: at each level a lane keeps one
 // half of its values and swaps the other half with its partner, so after
@@ -103,24 +104,19 @@ __device__ __forceinline__ bool tsum_owner(int lane) {
   return own;
 }
 
-// Position of intermediate row r in an h16 row: element e of each group of 8
-// sits at 2*(e & 3) + (e >> 2), so the 16 bytes of group g are the fp16 pairs
-// (h[8g + c], h[8g + c + 4]), c = 0..3, the operand order of dot_codes_f16.
-__device__ __forceinline__ int pos8(int r) { return (r & ~7) | ((r & 3) << 1) | ((r >> 2) & 1); }
-
 // Slot record written by the dispatch: expert, first expert-sorted pair
 // position, pair count (0 for slots past the last routed expert).
 struct SlotDesc { int e, pos0, n, pad; };
 
 // ------------------------------------------------------------------ gate/up + SiLU
 // Workgroup: 4 waves on rows [r0, r0 + 4*RW) of the expert in slot a, all of
-// its routed pairs, NT at a time; h16[pos * I + pos8(r)] = SiLU(G_e[r]·x_t) *
-// (U_e[r]·x_t) for the pair at expert-sorted position pos, t its token.
+// its routed pairs, NT at a time; h[pos * I + r] = SiLU(G_e[r]·x_t) *
+// (U_e[r]·x_t) (fp32) for the pair at expert-sorted position pos, t its token.
 template <int IPL, int LPR, int U, int NT, int FMT>
 __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const SlotDesc* __restrict__ slots,
-    _Float16* __restrict__ h16, int act) {
+    float* __restrict__ hbuf, int act) {
   constexpr int LG = ilog2(LPR), RPS = WAVE / LPR, RW = RPS * U, V = 2 * U * NT;
   static_assert((1 << LG) == LPR, "LPR must be a power of two");
   const int bpe = I / (4 * RW);                 // workgroups per expert
@@ -227,9 +223,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
     const int idx = tsum_index<V>(lane);
     const int u = (idx >> 1) / NT, tt = (idx >> 1) % NT;
     if (tsum_owner<V, LG>(lane) && !(idx & 1) && tt < nv) {
-      const int r = r0 + u * RPS + rho;
-      // super-blocks: stored as the down kernel's dot2 operand pairs; MXFP4: natural order
-      h16[(size_t)(pos0 + c0 + tt) * I + (FMT == FMT_MXFP4 ? r : pos8(r))] = (_Float16)gate_act(s, o, act);
+      hbuf[(size_t)(pos0 + c0 + tt) * I + r0 + u * RPS + rho] = gate_act(s, o, act);
     }
   }
 }
@@ -238,11 +232,12 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
 // Workgroup: 4 waves on output features [n0, n0 + 4*RW) of the expert in
 // slot a; one 32-code sub-block of the row per lane (lanes with j >= I/32
 // hold nothing); ypair[p * H + f] = D_e[f]·h_p for each of the expert's pairs
-// p = t*k + s.
+// p = t*k + s, with fp32 h (32 values per lane and token, NT tokens at a
+// time).
 template <int LPR, int U, int NT, int FMT>
 __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I,
-    const int32_t* __restrict__ pairs, const SlotDesc* __restrict__ slots, const _Float16* __restrict__ h16,
+    const int32_t* __restrict__ pairs, const SlotDesc* __restrict__ slots, const float* __restrict__ hbuf,
     float* __restrict__ ypair) {
   constexpr int LG = ilog2(LPR), RPS = WAVE / LPR, RW = RPS * U, V = U * NT;
   static_assert((1 << LG) == LPR, "LPR must be a power of two");
@@ -260,12 +255,12 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
   // the first chunk's h before the weights: a wait for a later load would
   // also wait for the weights
   const int jh = has ? j : 0;             // lanes past the row read its first block (in bounds)
-  u32x4 hq[NT][4];
+  u32x4 hq[NT][8];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt)
     if (tt < n)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) hq[tt][g] = load16(h16 + (size_t)(pos0 + tt) * I + 32 * jh + 8 * g);
+      for (int g = 0; g < 8; ++g) hq[tt][g] = load16(hbuf + (size_t)(pos0 + tt) * I + 32 * jh + 4 * g);
   using Hdr = std::conditional_t<FMT == FMT_MXFP4, u32, u32x4>;
   u32x4 cd[U];
   Hdr hd[U];
@@ -277,24 +272,24 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
     else hd[u] = has ? load_nt(row + hdr) : u32x4{0u, 0u, 0u, 0u};
   }
   __builtin_amdgcn_sched_barrier(0);
-  const u32 ONES = 0x3C003C00u;           // fp16 (1, 1)
   for (int c0 = 0; c0 < n; c0 += NT) {
     const int nv = min(NT, n - c0);
-    u32 X[NT][16];
+    float X[NT][32];
     float S[NT];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       if (tt < nv) {
-        const _Float16* hp = h16 + (size_t)(pos0 + c0 + tt) * I + 32 * jh;
+        const float* hp = hbuf + (size_t)(pos0 + c0 + tt) * I + 32 * jh;
         float s = 0.f;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x4 r = c0 == 0 ? hq[tt][g] : load16(hp + 8 * g);
-          X[tt][4 * g + 0] = r.x; X[tt][4 * g + 1] = r.y; X[tt][4 * g + 2] = r.z; X[tt][4 * g + 3] = r.w;
-          if constexpr (FMT != FMT_MXFP4) {    // the super-block min term needs sum(h)
-            s = dot2_f16(r.x, ONES, s); s = dot2_f16(r.y, ONES, s);
-            s = dot2_f16(r.z, ONES, s); s = dot2_f16(r.w, ONES, s);
-          }
+        for (int g = 0; g < 8; ++g) {
+          const u32x4 r = c0 == 0 ? hq[tt][g] : load16(hp + 4 * g);
+          X[tt][4 * g + 0] = as_f32(r.x); X[tt][4 * g + 1] = as_f32(r.y);
+          X[tt][4 * g + 2] = as_f32(r.z); X[tt][4 * g + 3] = as_f32(r.w);
+        }
+        if constexpr (FMT != FMT_MXFP4) {          // the super-block min term needs sum(h)
+#pragma unroll
+          for (int c = 0; c < 32; ++c) s += X[tt][c];
         }
         S[tt] = s;
       }
@@ -309,12 +304,12 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
         const float sc = e8m0_scale(hd[u]);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
-          if (tt < nv) v[u * NT + tt] = sc * dot_fp4_f16(cd[u], X[tt]);
+          if (tt < nv) v[u * NT + tt] = sc * dot_fp4_f32(cd[u], X[tt]);
       } else {
         const Affine af = header_affine(hd[u], j & 7);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
-          if (tt < nv) v[u * NT + tt] = af.a * dot_codes_f16(cd[u], X[tt]) - (1024.f * af.a + af.b) * S[tt];
+          if (tt < nv) v[u * NT + tt] = fmaf(af.a, dot_codes_f32(cd[u], X[tt]), -af.b * S[tt]);
       }
     }
     const float s = tsum<V, LG>(v);
@@ -326,51 +321,52 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
 
 template <int IPL, int LPR, int U, int NT, int FMT>
 static hipError_t gateup_go(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
-                            const SlotDesc* slots, _Float16* h16, int nslots, hipStream_t s) {
+                            const SlotDesc* slots, float* hbuf, int nslots, hipStream_t s) {
   constexpr int RW = (WAVE / LPR) * U;
   static_assert(RW <= 64, "four waves of RW rows must divide a multiple of 256");
   const long long blocks = (long long)nslots * (d.I / (4 * RW));
   hipLaunchKernelGGL((gateup_egemv_kernel<IPL, LPR, U, NT, FMT>), dim3((unsigned)blocks), dim3(BLOCK), 0, s,
-                     layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, slots, h16,
+                     layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, slots, hbuf,
                      d.act);
   return hipGetLastError();
 }
 
 template <int LPR, int U, int NT, int FMT>
 static hipError_t down_go(const Layout& d, const uint8_t* layer, const int32_t* pairs, const SlotDesc* slots,
-                          const _Float16* h16, float* ypair, int nslots, hipStream_t s) {
+                          const float* hbuf, float* ypair, int nslots, hipStream_t s) {
   constexpr int RW = (WAVE / LPR) * U;
   static_assert(RW <= 64, "four waves of RW rows must divide a multiple of 256");
   const long long blocks = (long long)nslots * (d.H / (4 * RW));
   hipLaunchKernelGGL((down_egemv_kernel<LPR, U, NT, FMT>), dim3((unsigned)blocks), dim3(BLOCK), 0, s, layer + d.dn_off,
-                     d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, pairs, slots, h16, ypair);
+                     d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, pairs, slots, hbuf, ypair);
   return hipGetLastError();
 }
 
-// Token chunk NT of both kernels: 2 while the routed experts average at most
-// 2 pairs (fewer registers, more waves in flight), else 4.
+// Token chunk NT of the gate/up kernel: 2 while the routed experts average
+// at most 2 pairs (fewer registers, more waves in flight), else 4; the down
+// kernel, whose fp32 h takes 32 registers per token, walks 2 at a time.
 template <int NT, int FMT>
 static hipError_t egemv_go(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* pairs,
-                           const SlotDesc* slots, _Float16* h16, float* ypair, int nslots, hipStream_t s) {
+                           const SlotDesc* slots, float* hbuf, float* ypair, int nslots, hipStream_t s) {
   hipError_t e;
   // gate/up: the per-token kernel's lane mapping of a hidden-size row
   switch (d.H) {
-    case 256: e = gateup_go<1, 8, 2, 2, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
-    case 512: e = gateup_go<1, 16, 2, NT, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
-    case 1024: e = gateup_go<1, 32, 4, NT, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
-    case 2048: e = gateup_go<1, 64, 4, NT, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
-    case 4096: e = gateup_go<2, 64, 2, 2, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
-    case 6144: e = gateup_go<3, 64, 1, 1, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
-    case 8192: e = gateup_go<4, 64, 1, 1, FMT>(d, layer, x, pairs, slots, h16, nslots, s); break;
+    case 256: e = gateup_go<1, 8, 2, 2, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
+    case 512: e = gateup_go<1, 16, 2, NT, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
+    case 1024: e = gateup_go<1, 32, 4, NT, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
+    case 2048: e = gateup_go<1, 64, 4, NT, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
+    case 4096: e = gateup_go<2, 64, 2, 2, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
+    case 6144: e = gateup_go<3, 64, 1, 1, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
+    case 8192: e = gateup_go<4, 64, 1, 1, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
   // down: a power-of-two lane group covering the I/32 sub-blocks of a row
   const int nsb = d.I / 32;
-  if (nsb <= 8) return down_go<8, 2, NT, FMT>(d, layer, pairs, slots, h16, ypair, nslots, s);
-  if (nsb <= 16) return down_go<16, 4, NT, FMT>(d, layer, pairs, slots, h16, ypair, nslots, s);
-  if (nsb <= 32) return down_go<32, 4, NT, FMT>(d, layer, pairs, slots, h16, ypair, nslots, s);
-  return down_go<64, 4, NT, FMT>(d, layer, pairs, slots, h16, ypair, nslots, s);
+  if (nsb <= 8) return down_go<8, 2, 2, FMT>(d, layer, pairs, slots, hbuf, ypair, nslots, s);
+  if (nsb <= 16) return down_go<16, 4, 2, FMT>(d, layer, pairs, slots, hbuf, ypair, nslots, s);
+  if (nsb <= 32) return down_go<32, 4, 2, FMT>(d, layer, pairs, slots, hbuf, ypair, nslots, s);
+  return down_go<64, 4, 2, FMT>(d, layer, pairs, slots, hbuf, ypair, nslots, s);
 }
 
 }  // namespace egemv
@@ -378,7 +374,7 @@ static hipError_t egemv_go(const Layout& d, const uint8_t* layer, const uint16_t
 bool egemv_supported(const Layout& d) { return d.I <= 2048; }
 
 hipError_t launch_egemv_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
-                            const int32_t* pairs, const void* slot_desc, _Float16* h16, float* ypair, float* out,
+                            const int32_t* pairs, const void* slot_desc, float* hbuf, float* ypair, float* out,
                             int T, hipStream_t s) {
   using namespace egemv;
   if (!egemv_supported(d)) return hipErrorInvalidValue;
@@ -388,11 +384,11 @@ hipError_t launch_egemv_ffn(const Layout& d, const uint8_t* layer, const uint16_
   const SlotDesc* slots = static_cast<const SlotDesc*>(slot_desc);
   hipError_t e;
   if (d.fmt == FMT_MXFP4)
-    e = P <= 2 * d.E ? egemv_go<2, FMT_MXFP4>(d, layer, x, pairs, slots, h16, ypair, nslots, s)
-                     : egemv_go<4, FMT_MXFP4>(d, layer, x, pairs, slots, h16, ypair, nslots, s);
+    e = P <= 2 * d.E ? egemv_go<2, FMT_MXFP4>(d, layer, x, pairs, slots, hbuf, ypair, nslots, s)
+                     : egemv_go<4, FMT_MXFP4>(d, layer, x, pairs, slots, hbuf, ypair, nslots, s);
   else
-    e = P <= 2 * d.E ? egemv_go<2, FMT_Q4K>(d, layer, x, pairs, slots, h16, ypair, nslots, s)
-                     : egemv_go<4, FMT_Q4K>(d, layer, x, pairs, slots, h16, ypair, nslots, s);
+    e = P <= 2 * d.E ? egemv_go<2, FMT_Q4K>(d, layer, x, pairs, slots, hbuf, ypair, nslots, s)
+                     : egemv_go<4, FMT_Q4K>(d, layer, x, pairs, slots, hbuf, ypair, nslots, s);
   if (e != hipSuccess) return e;
   return launch_combine(d, ypair, w, out, T, s);
 }

@@ -19,6 +19,8 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_device.h"
 
 namespace qmoe {
@@ -353,15 +355,15 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
 // G = k*I/32 <= 256 items. A block computes R consecutive output rows of one
 // token; wave w takes the contiguous item range [w*IW, (w+1)*IW), IW =
 // ceil(G/4) <= 64, one item per lane, for all R rows, so a lane loads its
-// 32 values of h once (straight into registers) and one 16-byte code chunk
-// and header per row. The routing is read directly, so the weight loads
-// leave as soon as the expert ids arrive. The four wave partials of a row are
-// added in wave order. h is rounded to fp16 for v_dot2_f32_f16 (relative
-// rounding 2^-11 per value); products and sums are fp32.
+// 32 values of h once (fp32, straight into registers) and one 16-byte code
+// chunk and header per row. The routing is read directly, so the weight
+// loads leave as soon as the expert ids arrive. The four wave partials of a
+// row are added in wave order. h stays fp32: the codes are converted exactly
+// and every product and sum is an fp32 operation, so h keeps its full range
+// and precision.
 // y[t*H + n] = sum_s w_s * D_{e_s}[n]·h_{t,s}. With MXFP4 weights an item's
-// 32 codes share one E8M0 scale byte and the fp16 pairs of h are in natural
-// order.
-template <int R, int FMT, int PH>
+// 32 codes share one E8M0 scale byte.
+template <int R, int FMT>
 __global__ __launch_bounds__(BLOCK) void down_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I, int k,
     const int32_t* __restrict__ ids, const float* __restrict__ wts, const float* __restrict__ h,
@@ -389,71 +391,36 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
 #pragma unroll
   for (int c = 0; c < 8; ++c) hr[c] = valid ? load16(hp + 4 * c) : u32x4{0u, 0u, 0u, 0u};
   const uint8_t* row0 = dn + (size_t)e * dn_expert_bytes + (size_t)n0 * drow_bytes;
+  using Hdr = std::conditional_t<FMT == FMT_MXFP4, u32, u32x4>;
+  u32x4 cd[R];
+  Hdr hd[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint8_t* row = row0 + (size_t)r * drow_bytes;
+    cd[r] = load_nt(row + 16 * j);
+    if constexpr (FMT == FMT_MXFP4) hd[r] = __builtin_nontemporal_load(row + I / 2 + j);
+    else hd[r] = load_nt(row + I / 2 + QHDR * (j >> 3));
+  }
+  // every weight load in flight before the first use of h
+  __builtin_amdgcn_sched_barrier(0);
+  float hv[32];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    hv[4 * c] = as_f32(hr[c].x); hv[4 * c + 1] = as_f32(hr[c].y);
+    hv[4 * c + 2] = as_f32(hr[c].z); hv[4 * c + 3] = as_f32(hr[c].w);
+  }
   float p[R];
   if constexpr (FMT == FMT_MXFP4) {
-    u32x4 cd[R];
-    u32 sd[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) p[r] = group_sum<WAVE>(ws * (e8m0_scale(hd[r]) * dot_fp4_f32(cd[r], hv)));
+  } else {
+    float S = 0.f;                                 // sum of the sub-block's h (the min term)
+#pragma unroll
+    for (int c = 0; c < 32; ++c) S += hv[c];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const uint8_t* row = row0 + (size_t)r * drow_bytes;
-      cd[r] = load_nt(row + 16 * j);
-      sd[r] = __builtin_nontemporal_load(row + I / 2 + j);
-    }
-    // every weight load in flight before the h conversion waits for h
-    __builtin_amdgcn_sched_barrier(0);
-    u32 X[16];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const u32 v[4] = {hr[c].x, hr[c].y, hr[c].z, hr[c].w};
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const _Float16 lo = (_Float16)as_f32(v[2 * m]), hi = (_Float16)as_f32(v[2 * m + 1]);
-        X[2 * c + m] = (u32)__builtin_bit_cast(unsigned short, lo) | ((u32)__builtin_bit_cast(unsigned short, hi) << 16);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) p[r] = group_sum<WAVE>(ws * (e8m0_scale(sd[r]) * dot_fp4_f16(cd[r], X)));
-  } else {
-    // the rows in PH phases: a phase's loads are issued once the previous
-    // phase's rows are summed (measured faster than all 2R loads at once)
-    const int hdr = I / 2 + QHDR * (j >> 3);
-    u32x4 cd[R], hd[R];
-    u32 X[16];
-    float S = 0.f;
-#pragma unroll
-    for (int ph = 0; ph < PH; ++ph) {
-#pragma unroll
-      for (int r = ph * (R / PH); r < (ph + 1) * (R / PH); ++r) {
-        const uint8_t* row = row0 + (size_t)r * drow_bytes;
-        cd[r] = load_nt(row + 16 * j);
-        hd[r] = load_nt(row + hdr);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (ph == 0) {
-        // h -> fp16 pairs in nibble order; S is the sum of the rounded values
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const u32 v[8] = {hr[2 * d].x, hr[2 * d].y, hr[2 * d].z, hr[2 * d].w,
-                            hr[2 * d + 1].x, hr[2 * d + 1].y, hr[2 * d + 1].z, hr[2 * d + 1].w};
-          _Float16 hh[8];
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            hh[c] = (_Float16)as_f32(v[c]);
-            S += (float)hh[c];
-          }
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            X[4 * d + c] = (u32)__builtin_bit_cast(unsigned short, hh[c]) |
-                           ((u32)__builtin_bit_cast(unsigned short, hh[c + 4]) << 16);
-        }
-      }
-#pragma unroll
-      for (int r = ph * (R / PH); r < (ph + 1) * (R / PH); ++r) {
-        const Affine a = header_affine(hd[r], j & 7);
-        const float dq = dot_codes_f16(cd[r], X);
-        p[r] = group_sum<WAVE>(ws * (a.a * dq - (1024.f * a.a + a.b) * S));
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      const Affine a = header_affine(hd[r], j & 7);
+      p[r] = group_sum<WAVE>(ws * fmaf(a.a, dot_codes_f32(cd[r], hv), -a.b * S));
     }
   }
   if (lane == 0) {
@@ -469,9 +436,13 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
 
 // ------------------------------------------------------------------ standalone residual + RMSNorm
 // One block per token: v = x + y (fp32), x_next = bf16(v / sqrt(mean(v^2) + eps)),
-// in the element order of the router prologue (H a multiple of 4).
-__global__ __launch_bounds__(BLOCK) void resid_norm_kernel(const uint16_t* __restrict__ x, const float* __restrict__ y,
-                                                           uint16_t* __restrict__ xn, int H, float eps) {
+// in the element order of the router prologue (H a multiple of 4). xn may be
+// x itself (a one-layer stack writes the next step's input in place): every
+// element is read by the thread that writes it, and the first pass's reads
+// complete before the block barrier inside the sum, so x and xn are not
+// declared restrict.
+__global__ __launch_bounds__(BLOCK) void resid_norm_kernel(const uint16_t* x, const float* __restrict__ y, uint16_t* xn,
+                                                           int H, float eps) {
   __shared__ float part[BLOCK / WAVE];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -526,11 +497,9 @@ __device__ __forceinline__ void excl_scan256x2(int a, int b, int& ea, int& eb, i
 
 // Single block of 1024 threads (16 waves). counts[e] = #pairs routed to e,
 // offsets = exclusive scan (E+1 entries), pairs = pair indices p = t*k+s
-// ordered by (expert, p), and the batched paths' work list: the tiles of
-// mt pairs of each expert, either as tile_off, the exclusive scan of
-// ceil(counts[e] / mt) (E+1 entries), or as slots, one record {e, first
-// pair position, pairs} per tile in expert order, then zero records up to
-// max_slots.
+// ordered by (expert, p), and (slots given) the batched paths' work list:
+// one record {e, first pair position, pairs} per tile of mt pairs in expert
+// order, then zero records up to max_slots.
 // Deterministic: ranks come from ballots, not from the order of atomics.
 // NPL: a wave's ids are read NPL per lane at a time, all loads in flight
 // before the first use (32 for large P; 1, the plain loop, for small P,
@@ -540,7 +509,6 @@ constexpr int DISP_WAVES = DISP_THREADS / WAVE;
 template <int NPL>
 __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
                                                                 int32_t* __restrict__ offsets, int32_t* __restrict__ pairs,
-                                                                int32_t* __restrict__ tile_off,
                                                                 int4* __restrict__ slots, int E, int P, int mt,
                                                                 int max_slots) {
   __shared__ int cnt[DISP_WAVES][256];
@@ -577,15 +545,11 @@ __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* _
   if (tid < E) {
     counts[tid] = tot;
     offsets[tid] = ex_tot;
-    if (tile_off) tile_off[tid] = ex_tiles;
     if (slots)
       for (int q = 0; q < tiles; ++q) slots[ex_tiles + q] = make_int4(tid, ex_tot + q * mt, min(mt, tot - q * mt), 0);
     for (int w = 0; w < DISP_WAVES; ++w) cnt[w][tid] += ex_tot;
   }
-  if (tid == 0) {
-    offsets[E] = all_tot;
-    if (tile_off) tile_off[E] = all_tiles;
-  }
+  if (tid == 0) offsets[E] = all_tot;
   if (slots)
     for (int i = all_tiles + tid; i < max_slots; i += DISP_THREADS) slots[i] = make_int4(0, 0, 0, 0);
   __syncthreads();
@@ -762,10 +726,10 @@ hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids
   if (d.k * (d.I / 32) > 4 * WAVE || d.H % RM) return hipErrorInvalidValue;
   if (T <= 0) return hipSuccess;
   if (d.fmt == FMT_MXFP4)
-    hipLaunchKernelGGL((down_kernel<RM, FMT_MXFP4, 1>), dim3(T * (d.H / RM)), dim3(BLOCK), 0, s, layer + d.dn_off,
+    hipLaunchKernelGGL((down_kernel<RM, FMT_MXFP4>), dim3(T * (d.H / RM)), dim3(BLOCK), 0, s, layer + d.dn_off,
                        d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
   else
-    hipLaunchKernelGGL((down_kernel<RQ, FMT_Q4K, 1>), dim3(T * (d.H / RQ)), dim3(BLOCK), 0, s, layer + d.dn_off,
+    hipLaunchKernelGGL((down_kernel<RQ, FMT_Q4K>), dim3(T * (d.H / RQ)), dim3(BLOCK), 0, s, layer + d.dn_off,
                        d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
   return hipGetLastError();
 }
@@ -776,24 +740,23 @@ hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y,
 }
 
 hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* pairs, int T,
-                           hipStream_t s, int32_t* tile_off, int mt, void* slots, int max_slots) {
-  if (mt < 1 || (tile_off && slots)) return hipErrorInvalidValue;
+                           hipStream_t s, int mt, void* slots, int max_slots) {
+  if (mt < 1) return hipErrorInvalidValue;
   // the slot records must cover every tile: at most ceil(T*k / mt) + min(E, T*k)
   const int P = T * d.k;
   if (slots && max_slots < (P + mt - 1) / mt + (P < d.E ? P : d.E)) return hipErrorInvalidValue;
   if (P > 4 * DISP_THREADS)
-    hipLaunchKernelGGL((dispatch_kernel<32>), dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs, tile_off,
+    hipLaunchKernelGGL((dispatch_kernel<32>), dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs,
                        static_cast<int4*>(slots), d.E, P, mt, slots ? max_slots : 0);
   else
-    hipLaunchKernelGGL((dispatch_kernel<1>), dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs, tile_off,
+    hipLaunchKernelGGL((dispatch_kernel<1>), dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs,
                        static_cast<int4*>(slots), d.E, P, mt, slots ? max_slots : 0);
   return hipGetLastError();
 }
 
 // The batched paths' work list from given dispatch offsets (E+1 entries),
 // as the dispatch kernel writes it. One block of 256 threads.
-__global__ __launch_bounds__(BLOCK) void work_list_kernel(const int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ tile_off, int4* __restrict__ slots,
+__global__ __launch_bounds__(BLOCK) void work_list_kernel(const int32_t* __restrict__ offsets, int4* __restrict__ slots,
                                                          int E, int mt, int max_slots) {
   __shared__ int wsum[8];
   const int tid = threadIdx.x;
@@ -801,23 +764,18 @@ __global__ __launch_bounds__(BLOCK) void work_list_kernel(const int32_t* __restr
   const int units = (n + mt - 1) / mt;
   int ex, ex2, tot, tot2;
   excl_scan256x2(units, 0, ex, ex2, tot, tot2, wsum);
-  if (tid < E) {
-    if (tile_off) tile_off[tid] = ex;
-    if (slots)
-      for (int q = 0; q < units; ++q) slots[ex + q] = make_int4(tid, offsets[tid] + q * mt, min(mt, n - q * mt), 0);
-  }
-  if (tid == 0 && tile_off) tile_off[E] = tot;
-  if (slots)
-    for (int i = tot + tid; i < max_slots; i += BLOCK) slots[i] = make_int4(0, 0, 0, 0);
+  if (tid < E)
+    for (int q = 0; q < units; ++q) slots[ex + q] = make_int4(tid, offsets[tid] + q * mt, min(mt, n - q * mt), 0);
+  for (int i = tot + tid; i < max_slots; i += BLOCK) slots[i] = make_int4(0, 0, 0, 0);
 }
 
-hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int T, int32_t* tile_off, int mt, void* slots,
-                            int max_slots, hipStream_t s) {
-  if ((!tile_off) == (!slots) || mt < 1) return hipErrorInvalidValue;
+hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int T, int mt, void* slots, int max_slots,
+                            hipStream_t s) {
+  if (!slots || mt < 1) return hipErrorInvalidValue;
   const int P = T * d.k;
-  if (slots && max_slots < (P + mt - 1) / mt + (P < d.E ? P : d.E)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(work_list_kernel, dim3(1), dim3(BLOCK), 0, s, offsets, tile_off, static_cast<int4*>(slots), d.E,
-                     mt, slots ? max_slots : 0);
+  if (max_slots < (P + mt - 1) / mt + (P < d.E ? P : d.E)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(work_list_kernel, dim3(1), dim3(BLOCK), 0, s, offsets, static_cast<int4*>(slots), d.E, mt,
+                     max_slots);
   return hipGetLastError();
 }
 

@@ -77,7 +77,7 @@ struct BlobHeader {
 
 // Scratch carve-up for T tokens (offsets 256-aligned).
 struct Scratch {
-  size_t logits, ids, w, h, counts, offsets, pairs, tile_off, slots, h16, ypair, total;
+  size_t logits, ids, w, h, counts, offsets, pairs, slots, hbuf, ypair, total;
   void init(const Layout& d, int T) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
@@ -88,12 +88,12 @@ struct Scratch {
     counts = take((size_t)d.E * 4);
     offsets = take((size_t)(d.E + 1) * 4);
     pairs = take((size_t)T * d.k * 4);
-    tile_off = take((size_t)(d.E + 1) * 4);
     // work records {expert, first pair, pairs}: one per routed expert, or per 16-pair tile
     slots = take((size_t)((T * d.k + 15) / 16 + d.E) * 16);
-    // batched paths only (T > 1): fp16 h in expert-sorted pair order (MXFP4 on
-    // the 16-pair tiles: bf16 hi and lo planes), one fp32 output row per pair
-    h16 = take(T > 1 ? (size_t)T * d.k * d.I * (d.fmt == FMT_MXFP4 ? 4 : 2) : 0);
+    // batched paths only (T > 1): h in expert-sorted pair order, 4 bytes per
+    // value (fp32 on the expert-major GEMV, bf16 hi and lo planes on the MFMA
+    // tiles), and one fp32 output row per pair
+    hbuf = take(T > 1 ? (size_t)T * d.k * d.I * 4 : 0);
     ypair = take(T > 1 ? (size_t)T * d.k * d.H * 4 : 0);
     total = o;
   }
@@ -118,30 +118,23 @@ hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids
 hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y, uint16_t* x_next, int T,
                              hipStream_t s);
 // Batched-path work lists, written by the dispatch or, from given dispatch
-// lists, by launch_work_list: the tiles of mt pairs of every expert, as
-// tile_off (exclusive scan of ceil(counts[e] / mt), E+1 entries) or as slots,
-// one record {expert, first pair position, pairs} per tile in expert order
-// followed by {0, 0, 0} records up to max_slots (at least ceil(T*k / mt) +
-// min(E, T*k)).
+// lists, by launch_work_list: slot records {expert, first pair position,
+// pairs}, one per tile of mt pairs of every expert in expert order (mt = T*k:
+// one per routed expert), followed by {0, 0, 0} records up to max_slots (at
+// least ceil(T*k / mt) + min(E, T*k)).
 hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets,
-                           int32_t* pairs, int T, hipStream_t s, int32_t* tile_off = nullptr, int mt = 1,
-                           void* slots = nullptr, int max_slots = 0);
-hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int T, int32_t* tile_off, int mt, void* slots,
-                            int max_slots, hipStream_t s);
+                           int32_t* pairs, int T, hipStream_t s, int mt = 1, void* slots = nullptr, int max_slots = 0);
+hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int T, int mt, void* slots, int max_slots,
+                            hipStream_t s);
 
-// grouped MFMA path (T > 1)
-int grouped_mt(const Layout& d, int T);          // pairs per tile of the grouped GEMMs for a T-token call
-int grouped_max_tiles(const Layout& d, int T);
-hipError_t launch_grouped_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
-                              const int32_t* offsets, const int32_t* pairs, const int32_t* tile_off, _Float16* h16,
-                              float* ypair, float* out, int T, hipStream_t s);
-// 16-pair MFMA tiles with every weight load in flight (T > 1, a few to a
-// few dozen pairs per expert); tiles = slot records of mt = 16
+// MFMA tiles of 16, 64 or 128 pairs (T > 1; hidden 512, 1024 or 2048, inter
+// <= 1024); tiles = slot records of g16_mt pairs. hb: h as bf16 hi and lo
+// planes (T*k*I values each).
 bool g16_supported(const Layout& d);
 int g16_mt(const Layout& d, int T);
 int g16_max_tiles(const Layout& d, int T);
 hipError_t launch_g16_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
-                          const int32_t* pairs, const void* tiles, _Float16* h16, float* ypair, float* out, int T,
+                          const int32_t* pairs, const void* tiles, uint16_t* hb, float* ypair, float* out, int T,
                           hipStream_t s);
 // out[t] = sum_s w[t][s] * ypair[t*k + s], slot order
 hipError_t launch_combine(const Layout& d, const float* ypair, const float* w, float* out, int T, hipStream_t s);
@@ -149,7 +142,7 @@ hipError_t launch_combine(const Layout& d, const float* ypair, const float* w, f
 // expert-major GEMV path (T > 1, few pairs per expert); slots from the dispatch
 bool egemv_supported(const Layout& d);
 hipError_t launch_egemv_ffn(const Layout& d, const uint8_t* layer, const uint16_t* x, const float* w,
-                            const int32_t* pairs, const void* slots, _Float16* h16, float* ypair, float* out,
+                            const int32_t* pairs, const void* slots, float* hbuf, float* ypair, float* out,
                             int T, hipStream_t s);
 
 }  // namespace qmoe

@@ -58,6 +58,10 @@ def test_status_strings():
     ((2048, 128, 8, 768, 1, 1, 0x24, 1e-6), True),  # MXFP4 with the expert-major GEMV forced
     ((256, 8, 2, 2304, 1, 1, 0x24, 1e-6), False),   # ... which needs inter <= 2048
     ((2048, 128, 8, 768, 1, 1, 0x40, 1e-6), False), # unknown flag
+    ((2048, 128, 8, 768, 1, 1, 0x2, 1e-6), True),   # MFMA tiles forced
+    ((4096, 32, 4, 512, 1, 1, 0x2, 1e-6), False),   # ... which hidden 4096 does not have
+    ((2048, 128, 8, 768, 1, 131071, 0, 1e-6), True),   # T*k*max(H, I) just below 2^31
+    ((2048, 128, 8, 768, 1, 131072, 0, 1e-6), False),  # ... and at 2^31 (32-bit device indexing)
     ((300, 8, 2, 512, 1, 1, 0, 1e-6), False),       # hidden not a multiple of 256
     ((768, 8, 2, 512, 1, 1, 0, 1e-6), False),       # hidden lane mapping unsupported
     ((256, 8, 9, 512, 1, 1, 0, 1e-6), False),       # k > E

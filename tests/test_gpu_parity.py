@@ -9,7 +9,8 @@ import torch
 import oracle
 import synth
 import quantized_moe_decode_gemv_amd as q
-from helpers import REL_TOL, check_bf16_vector, check_routing, layer_source, rel_err
+from helpers import (REL_TOL, check_bf16_vector, check_outputs, check_routing, layer_source, reference_outputs,
+                     rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,16 +64,18 @@ def qwen(dev):
     return Setup(synth.QWEN3_30B_A3B, dev, n_layers=1, max_tokens=256)
 
 
-def _check_layer(setup, xb, got, layer=0, exact=False, sample=None):
-    """Routing and output of the tokens in `sample` (default: all) against the oracle."""
+def _check_layer(setup, xb, got, layer=0, exact=False, sample=None, act=oracle.ACT_SILU, src=None, label=""):
+    """Routing and output of the tokens in `sample` (default: all) against the
+    oracle; every token's output is compared (a near-tie token under the
+    GPU's own selection)."""
+    src = setup.src if src is None else src
     if sample is not None:
         xb = xb[sample]
         got = {key: val[sample] for key, val in got.items()}
-    ref = oracle.moe_layer(setup.src, layer, xb)
-    exempt = check_routing(got["ids"], got["w"], ref, exact=exact)
-    keep = [t for t in range(xb.shape[0]) if t not in exempt]
-    err = rel_err(got["y"][keep], ref["y"][keep])
-    assert err <= REL_TOL, f"max|err|/max|ref| = {err:.3e}"
+    ref = oracle.moe_layer(src, layer, xb, act=act)
+    exempt = check_routing(got["ids"], got["w"], ref, exact=exact, label=label)
+    yref = reference_outputs(src, layer, xb, ref, got["ids"], exempt, act=act)
+    err = check_outputs(got["y"], yref, label=label)
     return ref, err, exempt
 
 
@@ -221,28 +224,29 @@ def test_zipf_skewed_prefill_4096_grouped(qwen):
           f"sampled {len(sample)} tokens, max|err|/max|ref| = {err:.3e}")
 
 
-def test_forward_batched_auto_grouped_tiny(tiny):
-    """moe_forward with T*k > 8*E (40 tokens, 80 pairs over 8 experts) takes
-    the grouped path on its own (router GEMV, top-k, dispatch, grouped GEMMs,
-    combine) and keeps the norm epilogue."""
+def test_forward_batched_auto_batched_path_tiny(tiny):
+    """moe_forward with T*k > 8*E (40 tokens, 80 pairs over 8 experts) on
+    the tiny layer (hidden 256, which has no MFMA tiles) takes the
+    expert-major GEMV on its own (router GEMV, top-k, dispatch, expert-major
+    GEMVs, combine) and keeps the norm epilogue."""
     S = tiny.shape
     xb = synth.x_bf16(S, 9, 40, T=40)
     got = tiny.forward(xb, with_next=True)
     ref, err, exempt = _check_layer(tiny, xb, got)
+    yref = reference_outputs(tiny.src, 0, xb, ref, got["ids"], exempt)
     for t in range(40):
-        if t in exempt:
-            continue
-        _, ref_next = oracle.resid_rmsnorm(xb[t], ref["y"][t])
+        _, ref_next = oracle.resid_rmsnorm(xb[t], yref[t])
         check_bf16_vector(got["xn"][t], ref_next)
 
 
-@pytest.mark.parametrize("T", [1, 7, 8, 16, 17, 192, 193])
+@pytest.mark.parametrize("T", [1, 7, 8, 16, 17, 96, 97, 192, 193])
 def test_forward_auto_path_boundary_qwen(qwen, T):
     """Without flags moe_forward runs the per-token GEMV path while T*k < E/2
-    (T <= 7 here), the expert-major GEMV path while T*k <= E (T <= 16), the
-    grouped GEMMs on 16-pair tiles while T*k <= 12E (T <= 192) and on 32-pair
-    tiles beyond: both sides of each switch against the oracle (every 3rd
-    token and the last above 16 tokens)."""
+    (T <= 7 here), the expert-major GEMV path while T*k <= E (T <= 16), then
+    the MFMA tiles: multi-row kernels up to 6 pairs per expert (T <= 96), the
+    multi-row gate/up on 64-pair tiles up to 12 (T <= 192) and the
+    K-outermost gate/up beyond: both sides of each switch against the oracle
+    (every 3rd token and the last above 16 tokens)."""
     xb = synth.x_bf16(qwen.shape, 10, T, T=T)
     sample = None if T <= 16 else sorted(set(range(0, T, 3)) | {T - 1})
     _check_layer(qwen, xb, qwen.forward(xb), sample=sample)
@@ -274,37 +278,96 @@ def _forward_with(plan, blob, xb, S, dev):
 def test_gate_activations_every_path_qwen(qwen, name, flag, act, scale):
     """Each non-default gate activation on every path of the Qwen3-30B-A3B-
     shaped layer: one token (fused per-token GEMV), 8 tokens (expert-major
-    GEMV, and the per-token GEMV forced), 32 (16-pair MFMA tiles) and 256
-    (32-pair tiles), against the oracle with the same activation. Scaling x
-    by 8 (exact in bf16) puts the gate values past the SwiGLU clamps for a
-    good share of rows."""
+    GEMV, and the per-token GEMV forced), 32 (multi-row MFMA tiles) and 256
+    (K-outermost MFMA tiles), against the oracle with the same activation.
+    Scaling x by 8 (exact in bf16) puts the gate values past the SwiGLU
+    clamps for a good share of rows."""
     S = qwen.shape
     for T, extra in ((1, 0), (8, 0), (8, q.FLAG_FORCE_GEMV), (32, 0), (256, 0)):
         plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=T, flags=flag | extra)
         xb = _scaled_bf16(synth.x_bf16(S, 13, T, T=T), scale)
         got = _forward_with(plan, qwen.blob, xb, S, qwen.dev)
         sample = list(range(T)) if T <= 32 else list(range(0, T, 8)) + [T - 1]
-        ref = oracle.moe_layer(qwen.src, 0, xb[sample], act=act)
-        exempt = check_routing(got["ids"][sample], got["w"][sample], ref)
-        keep = [i for i in range(len(sample)) if i not in exempt]
-        err = rel_err(got["y"][sample][keep], ref["y"][keep])
-        assert err <= REL_TOL, f"{name} x{scale} T={T} flags={extra}: {err:.3e}"
+        _check_layer(qwen, xb, got, sample=sample, act=act, label=f"{name} x{scale} T={T} flags={extra}")
 
 
 @pytest.mark.parametrize("name,flag,act", ACTS, ids=[a[0] for a in ACTS])
 def test_gate_activations_tiny(tiny, name, flag, act):
-    """Tiny layer (hidden 256: no 16-pair tiles): T = 1, 5 (expert-major
-    GEMV) and 40 (32-pair tiles), x scaled by 8."""
+    """Tiny layer (hidden 256: no MFMA tiles): T = 1, 5 and 40 (expert-major
+    GEMV), x scaled by 8."""
     S = tiny.shape
     for T in (1, 5, 40):
         plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=2, max_tokens=T, flags=flag)
         xb = _scaled_bf16(synth.x_bf16(S, 14, T, T=T), 8)
         got = _forward_with(plan, tiny.blob, xb, S, tiny.dev)
-        ref = oracle.moe_layer(tiny.src, 0, xb, act=act)
-        exempt = check_routing(got["ids"], got["w"], ref)
-        keep = [t for t in range(T) if t not in exempt]
-        err = rel_err(got["y"][keep], ref["y"][keep])
-        assert err <= REL_TOL, f"{name} T={T}: {err:.3e}"
+        _check_layer(tiny, xb, got, act=act, label=f"{name} T={T}")
+
+
+# ------------------------------------------------------------------ input range
+# Paths of the Qwen3-30B-A3B-shaped layer and the token counts that reach
+# them with N(0, 1) logits: the fused per-token GEMV (1), the per-token GEMV
+# forced (8), the expert-major GEMV (8), and the MFMA tiles: one 16-pair
+# block per workgroup (16, forced), multi-row (32), above 6 pairs per expert
+# (128: multi-row super-block gate/up, row-split MXFP4 gate/up) and above 12
+# (256: K outermost).
+RANGE_PATHS = ((1, 0), (8, q.FLAG_FORCE_GEMV), (8, q.FLAG_FORCE_EXPERT_GEMV), (16, q.FLAG_FORCE_GROUPED), (32, 0),
+               (128, 0), (256, 0))
+# (activation, exact bf16 scale of x): small and large SiLU inputs, the
+# squared ReLU at 16x and 32x (h beyond the fp16 range), clamped SwiGLU at 32x
+RANGE_CASES = (("silu", 0, oracle.ACT_SILU, 2.0 ** -8), ("silu", 0, oracle.ACT_SILU, 2.0 ** 7),
+               ("relu2", q.FLAG_ACT_RELU2, oracle.ACT_RELU2, 16.0), ("relu2", q.FLAG_ACT_RELU2, oracle.ACT_RELU2, 32.0),
+               ("swiglu_oai", q.FLAG_ACT_SWIGLU_OAI, oracle.ACT_SWIGLU_OAI, 32.0))
+
+
+def _run_path(st, xb, T, flags, lg=None):
+    """Forward through the router GEMV (T = 1) or route from the given fp32
+    logits and run the expert FFN (T > 1) with a plan of these flags."""
+    S = st.shape
+    d = st.dev
+    plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=T, flags=flags)
+    scratch = plan.new_scratch(T, device=d)
+    x = st.xdev(xb)
+    out = torch.empty(T, S.hidden, dtype=torch.float32, device=d)
+    ids = torch.empty(T, S.top_k, dtype=torch.int32, device=d)
+    w = torch.empty(T, S.top_k, dtype=torch.float32, device=d)
+    if lg is None:
+        plan.forward(st.blob, 0, x, T, out, ids=ids, w=w, scratch=scratch)
+    else:
+        counts = torch.empty(S.n_experts, dtype=torch.int32, device=d)
+        offsets = torch.empty(S.n_experts + 1, dtype=torch.int32, device=d)
+        pairs = torch.empty(T * S.top_k, dtype=torch.int32, device=d)
+        plan.route(st.blob, 0, None, torch.from_numpy(lg).to(d), T, ids, w, counts, offsets, pairs, scratch=scratch)
+        plan.expert_ffn(st.blob, 0, x, T, ids, w, out, counts, offsets, pairs, scratch=scratch)
+    torch.cuda.synchronize()
+    return dict(y=out.cpu().numpy(), ids=ids.cpu().numpy(), w=w.cpu().numpy())
+
+
+@pytest.mark.parametrize("case", RANGE_CASES, ids=[f"{c[0]}-x{c[3]:g}" for c in RANGE_CASES])
+@pytest.mark.parametrize("mx", [False, True], ids=["q4k", "mxfp4"])
+def test_input_range_every_path(qwen, mx_qwen, mx, case):
+    """Inputs scaled by exact powers of two on every path and both weight
+    encodings: x * 2^-8 puts SiLU's h around 1e-5 and below (fp16
+    subnormals), x * 2^7 makes g and u large, and the squared ReLU at 16x and
+    32x pushes h past 65504; h, weights and activations must keep their
+    range and precision everywhere. T = 1 routes through the router GEMV;
+    larger T route from shared fp32 logits (ids exact). Sampled tokens of
+    each run against the oracle element by element."""
+    name, flag, act, scale = case
+    st = mx_qwen if mx else qwen
+    S = st.shape
+    fmt = q.FLAG_WEIGHTS_MXFP4 if mx else 0
+    for T, path in RANGE_PATHS:
+        xb = _scaled_bf16(synth.x_bf16(S, 70, T, T=T), scale)
+        lg = None if T == 1 else synth.logits_f32(S, 70, T)
+        got = _run_path(st, xb, T, flag | fmt | path, lg)
+        sample = list(range(T)) if T <= 8 else sorted({0, 1, T // 3, T // 2, T - 2, T - 1})
+        label = f"{'mxfp4' if mx else 'q4k'} {name} x{scale:g} T={T} flags={path:#x}"
+        xs = xb[sample]
+        ref = oracle.moe_layer(st.src, 0, xs, logits=None if lg is None else lg[sample], act=act)
+        g = {key: val[sample] for key, val in got.items()}
+        exempt = check_routing(g["ids"], g["w"], ref, exact=lg is not None, label=label)
+        check_outputs(g["y"], reference_outputs(st.src, 0, xs, ref, g["ids"], exempt, act=act), label=label)
+        assert np.isfinite(got["y"]).all(), label
 
 
 # ------------------------------------------------------------------ routing and dispatch lists
@@ -465,10 +528,16 @@ def test_edge_shapes(dev, shape):
 def test_edge_shapes_batched_paths(dev, shape, path):
     """Each forced path on every edge shape (lane mappings of every hidden and
     intermediate size, k = 1, k = E, many experts); 70 tokens give ragged
-    tiles and multi-chunk experts; on the grouped path 140 more tokens (every
-    7th and the last checked) put most shapes on the 32- or 96-pair tiles."""
+    tiles and multi-chunk experts; on the MFMA tiles 140 more tokens (every
+    7th and the last checked) put the shapes past 12 pairs per expert (K
+    outermost gate/up). Shapes without the MFMA tiles refuse that flag."""
     Ts = (2, 5, 70, 140) if path == "grouped" else (2, 5, 70)
-    st = Setup(shape, dev, n_layers=1, max_tokens=max(Ts), flags=dict(PATH_FLAGS)[path])
+    flags = dict(PATH_FLAGS)[path]
+    if path == "grouped" and not (shape.hidden in (512, 1024, 2048) and shape.inter <= 1024):
+        cfg = q.Config(shape.hidden, shape.n_experts, shape.top_k, shape.inter, 1, max(Ts), flags, 1e-6)
+        assert q.is_supported(cfg) == 0
+        return
+    st = Setup(shape, dev, n_layers=1, max_tokens=max(Ts), flags=flags)
     for T in Ts:
         xb = synth.x_bf16(shape, 12, T, T=T)
         sample = sorted(set(range(0, T, 7)) | {T - 1}) if T > 70 else None
@@ -661,11 +730,7 @@ def test_mx_gate_activations(dev, name, flag, act):
     st = Setup(S, dev, n_layers=1, max_tokens=16, flags=MX | flag)
     for T in (1, 4, 16):
         xb = synth.x_bf16(S, 9, T, T=T)
-        got = st.forward(xb)
-        ref = oracle.moe_layer(st.src, 0, xb, act=act)
-        exempt = check_routing(got["ids"], got["w"], ref)
-        keep = [t for t in range(T) if t not in exempt]
-        assert rel_err(got["y"][keep], ref["y"][keep]) <= REL_TOL
+        _check_layer(st, xb, st.forward(xb), act=act, label=f"{name} T={T}")
 
 
 def test_mx_and_q4k_blobs_are_not_interchangeable(dev):
@@ -703,14 +768,14 @@ def test_host_side_errors(tiny):
 
 
 class _RescaledSource(oracle.ExpertSource):
-    """MXFP4 blocks of a shape with every scale byte replaced by a seeded
-    draw from [lo, hi]: the kernels' scale decoding across many codes
-    (values stay where fp16 h, used by the GEMV down paths, cannot
-    overflow)."""
+    """Expert blocks of a shape with their scales redrawn: MXFP4 blocks get a
+    seeded E8M0 scale code from a per-matrix range; 4-bit super-blocks get d
+    and dmin multiplied by a seeded power of two per block from a per-matrix
+    range (kept finite in fp16). The ranges go per matrix (gate, up, down)."""
 
-    def __init__(self, shape, lo, hi, seed):
+    def __init__(self, shape, ranges, seed):
         super().__init__(shape)
-        self.lo, self.hi, self.seed = lo, hi, seed
+        self.ranges, self.seed = ranges, seed
 
     def blocks(self, layer, expert):
         key = (layer, int(expert))
@@ -718,41 +783,124 @@ class _RescaledSource(oracle.ExpertSource):
             mats = []
             for m in (synth.GATE, synth.UP, synth.DOWN):
                 b = synth.expert_matrix(self.shape, layer, int(expert), m).copy()
+                lo, hi = self.ranges[m]
                 rng = np.random.default_rng([self.seed, layer, int(expert), m])
-                b[..., 0] = rng.integers(self.lo, self.hi + 1, size=b.shape[:-1], dtype=np.uint8)
+                if self.shape.fmt == synth.FMT_MXFP4:
+                    b[..., 0] = rng.integers(lo, hi + 1, size=b.shape[:-1], dtype=np.uint8)
+                else:
+                    sh = rng.integers(lo, hi + 1, size=b.shape[:-1])
+                    # clamp per block so that d and dmin stay normal, finite fp16 numbers
+                    dd = [np.abs(b[..., f:f + 2].copy().view(np.float16)[..., 0].astype(np.float64)) for f in (0, 2)]
+                    big = np.maximum(dd[0], dd[1])
+                    small = np.where(dd[0] > 0, dd[0], np.inf)
+                    small = np.minimum(small, np.where(dd[1] > 0, dd[1], np.inf))
+                    smax = np.floor(np.log2(65504.0 / np.where(big > 0, big, 1.0)))
+                    smin = np.ceil(np.log2(2.0 ** -14 / np.where(np.isfinite(small), small, 1.0)))
+                    sh = np.clip(sh, smin, smax).astype(np.int64)
+                    for f in (0, 2):                   # d, dmin (fp16, little-endian)
+                        v = b[..., f:f + 2].copy().view(np.float16)[..., 0].astype(np.float64)
+                        v = np.ldexp(v, sh)
+                        assert np.all(np.abs(v) <= 65504) and np.all((v == 0) | (np.abs(v) >= 2.0 ** -24))
+                        b[..., f:f + 2] = v.astype(np.float16)[..., None].view(np.uint8)
+                    assert np.array_equal(np.ldexp(
+                        b[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64), -sh),
+                        synth.expert_matrix(self.shape, layer, int(expert), m)[..., 0:2].copy()
+                        .view(np.float16)[..., 0].astype(np.float64))
                 mats.append(b)
             self._cache[key] = tuple(mats)
         return self._cache[key]
 
 
-@pytest.mark.parametrize("flags,Ts", [(0, (1, 3)), (q.FLAG_FORCE_EXPERT_GEMV, (5, 40)),
-                                      (q.FLAG_FORCE_GROUPED, (5, 70))],
-                         ids=["gemv", "expert_gemv", "mfma_tiles"])
-def test_mx_scale_codes_across_range(dev, flags, Ts):
-    """MXFP4 blocks whose scale bytes are drawn from 100..124 (2^-27 .. 2^-3,
-    24 distinct powers of two within every row) on each path, against the
-    oracle on the same blocks."""
-    S = synth.Shape("h512-mx-scales", 31, 512, 8, 2, 256, synth.FMT_MXFP4)
-    src = _RescaledSource(S, 100, 124, 5)
-    plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=max(Ts), flags=MX | flags)
+# Scale ranges per matrix (gate, up, down) and the exact power of two on x
+# that keeps every intermediate inside fp32's normal range while the blocks
+# span the whole accepted scale range: (a) gate/up scales over all codes
+# 2..252, x * 2^-110, down scales 100..140; (b) gate/up 110..140, x * 2^-40,
+# down over all codes. In a row the largest scales dominate; blocks whose
+# products fall below fp32's range contribute nothing measurable. With these
+# scales h reaches about 2^36 in (a) and 2^-44 in (b), beyond fp16 both ways.
+MX_SCALE_TIERS = (("gateup_all_codes", ((2, 252), (2, 252), (100, 140)), 2.0 ** -110),
+                  ("down_all_codes", ((110, 140), (110, 140), (2, 252)), 2.0 ** -40))
+# 4-bit super-blocks: d and dmin (about 2^-13 here) times 2^s; s over the
+# whole exponent span that keeps them finite fp16 numbers (d up to ~2^15).
+Q4K_SCALE_TIERS = (("gateup_wide_d", ((-10, 27), (-10, 27), (0, 4)), 2.0 ** -30),
+                   ("down_wide_d", ((0, 4), (0, 4), (-10, 27)), 2.0 ** -4))
+
+
+def _rescaled_setup(dev, S, src, flags, T):
+    plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=T, flags=flags)
 
     def layer(l):
         bl = [src.blocks(l, e) for e in range(S.n_experts)]
         return (np.stack([b[0] for b in bl]), np.stack([b[1] for b in bl]), np.stack([b[2] for b in bl]),
                 synth.router(S, l))
 
-    blob = plan.upload_blob(layer, device=dev)
-    scratch = plan.new_scratch(max(Ts), device=dev)
+    return plan, plan.upload_blob(layer, device=dev), plan.new_scratch(T, device=dev)
+
+
+@pytest.mark.parametrize("flags,Ts", [(0, (1, 3)), (q.FLAG_FORCE_EXPERT_GEMV, (5, 40)),
+                                      (q.FLAG_FORCE_GROUPED, (5, 70, 140))],
+                         ids=["gemv", "expert_gemv", "mfma_tiles"])
+@pytest.mark.parametrize("mx", [True, False], ids=["mxfp4", "q4k"])
+@pytest.mark.parametrize("tier", [0, 1], ids=["gateup_wide", "down_wide"])
+def test_block_scales_across_range(dev, flags, Ts, mx, tier):
+    """Weights whose block scales cover the whole range the packer accepts
+    (MXFP4: every E8M0 code 2..252; super-blocks: d and dmin over their whole
+    fp16 range), one matrix kind at a time, on each path, against the oracle
+    on the same blocks; x is scaled so that the exact result stays inside
+    fp32's range."""
+    name, ranges, xscale = (MX_SCALE_TIERS if mx else Q4K_SCALE_TIERS)[tier]
+    S = synth.Shape("h512-scales" + ("-mx" if mx else ""), 31, 512, 8, 2, 256,
+                    synth.FMT_MXFP4 if mx else synth.FMT_Q4K)
+    src = _RescaledSource(S, ranges, 5)
+    plan, blob, scratch = _rescaled_setup(dev, S, src, (MX if mx else 0) | flags, max(Ts))
     for T in Ts:
-        xb = synth.x_bf16(S, 14, T, T=T)
+        xb = _scaled_bf16(synth.x_bf16(S, 14, T, T=T), xscale)
         x = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).to(dev)
         out = torch.empty(T, S.hidden, dtype=torch.float32, device=dev)
         ids = torch.empty(T, S.top_k, dtype=torch.int32, device=dev)
         w = torch.empty(T, S.top_k, dtype=torch.float32, device=dev)
-        plan.forward(blob, 0, x, T, out, ids=ids, w=w, scratch=scratch)
+        # routing from the router GEMV on scaled x: logits shrink with x, so
+        # route from unscaled-x logits given explicitly (shared fp32 inputs)
+        lg = synth.logits_f32(S, 14, T)
+        counts = torch.empty(S.n_experts, dtype=torch.int32, device=dev)
+        offsets = torch.empty(S.n_experts + 1, dtype=torch.int32, device=dev)
+        pairs = torch.empty(T * S.top_k, dtype=torch.int32, device=dev)
+        plan.route(blob, 0, None, torch.from_numpy(lg).to(dev), T, ids, w, counts, offsets, pairs, scratch=scratch)
+        plan.expert_ffn(blob, 0, x, T, ids, w, out, counts, offsets, pairs, scratch=scratch)
         torch.cuda.synchronize()
-        ref = oracle.moe_layer(src, 0, xb)
-        got_ids, y = ids.cpu().numpy(), out.cpu().numpy()
-        exempt = check_routing(got_ids, w.cpu().numpy(), ref)
-        keep = [t for t in range(T) if t not in exempt]
-        assert rel_err(y[keep], ref["y"][keep]) <= REL_TOL, (T, rel_err(y[keep], ref["y"][keep]))
+        ref = oracle.moe_layer(src, 0, xb, logits=lg)
+        check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref, exact=True)
+        y = out.cpu().numpy()
+        assert np.isfinite(y).all()
+        m = np.abs(ref["y"]).max()
+        assert 2.0 ** -100 < m < 2.0 ** 100, m           # the tier keeps the result inside fp32
+        check_outputs(y, ref["y"], label=f"{name} T={T} flags={flags:#x}")
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_forward_fills_requested_dispatch_lists(qwen, T):
+    """moe_forward with dispatch-list buffers in its routing output writes
+    counts, offsets and pairs there on every path (the per-token path at
+    T = 1, the expert-major GEMV at 8, the MFMA tiles at 64), equal to the
+    library routines' counts, cumulative sum and stable sort of its ids."""
+    S = qwen.shape
+    d = qwen.dev
+    plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=T)
+    xb = synth.x_bf16(S, 71, T, T=T)
+    out = torch.empty(T, S.hidden, dtype=torch.float32, device=d)
+    ids = torch.empty(T, S.top_k, dtype=torch.int32, device=d)
+    w = torch.empty(T, S.top_k, dtype=torch.float32, device=d)
+    counts = torch.full((S.n_experts,), -1, dtype=torch.int32, device=d)
+    offsets = torch.full((S.n_experts + 1,), -1, dtype=torch.int32, device=d)
+    pairs = torch.full((T * S.top_k,), -1, dtype=torch.int32, device=d)
+    plan.forward(qwen.blob, 0, qwen.xdev(xb), T, out, ids=ids, w=w, scratch=plan.new_scratch(T, device=d),
+                 counts=counts, offsets=offsets, pairs=pairs)
+    torch.cuda.synchronize()
+    flat = ids.cpu().numpy().reshape(-1)
+    bc = np.bincount(flat, minlength=S.n_experts)
+    assert np.array_equal(counts.cpu().numpy(), bc)
+    assert np.array_equal(offsets.cpu().numpy(), np.concatenate([[0], np.cumsum(bc)]))
+    assert np.array_equal(pairs.cpu().numpy(), np.argsort(flat, kind="stable"))
+    with pytest.raises(q.MoeError):                 # the three lists together or none
+        plan.forward(qwen.blob, 0, qwen.xdev(xb), T, out, ids=ids, w=w, scratch=plan.new_scratch(T, device=d),
+                     counts=counts)

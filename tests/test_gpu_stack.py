@@ -10,7 +10,8 @@ import torch
 import oracle
 import synth
 import quantized_moe_decode_gemv_amd as q
-from helpers import REL_TOL, TAU, check_bf16_vector, check_routing, layer_source, rel_err
+from helpers import (REL_TOL, TAU, check_bf16_vector, check_outputs, check_routing, layer_source, reference_outputs,
+                     rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -140,7 +141,7 @@ def test_full_stack_every_layer_on_seeded_inputs(dev, qwen_stack):
     S, plan, blob, _ = qwen_stack
     src = oracle.ExpertSource(S, max_cached=16)
     scratch = plan.new_scratch(1, device=dev)
-    worst = 0.0
+    worst, exempted = 0.0, 0
     for l in range(48):
         xb = synth.x_bf16(S, 10, l)
         x = torch.from_numpy(xb.view(np.int16)).to(dev)
@@ -151,15 +152,17 @@ def test_full_stack_every_layer_on_seeded_inputs(dev, qwen_stack):
         plan.forward(blob, l, x, 1, y, x_next=xn, ids=ids, w=w, scratch=scratch)
         torch.cuda.synchronize()
         ref = oracle.moe_layer(src, l, xb)
-        exempt = check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref)
-        if exempt:
-            continue
-        err = rel_err(y.cpu().numpy(), ref["y"])
+        gid = ids.cpu().numpy()
+        exempt = check_routing(gid, w.cpu().numpy(), ref, label=f"layer {l}")
+        exempted += len(exempt)
+        yref = reference_outputs(src, l, xb, ref, gid, exempt)
+        err = rel_err(y.cpu().numpy(), yref)
         assert err <= REL_TOL, f"layer {l}: {err:.3e}"
         worst = max(worst, err)
-        _, ref_next = oracle.resid_rmsnorm(xb[0], ref["y"][0])
+        _, ref_next = oracle.resid_rmsnorm(xb[0], yref[0])
         check_bf16_vector(xn.cpu().numpy().view(np.uint16)[0], ref_next)
-    print(f"48 layers on seeded inputs: worst max|err|/max|ref| = {worst:.3e}")
+    print(f"48 layers on seeded inputs: worst max|err|/max|ref| = {worst:.3e}, near-tie exemptions {exempted}")
+    assert exempted <= 2
 
 
 def test_full_stack_chained_step_in_bench_configuration(qwen_stack):
@@ -270,3 +273,83 @@ def test_full_stack_step_equals_chained_forward(dev, qwen_stack):
     _assert_same(_stack_once(plan, blob, 48, H, k, x0, dev, graph=False)[0], ref, "eager")
     for i, o in enumerate(_stack_once(plan, blob, 48, H, k, x0, dev, graph=True, replays=2)):
         _assert_same(o, ref, f"graph replay {i}")
+
+
+def _chained_forward_T(plan, blob, L, H, k, T, x0, dev):
+    """A T-token step as L chained moe_forward calls with the RMSNorm
+    epilogue (x_next of the last layer into a separate buffer)."""
+    xs = torch.zeros(L, T, H, dtype=torch.int16, device=dev)
+    ys = torch.zeros(L, T, H, dtype=torch.float32, device=dev)
+    ids = torch.zeros(L, T, k, dtype=torch.int32, device=dev)
+    ws = torch.zeros(L, T, k, dtype=torch.float32, device=dev)
+    xs[0].copy_(x0)
+    last = torch.zeros(T, H, dtype=torch.int16, device=dev)
+    scratch = plan.new_scratch(T, device=dev)
+    for l in range(L):
+        nxt = xs[l + 1] if l + 1 < L else last
+        plan.forward(blob, l, xs[l], T, ys[l], x_next=nxt, ids=ids[l], w=ws[l], scratch=scratch)
+    torch.cuda.synchronize()
+    xs[0].copy_(last)
+    return xs, ys, ids, ws
+
+
+def _stack_once_T(plan, blob, L, H, k, T, x0, dev, graph, replays=1):
+    xs = torch.zeros(L, T, H, dtype=torch.int16, device=dev)
+    ys = torch.zeros(L, T, H, dtype=torch.float32, device=dev)
+    ids = torch.zeros(L, T, k, dtype=torch.int32, device=dev)
+    ws = torch.zeros(L, T, k, dtype=torch.float32, device=dev)
+    scratch = plan.new_scratch(T, device=dev)
+    stream = torch.cuda.Stream()
+    if not graph:
+        xs[0].copy_(x0)
+        torch.cuda.synchronize()
+        plan.stack_step(blob, xs, ys, T, ids, ws, scratch=scratch, stream=stream)
+        torch.cuda.synchronize()
+        return [(xs.clone(), ys.clone(), ids.clone(), ws.clone())]
+    g = plan.capture_step(blob, xs, ys, T, ids, ws, scratch=scratch, stream=stream)
+    outs = []
+    for _ in range(replays):
+        xs.zero_(), ys.zero_(), ids.zero_(), ws.zero_()
+        xs[0].copy_(x0)
+        other = torch.randn(1000, device=dev).sum()   # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.launch(stream)
+        torch.cuda.synchronize()
+        assert other.isfinite()
+        outs.append((xs.clone(), ys.clone(), ids.clone(), ws.clone()))
+    return outs
+
+
+@pytest.mark.parametrize("T,L", [(8, 3), (128, 3), (1, 1), (8, 1), (128, 1)])
+def test_stack_step_tokens_and_single_layer(dev, T, L):
+    """The stacked step at T = 8 and 128 tokens (the batched paths and the
+    router's norm prologue over several tokens) and with a single layer
+    (whose epilogue writes the next step's input over its own input):
+    eager and graph replays equal the chained moe_forward calls bit for bit;
+    layer 0 (seeded input) is held against the oracle token by token (ids,
+    y, x_next), later layers for properties."""
+    S = synth.Shape(f"stack-T{T}-L{L}", 40 + L, 2048, 128, 8, 768)
+    H, k = S.hidden, S.top_k
+    plan = q.Plan(H, S.n_experts, k, S.inter, n_layers=L, max_tokens=T)
+    blob = plan.upload_blob(layer_source(S), device=dev)
+    xb0 = synth.x_bf16(S, 44, T, T=T)
+    x0 = torch.from_numpy(xb0.view(np.int16)).to(dev)
+    ref = _chained_forward_T(plan, blob, L, H, k, T, x0, dev)
+    _assert_same(_stack_once_T(plan, blob, L, H, k, T, x0, dev, graph=False)[0], ref, "eager")
+    for i, o in enumerate(_stack_once_T(plan, blob, L, H, k, T, x0, dev, graph=True, replays=2)):
+        _assert_same(o, ref, f"graph replay {i}")
+    xs, ys, ids, ws = (t.cpu().numpy() for t in ref)
+    xs = xs.view(np.uint16)
+    for l in range(L):
+        for t in range(T):
+            assert len(set(ids[l, t].tolist())) == k and np.isfinite(ys[l, t]).all()
+    src = oracle.ExpertSource(S)
+    sample = list(range(T)) if T <= 8 else sorted({0, 1, 31, 64, 100, T - 1})
+    oref = oracle.moe_layer(src, 0, xb0[sample])
+    exempt = check_routing(ids[0][sample], ws[0][sample], oref, label=f"T={T} L={L} layer 0")
+    yref = reference_outputs(src, 0, xb0[sample], oref, ids[0][sample], exempt)
+    check_outputs(ys[0][sample], yref, label=f"T={T} L={L} layer 0")
+    nxt = xs[1] if L > 1 else xs[0]             # L = 1: the step's output is the next step's input
+    for i, t in enumerate(sample):
+        _, rn = oracle.resid_rmsnorm(xb0[t], yref[i])
+        check_bf16_vector(nxt[t], rn)
