@@ -198,6 +198,23 @@ int moe_forward(const moe_plan* plan, const void* blob, int32_t layer, const uin
                 int32_t T, float* out, uint16_t* x_next, const moe_route_out* route_out,
                 void* scratch, size_t scratch_bytes, hipStream_t stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same launches and results, with the workspace taken from a device array
+ * the library holds, MOE_STATIC_SCRATCH_BYTES per GPU, instead of a caller
+ * buffer. It calls no allocating routine; the array's device address is
+ * looked up once per GPU, on the first call with that GPU current. Returns
+ * MOE_ERR_SCRATCH_TOO_SMALL when moe_scratch_bytes(plan, T) exceeds the
+ * array (about 145 tokens of the Qwen3-30B-A3B-shaped layer), otherwise as
+ * moe_forward. Every call on a GPU shares that GPU's array: calls that may
+ * overlap on one GPU (different streams without ordering, several host
+ * threads) race and must be serialised by the caller. No kernel reads the
+ * workspace before writing it in the same call, so nothing is cleared. */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int moe_forward_static_scratch(const moe_plan* plan, const void* blob, int32_t layer, const uint16_t* x_bf16,
+                               int32_t T, float* out, uint16_t* x_next, const moe_route_out* route_out,
+                               hipStream_t stream);
+
 /* One decode step of the whole stack for T tokens (the greedy bs=1 decode
  * the pages time: sparkinfer README, opening paragraph): for l = 0..n_layers-1,
  * moe_forward(layer l, x = xs[l], out = ys[l], x_next = xs[(l+1) % n_layers]),

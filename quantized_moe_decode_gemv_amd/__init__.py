@@ -33,7 +33,9 @@ EXPORTS = [
     "moe_layer_bytes", "moe_layer_offset", "moe_scratch_bytes", "moe_pack_header", "moe_pack_layer",
     "moe_unpack_layer", "moe_blob_check", "moe_route", "moe_expert_ffn", "moe_forward", "moe_stack_step",
     "moe_graph_capture_step", "moe_graph_launch", "moe_graph_destroy", "moe_profile_gate_up", "moe_status_string",
+    "moe_forward_static_scratch",
 ]
+STATIC_SCRATCH_BYTES = 16 << 20   # MOE_STATIC_SCRATCH_BYTES
 
 
 class MoeError(RuntimeError):
@@ -97,6 +99,8 @@ def load():
     L.moe_expert_ffn.argtypes = [P, vp, i32, vp, i32, ctypes.POINTER(RouteOut), vp, vp, sz, vp]
     L.moe_forward.restype = ctypes.c_int
     L.moe_forward.argtypes = [P, vp, i32, vp, i32, vp, vp, ctypes.POINTER(RouteOut), vp, sz, vp]
+    L.moe_forward_static_scratch.restype = ctypes.c_int
+    L.moe_forward_static_scratch.argtypes = [P, vp, i32, vp, i32, vp, vp, ctypes.POINTER(RouteOut), vp]
     L.moe_stack_step.restype = ctypes.c_int
     L.moe_stack_step.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.moe_graph_capture_step.restype = ctypes.c_int
@@ -249,6 +253,16 @@ class Plan:
         sb = scratch.numel() * scratch.element_size() if scratch is not None else 0
         _check(load().moe_forward(self._h, _dptr(blob), layer, _dptr(x), T, _dptr(out), _dptr(x_next), ro,
                                   _dptr(scratch), sb, _stream(stream)), "moe_forward")
+
+    def forward_static_scratch(self, blob, layer, x, T, out, x_next=None, ids=None, w=None, stream=None,
+                               counts=None, offsets=None, pairs=None):
+        """moe_forward on the library's own device workspace (no scratch
+        argument; see moe_forward_static_scratch)."""
+        ro = None
+        if ids is not None or w is not None:
+            ro = ctypes.byref(RouteOut(_dptr(ids), _dptr(w), _dptr(counts), _dptr(offsets), _dptr(pairs)))
+        _check(load().moe_forward_static_scratch(self._h, _dptr(blob), layer, _dptr(x), T, _dptr(out), _dptr(x_next),
+                                                 ro, _stream(stream)), "moe_forward_static_scratch")
 
     def profile_gate_up(self, blob, layer, x, T, start, stop, scratch=None, stream=None):
         """moe_forward's launches up to the gate/up GEMV kernel, whose

@@ -5,7 +5,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmoe.so")
-SOURCES = ["moe_gemv.hip", "moe_egemv.hip", "moe_grouped.hip", "moe_api.cpp"]
+SOURCES = ["moe_gemv.hip", "moe_egemv.hip", "moe_grouped.hip", "moe_api.cpp", "moe_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU forms are kept out of generated code on purpose.
