@@ -49,6 +49,9 @@ def main():
     ap.add_argument("--no-batched", action="store_true", help="skip the small-batch / prefill measurements")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the single-step percentiles and the single-layer calls (for counter runs)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="instead of the benchmark line: per-layer timeline of replayed decode steps from the "
+                         "in-kernel stamps of the profiling build (libqmoe_timeline.so)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (reference kernel for hardware byte counters)")
     args = ap.parse_args()
@@ -62,6 +65,12 @@ def main():
 
     import synth
     import quantized_moe_decode_gemv_amd as q
+    from quantized_moe_decode_gemv_amd import build as qbuild
+
+    if args.timeline:
+        if not os.path.exists(qbuild.LIB_TIMELINE):
+            sys.exit(f"{qbuild.LIB_TIMELINE} is not built: python -m quantized_moe_decode_gemv_amd.build --timeline")
+        q.LIB_PATH = qbuild.LIB_TIMELINE
 
     S = synth.QWEN3_30B_A3B
     L = args.layers
@@ -134,6 +143,9 @@ def main():
     gbps = expert_bytes_per_token * tok_s / 1e9
     log(f"decode: {ms_per_step * 1e3:.1f} us/step, {tok_s:.1f} tok/s, expert bytes {gbps:.0f} GB/s")
     finite = bool(torch.isfinite(ys).all().item())
+    if args.timeline:
+        print(json.dumps(decode_timeline(plan, blob, graph, stream, L, ms_per_step, q, np, torch)), flush=True)
+        return
     # spread of single steps (after the timed region, each replay between its own events)
     step_pct = None
     if not args.no_extras:
@@ -247,6 +259,110 @@ def main():
         "outputs_finite": finite,
     }
     print(json.dumps(result), flush=True)
+
+
+def decode_timeline(plan, blob, graph, stream, L, ms_per_step, q, np, torch, reps=6, batch=48):
+    """Per-layer timeline of the captured decode step from the profiling
+    build's s_memrealtime stamps (the tick measured here against the host
+    clock): for each layer the router, gate/up
+    and down spans (first workgroup start to last wave end) and the gaps
+    between consecutive launches, plus two in-kernel marks: the router's norm
+    (sum of squares reduced), gate/up's routing (top-k done) and first row's
+    dot products, down's row partials (medians over workgroups, from the
+    kernel's start). Medians over layers and over `reps` samples, each the
+    last of `batch` back-to-back replays."""
+    import ctypes
+    lib = q.load()
+    lib.moe_timeline_setup.restype = ctypes.c_int
+    lib.moe_timeline_setup.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong]
+    lib.moe_timeline_reset.restype = ctypes.c_int
+    lib.moe_timeline_read.restype = ctypes.c_int
+    lib.moe_timeline_read.argtypes = [ctypes.c_void_p]
+    assert lib.moe_timeline_setup(blob.data_ptr() + plan.layer_offset(0), plan.layer_bytes()) == 0
+    assert L <= 64
+    rec = np.zeros((256, 1024, 8), dtype=np.uint64)
+
+    # the stamp clock against the host clock: two replays 0.5 s apart, each
+    # submitted to an idle GPU; the first router's start stamps differ by the
+    # submit interval up to the (small, similar) submit-to-start latencies
+    def first_start():
+        assert lib.moe_timeline_read(rec.ctypes.data) == 0
+        v = rec[0, :, 0]
+        return float(v[v > 0].min())
+    torch.cuda.synchronize()
+    t_a = time.perf_counter()
+    graph.launch(stream)
+    torch.cuda.synchronize()
+    s_a = first_start()
+    time.sleep(0.5)
+    t_b = time.perf_counter()
+    graph.launch(stream)
+    torch.cuda.synchronize()
+    s_b = first_start()
+    tick_mhz = (s_b - s_a) / (t_b - t_a) / 1e6
+    us_per_tick = 1.0 / tick_mhz
+    rows, step_stamps, batch_step_us = [], [], []
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    assert lib.moe_timeline_reset() == 0
+    for _ in range(reps):
+        # the stamps of the last of `batch` back-to-back replays (every
+        # workgroup rewrites its record each step), i.e. of a step in the
+        # steady state that the timed decode loop runs in
+        ev0.record(stream)
+        for _ in range(batch):
+            graph.launch(stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        batch_step_us.append(ev0.elapsed_time(ev1) * 1e3 / batch)
+        assert lib.moe_timeline_read(rec.ctypes.data) == 0
+        r = rec.astype(np.float64)
+
+        def span(slot):
+            st = r[slot, :, 0]
+            en = r[slot, :, 1:5]
+            return st[st > 0].min(), en[en > 0].max()
+
+        def mark(slot, field, t0):
+            v = r[slot, :, field]
+            v = v[v > 0]
+            return float(np.median(v) - t0) * us_per_tick if len(v) else None
+
+        base = span(0)[0]
+        for l in range(L):
+            rs, re_ = span(4 * l)
+            gs, ge = span(4 * l + 1)
+            ds, de = span(4 * l + 2)
+            ns = span(4 * (l + 1))[0] if l + 1 < L else span(3)[0]
+            row = {"router": re_ - rs, "gap_router_gateup": gs - re_, "gateup": ge - gs, "gap_gateup_down": ds - ge,
+                   "down": de - ds, "gap_down_next": ns - de}
+            row = {k2: v * us_per_tick for k2, v in row.items()}
+            row["layer_period"] = (ns - rs) * us_per_tick
+            if l > 0:
+                row["router_norm_mark"] = mark(4 * l, 5, rs)
+            row["gateup_topk_mark"] = mark(4 * l + 1, 5, gs)
+            row["gateup_row0_mark"] = mark(4 * l + 1, 6, gs)
+            row["down_partials_mark"] = mark(4 * l + 2, 6, ds)
+            rows.append(row)
+        step_stamps.append((span(3)[1] - base) * us_per_tick)
+    keys = list(rows[-1].keys())
+    med = {k2: round(float(np.median([rw[k2] for rw in rows if rw.get(k2) is not None])), 3) for k2 in keys}
+    parts = ("router", "gap_router_gateup", "gateup", "gap_gateup_down", "down", "gap_down_next")
+    return {
+        "timeline": {
+            "per_layer_median_us": med,
+            "sum_of_parts_us": round(sum(med[p] for p in parts), 3),
+            "layers": L,
+            "samples": reps,
+            "replays_per_sample": batch,
+            "step_us_stamps_median": round(float(np.median(step_stamps)), 1),
+            "step_us_events_instrumented": round(ms_per_step * 1e3, 1),
+            "step_us_events_sampled_batches": round(float(np.median(batch_step_us)), 1),
+            "clock": "s_memrealtime",
+            "clock_mhz_measured": round(tick_mhz, 3),
+        },
+        "config": {"workload": f"Qwen3-30B-A3B-shaped {L}-layer quantized MoE stack, bs=1 decode step, hipGraph",
+                   "library": "libqmoe_timeline.so (-DQMOE_TIMELINE)"},
+    }
 
 
 MFMA_FP16_PEAK_TFLOPS = 2500.0

@@ -1,10 +1,17 @@
-"""Compile the gfx950 HIP library ``libqmoe.so`` in-tree with hipcc."""
+"""Compile the gfx950 HIP library ``libqmoe.so`` in-tree with hipcc.
+
+``build(timeline=True)`` (``python -m quantized_moe_decode_gemv_amd.build
+--timeline``) compiles the profiling variant ``libqmoe_timeline.so`` instead:
+the same sources with -DQMOE_TIMELINE, whose decode kernels write
+s_memrealtime stamps (csrc/moe_timeline.h) that ``bench.py --timeline`` reads.
+"""
 import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmoe.so")
+LIB_TIMELINE = os.path.join(HERE, "libqmoe_timeline.so")
 SOURCES = ["moe_gemv.hip", "moe_egemv.hip", "moe_grouped.hip", "moe_api.cpp", "moe_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -19,24 +26,26 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
 
 
-def build(verbose=False):
+def build(verbose=False, timeline=False):
     """Always recompiles (the caller asked for a build)."""
+    out = LIB_TIMELINE if timeline else LIB
     srcs = []
     for s in sources():
         if s.endswith(".cpp"):
             srcs += ["-x", "hip", s]
         else:
             srcs.append(s)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [HIPCC] + FLAGS + (["-DQMOE_TIMELINE"] if timeline else []) + srcs + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     if verbose:
         print(" ".join(cmd))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, timeline="--timeline" in sys.argv[1:]))

@@ -22,6 +22,7 @@
 #include <type_traits>
 
 #include "moe_device.h"
+#include "moe_timeline.h"
 
 namespace qmoe {
 
@@ -169,6 +170,7 @@ __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__
                                                        const float* __restrict__ y_prev, uint16_t* __restrict__ x_out,
                                                        float eps, float* __restrict__ logits, int E, int H, int T) {
   __shared__ float part[BLOCK / WAVE];
+  QMOE_TL_SCOPE(wr, 0);
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
   float w[CH][4];
@@ -203,6 +205,7 @@ __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__
         for (int i = 0; i < 4; ++i) ss = fmaf(xv[c][i], xv[c][i], ss);
       }
       const float inv = 1.0f / sqrtf(block_sum4(ss, part) / (float)H + eps);
+      QMOE_TL_MARK(5);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         uint16_t b[4];
@@ -240,6 +243,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ h, int T, int fused_topk) {
   constexpr int RPS = WAVE / LPR;
   __shared__ TopkSmem s_topk;
+  QMOE_TL_SCOPE(gu, 1);
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x / WAVE;
   const int unit = blockIdx.x * (BLOCK / WAVE) + wid;
@@ -281,6 +285,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
       }
     }
     __syncthreads();
+    QMOE_TL_MARK(5);
   }
   if (!active) return;
   const int e = fused_topk ? s_topk.sid[ts] : ids_in[ts];
@@ -313,6 +318,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
       }
       pg = group_sum<LPR>(pg);
       pu = group_sum<LPR>(pu);
+      if (u == 0) QMOE_TL_MARK(6);
       if (lam == 0) h[(size_t)ts * I + r0 + u * RPS + rho] = gate_act(pg, pu, ACT);
     }
     return;
@@ -346,6 +352,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
     }
     pg = group_sum<LPR>(pg);
     pu = group_sum<LPR>(pu);
+    if (u == 0) QMOE_TL_MARK(6);
     if (lam == 0) h[(size_t)ts * I + r0 + u * RPS + rho] = gate_act(pg, pu, ACT);
   }
 }
@@ -369,6 +376,7 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, const float* __restrict__ h,
     float* __restrict__ y, int T) {
   __shared__ float part[BLOCK / WAVE][R];
+  QMOE_TL_SCOPE(dn, 2);
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x / WAVE;
   const int bpt = H / R;                           // blocks per token
@@ -423,6 +431,7 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
       p[r] = group_sum<WAVE>(ws * fmaf(a.a, dot_codes_f32(cd[r], hv), -a.b * S));
     }
   }
+  QMOE_TL_MARK(6);
   if (lane == 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r) part[wid][r] = p[r];
@@ -444,6 +453,7 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
 __global__ __launch_bounds__(BLOCK) void resid_norm_kernel(const uint16_t* x, const float* __restrict__ y, uint16_t* xn,
                                                            int H, float eps) {
   __shared__ float part[BLOCK / WAVE];
+  QMOE_TL_SCOPE(nullptr, 3);
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   float ss = 0.f;
@@ -780,3 +790,32 @@ hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int T, int 
 }
 
 }  // namespace qmoe
+
+#ifdef QMOE_TIMELINE
+namespace qmoe {
+__device__ unsigned long long tl_rec[TL_SLOTS][TL_WGS][TL_FIELDS];
+__device__ const uint8_t* tl_base;
+__device__ unsigned long long tl_layer_bytes;
+}  // namespace qmoe
+
+extern "C" int moe_timeline_setup(const void* layer0, unsigned long long layer_bytes) {
+  const uint8_t* b = static_cast<const uint8_t*>(layer0);
+  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(qmoe::tl_base), &b, sizeof(b));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(qmoe::tl_layer_bytes), &layer_bytes, sizeof(layer_bytes));
+  return (int)e;
+}
+
+extern "C" int moe_timeline_reset(void) {
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(qmoe::tl_rec));
+  if (e == hipSuccess) e = hipMemset(p, 0, sizeof(qmoe::tl_rec));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  return (int)e;
+}
+
+extern "C" int moe_timeline_read(unsigned long long* host) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(host, HIP_SYMBOL(qmoe::tl_rec), sizeof(qmoe::tl_rec));
+  return (int)e;
+}
+#endif

@@ -1,0 +1,64 @@
+// In-kernel timeline stamps of the decode kernels, compiled only into the
+// profiling build of the library (-DQMOE_TIMELINE, libqmoe_timeline.so);
+// in the product build every macro here expands to nothing.
+//
+// Each launch of an instrumented kernel owns a slot, 4 * layer + kind (kind
+// 0 router, 1 gate/up, 2 down, 3 the stand-alone residual + RMSNorm), where
+// the layer is found from the kernel's weight pointer: (pointer - base) /
+// layer_bytes, with base and layer_bytes set by moe_timeline_setup. Per slot
+// and workgroup (the first TL_WGS workgroups) the record holds
+//   [0] s_memrealtime (100 MHz) when thread 0 starts,
+//   [1..4] s_memrealtime when each of the four waves leaves the kernel,
+//   [5], [6] two marks a kernel sets at points of its own.
+// Host exports of the profiling build (extern "C", return hipError_t as int):
+//   moe_timeline_setup(const void* layer0, unsigned long long layer_bytes)
+//   moe_timeline_reset()                 zeroes every record
+//   moe_timeline_read(unsigned long long* host)   copies TL_SLOTS*TL_WGS*8 words
+// Launches whose pointer falls outside the layers, and workgroups past
+// TL_WGS, record nothing.
+#pragma once
+
+#ifdef QMOE_TIMELINE
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+constexpr int TL_LAYERS = 64, TL_SLOTS = 4 * TL_LAYERS, TL_WGS = 1024, TL_FIELDS = 8;
+extern __device__ unsigned long long tl_rec[TL_SLOTS][TL_WGS][TL_FIELDS];
+extern __device__ const uint8_t* tl_base;
+extern __device__ unsigned long long tl_layer_bytes;
+
+__device__ inline int tl_slot(const void* p, int kind) {
+  if (kind == 3) return 3;
+  const uint8_t* b = tl_base;
+  const unsigned long long lb = tl_layer_bytes;
+  if (!b || lb == 0 || (const uint8_t*)p < b) return -1;
+  const unsigned long long layer = (unsigned long long)((const uint8_t*)p - b) / lb;
+  return layer < (unsigned long long)TL_LAYERS ? 4 * (int)layer + kind : -1;
+}
+
+struct TLScope {
+  int slot;
+  __device__ TLScope(const void* p, int kind) : slot(tl_slot(p, kind)) {
+    if (threadIdx.x == 0 && slot >= 0 && blockIdx.x < TL_WGS)
+      tl_rec[slot][blockIdx.x][0] = __builtin_amdgcn_s_memrealtime();
+  }
+  __device__ ~TLScope() {
+    if ((threadIdx.x & 63) == 0 && threadIdx.x < 256 && slot >= 0 && blockIdx.x < TL_WGS)
+      tl_rec[slot][blockIdx.x][1 + threadIdx.x / 64] = __builtin_amdgcn_s_memrealtime();
+  }
+  __device__ void mark(int field) const {
+    if (threadIdx.x == 0 && slot >= 0 && blockIdx.x < TL_WGS)
+      tl_rec[slot][blockIdx.x][field] = __builtin_amdgcn_s_memrealtime();
+  }
+};
+}  // namespace qmoe
+
+#define QMOE_TL_SCOPE(ptr, kind) const qmoe::TLScope qmoe_tl_scope_((ptr), (kind))
+#define QMOE_TL_MARK(field) qmoe_tl_scope_.mark(field)
+#else
+#define QMOE_TL_SCOPE(ptr, kind)
+#define QMOE_TL_MARK(field) \
+  do {                     \
+  } while (0)
+#endif
