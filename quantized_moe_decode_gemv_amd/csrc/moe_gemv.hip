@@ -148,13 +148,14 @@ __global__ __launch_bounds__(WAVE) void topk_kernel(const float* __restrict__ lo
 // (so both produce the same bits): thread tid owns the 4-element chunks
 // starting at 4*(tid + 256c); the sum of squares is accumulated chunk by
 // chunk, then reduced over the wave (butterfly) and over the 4 waves.
+// One barrier: a caller that reduces again uses another part array, and
+// reuses one only after a later reduction's barrier (by then every wave has
+// read it).
 __device__ __forceinline__ float block_sum4(float v, float* part) {
   v = group_sum<WAVE>(v);
   if ((threadIdx.x & (WAVE - 1)) == 0) part[threadIdx.x / WAVE] = v;
   __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  __syncthreads();
-  return tot;
+  return (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // ------------------------------------------------------------------ router GEMV
@@ -169,7 +170,9 @@ template <int CH, bool NORM>  // chunks of 4 weights per thread: H = CH * 1024
 __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__ wr, const uint16_t* __restrict__ x,
                                                        const float* __restrict__ y_prev, uint16_t* __restrict__ x_out,
                                                        float eps, float* __restrict__ logits, int E, int H, int T) {
-  __shared__ float part[BLOCK / WAVE];
+  // the norm's and the dot's reductions use one part array each (without the
+  // norm, tokens alternate between the two)
+  __shared__ float part[2][BLOCK / WAVE];
   QMOE_TL_SCOPE(wr, 0);
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__
 #pragma unroll
         for (int i = 0; i < 4; ++i) ss = fmaf(xv[c][i], xv[c][i], ss);
       }
-      const float inv = 1.0f / sqrtf(block_sum4(ss, part) / (float)H + eps);
+      const float inv = 1.0f / sqrtf(block_sum4(ss, part[0]) / (float)H + eps);
       QMOE_TL_MARK(5);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__
     for (int c = 0; c < CH; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc = fmaf(w[c][i], xv[c][i], acc);
-    const float tot = block_sum4(acc, part);
+    const float tot = block_sum4(acc, part[NORM ? 1 : (t & 1)]);
     if (tid == 0) logits[(size_t)t * E + e] = tot;
   }
 }
