@@ -80,10 +80,10 @@ enum moe_status {
 #define MOE_FLAG_WEIGHTS_MXFP4 0x20u
 
 typedef struct moe_config {
-  int32_t hidden;      /* H: 256, 512, 1024 or a multiple of 2048 up to 8192 */
+  int32_t hidden;      /* H: 256, 512, 1024, 3072 or a multiple of 2048 up to 8192 */
   int32_t n_experts;   /* E: 1..256 */
   int32_t top_k;       /* k: 1..min(E, 16) */
-  int32_t inter;       /* I: expert intermediate size, multiple of 256, up to 4096 */
+  int32_t inter;       /* I: expert intermediate size, multiple of 256, with top_k*inter/32 <= 512 */
   int32_t n_layers;    /* layers held in one blob, >= 1 */
   int32_t max_tokens;  /* largest T any call will pass, >= 1, with max_tokens*top_k*max(hidden, inter) < 2^31 */
   uint32_t flags;      /* MOE_FLAG_* */

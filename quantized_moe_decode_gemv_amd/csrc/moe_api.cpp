@@ -23,11 +23,12 @@ static bool cfg_ok(const moe_config* c) {
   // device index arithmetic over (token, slot, row) runs in 32 bits
   if ((long long)c->max_tokens * k * (H > I ? H : I) >= (1LL << 31)) return false;
   // gate/up lane mapping: hidden/32 sub-blocks per row either fill a
-  // power-of-two lane group (256, 512, 1024) or whole waves (2048 * {1..4})
-  const bool h_ok = H == 256 || H == 512 || H == 1024 || (H % 2048 == 0 && H / 2048 <= 4);
+  // power-of-two lane group (256, 512, 1024), whole waves (2048 * {1..4}) or
+  // three per lane of 32-lane groups (3072)
+  const bool h_ok = H == 256 || H == 512 || H == 1024 || H == 3072 || (H % 2048 == 0 && H / 2048 <= 4);
   if (!h_ok) return false;
-  // down: k * inter/32 items per output row spread over at most 4 per lane
-  if ((long long)k * (I / 32) > 256) return false;
+  // down: k * inter/32 items per output row, one per lane of at most 8 waves
+  if ((long long)k * (I / 32) > 512) return false;
   const uint32_t force = c->flags & (MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_EXPERT_GEMV);
   const uint32_t act = c->flags & (MOE_FLAG_ACT_RELU2 | MOE_FLAG_ACT_SWIGLU_OAI);
   const uint32_t fmt = c->flags & MOE_FLAG_WEIGHTS_MXFP4;

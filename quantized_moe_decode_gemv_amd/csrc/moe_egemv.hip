@@ -355,6 +355,7 @@ static hipError_t egemv_go(const Layout& d, const uint8_t* layer, const uint16_t
     case 512: e = gateup_go<1, 16, 2, NT, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
     case 1024: e = gateup_go<1, 32, 4, NT, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
     case 2048: e = gateup_go<1, 64, 4, NT, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
+    case 3072: e = gateup_go<3, 32, 1, 1, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
     case 4096: e = gateup_go<2, 64, 2, 2, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
     case 6144: e = gateup_go<3, 64, 1, 1, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;
     case 8192: e = gateup_go<4, 64, 1, 1, FMT>(d, layer, x, pairs, slots, hbuf, nslots, s); break;

@@ -362,23 +362,23 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
 
 // ------------------------------------------------------------------ down GEMV + combine
 // Items of an output row: (slot s, sub-block j) for s < k, j < I/32, i.e.
-// G = k*I/32 <= 256 items. A block computes R consecutive output rows of one
-// token; wave w takes the contiguous item range [w*IW, (w+1)*IW), IW =
-// ceil(G/4) <= 64, one item per lane, for all R rows, so a lane loads its
-// 32 values of h once (fp32, straight into registers) and one 16-byte code
-// chunk and header per row. The routing is read directly, so the weight
-// loads leave as soon as the expert ids arrive. The four wave partials of a
-// row are added in wave order. h stays fp32: the codes are converted exactly
+// G = k*I/32 <= 64*NW items. A block of NW waves (4, or 8 when G > 256)
+// computes R consecutive output rows of one token; wave w takes the
+// contiguous item range [w*IW, (w+1)*IW), IW = ceil(G/NW) <= 64, one item
+// per lane, for all R rows, so a lane loads its 32 values of h once (fp32,
+// straight into registers) and one 16-byte code chunk and header per row.
+// The routing is read directly, so the weight loads leave as soon as the
+// expert ids arrive. The wave partials of a row are added in wave order. h stays fp32: the codes are converted exactly
 // and every product and sum is an fp32 operation, so h keeps its full range
 // and precision.
 // y[t*H + n] = sum_s w_s * D_{e_s}[n]·h_{t,s}. With MXFP4 weights an item's
 // 32 codes share one E8M0 scale byte.
-template <int R, int FMT>
-__global__ __launch_bounds__(BLOCK) void down_kernel(
+template <int R, int FMT, int NW>
+__global__ __launch_bounds__(NW * WAVE) void down_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I, int k,
     const int32_t* __restrict__ ids, const float* __restrict__ wts, const float* __restrict__ h,
     float* __restrict__ y, int T) {
-  __shared__ float part[BLOCK / WAVE][R];
+  __shared__ float part[NW][R];
   QMOE_TL_SCOPE(dn, 2);
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x / WAVE;
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
   const int n0 = (blockIdx.x % bpt) * R;
   const int nsb = I / 32;
   const int G = k * nsb;
-  const int IW = (G + 3) / 4;
+  const int IW = (G + NW - 1) / NW;
   const int i = wid * IW + lane;
   const bool valid = lane < IW && i < G;
   // an idle lane takes the item of the wave's last busy lane: its loads hit
@@ -442,7 +442,10 @@ __global__ __launch_bounds__(BLOCK) void down_kernel(
   __syncthreads();
   if (threadIdx.x < R) {
     const int r = threadIdx.x;
-    y[(size_t)t * H + n0 + r] = ((part[0][r] + part[1][r]) + part[2][r]) + part[3][r];
+    float acc = ((part[0][r] + part[1][r]) + part[2][r]) + part[3][r];
+#pragma unroll
+    for (int w = 4; w < NW; ++w) acc += part[w][r];
+    y[(size_t)t * H + n0 + r] = acc;
   }
 }
 
@@ -623,6 +626,7 @@ static hipError_t launch_router_big(const Layout& d, const float* wr, const uint
   switch (CH) {
     case 1: QMOE_ROUTER(1); break;
     case 2: QMOE_ROUTER(2); break;
+    case 3: QMOE_ROUTER(3); break;
     case 4: QMOE_ROUTER(4); break;
     case 6: QMOE_ROUTER(6); break;
     case 8: QMOE_ROUTER(8); break;
@@ -634,7 +638,7 @@ static hipError_t launch_router_big(const Layout& d, const float* wr, const uint
 
 bool router_has_norm_prologue(const Layout& d) {
   const int CH = d.H / 1024;
-  return d.H % 1024 == 0 && (CH == 1 || CH == 2 || CH == 4 || CH == 6 || CH == 8);
+  return d.H % 1024 == 0 && (CH == 1 || CH == 2 || CH == 3 || CH == 4 || CH == 6 || CH == 8);
 }
 
 hipError_t launch_router_norm(const Layout& d, const float* wr, const uint16_t* x_prev, const float* y_prev,
@@ -711,7 +715,10 @@ hipError_t launch_gateup(const Layout& d, const uint8_t* layer, const uint16_t* 
                          hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int nsb = d.H / 32;
   // rows per wave unit must divide I (a multiple of 256): RPS*U <= 256
-  if (nsb >= 64) {
+  if (nsb == 96) {
+    // 96 sub-blocks: 32 lanes per row with three each, two rows per step
+    gateup_go<3, 32, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1);
+  } else if (nsb >= 64 && nsb % 64 == 0) {
     switch (nsb / 64) {
       case 1: gateup_go<1, 64, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
       case 2: gateup_go<2, 64, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
@@ -736,14 +743,23 @@ hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids
   // the 48-layer decode step: super-blocks 4 rows in one phase (8 rows in
   // two phases of 4: 0.6 % slower; 2 rows: 14 %), MXFP4 8 rows (4: 2 % slower)
   constexpr int RQ = 4, RM = 8;              // both divide every supported H
-  if (d.k * (d.I / 32) > 4 * WAVE || d.H % RM) return hipErrorInvalidValue;
+  const int G = d.k * (d.I / 32);
+  if (G > 8 * WAVE || d.H % RM) return hipErrorInvalidValue;
   if (T <= 0) return hipSuccess;
-  if (d.fmt == FMT_MXFP4)
-    hipLaunchKernelGGL((down_kernel<RM, FMT_MXFP4>), dim3(T * (d.H / RM)), dim3(BLOCK), 0, s, layer + d.dn_off,
-                       d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
-  else
-    hipLaunchKernelGGL((down_kernel<RQ, FMT_Q4K>), dim3(T * (d.H / RQ)), dim3(BLOCK), 0, s, layer + d.dn_off,
-                       d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);
+  // four waves cover up to 256 items of a row, eight up to 512
+#define QMOE_DOWN(NW)                                                                                              \
+  if (d.fmt == FMT_MXFP4)                                                                                          \
+    hipLaunchKernelGGL((down_kernel<RM, FMT_MXFP4, NW>), dim3(T * (d.H / RM)), dim3(NW * WAVE), 0, s,              \
+                       layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);    \
+  else                                                                                                             \
+    hipLaunchKernelGGL((down_kernel<RQ, FMT_Q4K, NW>), dim3(T * (d.H / RQ)), dim3(NW * WAVE), 0, s,                \
+                       layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T)
+  if (G > 4 * WAVE) {
+    QMOE_DOWN(8);
+  } else {
+    QMOE_DOWN(4);
+  }
+#undef QMOE_DOWN
   return hipGetLastError();
 }
 

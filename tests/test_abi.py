@@ -68,7 +68,14 @@ def test_status_strings():
     ((256, 8, 0, 512, 1, 1, 0, 1e-6), False),       # k = 0
     ((256, 300, 2, 512, 1, 1, 0, 1e-6), False),     # E > 256
     ((256, 8, 2, 500, 1, 1, 0, 1e-6), False),       # inter not a multiple of 256
-    ((2048, 128, 16, 1024, 1, 1, 0, 1e-6), False),  # k*inter/32 > 256
+    ((2048, 128, 16, 1024, 1, 1, 0, 1e-6), True),   # k*inter/32 = 512: eight waves per down row
+    ((2048, 128, 16, 1280, 1, 1, 0, 1e-6), False),  # k*inter/32 > 512
+    ((4096, 128, 8, 1536, 48, 1, 0, 1e-6), True),   # a Qwen3-235B-A22B-shaped stack
+    ((4096, 128, 8, 1536, 1, 64, 0x4, 1e-6), True), # ... with the expert-major GEMV forced
+    ((4096, 128, 8, 1536, 1, 64, 0x2, 1e-6), False),# ... but no MFMA tiles
+    ((3072, 32, 4, 768, 2, 8, 0, 1e-6), True),      # hidden 3072 (32-lane groups, three sub-blocks each)
+    ((3072, 32, 4, 768, 1, 8, 0x24, 1e-6), True),   # ... MXFP4 on the expert-major GEMV
+    ((5120, 32, 4, 768, 1, 1, 0, 1e-6), False),     # hidden 5120: no lane mapping
     ((256, 8, 2, 512, 0, 1, 0, 1e-6), False),       # no layers
     ((256, 8, 2, 512, 1, 0, 0, 1e-6), False),       # max_tokens 0
     ((256, 8, 2, 512, 1, 1, 0, -1.0), False),       # negative eps

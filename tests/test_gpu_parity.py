@@ -512,6 +512,7 @@ EDGE = [
     synth.Shape("h2048-e256-k8", 16, 2048, 256, 8, 256),
     synth.Shape("h8192-i256", 17, 8192, 4, 2, 256),
     synth.Shape("h256-i2048", 18, 256, 4, 2, 2048),
+    synth.Shape("h3072-e32-k4", 19, 3072, 32, 4, 768),
 ]
 
 
@@ -542,6 +543,31 @@ def test_edge_shapes_batched_paths(dev, shape, path):
         xb = synth.x_bf16(shape, 12, T, T=T)
         sample = sorted(set(range(0, T, 7)) | {T - 1}) if T > 70 else None
         _check_layer(st, xb, st.forward(xb), sample=sample)
+
+
+LARGE = synth.Shape("qwen3-235b-a22b-layer", 20, 4096, 128, 8, 1536)
+
+
+@pytest.fixture(scope="module")
+def large_layer(dev):
+    return {path: Setup(LARGE, dev, n_layers=1, max_tokens=40, flags=flags)
+            for path, flags in PATH_FLAGS if path != "grouped"}
+
+
+@pytest.mark.parametrize("path", ["expert_gemv", "gemv"])
+@pytest.mark.parametrize("T", [1, 3, 40])
+def test_qwen3_235b_shaped_layer(large_layer, path, T):
+    """A Qwen3-235B-A22B-shaped layer (hidden 4096, 128 experts, top-8,
+    inter 1536: 384 down items per output row, eight waves per down
+    workgroup) on each path it has: the per-token GEMV and the expert-major
+    GEMV (the MFMA tiles stop at hidden 2048 / inter 1024 and refuse the
+    shape); 40 tokens checked on a sample."""
+    st = large_layer[path]
+    xb = synth.x_bf16(LARGE, 21, T, T=T)
+    sample = None if T <= 3 else [0, 1, 17, T - 2, T - 1]
+    _check_layer(st, xb, st.forward(xb), sample=sample)
+    cfg = q.Config(LARGE.hidden, LARGE.n_experts, LARGE.top_k, LARGE.inter, 1, 40, q.FLAG_FORCE_GROUPED, 1e-6)
+    assert q.is_supported(cfg) == 0
 
 
 # ------------------------------------------------------------------ MXFP4 expert weights

@@ -320,15 +320,22 @@ def _stack_once_T(plan, blob, L, H, k, T, x0, dev, graph, replays=1):
     return outs
 
 
-@pytest.mark.parametrize("T,L", [(8, 3), (128, 3), (1, 1), (8, 1), (128, 1)])
-def test_stack_step_tokens_and_single_layer(dev, T, L):
+QWEN = (2048, 128, 8, 768)
+
+
+@pytest.mark.parametrize("T,L,dims", [(8, 3, QWEN), (128, 3, QWEN), (1, 1, QWEN), (8, 1, QWEN), (128, 1, QWEN),
+                                      (1, 2, (3072, 32, 4, 768)), (8, 2, (3072, 32, 4, 768)),
+                                      (1, 2, (4096, 128, 8, 1536))])
+def test_stack_step_tokens_and_single_layer(dev, T, L, dims):
     """The stacked step at T = 8 and 128 tokens (the batched paths and the
-    router's norm prologue over several tokens) and with a single layer
-    (whose epilogue writes the next step's input over its own input):
-    eager and graph replays equal the chained moe_forward calls bit for bit;
-    layer 0 (seeded input) is held against the oracle token by token (ids,
-    y, x_next), later layers for properties."""
-    S = synth.Shape(f"stack-T{T}-L{L}", 40 + L, 2048, 128, 8, 768)
+    router's norm prologue over several tokens), with a single layer (whose
+    epilogue writes the next step's input over its own input), and on
+    hidden 3072 and a Qwen3-235B-A22B-shaped layer (hidden 4096, inter
+    1536): eager and graph replays equal the chained moe_forward calls bit
+    for bit; layer 0 (seeded input) is held against the oracle token by
+    token (ids, y, x_next), later layers for properties."""
+    H_, E_, k_, I_ = dims
+    S = synth.Shape(f"stack-T{T}-L{L}-h{H_}", 40 + L + (H_ != 2048), H_, E_, k_, I_)
     H, k = S.hidden, S.top_k
     plan = q.Plan(H, S.n_experts, k, S.inter, n_layers=L, max_tokens=T)
     blob = plan.upload_blob(layer_source(S), device=dev)
