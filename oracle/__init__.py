@@ -106,9 +106,11 @@ def lib():
         L.oracle_moe_token_act.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, ctypes.c_int32]
         L.oracle_resid_rmsnorm.restype = None
         L.oracle_resid_rmsnorm.argtypes = [vp, vp, i64, f64, vp, vp]
-        for fn in (L.oracle_emul_bf16, L.oracle_emul_fp16, L.oracle_emul_fp16_rtz):
+        for fn in (L.oracle_emul_bf16, L.oracle_emul_fp16, L.oracle_emul_fp16_rtz, L.oracle_emul_e4m3):
             fn.restype = f64
             fn.argtypes = [f64]
+        L.oracle_emul_fp8_hilo.restype = None
+        L.oracle_emul_fp8_hilo.argtypes = [vp, i64]
         L.oracle_emul_moe_token.restype = None
         L.oracle_emul_moe_token.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp] + [ctypes.c_int32] * 5
         _lib = L
@@ -355,8 +357,8 @@ def moe_layer(src, layer, x_bf16, logits=None, wr=None, act=ACT_SILU):
 # Weight, h and activation modes of the recipe emulation (see oracle.c): it
 # predicts a GPU arithmetic recipe's error; parity checks never use it.
 W_EXACT_CODES, W_BF16, W_FP16, W_BF16_HILO = 0, 1, 2, 3
-H_FP32, H_BF16, H_FP16, H_BF16_HILO = 0, 1, 2, 3
-X_BF16, X_FP16_RTZ = 0, 1
+H_FP32, H_BF16, H_FP16, H_BF16_HILO, H_FP8_HILO = 0, 1, 2, 3, 4
+X_BF16, X_FP16_RTZ, X_FP8_HILO = 0, 1, 2
 
 
 def emul_bf16(v):
@@ -369,6 +371,19 @@ def emul_fp16(v):
 
 def emul_fp16_rtz(v):
     return lib().oracle_emul_fp16_rtz(float(v))
+
+
+def emul_e4m3(v):
+    return lib().oracle_emul_e4m3(float(v))
+
+
+def emul_fp8_hilo(v):
+    """v (fp32, length a multiple of 32) as FP8 E4M3 hi + lo operands with
+    per-32 power-of-two scales (the recipe emulation's hmode 4 / xmode 2)."""
+    out = np.array(v, dtype=np.float32, copy=True)
+    assert out.ndim == 1 and out.size % 32 == 0
+    lib().oracle_emul_fp8_hilo(_p(out), out.size)
+    return out
 
 
 def emulate_moe_token(gates, ups, downs, w, x_bf16, wmode, hmode, xmode=X_BF16, act=ACT_SILU):

@@ -324,9 +324,16 @@ void oracle_resid_rmsnorm(const uint16_t* x_bf16, const double* y, int64_t n, do
  *          2: each weight rounded to fp16 (nearest even);
  *          3: each weight as bf16 hi + lo (hi = bf16(w), lo = bf16(w - hi)).
  *   hmode  0: h stored in fp32; 1: bf16; 2: fp16 (nearest even, overflow to
- *          infinity); 3: bf16 hi + lo.
+ *          infinity); 3: bf16 hi + lo; 4: FP8 E4M3 hi + lo with one
+ *          power-of-two scale per 32 consecutive values and plane (below).
  *   xmode  0: the bf16 activations as they are; 1: converted to fp16 toward
- *          zero (saturating at 65504), as a round-toward-zero conversion does.
+ *          zero (saturating at 65504), as a round-toward-zero conversion does;
+ *          2: FP8 E4M3 hi + lo with per-32 scales (below).
+ * FP8 hi + lo (the operand form of a block-scaled FP8 x FP4 matrix product
+ * with two passes over the activations): per block of 32 values v, the hi
+ * plane's scale is the smallest power of two s with max|v| / s <= 448 (the
+ * largest E4M3 value, so nothing saturates), hi = E4M3(v / s) * s; the lo
+ * plane does the same for the residual r = v - hi; the operand is hi + lo.
  */
 /* nearest value (ties to even), or toward zero, with p significant bits and
  * smallest normal exponent emin (below it the spacing stays 2^(emin-p+1)) */
@@ -353,6 +360,36 @@ double oracle_emul_bf16(double v) { return round_sig(v, 8, -126, 0); }
 double oracle_emul_fp16(double v) {
   double r = round_sig(v, 11, -14, 0);
   return fabs(r) > 65504.0 ? copysign(INFINITY, v) : r;
+}
+
+/* FP8 E4M3 (4 significant bits, smallest normal 2^-6, largest 448),
+ * nearest even; values beyond 448 saturate */
+double oracle_emul_e4m3(double v) {
+  double r = round_sig(v, 4, -6, 0);
+  return fabs(r) > 448.0 ? copysign(448.0, v) : r;
+}
+
+/* v[0..n) in place as FP8 hi + lo operands, blocks of 32 (n a multiple of 32) */
+static double pow2_scale(double amax) {
+  if (!(amax > 0.0)) return 1.0;
+  double s = ldexp(1.0, (int)ceil(log2(amax / 448.0)));
+  while (amax / s > 448.0) s *= 2.0;                   /* guard the log2 rounding */
+  while (s > 0.0 && amax / (s / 2.0) <= 448.0) s /= 2.0;
+  return s;
+}
+void oracle_emul_fp8_hilo(float* v, int64_t n) {
+  for (int64_t b = 0; b < n; b += 32) {
+    double amax = 0.0, rmax = 0.0, hi[32], r[32];
+    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)v[b + i]));
+    const double sh = pow2_scale(amax);
+    for (int i = 0; i < 32; ++i) {
+      hi[i] = oracle_emul_e4m3((double)v[b + i] / sh) * sh;
+      r[i] = (double)v[b + i] - hi[i];
+      rmax = fmax(rmax, fabs(r[i]));
+    }
+    const double sl = pow2_scale(rmax);
+    for (int i = 0; i < 32; ++i) v[b + i] = (float)(hi[i] + oracle_emul_e4m3(r[i] / sl) * sl);
+  }
 }
 
 double oracle_emul_fp16_rtz(double v) {
@@ -435,10 +472,12 @@ void oracle_emul_moe_token(const uint8_t* const* gate, const uint8_t* const* up,
     x[i] = (float)(xmode == 1 ? oracle_emul_fp16_rtz(xv) : xv);
     acc[i] = 0.0f;
   }
+  if (xmode == 2) oracle_emul_fp8_hilo(x, H);
   for (int64_t s = 0; s < k; ++s) {
     emul_qgemv(gate[s], I, H, x, g, fmt, wmode);
     emul_qgemv(up[s], I, H, x, u, fmt, wmode);
     for (int64_t i = 0; i < I; ++i) g[i] = emul_store_h((float)oracle_act(g[i], u[i], act), hmode);
+    if (hmode == 4) oracle_emul_fp8_hilo(g, I);
     emul_qgemv(down[s], H, I, g, ye, fmt, wmode);
     for (int64_t i = 0; i < H; ++i) acc[i] = fmaf((float)w[s], ye[i], acc[i]);
   }

@@ -631,3 +631,69 @@ def test_recipe_emulation_predicts_fp16_range_failure():
     for hm in (oracle.H_FP32, oracle.H_BF16_HILO):
         y, _ = oracle.emulate_moe_layer(src, 0, xs, oracle.W_EXACT_CODES, hm, act=R)
         assert np.abs(y - ref["y"]).max() / m < 2e-5, hm
+
+
+# ---------------------------------------------------------------- FP8 hi + lo operands (block-scaled MFMA recipe)
+def test_e4m3_rounding_against_torch():
+    """The emulation's FP8 E4M3 rounding equals torch's float8_e4m3fn
+    conversion (nearest even) on every E4M3 value, the midpoints between
+    neighbours (ties), points a quarter step either side, subnormals and
+    values up to 448; above 448 it saturates (torch's conversion does not,
+    so only the in-range values are compared)."""
+    import torch
+    codes = torch.arange(0, 256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    vals = np.sort(np.unique(codes[np.isfinite(codes)]))
+    pos = vals[vals >= 0]
+    mids = (pos[1:] + pos[:-1]) / 2
+    quarter = np.concatenate([pos[:-1] + (pos[1:] - pos[:-1]) / 4, pos[1:] - (pos[1:] - pos[:-1]) / 4])
+    probe = np.concatenate([pos, mids, quarter, -pos, -mids, -quarter, [2.0 ** -12, 3.3e-3, 100.5, 447.9]])
+    probe = probe[np.abs(probe) <= 448.0]
+    want = torch.from_numpy(probe.astype(np.float32)).to(torch.float8_e4m3fn).float().numpy()
+    got = np.array([oracle.emul_e4m3(v) for v in probe])
+    assert np.array_equal(got, want.astype(np.float64))
+    assert oracle.emul_e4m3(500.0) == 448.0 and oracle.emul_e4m3(-1e9) == -448.0
+    assert oracle.emul_e4m3(240.0) == 240.0 and oracle.emul_e4m3(232.0) == 224.0   # tie to the even code
+
+
+def test_fp8_hilo_operands():
+    """Per block of 32: the hi plane's scale is the smallest power of two
+    that keeps max|v| / s within 448, so small integers (4 significant bits)
+    come back exactly; a scaled block comes back scaled (powers of two
+    commute with the split); the error is below 2^-8 of the block's largest
+    magnitude; blocks are independent; zeros stay zero."""
+    rng = np.random.default_rng(5)
+    ints = rng.integers(-15, 16, size=64).astype(np.float32)
+    assert np.array_equal(oracle.emul_fp8_hilo(ints), ints)
+    v = rng.standard_normal(32 * 40).astype(np.float32) * np.repeat(2.0 ** rng.integers(-20, 20, 40), 32)
+    out = oracle.emul_fp8_hilo(v)
+    for b in range(40):
+        blk, ob = v[32 * b:32 * b + 32].astype(np.float64), out[32 * b:32 * b + 32].astype(np.float64)
+        assert np.abs(ob - blk).max() <= 2.0 ** -8 * np.abs(blk).max()
+    assert np.array_equal(oracle.emul_fp8_hilo(v * np.float32(2.0 ** 7)), out * np.float32(2.0 ** 7))
+    w = v.copy()
+    w[32:64] *= np.float32(1e6)                       # a loud neighbour does not change a block
+    assert np.array_equal(oracle.emul_fp8_hilo(w)[:32], out[:32])
+    assert np.array_equal(oracle.emul_fp8_hilo(np.zeros(32, np.float32)), np.zeros(32, np.float32))
+    # the hi plane alone would miss by up to 2^-4 relative: the lo plane is used
+    one = np.full(32, 1.0 + 2.0 ** -6, np.float32)
+    assert np.array_equal(oracle.emul_fp8_hilo(one), one)
+
+
+def test_recipe_emulation_block_scaled_fp8():
+    """P14: the block-scaled FP8 x FP4 recipe for MXFP4 experts (weights
+    exact, activations and h as FP8 hi + lo with per-32 scales) on the
+    Qwen3-30B-A3B-shaped MXFP4 layer: FP8 activations alone stay at fp32
+    level (< 1e-5 of max|y|: bf16 inputs fit hi + lo almost exactly) while
+    FP8 h costs about 7e-4, a third of the 2e-3 tolerance (between 3e-4
+    and 1.5e-3 on two tokens); h in bf16 hi + lo stays below 1e-5."""
+    S = synth.QWEN3_30B_A3B_MXFP4
+    src = oracle.ExpertSource(S)
+    xb = synth.x_bf16(S, 50, 4, T=2)
+    ref = oracle.moe_layer(src, 0, xb)
+    m = np.abs(ref["y"]).max()
+    def err(hm, xm):
+        y, _ = oracle.emulate_moe_layer(src, 0, xb, oracle.W_EXACT_CODES, hm, xm)
+        return np.abs(y - ref["y"]).max() / m
+    assert err(oracle.H_FP32, oracle.X_FP8_HILO) < 1e-5
+    assert 3e-4 <= err(oracle.H_FP8_HILO, oracle.X_FP8_HILO) <= 1.5e-3
+    assert err(oracle.H_BF16_HILO, oracle.X_FP8_HILO) < 1e-5
