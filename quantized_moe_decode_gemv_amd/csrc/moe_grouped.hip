@@ -10,19 +10,15 @@
 // v_mfma_f32_16x16x32_bf16 (lane layouts checked on the box:
 // A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], D[4(l/16)+r][l%16]).
 //
-// The MFMA operands are exact or split into exact parts, so the roundings
-// are fp32 accumulation, the storage of h and (on one kernel) a 2^-16 split:
+// Every MFMA operand is exact, so the only roundings are fp32 accumulation
+// and the storage of h:
 //  - activations: the bf16 inputs as they are;
 //  - MXFP4 weights: each code converted together with its block's E8M0 scale
 //    to the exact weight as a bf16 (scale codes 2..252 keep it normal);
 //  - 4-bit super-block weights: each code converted to the exact bf16 value q;
 //    one MFMA covers one 32-weight sub-block, P = A·q, the MFMA against ones
 //    gives S = A·1, and the sub-block affine (a = d*sc, b = dmin*m, weight =
-//    a q - b) is applied in fp32: acc += a P - b S. The K-outermost gate/up
-//    (above 12 pairs per expert), whose converted weights serve all of a
-//    tile's 16-pair blocks, instead forms w = a q - b in fp32 once per K
-//    chunk and feeds it as two bf16 operands hi + lo (w to about 2^-16
-//    relative), so its MFMAs accumulate over the whole K;
+//    a q - b) is applied in fp32: acc += a P - b S;
 //  - h = act(gate, up) is stored as two bf16 planes, hi = bf16(h) and lo =
 //    bf16(h - hi), so h = hi + lo to about 2^-17 relative with bf16's (fp32's)
 //    exponent range; the down GEMM runs its MFMAs on both planes.
@@ -107,37 +103,6 @@ __device__ __forceinline__ bf16x8 codes8_bf16(u32 v) {
   o.z = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false));   // (q1, q3)
   o.w = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true));    // (q5, q7)
   return __builtin_bit_cast(bf16x8, o);
-}
-
-// The eight weights w = a q - b of one code dword (a = d*sc, b = dmin*m of
-// their sub-block), in unpack order, as two bf16 operands with w = hi + lo
-// to about 2^-16 relative: hi is w truncated to its upper 16 bits (exact in
-// bf16), lo = w - hi (exact in fp32) rounded to bf16. q comes out exact from
-// the FP8 E4M3 byte 0x0q (q * 2^-9) at scale 2^9; a q and b are exact in
-// fp32 (a: 17 significant bits, q: 4), so w carries one fp32 rounding.
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void dequant8_hilo(u32 v, float a, float b, bf16x8& hi, bf16x8& lo) {
-  const u32 lo4 = v & 0x0F0F0F0Fu, hi4 = (v >> 4) & 0x0F0F0F0Fu;
-  const f32x2 q01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo4, 512.0f, false);   // (q0, q2)
-  const f32x2 q23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo4, 512.0f, true);    // (q4, q6)
-  const f32x2 q45 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi4, 512.0f, false);   // (q1, q3)
-  const f32x2 q67 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi4, 512.0f, true);    // (q5, q7)
-  const f32x2 qq[4] = {q01, q23, q45, q67};
-  u32x4 h, l;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float w0 = fmaf(a, qq[p][0], -b), w1 = fmaf(a, qq[p][1], -b);
-    const u32 b0 = __builtin_bit_cast(u32, w0), b1 = __builtin_bit_cast(u32, w1);
-    const u32 hp = __builtin_amdgcn_perm(b1, b0, 0x07060302u);       // (upper half of w0, of w1)
-    const f32x2 r = {w0 - __builtin_bit_cast(float, b0 & 0xFFFF0000u), w1 - __builtin_bit_cast(float, b1 & 0xFFFF0000u)};
-    const u32 lp = __builtin_bit_cast(u32, __builtin_convertvector(r, bf16x2v));
-    if (p == 0) { h.x = hp; l.x = lp; }
-    else if (p == 1) { h.y = hp; l.y = lp; }
-    else if (p == 2) { h.z = hp; l.z = lp; }
-    else { h.w = hp; l.w = lp; }
-  }
-  hi = __builtin_bit_cast(bf16x8, h);
-  lo = __builtin_bit_cast(bf16x8, l);
 }
 
 // Eight bf16 values (16 bytes, natural order) in unpack order.
@@ -605,6 +570,7 @@ __device__ __forceinline__ void g16k_body(const uint8_t* __restrict__ rec, int H
   f32x4 accg[NBR], accu[NBR];
 #pragma unroll
   for (int b = 0; b < NBR; ++b) accg[b] = accu[b] = ZERO4;
+  const bf16x8 one = ones8();
   load_x(0);
   load_codes(0);
   for (int c0 = 0; c0 < H; c0 += KCH) {
@@ -636,26 +602,27 @@ __device__ __forceinline__ void g16k_body(const uint8_t* __restrict__ rec, int H
         }
       }
     } else {
-      // each weight dequantized once per chunk into exact bf16 hi + lo
-      // operands shared by all of the tile's 16-pair blocks; the MFMAs
-      // accumulate over the whole K with no per-sub-block epilogue
       transpose4(ncg);
       transpose4(ncu);
       const Affine4 ag = affine4(nsg, sb_own), au = affine4(nsu, sb_own);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        bf16x8 bgh, bgl, buh, bul;
-        dequant8_hilo(dword_of(ncg, i), ag.a[i], ag.b[i], bgh, bgl);
-        dequant8_hilo(dword_of(ncu, i), au.a[i], au.b[i], buh, bul);
+        const bf16x8 bg = codes8_bf16(dword_of(ncg, i));
+        const bf16x8 bu = codes8_bf16(dword_of(ncu, i));
 #pragma unroll
         for (int b = 0; b < NBR; ++b) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(&xs[16 * b + r][32 * i + 8 * kg]);
-          accg[b] = mfma(a, bgh, accg[b]);
-          accu[b] = mfma(a, buh, accu[b]);
-          accg[b] = mfma(a, bgl, accg[b]);
-          accu[b] = mfma(a, bul, accu[b]);
+          const f32x4 S = mfma(a, one, ZERO4);
+          const f32x4 Pg = mfma(a, bg, ZERO4), Pu = mfma(a, bu, ZERO4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            accg[b][q] = fmaf(ag.a[i], Pg[q], fmaf(-ag.b[i], S[q], accg[b][q]));
+            accu[b][q] = fmaf(au.a[i], Pu[q], fmaf(-au.b[i], S[q], accu[b][q]));
+          }
         }
       }
+      pin<NBR>(accg);
+      pin<NBR>(accu);
     }
   }
   // D[tt][rr] of block b: pair 16 b + tt, tt = 4 kg + q; row rr = lane % 16
