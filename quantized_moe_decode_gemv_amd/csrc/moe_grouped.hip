@@ -867,7 +867,7 @@ __global__ __launch_bounds__(BLOCK) void combine_kernel(const float* __restrict_
 
 // ------------------------------------------------------------------ launchers
 // rows: 0 one row block per gate/up workgroup and per down wave; 1 the
-// multi-row kernels (2 row blocks per gate/up wave, 4 per down wave), which
+// multi-row kernels (2 row blocks per gate/up wave, 2 or 4 per down wave), which
 // read a tile's activations and h fewer times but run fewer workgroups; 2
 // (above 6 pairs per expert) MXFP4 gate/up splits rows over the waves; 3
 // (above 12 pairs per expert) gate/up runs K outermost and reuses each
@@ -894,7 +894,10 @@ static hipError_t launch_g16_f(const Layout& d, const uint8_t* layer, const uint
                        d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.k, x, pairs, tiles, hb, d.act, hlo);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int NW = 4;                          // row blocks per wave of the multi-row down
+  // row blocks per wave of the multi-row down: 4 for MXFP4; 2 for
+  // super-blocks, whose affine epilogue needs more registers (239 -> 143,
+  // two -> three waves per SIMD: 3-6 % faster from 32 to 1024 tokens)
+  constexpr int NW = FMT == FMT_Q4K ? 2 : 4;
   if (rows && d.H % (64 * NW) == 0) {
     hipLaunchKernelGGL((down_g16m_kernel<GD, NW, FMT>), dim3(tile_unit_grid(ntiles, d.H / (64 * NW))), dim3(BLOCK), 0, s,
                        layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, pairs, tiles, hb, ypair, hlo,
