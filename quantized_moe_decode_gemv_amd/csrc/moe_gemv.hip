@@ -75,9 +75,14 @@ __device__ void wave_topk(const float* __restrict__ lg, int E, int k, bool want_
 #pragma unroll
   for (int b = 31; b >= 0; --b) {
     const u32 cand = thr | (1u << b);
+    // all compares first, into masks of their own, so their latencies
+    // overlap before the counts read them
+    unsigned long long m[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) m[c] = __builtin_amdgcn_uicmp(key[c], cand, 35);   // 35: unsigned >=
     int cnt = 0;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) cnt += __popcll(__ballot(key[c] >= cand));
+    for (int c = 0; c < NC; ++c) cnt += __popcll(m[c]);
     if (cnt >= k) {
       thr = cand;
       if (cnt == k) break;
