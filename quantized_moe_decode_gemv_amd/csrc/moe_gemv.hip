@@ -89,19 +89,30 @@ __device__ void wave_topk(const float* __restrict__ lg, int E, int k, bool want_
     }
   }
   const unsigned long long below = lane ? (~0ull >> (WAVE - lane)) : 0ull;
+  // the selection's compares up front, into masks of their own: keys above
+  // T, and keys equal to T among ids < E
+  unsigned long long gtm[NC], eqm[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int nv = E - WAVE * c;                   // ids < E in this group of 64
+    const unsigned long long vm = nv >= WAVE ? ~0ull : (nv > 0 ? (1ull << nv) - 1 : 0ull);
+    gtm[c] = __builtin_amdgcn_uicmp(key[c], thr, 34);          // 34: unsigned >
+    eqm[c] = __builtin_amdgcn_uicmp(key[c], thr, 32) & vm;     // 32: ==
+  }
   int gt = 0;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) gt += __popcll(__ballot(key[c] > thr));
+  for (int c = 0; c < NC; ++c) gt += __popcll(gtm[c]);
   const int need = k - gt;                         // >= 1 places left for keys equal to T
   int ties_before = 0, base = 0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int id = lane + WAVE * c;
-    const bool eq = key[c] == thr && id < E;
-    const unsigned long long em = __ballot(eq);
-    const bool sel = key[c] > thr || (eq && ties_before + __popcll(em & below) < need);
+    const unsigned long long em = eqm[c];
+    const bool eq = (em >> lane) & 1ull;
+    const bool sel = ((gtm[c] >> lane) & 1ull) || (eq && ties_before + __popcll(em & below) < need);
     ties_before += __popcll(em);
-    const unsigned long long sm_mask = __ballot(sel);
+    // without keys equal to T in the group the selection is the keys above it
+    const unsigned long long sm_mask = em ? __ballot(sel) : gtm[c];
     if (sel) {
       const int pos = base + __popcll(sm_mask & below);
       sm.ckey[pos] = ((unsigned long long)key[c] << 32) | (u32)~(u32)id;
