@@ -166,18 +166,9 @@ def main():
     # kernel's execution, rotating over all layers (so no layer's experts are
     # cache-resident from the previous launch)
     gu_bytes = S.top_k * S.inter * 2 * (S.hidden // 256) * 144
-    times = []
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
-    for a, b in evs:            # torch creates the HIP event on first record
-        a.record(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    for rep in range(args.kernel_reps):
-        for l in range(L):
-            plan.profile_gate_up(blob, l, xs[l], 1, evs[l][0], evs[l][1], scratch=scratch, stream=stream)
-        torch.cuda.synchronize()
-        times += [a.elapsed_time(b) for a, b in evs]
+    times = gate_up_launch_times(plan, blob, xs, L, args.kernel_reps, scratch, stream, torch)
     gu_us = float(np.mean(times)) * 1e3
+    gu_p50 = float(np.median(times)) * 1e3
     gu_gbps = gu_bytes / (gu_us * 1e-6) / 1e9
     log(f"gate/up kernel: {gu_us:.2f} us avg over {len(times)} launches, {gu_gbps:.0f} GB/s")
 
@@ -249,6 +240,8 @@ def main():
             "traffic": traffic,
             "bytes_per_launch": gu_bytes,
             "avg_launch_us": round(gu_us, 3),
+            "median_launch_us": round(gu_p50, 3),
+            "launches": len(times),
         },
         "step_time": step_pct,
         "single_layer": single,
@@ -259,6 +252,25 @@ def main():
         "outputs_finite": finite,
     }
     print(json.dumps(result), flush=True)
+
+
+def gate_up_launch_times(plan, blob, xs, L, reps, scratch, stream, torch):
+    """Durations (ms) of reps x L gate/up launches (router, then gate/up with
+    HIP events around it, rotating over the layers so no layer's experts are
+    cache-resident from the previous launch), preceded by one pass over the
+    layers that is not kept; every launch has events of its own and all
+    passes are queued back to back, so the GPU does not idle between them."""
+    n = (reps + 1) * L
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:            # torch creates the HIP event on first record
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        l = i % L
+        plan.profile_gate_up(blob, l, xs[l], 1, a, b, scratch=scratch, stream=stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs[L:]]
 
 
 def decode_timeline(plan, blob, graph, stream, L, ms_per_step, q, np, torch, reps=6, batch=48):
@@ -412,17 +424,7 @@ def mxfp4_decode(L, dev, stream, args, q, np, torch, synth):
     expert_bytes = L * S.top_k * S.expert_bytes
     # gate/up kernel alone, rotating over the layers
     gu_bytes = S.top_k * S.inter * 2 * S.hidden // 32 * 17
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
-    for a, b in evs:
-        a.record(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    times = []
-    for rep in range(args.kernel_reps):
-        for l in range(L):
-            plan.profile_gate_up(blob, l, xs[l], 1, evs[l][0], evs[l][1], scratch=scratch, stream=stream)
-        torch.cuda.synchronize()
-        times += [a.elapsed_time(b) for a, b in evs]
+    times = gate_up_launch_times(plan, blob, xs, L, args.kernel_reps, scratch, stream, torch)
     gu_us = float(np.mean(times)) * 1e3
     batched = None
     if not args.no_batched:
