@@ -275,22 +275,22 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
   const int t = ts / k;
   const int rho = lane / LPR, lam = lane % LPR;
   // the activation slice does not depend on the routing: load it first so
-  // its round trip overlaps the routing's
+  // its round trip overlaps the routing's (super-blocks: its pairing and
+  // sums wait until the weight loads have left, below)
   u32 X[IPL][16];
   float S[IPL];
+  u32x4 xr[IPL][4];
 #pragma unroll
   for (int q = 0; q < IPL; ++q) {
     const int j = lam + LPR * q;
+    load_x_raw(x + (size_t)t * H + 32 * j, xr[q]);
     if constexpr (FMT == FMT_MXFP4) {
-      u32x4 r[4];
-      load_x_raw(x + (size_t)t * H + 32 * j, r);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        X[q][4 * m] = r[m].x; X[q][4 * m + 1] = r[m].y; X[q][4 * m + 2] = r[m].z; X[q][4 * m + 3] = r[m].w;
+        X[q][4 * m] = xr[q][m].x; X[q][4 * m + 1] = xr[q][m].y;
+        X[q][4 * m + 2] = xr[q][m].z; X[q][4 * m + 3] = xr[q][m].w;
       }
       S[q] = 0.f;
-    } else {
-      S[q] = load_x_pairs(x + (size_t)t * H + 32 * j, X[q]);
     }
   }
   if (fused_topk) {
@@ -354,6 +354,14 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
       cu[u][q] = load_nt(rp + half + 16 * j);
       hg[u][q] = load_nt(rp + hdr + QHDR * (j >> 3));
       hu[u][q] = load_nt(rp + hdr + QHDR * nb + QHDR * (j >> 3));
+    }
+    if (u == 0) {
+      // the activation pairing and sums after the first row's loads have
+      // left, so they overlap its round trip instead of delaying its start;
+      // the later rows keep the compiler's placement
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < IPL; ++q) S[q] = x_pairs(xr[q], X[q]);
     }
   }
 #pragma unroll
