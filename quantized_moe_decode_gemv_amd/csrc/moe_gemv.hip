@@ -414,17 +414,20 @@ __global__ __launch_bounds__(NW * WAVE) void down_kernel(
   const int IW = (G + NW - 1) / NW;
   const int i = wid * IW + lane;
   const bool valid = lane < IW && i < G;
-  // an idle lane takes the item of the wave's last busy lane: its loads hit
-  // lines already fetched, and ws = 0 and a zero h make its share zero
+  // an idle lane takes the item of the wave's last busy lane, so every load
+  // below is in bounds and none is conditional: the weight loads then wait
+  // for the expert id alone, not for h and ws as well (a conditional load
+  // makes the compiler drain every load in flight). An idle lane's ws and h
+  // are zeroed where they are used, and its loads hit lines already fetched.
   const int ic = min(wid * IW + min(lane, IW - 1), G - 1);
   const int s = ic / nsb;
   const int j = ic % nsb;
   const int e = ids[(size_t)t * k + s];
-  const float ws = valid ? wts[(size_t)t * k + s] : 0.f;
+  const float ws_raw = wts[(size_t)t * k + s];
   u32x4 hr[8];
   const float* hp = h + ((size_t)t * k + s) * I + 32 * j;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) hr[c] = valid ? load16(hp + 4 * c) : u32x4{0u, 0u, 0u, 0u};
+  for (int c = 0; c < 8; ++c) hr[c] = load16(hp + 4 * c);
   const uint8_t* row0 = dn + (size_t)e * dn_expert_bytes + (size_t)n0 * drow_bytes;
   using Hdr = std::conditional_t<FMT == FMT_MXFP4, u32, u32x4>;
   u32x4 cd[R];
@@ -438,11 +441,12 @@ __global__ __launch_bounds__(NW * WAVE) void down_kernel(
   }
   // every weight load in flight before the first use of h
   __builtin_amdgcn_sched_barrier(0);
+  const float ws = valid ? ws_raw : 0.f;
   float hv[32];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    hv[4 * c] = as_f32(hr[c].x); hv[4 * c + 1] = as_f32(hr[c].y);
-    hv[4 * c + 2] = as_f32(hr[c].z); hv[4 * c + 3] = as_f32(hr[c].w);
+    hv[4 * c] = valid ? as_f32(hr[c].x) : 0.f; hv[4 * c + 1] = valid ? as_f32(hr[c].y) : 0.f;
+    hv[4 * c + 2] = valid ? as_f32(hr[c].z) : 0.f; hv[4 * c + 3] = valid ? as_f32(hr[c].w) : 0.f;
   }
   float p[R];
   if constexpr (FMT == FMT_MXFP4) {
