@@ -50,27 +50,20 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Top-k of E <= 64*NC logits by one wave (k <= 16 <= E; descending, equal
-// logits -> lower id first), into sm.sid / sm.val, and with want_weights the
-// softmax restricted to the selection into sm.sw. Lane l holds the logits of
-// ids l + 64c (c < NC) as order keys (a > b <=> key(a) > key(b)).
-// A threshold T is built bit by bit from the top: a bit stays set when at
-// least k keys reach the prefix with it set (ballot + popcount per 64 keys);
-// the search stops early once exactly k keys reach T. Every key above T is
-// selected and keys equal to T fill the remaining places in id order (after
-// a full search T is the k-th largest key; after an early stop the keys
-// reaching T are exactly the k largest). Only the k selected keys are then
-// ranked, against each other. Ids >= E are never selected.
+// logits -> lower id first), in three steps that a caller may separate:
+// topk_threshold, topk_select (the selection, in id order, into sm.ckey /
+// sm.cval) and topk_rank (its order, into sm.sid / sm.val, and optionally
+// the softmax restricted to the selection into sm.sw). Lane l holds the
+// logits of ids l + 64c (c < NC) as order keys (a > b <=> key(a) > key(b)),
+// and key 0 for ids >= E.
+//
+// topk_threshold: a threshold T is built bit by bit from the top: a bit stays
+// set when at least k keys reach the prefix with it set (compare masks +
+// popcount per 64 keys); the search stops early once exactly k keys reach T.
+// After a full search T is the k-th largest key; after an early stop the keys
+// reaching T are exactly the k largest.
 template <int NC>
-__device__ void wave_topk(const float* __restrict__ lg, int E, int k, bool want_weights, TopkSmem& sm) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  float v[NC];
-  u32 key[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int id = lane + WAVE * c;
-    v[c] = id < E ? lg[id] : 0.f;
-    key[c] = id < E ? order_key(v[c]) : 0u;
-  }
+__device__ __forceinline__ u32 topk_threshold(const u32 (&key)[4], int k) {
   u32 thr = 0u;
 #pragma unroll
   for (int b = 31; b >= 0; --b) {
@@ -88,6 +81,18 @@ __device__ void wave_topk(const float* __restrict__ lg, int E, int k, bool want_
       if (cnt == k) break;
     }
   }
+  return thr;
+}
+
+// topk_select: every key above T is selected and keys equal to T fill the
+// remaining places in id order; ids >= E are never selected. The selection
+// is stored in id order: sm.ckey[p] = key << 32 | ~id (distinct, a larger
+// value means a higher logit or, on equal logits, a lower id), sm.cval[p]
+// its logit, p < k. No wait on the stores: the caller orders them.
+template <int NC>
+__device__ __forceinline__ void topk_select(const u32 (&key)[4], const float (&v)[4], int E, int k, u32 thr,
+                                            TopkSmem& sm) {
+  const int lane = threadIdx.x & (WAVE - 1);
   const unsigned long long below = lane ? (~0ull >> (WAVE - lane)) : 0ull;
   // the selection's compares up front, into masks of their own: keys above
   // T, and keys equal to T among ids < E
@@ -120,7 +125,13 @@ __device__ void wave_topk(const float* __restrict__ lg, int E, int k, bool want_
     }
     base += __popcll(sm_mask);
   }
-  wave_lds_sync();
+}
+
+// topk_rank: the rank of a selected key is the number of selected keys
+// above it; only the k selected keys are compared, against each other.
+// Reads the selection topk_select stored (visible to this wave).
+__device__ __forceinline__ void topk_rank(int k, bool want_weights, TopkSmem& sm) {
+  const int lane = threadIdx.x & (WAVE - 1);
   if (lane < k) {
     const unsigned long long mk = sm.ckey[lane];
     int r = 0;
@@ -137,6 +148,36 @@ __device__ void wave_topk(const float* __restrict__ lg, int E, int k, bool want_
     sm.sw[lane] = __expf(sm.val[lane] - l0) / den;
   }
   wave_lds_sync();
+}
+
+// The rank of selection entry p (id order) among the k selected: every
+// lane reads all 16 entries at once and counts those above entry p.
+__device__ __forceinline__ int topk_entry_rank(const TopkSmem& sm, int p, int k) {
+  unsigned long long c[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) c[j] = sm.ckey[j];
+  const unsigned long long mine = sm.ckey[p];
+  int r = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) r += (j < k && c[j] > mine) ? 1 : 0;
+  return r;
+}
+
+template <int NC>
+__device__ void wave_topk(const float* __restrict__ lg, int E, int k, bool want_weights, TopkSmem& sm) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  float v[4];
+  u32 key[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int id = lane + WAVE * c;
+    v[c] = (c < NC && id < E) ? lg[id] : 0.f;
+    key[c] = (c < NC && id < E) ? order_key(v[c]) : 0u;
+  }
+  const u32 thr = topk_threshold<NC>(key, k);
+  topk_select<NC>(key, v, E, k, thr, sm);
+  wave_lds_sync();
+  topk_rank(k, want_weights, sm);
 }
 
 __device__ __forceinline__ void wave_topk_any(const float* __restrict__ lg, int E, int k, bool want_weights,
@@ -252,6 +293,24 @@ __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__
 // Wave work unit: RPS*U consecutive intermediate rows of one (token, slot);
 // RPS = 64/LPR rows per step, LPR lanes per row, IPL sub-blocks per lane.
 // h[(t*k + s)*I + r] = SiLU(G_e[r]·x_t) * (U_e[r]·x_t).
+// Fused routing, after a wave's weight loads have left: the output row of
+// its slot (selection entry p, T == 1) is the entry's rank; wave 0 of block 0
+// also ranks the whole selection, forms the softmax over it and publishes
+// ids and weights in rank order.
+__device__ __forceinline__ int fused_rank_publish(TopkSmem& sm, int p, int k, int wid, int32_t* __restrict__ ids_out,
+                                                  float* __restrict__ w_out) {
+  const int r = topk_entry_rank(sm, p, k);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && wid == 0) {
+    topk_rank(k, true, sm);
+    const int lane = threadIdx.x & (WAVE - 1);
+    if (lane < k) {
+      ids_out[lane] = sm.sid[lane];
+      w_out[lane] = sm.sw[lane];
+    }
+  }
+  return r;
+}
+
 // ACT: the gate activation as a template argument, so the epilogue on this
 // kernel's critical path carries no branch. FMT: the weight encoding; with
 // MXFP4 a lane's sub-block is one 32-code block with its E8M0 scale byte.
@@ -265,16 +324,53 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
   QMOE_TL_SCOPE(gu, 1);
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x / WAVE;
-  const int unit = blockIdx.x * (BLOCK / WAVE) + wid;
-  const int rows_per_unit = RPS * U;
-  const int total_units = T * k * I / rows_per_unit;
-  const bool active = unit < total_units;
-  const int flat0 = active ? unit * rows_per_unit : 0;   // flat row index over (t, s, r)
-  const int ts = flat0 / I;                               // t*k + s
-  const int r0 = flat0 % I;
-  const int t = ts / k;
+  // fused routing (T == 1): wave 0's logit loads leave first (every one in
+  // bounds, so the search waits for them alone)
+  float lv[4];
+  u32 lk[4];
+  if (fused_topk && wid == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int id = lane + WAVE * c;
+      lv[c] = logits[id < E ? id : E - 1];
+    }
+  }
+  // grid (I / (4 * RPS * U), k, T): no division stands before a load
+  const int t = blockIdx.z;
+  const int ts = t * k + blockIdx.y;                      // t*k + s
+  const int r0 = (blockIdx.x * (BLOCK / WAVE) + wid) * (RPS * U);
   const int rho = lane / LPR, lam = lane % LPR;
-  // the activation slice does not depend on the routing: load it first so
+  // the expert stride in registers and the lane's row offsets (bytes from
+  // the expert's base; an expert spans less than 4 GiB) formed before the
+  // routing, so only the expert's base is left to form after it
+  size_t geb = gu_expert_bytes;
+  float* hout = h;
+  asm volatile("" : "+s"(geb), "+s"(hout));
+  const int half = H / 2;                 // code bytes per matrix row
+  const int hdr = H / 2 * 2;              // headers start after both code areas
+  // per row and sub-block: gate codes, up codes, gate header, up header
+  // (super-blocks) or gate codes, up codes, gate scale, up scale (MXFP4)
+  u32 off[U][IPL][4];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const u32 ro = (u32)(r0 + u * RPS + rho) * (u32)rp_bytes;
+#pragma unroll
+    for (int q = 0; q < IPL; ++q) {
+      const u32 j = lam + LPR * q;
+      off[u][q][0] = ro + 16 * j;
+      off[u][q][1] = ro + half + 16 * j;
+      if constexpr (FMT == FMT_MXFP4) {
+        off[u][q][2] = ro + hdr + j;
+        off[u][q][3] = ro + hdr + H / MXK + j;
+      } else {
+        off[u][q][2] = ro + hdr + QHDR * (j >> 3);
+        off[u][q][3] = ro + hdr + QHDR * (H / QK) + QHDR * (j >> 3);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) asm volatile("" : "+v"(off[u][q][m]));
+    }
+  }
+  // the activation slice does not depend on the routing: load it next so
   // its round trip overlaps the routing's (super-blocks: its pairing and
   // sums wait until the weight loads have left, below)
   u32 X[IPL][16];
@@ -294,38 +390,45 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
     }
   }
   if (fused_topk) {
-    // T == 1: wave 0 of every block derives the same routing from the logits;
-    // block 0 also publishes it with the weights.
+    // T == 1: wave 0 of every block derives the same selection from the
+    // logits, in id order; a wave's slot is an entry of it. Only the
+    // threshold search and the selection stand before the weight loads: the
+    // order of the selection (where a slot's output row goes) is taken after
+    // they have left, and so is block 0's publication of the routing.
     if (wid == 0) {
-      wave_topk_any(logits, E, k, blockIdx.x == 0, s_topk);
-      if (blockIdx.x == 0 && lane < k) {
-        ids_out[lane] = s_topk.sid[lane];
-        w_out[lane] = s_topk.sw[lane];
-      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lk[c] = lane + WAVE * c < E ? order_key(lv[c]) : 0u;
+      if (E <= WAVE) topk_select<1>(lk, lv, E, k, topk_threshold<1>(lk, k), s_topk);
+      else if (E <= 2 * WAVE) topk_select<2>(lk, lv, E, k, topk_threshold<2>(lk, k), s_topk);
+      else if (E <= 3 * WAVE) topk_select<3>(lk, lv, E, k, topk_threshold<3>(lk, k), s_topk);
+      else topk_select<4>(lk, lv, E, k, topk_threshold<4>(lk, k), s_topk);
     }
     __syncthreads();
     QMOE_TL_MARK(5);
   }
-  if (!active) return;
-  const int e = fused_topk ? s_topk.sid[ts] : ids_in[ts];
-  const uint8_t* base = gu + (size_t)e * gu_expert_bytes;
-  const int half = H / 2;                 // code bytes per matrix row
-  const int hdr = H / 2 * 2;              // headers start after both code areas
+  // the selection entry is read unconditionally (any in-bounds entry when
+  // not fused), so the routing read stays an LDS read
+  const unsigned long long sel_key = s_topk.ckey[ts < 16 ? ts : 0];
+  const int e = fused_topk ? (int)~(u32)sel_key : ids_in[ts];
+  int hrow = ts;                          // output row of h: t*k + rank of the slot
+  const uint8_t* base = gu + (size_t)e * geb;
   if constexpr (FMT == FMT_MXFP4) {
     // scale bytes: gate's H/32, then up's
     u32x4 cg[U][IPL], cu[U][IPL];
     u32 sg[U][IPL], su[U][IPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint8_t* rp = base + (size_t)(r0 + u * RPS + rho) * rp_bytes;
 #pragma unroll
       for (int q = 0; q < IPL; ++q) {
-        const int j = lam + LPR * q;
-        cg[u][q] = load_nt(rp + 16 * j);
-        cu[u][q] = load_nt(rp + half + 16 * j);
-        sg[u][q] = __builtin_nontemporal_load(rp + hdr + j);
-        su[u][q] = __builtin_nontemporal_load(rp + hdr + H / MXK + j);
+        cg[u][q] = load_nt(base + off[u][q][0]);
+        cu[u][q] = load_nt(base + off[u][q][1]);
+        sg[u][q] = __builtin_nontemporal_load(base + off[u][q][2]);
+        su[u][q] = __builtin_nontemporal_load(base + off[u][q][3]);
       }
+    }
+    if (fused_topk) {
+      __builtin_amdgcn_sched_barrier(0);
+      hrow = fused_rank_publish(s_topk, ts, k, wid, ids_out, w_out);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -338,32 +441,36 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
       pg = group_sum<LPR>(pg);
       pu = group_sum<LPR>(pu);
       if (u == 0) QMOE_TL_MARK(6);
-      if (lam == 0) h[(size_t)ts * I + r0 + u * RPS + rho] = gate_act(pg, pu, ACT);
+      if (lam == 0) hout[(size_t)hrow * I + r0 + u * RPS + rho] = gate_act(pg, pu, ACT);
     }
     return;
   }
-  const int nb = H / QK;
   u32x4 cg[U][IPL], cu[U][IPL], hg[U][IPL], hu[U][IPL];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint8_t* rp = base + (size_t)(r0 + u * RPS + rho) * rp_bytes;
 #pragma unroll
     for (int q = 0; q < IPL; ++q) {
-      const int j = lam + LPR * q;
-      cg[u][q] = load_nt(rp + 16 * j);
-      cu[u][q] = load_nt(rp + half + 16 * j);
-      hg[u][q] = load_nt(rp + hdr + QHDR * (j >> 3));
-      hu[u][q] = load_nt(rp + hdr + QHDR * nb + QHDR * (j >> 3));
+      cg[u][q] = load_nt(base + off[u][q][0]);
+      cu[u][q] = load_nt(base + off[u][q][1]);
+      hg[u][q] = load_nt(base + off[u][q][2]);
+      hu[u][q] = load_nt(base + off[u][q][3]);
     }
     if (u == 0) {
       // the activation pairing and sums after the first row's loads have
-      // left, so they overlap its round trip instead of delaying its start;
-      // the later rows keep the compiler's placement
+      // left, so they overlap its round trip instead of delaying its start,
+      // and before the later rows' loads (the empty asm keeps the compiler
+      // from sinking them below the routing epilogue)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < IPL; ++q) S[q] = x_pairs(xr[q], X[q]);
+      for (int q = 0; q < IPL; ++q) {
+        S[q] = x_pairs(xr[q], X[q]);
+        asm volatile("" : "+v"(S[q]));
+#pragma unroll
+        for (int m = 0; m < 16; ++m) asm volatile("" : "+v"(X[q][m]));
+      }
     }
   }
+  if (fused_topk) hrow = fused_rank_publish(s_topk, ts, k, wid, ids_out, w_out);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     float pg = 0.f, pu = 0.f;
@@ -380,7 +487,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
     pg = group_sum<LPR>(pg);
     pu = group_sum<LPR>(pu);
     if (u == 0) QMOE_TL_MARK(6);
-    if (lam == 0) h[(size_t)ts * I + r0 + u * RPS + rho] = gate_act(pg, pu, ACT);
+    if (lam == 0) hout[(size_t)hrow * I + r0 + u * RPS + rho] = gate_act(pg, pu, ACT);
   }
 }
 
@@ -401,14 +508,14 @@ template <int R, int FMT, int NW>
 __global__ __launch_bounds__(NW * WAVE) void down_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I, int k,
     const int32_t* __restrict__ ids, const float* __restrict__ wts, const float* __restrict__ h,
-    float* __restrict__ y, int T) {
+    float* __restrict__ y, int T, u32 nsb_inv) {
   __shared__ float part[NW][R];
   QMOE_TL_SCOPE(dn, 2);
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x / WAVE;
-  const int bpt = H / R;                           // blocks per token
-  const int t = blockIdx.x / bpt;
-  const int n0 = (blockIdx.x % bpt) * R;
+  // grid (H / R, T): no division stands before a load
+  const int t = blockIdx.y;
+  const int n0 = blockIdx.x * R;
   const int nsb = I / 32;
   const int G = k * nsb;
   const int IW = (G + NW - 1) / NW;
@@ -420,8 +527,10 @@ __global__ __launch_bounds__(NW * WAVE) void down_kernel(
   // makes the compiler drain every load in flight). An idle lane's ws and h
   // are zeroed where they are used, and its loads hit lines already fetched.
   const int ic = min(wid * IW + min(lane, IW - 1), G - 1);
-  const int s = ic / nsb;
-  const int j = ic % nsb;
+  // ic / nsb as a multiply by nsb_inv = ceil(2^32 / nsb): exact for every
+  // ic < 2^32 / nsb (here ic < 512), the rounding error staying below 1/nsb
+  const int s = (int)__umulhi((u32)ic, nsb_inv);
+  const int j = ic - s * nsb;
   const int e = ids[(size_t)t * k + s];
   const float ws_raw = wts[(size_t)t * k + s];
   u32x4 hr[8];
@@ -705,16 +814,18 @@ static void gateup_go_act(const Layout& d, const uint8_t* layer, const uint16_t*
                           const float* logits, int32_t* ids_out, float* w_out, float* h, int T, bool fused,
                           hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr int RPS = WAVE / LPR;
-  const long long units = (long long)T * d.k * d.I / (RPS * U);
-  const int blocks = (int)((units + 3) / 4);
+  // a block's four waves take 4 * RPS * U consecutive rows of one (token,
+  // slot); I is a multiple of 256, so every block is full
+  const dim3 grid(d.I / (4 * RPS * U), d.k, T);
+  if (T <= 0) return;
   if (ev0 || ev1) {
     // measurement launch: the events bracket this kernel's execution
-    hipExtLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s, ev0, ev1,
+    hipExtLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT>), grid, dim3(BLOCK), 0, s, ev0, ev1,
                           0, layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
                           ids_out, w_out, h, T, fused ? 1 : 0);
     return;
   }
-  hipLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT>), dim3(blocks > 0 ? blocks : 1), dim3(BLOCK), 0, s,
+  hipLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT>), grid, dim3(BLOCK), 0, s,
                      layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
                      ids_out, w_out, h, T, fused ? 1 : 0);
 }
@@ -774,14 +885,18 @@ hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids
   const int G = d.k * (d.I / 32);
   if (G > 8 * WAVE || d.H % RM) return hipErrorInvalidValue;
   if (T <= 0) return hipSuccess;
+  const int nsb = d.I / 32;                  // >= 8
+  const u32 nsb_inv = (u32)((0x100000000ull + nsb - 1) / nsb);
   // four waves cover up to 256 items of a row, eight up to 512
 #define QMOE_DOWN(NW)                                                                                              \
   if (d.fmt == FMT_MXFP4)                                                                                          \
-    hipLaunchKernelGGL((down_kernel<RM, FMT_MXFP4, NW>), dim3(T * (d.H / RM)), dim3(NW * WAVE), 0, s,              \
-                       layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T);    \
+    hipLaunchKernelGGL((down_kernel<RM, FMT_MXFP4, NW>), dim3(d.H / RM, T), dim3(NW * WAVE), 0, s,                 \
+                       layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T,     \
+                       nsb_inv);                                                                                   \
   else                                                                                                             \
-    hipLaunchKernelGGL((down_kernel<RQ, FMT_Q4K, NW>), dim3(T * (d.H / RQ)), dim3(NW * WAVE), 0, s,                \
-                       layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T)
+    hipLaunchKernelGGL((down_kernel<RQ, FMT_Q4K, NW>), dim3(d.H / RQ, T), dim3(NW * WAVE), 0, s,                   \
+                       layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T,     \
+                       nsb_inv)
   if (G > 4 * WAVE) {
     QMOE_DOWN(8);
   } else {

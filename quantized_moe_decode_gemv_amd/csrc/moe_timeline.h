@@ -6,7 +6,7 @@
 // 0 router, 1 gate/up, 2 down, 3 the stand-alone residual + RMSNorm), where
 // the layer is found from the kernel's weight pointer: (pointer - base) /
 // layer_bytes, with base and layer_bytes set by moe_timeline_setup. Per slot
-// and workgroup (the first TL_WGS workgroups) the record holds
+// and workgroup (the first TL_WGS workgroups, by linear index) the record holds
 //   [0] s_memrealtime (100 MHz) when thread 0 starts,
 //   [1..4] s_memrealtime when each of the four waves leaves the kernel,
 //   [5], [6] two marks a kernel sets at points of its own.
@@ -37,19 +37,23 @@ __device__ inline int tl_slot(const void* p, int kind) {
   return layer < (unsigned long long)TL_LAYERS ? 4 * (int)layer + kind : -1;
 }
 
+// the workgroup's linear index (x fastest, then y, then z)
+__device__ inline unsigned tl_wg() { return blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z); }
+
 struct TLScope {
   int slot;
-  __device__ TLScope(const void* p, int kind) : slot(tl_slot(p, kind)) {
-    if (threadIdx.x == 0 && slot >= 0 && blockIdx.x < TL_WGS)
-      tl_rec[slot][blockIdx.x][0] = __builtin_amdgcn_s_memrealtime();
+  unsigned wg;
+  __device__ TLScope(const void* p, int kind) : slot(tl_slot(p, kind)), wg(tl_wg()) {
+    if (threadIdx.x == 0 && slot >= 0 && wg < TL_WGS)
+      tl_rec[slot][wg][0] = __builtin_amdgcn_s_memrealtime();
   }
   __device__ ~TLScope() {
-    if ((threadIdx.x & 63) == 0 && threadIdx.x < 256 && slot >= 0 && blockIdx.x < TL_WGS)
-      tl_rec[slot][blockIdx.x][1 + threadIdx.x / 64] = __builtin_amdgcn_s_memrealtime();
+    if ((threadIdx.x & 63) == 0 && threadIdx.x < 256 && slot >= 0 && wg < TL_WGS)
+      tl_rec[slot][wg][1 + threadIdx.x / 64] = __builtin_amdgcn_s_memrealtime();
   }
   __device__ void mark(int field) const {
-    if (threadIdx.x == 0 && slot >= 0 && blockIdx.x < TL_WGS)
-      tl_rec[slot][blockIdx.x][field] = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0 && slot >= 0 && wg < TL_WGS)
+      tl_rec[slot][wg][field] = __builtin_amdgcn_s_memrealtime();
   }
 };
 }  // namespace qmoe

@@ -9,8 +9,8 @@ import torch
 import oracle
 import synth
 import quantized_moe_decode_gemv_amd as q
-from helpers import (REL_TOL, check_bf16_vector, check_outputs, check_routing, layer_source, reference_outputs,
-                     rel_err)
+from helpers import (REL_TOL, TAU, W_TOL, check_bf16_vector, check_outputs, check_routing, layer_source,
+                     reference_outputs, rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -396,6 +396,71 @@ def test_route_from_logits_and_dispatch_lists(qwen, T, zipf):
     assert np.array_equal(counts.cpu().numpy(), np.bincount(flat, minlength=S.n_experts))
     assert np.array_equal(offsets.cpu().numpy(), np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=S.n_experts))]))
     assert np.array_equal(pairs.cpu().numpy(), np.argsort(flat, kind="stable"))
+
+
+# ------------------------------------------------------------------ exact ties in the fused routing
+def _tied_router(S, xrow):
+    """The seeded router with rows copied so that the layer input's logits
+    tie exactly: the largest logit's row copied into one more expert (a tie
+    inside the selection), and the row of the expert that then ranks k-th
+    copied into one lower and one higher id from outside the selection (a tie
+    across the selection boundary, which the lowest id of the three wins).
+    Returns the router, or None when this input leaves a distinct logit
+    within the near-tie margin of another or no such ids exist."""
+    wr = synth.router(S, 0).copy()
+    k = S.top_k
+    order = np.argsort(-oracle.router_logits(wr, xrow), kind="stable")
+    a, b = int(order[0]), int(order[-1])
+    wr[b] = wr[a]
+    c = int(order[k - 2])                          # k-th once b has joined the top
+    rest = [int(e) for e in order[k - 1:-1]]
+    lo = [e for e in rest if e < c]
+    hi = [e for e in rest if e > c]
+    if not lo or not hi:
+        return None
+    wr[min(lo)] = wr[c]
+    wr[max(hi)] = wr[c]
+    d = np.unique(oracle.router_logits(wr, xrow))
+    if np.diff(d).min() <= TAU:
+        return None
+    return wr
+
+
+TIE_SHAPES = [
+    synth.Shape("ties-e128-k8", 21, 512, 128, 8, 256),
+    synth.Shape("ties-e200-k16", 22, 512, 200, 16, 256),
+    synth.Shape("ties-e40-k4", 23, 256, 40, 4, 256),
+    synth.Shape("ties-e128-k8-mxfp4", 21, 512, 128, 8, 256, synth.FMT_MXFP4),
+]
+
+
+@pytest.mark.parametrize("shape", TIE_SHAPES, ids=[s.name for s in TIE_SHAPES])
+def test_fused_routing_exact_ties(dev, shape):
+    """Single-token layers take their routing inside the gate/up kernel. With
+    logits tied bit for bit (copied router rows), the selection and its order
+    must be the oracle's (equal logits: lower id first) exactly, and so must
+    the weights and outputs, for one, two and four groups of 64 logits, a
+    ragged expert count, k = 16 and both encodings."""
+    for case in range(40):
+        xb = synth.x_bf16(shape, 30 + case, 0, T=1)
+        wr = _tied_router(shape, xb[0])
+        if wr is not None:
+            break
+    assert wr is not None, "no input gave a usable tie pattern"
+
+    def src(layer):
+        return (synth.layer_experts(shape, layer, synth.GATE), synth.layer_experts(shape, layer, synth.UP),
+                synth.layer_experts(shape, layer, synth.DOWN), wr)
+
+    st = Setup(shape, dev, n_layers=1, max_tokens=1, flags=MX if shape.fmt == synth.FMT_MXFP4 else 0)
+    st.blob = st.plan.upload_blob(src, device=dev)
+    got = st.forward(xb)
+    ref = oracle.moe_layer(st.src, 0, xb, wr=wr)
+    lg = ref["logits"][0]
+    assert len(set(lg[ref["ids"][0]].tolist())) < shape.top_k        # ties inside the selection
+    assert np.array_equal(got["ids"][0], ref["ids"][0]), (got["ids"][0], ref["ids"][0])
+    assert np.abs(got["w"][0] - ref["w"][0]).max() <= W_TOL
+    check_outputs(got["y"], ref["y"], label=shape.name)
 
 
 # ------------------------------------------------------------------ stacked-layer epilogue
