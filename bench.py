@@ -114,6 +114,10 @@ def main():
     stream = torch.cuda.Stream()
     xs[0].copy_(torch.from_numpy(x0[0].view(np.int16)))
     torch.cuda.synchronize()
+    if args.timeline:
+        # the profiling build takes the layer base as kernel arguments, which
+        # the graph keeps from its capture
+        timeline_setup(plan, blob, q)
     graph = plan.capture_step(blob, xs, ys, 1, ids, ws, scratch=scratch, stream=stream)
     log("decode step captured as one graph")
 
@@ -273,6 +277,16 @@ def gate_up_launch_times(plan, blob, xs, L, reps, scratch, stream, torch):
     return [a.elapsed_time(b) for a, b in evs[L:]]
 
 
+def timeline_setup(plan, blob, q):
+    """Hands the profiling build the blob's first layer and the layer size,
+    from which its kernels find their layer (before the step is captured)."""
+    import ctypes
+    lib = q.load()
+    lib.moe_timeline_setup.restype = ctypes.c_int
+    lib.moe_timeline_setup.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong]
+    assert lib.moe_timeline_setup(blob.data_ptr() + plan.layer_offset(0), plan.layer_bytes()) == 0
+
+
 def decode_timeline(plan, blob, graph, stream, L, ms_per_step, q, np, torch, reps=6, batch=48):
     """Per-layer timeline of the captured decode step from the profiling
     build's s_memrealtime stamps (the tick measured here against the host
@@ -285,12 +299,9 @@ def decode_timeline(plan, blob, graph, stream, L, ms_per_step, q, np, torch, rep
     last of `batch` back-to-back replays."""
     import ctypes
     lib = q.load()
-    lib.moe_timeline_setup.restype = ctypes.c_int
-    lib.moe_timeline_setup.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong]
     lib.moe_timeline_reset.restype = ctypes.c_int
     lib.moe_timeline_read.restype = ctypes.c_int
     lib.moe_timeline_read.argtypes = [ctypes.c_void_p]
-    assert lib.moe_timeline_setup(blob.data_ptr() + plan.layer_offset(0), plan.layer_bytes()) == 0
     assert L <= 64
     rec = np.zeros((256, 1024, 8), dtype=np.uint64)
 

@@ -226,7 +226,8 @@ __device__ __forceinline__ float block_sum4(float v, float* part) {
 template <int CH, bool NORM>  // chunks of 4 weights per thread: H = CH * 1024
 __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__ wr, const uint16_t* __restrict__ x,
                                                        const float* __restrict__ y_prev, uint16_t* __restrict__ x_out,
-                                                       float eps, float* __restrict__ logits, int E, int H, int T) {
+                                                       float eps, float* __restrict__ logits, int E, int H,
+                                                       int T QMOE_TL_PARAMS) {
   // the norm's and the dot's reductions use one part array each (without the
   // norm, tokens alternate between the two)
   __shared__ float part[2][BLOCK / WAVE];
@@ -318,7 +319,8 @@ template <int IPL, int LPR, int U, int ACT, int FMT>
 __global__ __launch_bounds__(BLOCK) void gateup_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int E, int k,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids_in, const float* __restrict__ logits,
-    int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ h, int T, int fused_topk) {
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ h, int T,
+    int fused_topk QMOE_TL_PARAMS) {
   constexpr int RPS = WAVE / LPR;
   __shared__ TopkSmem s_topk;
   QMOE_TL_SCOPE(gu, 1);
@@ -508,7 +510,7 @@ template <int R, int FMT, int NW>
 __global__ __launch_bounds__(NW * WAVE) void down_kernel(
     const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I, int k,
     const int32_t* __restrict__ ids, const float* __restrict__ wts, const float* __restrict__ h,
-    float* __restrict__ y, int T, u32 nsb_inv) {
+    float* __restrict__ y, int T, u32 nsb_inv QMOE_TL_PARAMS) {
   __shared__ float part[NW][R];
   QMOE_TL_SCOPE(dn, 2);
   const int lane = threadIdx.x & (WAVE - 1);
@@ -594,7 +596,7 @@ __global__ __launch_bounds__(NW * WAVE) void down_kernel(
 // complete before the block barrier inside the sum, so x and xn are not
 // declared restrict.
 __global__ __launch_bounds__(BLOCK) void resid_norm_kernel(const uint16_t* x, const float* __restrict__ y, uint16_t* xn,
-                                                           int H, float eps) {
+                                                           int H, float eps QMOE_TL_PARAMS) {
   __shared__ float part[BLOCK / WAVE];
   QMOE_TL_SCOPE(nullptr, 3);
   const int t = blockIdx.x;
@@ -757,9 +759,11 @@ static hipError_t launch_router_big(const Layout& d, const float* wr, const uint
   dim3 grid(d.E), block(BLOCK);
 #define QMOE_ROUTER(C)                                                                                        \
   if (y_prev)                                                                                                 \
-    hipLaunchKernelGGL((router_kernel<C, true>), grid, block, 0, s, wr, x, y_prev, x_out, d.eps, logits, d.E, d.H, T); \
+    hipLaunchKernelGGL((router_kernel<C, true>), grid, block, 0, s, wr, x, y_prev, x_out, d.eps, logits, d.E, d.H, \
+                       T QMOE_TL_ARGS);                                                                            \
   else                                                                                                        \
-    hipLaunchKernelGGL((router_kernel<C, false>), grid, block, 0, s, wr, x, y_prev, x_out, d.eps, logits, d.E, d.H, T)
+    hipLaunchKernelGGL((router_kernel<C, false>), grid, block, 0, s, wr, x, y_prev, x_out, d.eps, logits, d.E, d.H, \
+                       T QMOE_TL_ARGS)
   switch (CH) {
     case 1: QMOE_ROUTER(1); break;
     case 2: QMOE_ROUTER(2); break;
@@ -822,12 +826,12 @@ static void gateup_go_act(const Layout& d, const uint8_t* layer, const uint16_t*
     // measurement launch: the events bracket this kernel's execution
     hipExtLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT>), grid, dim3(BLOCK), 0, s, ev0, ev1,
                           0, layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
-                          ids_out, w_out, h, T, fused ? 1 : 0);
+                          ids_out, w_out, h, T, fused ? 1 : 0 QMOE_TL_ARGS);
     return;
   }
   hipLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT>), grid, dim3(BLOCK), 0, s,
                      layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
-                     ids_out, w_out, h, T, fused ? 1 : 0);
+                     ids_out, w_out, h, T, fused ? 1 : 0 QMOE_TL_ARGS);
 }
 
 template <int IPL, int LPR, int U>
@@ -892,11 +896,11 @@ hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids
   if (d.fmt == FMT_MXFP4)                                                                                          \
     hipLaunchKernelGGL((down_kernel<RM, FMT_MXFP4, NW>), dim3(d.H / RM, T), dim3(NW * WAVE), 0, s,                 \
                        layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T,     \
-                       nsb_inv);                                                                                   \
+                       nsb_inv QMOE_TL_ARGS);                                                                      \
   else                                                                                                             \
     hipLaunchKernelGGL((down_kernel<RQ, FMT_Q4K, NW>), dim3(d.H / RQ, T), dim3(NW * WAVE), 0, s,                   \
                        layer + d.dn_off, d.dn_expert_bytes, (int)d.drow_bytes, d.H, d.I, d.k, ids, w, h, y, T,     \
-                       nsb_inv)
+                       nsb_inv QMOE_TL_ARGS)
   if (G > 4 * WAVE) {
     QMOE_DOWN(8);
   } else {
@@ -907,7 +911,7 @@ hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids
 }
 
 hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y, uint16_t* x_next, int T, hipStream_t s) {
-  hipLaunchKernelGGL(resid_norm_kernel, dim3(T), dim3(BLOCK), 0, s, x, y, x_next, d.H, d.eps);
+  hipLaunchKernelGGL(resid_norm_kernel, dim3(T), dim3(BLOCK), 0, s, x, y, x_next, d.H, d.eps QMOE_TL_ARGS);
   return hipGetLastError();
 }
 
@@ -956,15 +960,15 @@ hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int T, int 
 #ifdef QMOE_TIMELINE
 namespace qmoe {
 __device__ unsigned long long tl_rec[TL_SLOTS][TL_WGS][TL_FIELDS];
-__device__ const uint8_t* tl_base;
-__device__ unsigned long long tl_layer_bytes;
+const uint8_t* tl_host_base = nullptr;
+float tl_host_inv = 0.f;
 }  // namespace qmoe
 
 extern "C" int moe_timeline_setup(const void* layer0, unsigned long long layer_bytes) {
-  const uint8_t* b = static_cast<const uint8_t*>(layer0);
-  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(qmoe::tl_base), &b, sizeof(b));
-  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(qmoe::tl_layer_bytes), &layer_bytes, sizeof(layer_bytes));
-  return (int)e;
+  if (!layer0 || layer_bytes == 0) return (int)hipErrorInvalidValue;
+  qmoe::tl_host_base = static_cast<const uint8_t*>(layer0);
+  qmoe::tl_host_inv = (float)(256.0 / (double)layer_bytes);
+  return (int)hipSuccess;
 }
 
 extern "C" int moe_timeline_reset(void) {

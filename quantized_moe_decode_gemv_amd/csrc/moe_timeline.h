@@ -4,10 +4,14 @@
 //
 // Each launch of an instrumented kernel owns a slot, 4 * layer + kind (kind
 // 0 router, 1 gate/up, 2 down, 3 the stand-alone residual + RMSNorm), where
-// the layer is found from the kernel's weight pointer: (pointer - base) /
-// layer_bytes, with base and layer_bytes set by moe_timeline_setup. Per slot
-// and workgroup (the first TL_WGS workgroups, by linear index) the record holds
-//   [0] s_memrealtime (100 MHz) when thread 0 starts,
+// the layer is found from the kernel's weight pointer: (pointer - base) *
+// (1 / layer_bytes), with base and 256 / layer_bytes passed as two extra kernel
+// arguments (QMOE_TL_PARAMS / QMOE_TL_ARGS) from the values
+// moe_timeline_setup stored on the host, so the instrumentation adds no
+// memory round trip before a kernel's own loads. A graph keeps the values it
+// was captured with: call moe_timeline_setup before capturing. Per slot and
+// workgroup (the first TL_WGS workgroups, by linear index) the record holds
+//   [0] s_memrealtime (100 MHz) when thread 0 starts (its first instruction),
 //   [1..4] s_memrealtime when each of the four waves leaves the kernel,
 //   [5], [6] two marks a kernel sets at points of its own.
 // Host exports of the profiling build (extern "C", return hipError_t as int):
@@ -25,16 +29,20 @@
 namespace qmoe {
 constexpr int TL_LAYERS = 64, TL_SLOTS = 4 * TL_LAYERS, TL_WGS = 1024, TL_FIELDS = 8;
 extern __device__ unsigned long long tl_rec[TL_SLOTS][TL_WGS][TL_FIELDS];
-extern __device__ const uint8_t* tl_base;
-extern __device__ unsigned long long tl_layer_bytes;
+extern const uint8_t* tl_host_base;     // set by moe_timeline_setup
+extern float tl_host_inv;               // 256 / layer_bytes
 
-__device__ inline int tl_slot(const void* p, int kind) {
+__device__ inline int tl_slot(const void* p, int kind, const uint8_t* b, float inv) {
   if (kind == 3) return 3;
-  const uint8_t* b = tl_base;
-  const unsigned long long lb = tl_layer_bytes;
-  if (!b || lb == 0 || (const uint8_t*)p < b) return -1;
-  const unsigned long long layer = (unsigned long long)((const uint8_t*)p - b) / lb;
-  return layer < (unsigned long long)TL_LAYERS ? 4 * (int)layer + kind : -1;
+  if (!b || (const uint8_t*)p < b) return -1;
+  // in units of 256 bytes (inv = 256 / layer_bytes)
+  const unsigned long long d = (unsigned long long)((const uint8_t*)p - b) >> 8;
+  if (d >> 32) return -1;
+  // a kernel's weight pointer lies less than 3/4 of a layer past its layer's
+  // start; the product's error (< 64 * 2^-22, plus the truncated bytes) is
+  // far below the 1/8 added
+  const int layer = (int)((float)(unsigned)d * inv + 0.125f);
+  return layer < TL_LAYERS ? 4 * layer + kind : -1;
 }
 
 // the workgroup's linear index (x fastest, then y, then z)
@@ -43,9 +51,12 @@ __device__ inline unsigned tl_wg() { return blockIdx.x + gridDim.x * (blockIdx.y
 struct TLScope {
   int slot;
   unsigned wg;
-  __device__ TLScope(const void* p, int kind) : slot(tl_slot(p, kind)), wg(tl_wg()) {
-    if (threadIdx.x == 0 && slot >= 0 && wg < TL_WGS)
-      tl_rec[slot][wg][0] = __builtin_amdgcn_s_memrealtime();
+  // the start is read before anything else and stored once the slot is known
+  __device__ TLScope(const void* p, int kind, const uint8_t* b, float inv) {
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    slot = tl_slot(p, kind, b, inv);
+    wg = tl_wg();
+    if (threadIdx.x == 0 && slot >= 0 && wg < TL_WGS) tl_rec[slot][wg][0] = t0;
   }
   __device__ ~TLScope() {
     if ((threadIdx.x & 63) == 0 && threadIdx.x < 256 && slot >= 0 && wg < TL_WGS)
@@ -58,9 +69,13 @@ struct TLScope {
 };
 }  // namespace qmoe
 
-#define QMOE_TL_SCOPE(ptr, kind) const qmoe::TLScope qmoe_tl_scope_((ptr), (kind))
+#define QMOE_TL_PARAMS , const uint8_t *qmoe_tl_b, float qmoe_tl_inv
+#define QMOE_TL_ARGS , qmoe::tl_host_base, qmoe::tl_host_inv
+#define QMOE_TL_SCOPE(ptr, kind) const qmoe::TLScope qmoe_tl_scope_((ptr), (kind), qmoe_tl_b, qmoe_tl_inv)
 #define QMOE_TL_MARK(field) qmoe_tl_scope_.mark(field)
 #else
+#define QMOE_TL_PARAMS
+#define QMOE_TL_ARGS
 #define QMOE_TL_SCOPE(ptr, kind)
 #define QMOE_TL_MARK(field) \
   do {                     \
