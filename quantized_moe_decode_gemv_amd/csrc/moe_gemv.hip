@@ -232,6 +232,9 @@ __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__
   // norm, tokens alternate between the two)
   __shared__ float part[2][BLOCK / WAVE];
   QMOE_TL_SCOPE(wr, 0);
+  // every kernel argument in registers before the first load (the compiler
+  // otherwise fetches them in dependent batches, each a scalar round trip)
+  asm volatile("" ::"s"(wr), "s"(x), "s"(y_prev), "s"(x_out), "s"(eps), "s"(logits), "s"(E), "s"(H), "s"(T));
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
   float w[CH][4];
@@ -240,7 +243,9 @@ __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + (size_t)e * H + 4 * (tid + BLOCK * c)));
     w[c][0] = as_f32(v.x); w[c][1] = as_f32(v.y); w[c][2] = as_f32(v.z); w[c][3] = as_f32(v.w);
   }
-  for (int t = 0; t < T; ++t) {
+  // T >= 1 (the launcher skips empty batches), so the first token's loads
+  // are not held behind a test of T
+  for (int t = 0;;) {
     uint2 xq[CH];
     u32x4 yq[CH];
 #pragma unroll
@@ -287,6 +292,7 @@ __global__ __launch_bounds__(BLOCK) void router_kernel(const float* __restrict__
       for (int i = 0; i < 4; ++i) acc = fmaf(w[c][i], xv[c][i], acc);
     const float tot = block_sum4(acc, part[NORM ? 1 : (t & 1)]);
     if (tid == 0) logits[(size_t)t * E + e] = tot;
+    if (++t >= T) break;
   }
 }
 
@@ -324,6 +330,10 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
   constexpr int RPS = WAVE / LPR;
   __shared__ TopkSmem s_topk;
   QMOE_TL_SCOPE(gu, 1);
+  // the kernel arguments the first loads need, in registers at once (the
+  // compiler otherwise fetches the logits pointer only after testing
+  // fused_topk, a second scalar round trip)
+  asm volatile("" ::"s"(logits), "s"(E), "s"(fused_topk), "s"(x), "s"(H), "s"(k));
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x / WAVE;
   // fused routing (T == 1): wave 0's logit loads leave first (every one in
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int id = lane + WAVE * c;
-      lv[c] = logits[id < E ? id : E - 1];
+      lv[c] = logits[(u32)(id < E ? id : E - 1)];
     }
   }
   // grid (I / (4 * RPS * U), k, T): no division stands before a load
@@ -757,6 +767,7 @@ static hipError_t launch_router_big(const Layout& d, const float* wr, const uint
                                     uint16_t* x_out, float* logits, int T, hipStream_t s) {
   const int CH = d.H / 1024;
   dim3 grid(d.E), block(BLOCK);
+  if (T <= 0) return hipSuccess;           // the kernel takes at least one token
 #define QMOE_ROUTER(C)                                                                                        \
   if (y_prev)                                                                                                 \
     hipLaunchKernelGGL((router_kernel<C, true>), grid, block, 0, s, wr, x, y_prev, x_out, d.eps, logits, d.E, d.H, \
