@@ -50,13 +50,14 @@ enum moe_status {
 
 /* Routing/FFN path choice for moe_expert_ffn and moe_forward (moe_config.flags,
  * at most one of them). T = 1 always takes the per-token GEMV. Without a flag
- * the choice goes by routed pairs per expert, P/E = T*top_k/n_experts: below
- * 1/2 the per-token GEMV (each routed expert streamed once per token); up to
- * 1 (MXFP4 weights: 1.75) the expert-major GEMV (each routed expert streamed
- * once, its tokens held in registers; needs inter <= 2048); beyond, the MFMA
- * tiles (grouped GEMMs on tiles of 16, 64 or 128 routed pairs of one expert;
- * hidden 512, 1024 or 2048 and inter <= 1024). Shapes without the tiles keep
- * the expert-major GEMV. Every path computes with exact operands and fp32
+ * the choice goes by routed pairs per expert, P/E = T*top_k/n_experts. Shapes
+ * with the MFMA tiles (grouped GEMMs on tiles of 16, 64 or 128 routed pairs of
+ * one expert; hidden 512, 1024 or 2048 and inter <= 1024): the per-token GEMV
+ * (each routed expert streamed once per token) below P/E = 1 (MXFP4 weights:
+ * up to 1), the tiles beyond. Other shapes: the per-token GEMV below 1/2,
+ * beyond it the expert-major GEMV (each routed expert streamed once, its
+ * tokens held in registers; needs inter <= 2048), which the flag below also
+ * selects for any shape. Every path computes with exact operands and fp32
  * accumulation (h in fp32, or as bf16 hi + lo planes on the tiles), so the
  * results agree to fp32-level rounding over the whole input range. */
 #define MOE_FLAG_FORCE_GEMV 0x1u         /* per-token dequant-on-read GEMV for every T */

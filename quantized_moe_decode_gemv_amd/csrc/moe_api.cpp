@@ -272,12 +272,15 @@ static const uint8_t* layer_ptr(const moe_plan* plan, const void* blob, int32_t 
 // tiles stream each routed expert once per batch, the former with the tokens
 // of an expert held in registers, the latter as GEMMs on tiles of 16, 64 or
 // 128 pairs, which pay off once experts carry several pairs. The switches
-// are in routed pairs per expert, P/E with P = T*k (measured on the
-// Qwen3-30B-A3B-shaped layer: the per-token GEMV ahead up to 6 tokens,
-// P/E = 0.375; the expert-major GEMV from 8 tokens, 0.5, up to P/E = 1 with
-// super-block weights and 1.75 with MXFP4 weights). Shapes without the MFMA
-// tiles keep the expert-major GEMV (or the per-token GEMV where that does
-// not apply either).
+// are in routed pairs per expert, P/E with P = T*k. Measured per call (route
+// + FFN) on the Qwen3-30B-A3B-shaped layer, T = 4..32: the per-token GEMV
+// is ahead while P < E (T <= 15; MXFP4 weights: P <= E, T <= 16) and the
+// tiles beyond, with the expert-major GEMV behind one of the two at every T
+// (e.g. T = 8: 53.0 / 59.5 / 63.7 us, T = 16: 87.3 / 92.2 / 83.4 us; MXFP4
+// T = 20: 86.5 / 114.8 / 80.9 us). Shapes without the tiles take the
+// expert-major GEMV from P/E = 1/2 (its reads per batch against the
+// per-token GEMV's per token), or the per-token GEMV where that does not
+// apply either.
 enum class Path { Gemv, ExpertGemv, Tiles };
 static Path choose_path(const moe_plan* plan, int32_t T) {
   const Layout& d = plan->d;
@@ -285,10 +288,9 @@ static Path choose_path(const moe_plan* plan, int32_t T) {
   if (d.flags & MOE_FLAG_FORCE_GROUPED) return Path::Tiles;       // cfg_ok: the shape has the tiles
   if (d.flags & MOE_FLAG_FORCE_EXPERT_GEMV) return Path::ExpertGemv;
   const long long P = (long long)T * d.k, E = d.E;
-  if (2 * P < E) return Path::Gemv;
-  const bool past_egemv = d.fmt == FMT_MXFP4 ? 4 * P > 7 * E : P > E;
-  if (g16_supported(d) && (past_egemv || !egemv_supported(d))) return Path::Tiles;
-  return egemv_supported(d) ? Path::ExpertGemv : Path::Gemv;
+  if (g16_supported(d)) return (d.fmt == FMT_MXFP4 ? P <= E : P < E) ? Path::Gemv : Path::Tiles;
+  if (2 * P < E || !egemv_supported(d)) return Path::Gemv;
+  return Path::ExpertGemv;
 }
 
 // Work list of each batched path in scratch: one record per MFMA tile, or

@@ -239,14 +239,14 @@ def test_forward_batched_auto_batched_path_tiny(tiny):
         check_bf16_vector(got["xn"][t], ref_next)
 
 
-@pytest.mark.parametrize("T", [1, 7, 8, 16, 17, 96, 97, 192, 193])
+@pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 96, 97, 192, 193])
 def test_forward_auto_path_boundary_qwen(qwen, T):
-    """Without flags moe_forward runs the per-token GEMV path while T*k < E/2
-    (T <= 7 here), the expert-major GEMV path while T*k <= E (T <= 16), then
-    the MFMA tiles: multi-row kernels up to 6 pairs per expert (T <= 96), the
-    multi-row gate/up on 64-pair tiles up to 12 (T <= 192) and the
-    K-outermost gate/up beyond: both sides of each switch against the oracle
-    (every 3rd token and the last above 16 tokens)."""
+    """Without flags moe_forward runs the per-token GEMV path while T*k < E
+    (T <= 15 here), then the MFMA tiles: 16-pair tiles at T*k = E (T = 16),
+    the multi-row kernels on 64-pair tiles up to 6 pairs per expert (T <= 96),
+    the multi-row gate/up up to 12 (T <= 192) and the K-outermost gate/up
+    beyond: both sides of each switch against the oracle (every 3rd token and
+    the last above 16 tokens)."""
     xb = synth.x_bf16(qwen.shape, 10, T, T=T)
     sample = None if T <= 16 else sorted(set(range(0, T, 3)) | {T - 1})
     _check_layer(qwen, xb, qwen.forward(xb), sample=sample)
@@ -654,12 +654,12 @@ def test_mx_qwen_forward_single_tokens(mx_qwen):
     print(f"MXFP4 decode, 6 tokens: worst max|err|/max|ref| = {worst:.3e}")
 
 
-@pytest.mark.parametrize("T", [7, 8, 16, 28, 29, 64])
+@pytest.mark.parametrize("T", [7, 8, 16, 17, 29, 64])
 def test_mx_qwen_batched_tokens(mx_qwen, T):
-    """Batches with MXFP4 weights: 7 tokens run the per-token GEMV path, 8 to
-    28 the expert-major GEMV, 29 and 64 the MFMA tiles (64-pair tiles walked
-    16 pairs at a time); 64 tokens are checked on a sample, routing and
-    outputs of every token for properties."""
+    """Batches with MXFP4 weights: up to 16 tokens (T*k <= E) run the
+    per-token GEMV path, 17 and more the MFMA tiles (64-pair tiles walked 16
+    pairs at a time); above 8 tokens a sample is checked, routing and outputs
+    of every token for properties."""
     xb = synth.x_bf16(mx_qwen.shape, 41, T, T=T)
     got = mx_qwen.forward(xb)
     sample = None if T <= 8 else [0, 1, T // 2, T - 2, T - 1]
