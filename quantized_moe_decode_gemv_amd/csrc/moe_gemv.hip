@@ -824,15 +824,26 @@ hipError_t launch_topk(const Layout& d, const float* logits, int32_t* ids, float
   return hipGetLastError();
 }
 
+// Grid dimensions past x hold at most this many blocks; longer batches are
+// launched in chunks of tokens.
+constexpr int GRID_YZ_MAX = 65535;
+
 template <int IPL, int LPR, int U, int ACT, int FMT>
 static void gateup_go_act(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids,
                           const float* logits, int32_t* ids_out, float* w_out, float* h, int T, bool fused,
                           hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr int RPS = WAVE / LPR;
+  if (T <= 0) return;
+  if (T > GRID_YZ_MAX) {   // per-token path only (fused routing and timed launches are single tokens)
+    for (int t0 = 0; t0 < T; t0 += GRID_YZ_MAX)
+      gateup_go_act<IPL, LPR, U, ACT, FMT>(d, layer, x + (size_t)t0 * d.H, ids + (size_t)t0 * d.k, logits, ids_out,
+                                           w_out, h + (size_t)t0 * d.k * d.I, min(GRID_YZ_MAX, T - t0), false, s,
+                                           nullptr, nullptr);
+    return;
+  }
   // a block's four waves take 4 * RPS * U consecutive rows of one (token,
   // slot); I is a multiple of 256, so every block is full
   const dim3 grid(d.I / (4 * RPS * U), d.k, T);
-  if (T <= 0) return;
   if (ev0 || ev1) {
     // measurement launch: the events bracket this kernel's execution
     hipExtLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT>), grid, dim3(BLOCK), 0, s, ev0, ev1,
@@ -900,6 +911,14 @@ hipError_t launch_down(const Layout& d, const uint8_t* layer, const int32_t* ids
   const int G = d.k * (d.I / 32);
   if (G > 8 * WAVE || d.H % RM) return hipErrorInvalidValue;
   if (T <= 0) return hipSuccess;
+  if (T > GRID_YZ_MAX) {
+    for (int t0 = 0; t0 < T; t0 += GRID_YZ_MAX) {
+      const hipError_t e = launch_down(d, layer, ids + (size_t)t0 * d.k, w + (size_t)t0 * d.k,
+                                       h + (size_t)t0 * d.k * d.I, y + (size_t)t0 * d.H, min(GRID_YZ_MAX, T - t0), s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   const int nsb = d.I / 32;                  // >= 8
   const u32 nsb_inv = (u32)((0x100000000ull + nsb - 1) / nsb);
   // four waves cover up to 256 items of a row, eight up to 512

@@ -589,6 +589,20 @@ def test_edge_shapes(dev, shape):
         _check_layer(st, xb, st.forward(xb))
 
 
+def test_per_token_path_past_grid_limit(dev):
+    """A batch of more tokens than a grid dimension past x holds (65535) on
+    the per-token GEMV path, whose gate/up and down grids carry the tokens
+    there: the launches go out in chunks of tokens. Tokens on both sides of
+    the chunk boundary, and the last, against the oracle; all outputs finite."""
+    S = synth.TINY
+    T = 65537
+    st = Setup(S, dev, n_layers=1, max_tokens=T, flags=q.FLAG_FORCE_GEMV)
+    xb = synth.x_bf16(S, 50, T, T=T)
+    got = st.forward(xb)
+    _check_layer(st, xb, got, sample=[0, 1, 65533, 65534, 65535, 65536])
+    assert np.isfinite(got["y"]).all()
+
+
 @pytest.mark.parametrize("shape", EDGE, ids=[s.name for s in EDGE])
 @pytest.mark.parametrize("path", ["grouped", "expert_gemv", "gemv"])
 def test_edge_shapes_batched_paths(dev, shape, path):
