@@ -319,8 +319,8 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16_kernel(
 // added in wave order through LDS, as in the one-block kernel.
 template <int G, int NW, int FMT>
 __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
-    const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles,
+    const uint8_t* gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
+    const uint16_t* x, const int32_t* pairs, const TileRec* __restrict__ tiles,
     uint16_t* __restrict__ hb, int act, size_t hlo, int ntiles) {
   constexpr bool MX = FMT == FMT_MXFP4;
   constexpr int NH = MX ? G : (G + 1) / 2;     // scale bytes, or super-block headers, per row
@@ -336,6 +336,21 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int r = lane & 15, kg = lane >> 4;
   const int sb0 = w * 4 * G;                    // first 32-block of the wave's K range
+  // the activations of a 16-pair block come at the end of a dependent chain
+  // (token ids, then activations): the first block's ids leave before the
+  // weights, its activations as soon as the ids arrive (before the code
+  // transposes wait for the weights), and each later block's ids and
+  // activations while the block before it is reduced and stored
+  int pid = pairs[tr.pos0 + min(lane & 15, min(16, tr.n) - 1)];
+  u32x4 xr[G][4];
+  auto load_x = [&](int tok) {
+#pragma unroll
+    for (int m = 0; m < G; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xr[m][i] = *reinterpret_cast<const u32x4*>(
+            x + (size_t)tok * H + (MX ? 32 * (sb0 + 4 * m + kg) + 8 * i : 32 * (sb0 + 4 * m + i) + 8 * kg));
+  };
   u32x4 cg[NW][G], cu[NW][G];
   Hdr sg[NW][NH], su[NW][NH];
 #pragma unroll
@@ -359,6 +374,11 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
       }
     }
   }
+  // compiler fences (no instruction): the loads above stay above, instead
+  // of being sunk to their first uses behind the code transposes
+  asm volatile("" ::: "memory");
+  load_x(pid / k);
+  asm volatile("" ::: "memory");
   if constexpr (!MX) {
 #pragma unroll
     for (int j = 0; j < NW; ++j)
@@ -368,19 +388,14 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
   const bf16x8 one = ones8();
   for (int b0 = 0; b0 < tr.n; b0 += 16) {
     const int nb = min(16, tr.n - b0);
+    const bool more = b0 + 16 < tr.n;
+    // the next block's token ids
+    if (more) pid = pairs[tr.pos0 + b0 + 16 + min(lane & 15, min(16, tr.n - b0 - 16) - 1)];
     // the codes stay the live state across blocks, converted again per block
 #pragma unroll
     for (int j = 0; j < NW; ++j)
 #pragma unroll
       for (int m = 0; m < G; ++m) asm volatile("" : "+v"(cg[j][m]), "+v"(cu[j][m]));
-    const int tok = pairs[tr.pos0 + b0 + min(lane & 15, nb - 1)] / k;
-    u32x4 xr[G][4];
-#pragma unroll
-    for (int m = 0; m < G; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xr[m][i] = *reinterpret_cast<const u32x4*>(
-            x + (size_t)tok * H + (MX ? 32 * (sb0 + 4 * m + kg) + 8 * i : 32 * (sb0 + 4 * m + i) + 8 * kg));
     f32x4 accg[NW], accu[NW];
 #pragma unroll
     for (int j = 0; j < NW; ++j) accg[j] = accu[j] = ZERO4;
@@ -417,6 +432,8 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
         pin<NW>(accu);
       }
     }
+    // the next block's activations, now that this block's are consumed
+    if (more) load_x(pid / k);
 #pragma unroll
     for (int j = 0; j < NW; ++j)
 #pragma unroll
@@ -743,8 +760,8 @@ __global__ __launch_bounds__(BLOCK) void down_g16_kernel(
 // times per tile instead of H/16.
 template <int GD, int NW, int FMT>
 __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
-    const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I,
-    const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles, const uint16_t* __restrict__ hb,
+    const uint8_t* dn, size_t dn_expert_bytes, int drow_bytes, int H, int I,
+    const int32_t* pairs, const TileRec* __restrict__ tiles, const uint16_t* hb,
     float* __restrict__ ypair, size_t hlo, int ntiles) {
   constexpr bool MX = FMT == FMT_MXFP4;
   constexpr int NH = MX ? GD : (GD + 1) / 2;
@@ -761,6 +778,31 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
   const int n0 = rb * 64 * NW + 16 * NW * w;
   const int r = lane & 15, kg = lane >> 4;
   const uint8_t* base = dn + (size_t)tr.e * dn_expert_bytes;
+  // a 16-pair block's h rows (staged in LDS) and pair ids: thread -> one
+  // (plane, row) and every TPR-th 16-byte column of it
+  constexpr int TPR = BLOCK / (2 * 16), NQ = CPR / TPR;
+  static_assert(CPR % TPR == 0, "h staging split");
+  const int prw = tid / TPR, pl = prw / 16, hrow = prw % 16, col0 = tid % TPR;
+  u32x4 st[NQ];
+  int pr[4];
+  auto load_block = [&](int b0) {
+    const int nb = min(16, tr.n - b0);
+    const uint16_t* src = hb + (pl ? hlo : 0) + (size_t)(tr.pos0 + b0 + min(hrow, nb - 1)) * I + 8 * col0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) st[q] = *reinterpret_cast<const u32x4*>(src + 8 * TPR * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pr[q] = pairs[tr.pos0 + b0 + min(4 * kg + q, nb - 1)];
+  };
+  auto stage_block = [&]() {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4*>(&hs[pl][hrow][8 * col0 + 8 * TPR * q]) = st[q];
+  };
+  // the first block's h and pair ids leave first, then the weights; h goes
+  // to LDS as soon as it arrives, ahead of the code transposes that wait for
+  // the weights (the fences keep the compiler from sinking the loads to
+  // their uses)
+  load_block(0);
+  asm volatile("" ::: "memory");
   u32x4 cd[NW][GD];
   Hdr sc[NW][NH];
 #pragma unroll
@@ -774,6 +816,8 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
       else sc[j][b] = *reinterpret_cast<const u32x4*>(row + I / 2 + QHDR * b);
     }
   }
+  asm volatile("" ::: "memory");
+  stage_block();
   if constexpr (!MX) {
 #pragma unroll
     for (int j = 0; j < NW; ++j)
@@ -788,23 +832,11 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
     for (int j = 0; j < NW; ++j)
 #pragma unroll
       for (int m = 0; m < GD; ++m) asm volatile("" : "+v"(cd[j][m]));
-    {
-      // thread -> one (plane, row) and every TPR-th 16-byte column of it:
-      // one address per thread, the rest immediate offsets
-      constexpr int TPR = BLOCK / (2 * 16), NQ = CPR / TPR;
-      static_assert(CPR % TPR == 0, "h staging split");
-      const int prw = tid / TPR, pl = prw / 16, row = prw % 16, col0 = tid % TPR;
-      const uint16_t* src = hb + (pl ? hlo : 0) + (size_t)(tr.pos0 + b0 + min(row, nb - 1)) * I + 8 * col0;
-      u32x4 st[NQ];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) st[q] = *reinterpret_cast<const u32x4*>(src + 8 * TPR * q);
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4*>(&hs[pl][row][8 * col0 + 8 * TPR * q]) = st[q];
-      __syncthreads();
+    if (b0 > 0) {
+      load_block(b0);
+      stage_block();
     }
-    int pr[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) pr[q] = 4 * kg + q < nb ? pairs[tr.pos0 + b0 + 4 * kg + q] : -1;
+    __syncthreads();
     f32x4 acc[NW];
 #pragma unroll
     for (int j = 0; j < NW; ++j) acc[j] = ZERO4;
@@ -842,7 +874,7 @@ __global__ __launch_bounds__(BLOCK) void down_g16m_kernel(
     for (int j = 0; j < NW; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (pr[q] >= 0) ypair[(size_t)pr[q] * H + n0 + 16 * j + r] = acc[j][q];
+        if (4 * kg + q < nb) ypair[(size_t)pr[q] * H + n0 + 16 * j + r] = acc[j][q];
     if (b0 + 16 < tr.n) __syncthreads();          // hs is rewritten by the next block
   }
 }
