@@ -466,8 +466,8 @@ __global__ __launch_bounds__(BLOCK) void gateup_g16m_kernel(
 // and no partial sums cross waves.
 template <int GK>   // GK = H/128 groups of 128 K
 __global__ __launch_bounds__(BLOCK, 2) void gateup_g16r_kernel(
-    const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const TileRec* __restrict__ tiles,
+    const uint8_t* gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
+    const uint16_t* x, const int32_t* pairs, const TileRec* __restrict__ tiles,
     uint16_t* __restrict__ hb, int act, size_t hlo, int ntiles) {
   constexpr int HK = 128 * GK, LS = HK + 8, CPR = HK / 8;
   __shared__ __align__(16) uint16_t xs[16][LS];
@@ -482,6 +482,10 @@ __global__ __launch_bounds__(BLOCK, 2) void gateup_g16r_kernel(
   const int f0 = rb * 64 + 16 * w;
   const int r = lane & 15, kg = lane >> 4;
   const uint8_t* rec = gu + (size_t)tr.e * gu_expert_bytes + (size_t)(f0 + r) * rp_bytes;
+  // the first block's token ids leave before the weights (the activations
+  // they address end the longest dependent chain); every thread loads one,
+  // in bounds, so the load is not conditional and its wait covers it alone
+  int tk = pairs[tr.pos0 + min(tid & 15, min(16, tr.n) - 1)];
   u32x4 cg[GK], cu[GK];
   u32 sg[GK], su[GK];
 #pragma unroll
@@ -492,11 +496,14 @@ __global__ __launch_bounds__(BLOCK, 2) void gateup_g16r_kernel(
     sg[m] = rec[H + sbi];
     su[m] = rec[H + H / MXK + sbi];
   }
-  for (int b0 = 0; b0 < tr.n; b0 += 16) {
+  asm volatile("" ::: "memory");    // the loads above stay above (not sunk to their uses)
+  // one 16-pair block; tkv: this thread's token id of the block (the
+  // first block's was loaded before the weights, the later ones' are
+  // loaded unconditionally in their own loop, so no wait drains the loads
+  // in flight)
+  auto block = [&](int b0, int tkv) {
     const int nb = min(16, tr.n - b0);
-#pragma unroll
-    for (int m = 0; m < GK; ++m) asm volatile("" : "+v"(cg[m]), "+v"(cu[m]));
-    if (tid < 16) tok_s[tid] = pairs[tr.pos0 + b0 + min(tid, nb - 1)] / k;
+    if (tid < 16) tok_s[tid] = tkv / k;
     __syncthreads();
     {
       u32x4 st[16 * CPR / BLOCK];
@@ -530,8 +537,15 @@ __global__ __launch_bounds__(BLOCK, 2) void gateup_g16r_kernel(
       if (tt < nb)
         store_h(hb + h_index<FMT_MXFP4>((size_t)tr.pos0 + b0 + tt, I, f0 + r), hlo, gate_act(accg[q], accu[q], act));
     }
+    // the codes and scale bytes stay the live state across blocks,
+    // converted again per block (pinned after their use, so the first block
+    // waits for them only where it converts them)
+#pragma unroll
+    for (int m = 0; m < GK; ++m) asm volatile("" : "+v"(cg[m]), "+v"(cu[m]), "+v"(sg[m]), "+v"(su[m]));
     if (b0 + 16 < tr.n) __syncthreads();          // xs and tok_s are rewritten by the next block
-  }
+  };
+  block(0, tk);
+  for (int b0 = 16; b0 < tr.n; b0 += 16) block(b0, pairs[tr.pos0 + b0 + min(tid & 15, min(16, tr.n - b0) - 1)]);
 }
 
 // ------------------------------------------------------------------ gate/up, K outermost
