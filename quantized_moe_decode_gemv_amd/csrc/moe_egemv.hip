@@ -114,8 +114,8 @@ struct SlotDesc { int e, pos0, n, pad; };
 // (U_e[r]·x_t) (fp32) for the pair at expert-sorted position pos, t its token.
 template <int IPL, int LPR, int U, int NT, int FMT>
 __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
-    const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ pairs, const SlotDesc* __restrict__ slots,
+    const uint8_t* gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int k,
+    const uint16_t* x, const int32_t* pairs, const SlotDesc* __restrict__ slots,
     float* __restrict__ hbuf, int act) {
   constexpr int LG = ilog2(LPR), RPS = WAVE / LPR, RW = RPS * U, V = 2 * U * NT;
   static_assert((1 << LG) == LPR, "LPR must be a power of two");
@@ -128,10 +128,16 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
   const int pos0 = sd.pos0, n = sd.n;
   const int rho = lane / LPR, lam = lane % LPR;
   // tokens of the first chunk before the weights: the activation loads wait
-  // on them, and a wait for a later load would also wait for the weights
+  // on them, and a wait for a later load would also wait for the weights.
+  // Every one in bounds (slots past the expert's pairs reload its last), so
+  // no load is conditional and that wait covers these loads alone.
   int t0[NT];
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) t0[tt] = tt < n ? pairs[pos0 + tt] / k : 0;
+  for (int tt = 0; tt < NT; ++tt) {
+    int pt = pos0 + min(tt, n - 1);
+    asm volatile("" : "+s"(pt));    // opaque: no load made conditional on pt == pos0
+    t0[tt] = pairs[pt] / k;
+  }
   const uint8_t* base = gu + (size_t)sd.e * gu_expert_bytes;
   const int half = H / 2;                 // code bytes per matrix row
   const int hdr = H;                      // headers (MXFP4: scale bytes) start after both code areas
@@ -157,14 +163,19 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
       }
     }
   }
+  // compiler fence: the loads above stay above, issued together (not sunk
+  // to their uses)
+  asm volatile("" ::: "memory");
   for (int c0 = 0; c0 < n; c0 += NT) {
     const int nv = min(NT, n - c0);             // tokens present in this chunk (wave-uniform)
     u32 X[NT][IPL][16];
     float S[NT][IPL];
+    // every token's activations loaded (slots past the chunk's pairs reload
+    // its last token, in bounds), so no load is conditional
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
-      if (tt < nv) {
-        const int t = c0 == 0 ? t0[tt] : pairs[pos0 + c0 + tt] / k;
+      {
+        const int t = c0 == 0 ? t0[tt] : pairs[pos0 + c0 + min(tt, nv - 1)] / k;
 #pragma unroll
         for (int q = 0; q < IPL; ++q) {
           const uint16_t* xp = x + (size_t)t * H + 32 * (lam + LPR * q);
@@ -225,6 +236,14 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
     if (tsum_owner<V, LG>(lane) && !(idx & 1) && tt < nv) {
       hbuf[(size_t)(pos0 + c0 + tt) * I + r0 + u * RPS + rho] = gate_act(s, o, act);
     }
+    // the codes and headers (scale bytes) stay raw across chunks: converted
+    // and decoded in each chunk, not ahead of the first chunk's activation
+    // loads (and without the registers of converted copies)
+#pragma unroll
+    for (int u2 = 0; u2 < U; ++u2)
+#pragma unroll
+      for (int q = 0; q < IPL; ++q)
+        asm volatile("" : "+v"(cg[u2][q]), "+v"(cu[u2][q]), "+v"(hg[u2][q]), "+v"(hu[u2][q]));
   }
 }
 
@@ -236,8 +255,8 @@ __global__ __launch_bounds__(BLOCK) void gateup_egemv_kernel(
 // time).
 template <int LPR, int U, int NT, int FMT>
 __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
-    const uint8_t* __restrict__ dn, size_t dn_expert_bytes, int drow_bytes, int H, int I,
-    const int32_t* __restrict__ pairs, const SlotDesc* __restrict__ slots, const float* __restrict__ hbuf,
+    const uint8_t* dn, size_t dn_expert_bytes, int drow_bytes, int H, int I,
+    const int32_t* pairs, const SlotDesc* __restrict__ slots, const float* hbuf,
     float* __restrict__ ypair) {
   constexpr int LG = ilog2(LPR), RPS = WAVE / LPR, RW = RPS * U, V = U * NT;
   static_assert((1 << LG) == LPR, "LPR must be a power of two");
@@ -251,27 +270,45 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
   const int rho = lane / LPR, j = lane % LPR;
   const bool has = j < I / 32;
   const uint8_t* base = dn + (size_t)sd.e * dn_expert_bytes;
-  const int hdr = I / 2 + QHDR * (j >> 3);
-  // the first chunk's h before the weights: a wait for a later load would
-  // also wait for the weights
-  const int jh = has ? j : 0;             // lanes past the row read its first block (in bounds)
+  // the first chunk's h and pair ids before the weights: a wait for a later
+  // load would also wait for the weights. Every load in bounds (lanes past
+  // the row read its first block, slots past the expert's pairs its last
+  // pair), so none is conditional and no wait drains the loads in flight.
+  const int jh = has ? j : 0;
   u32x4 hq[NT][8];
+  int pq[NT];
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt)
-    if (tt < n)
+  for (int tt = 0; tt < NT; ++tt) {
+    int pt = pos0 + min(tt, n - 1);
+    asm volatile("" : "+s"(pt));    // opaque: no load made conditional on pt == pos0
 #pragma unroll
-      for (int g = 0; g < 8; ++g) hq[tt][g] = load16(hbuf + (size_t)(pos0 + tt) * I + 32 * jh + 4 * g);
+    for (int g = 0; g < 8; ++g) hq[tt][g] = load16(hbuf + (size_t)pt * I + 32 * jh + 4 * g);
+    pq[tt] = pairs[pt];
+  }
   using Hdr = std::conditional_t<FMT == FMT_MXFP4, u32, u32x4>;
   u32x4 cd[U];
   Hdr hd[U];
+  const int hdr = I / 2 + QHDR * (jh >> 3);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint8_t* row = base + (size_t)(n0 + u * RPS + rho) * drow_bytes;
-    cd[u] = has ? load_nt(row + 16 * j) : u32x4{0u, 0u, 0u, 0u};
-    if constexpr (FMT == FMT_MXFP4) hd[u] = has ? (u32)__builtin_nontemporal_load(row + I / 2 + j) : 0u;
-    else hd[u] = has ? load_nt(row + hdr) : u32x4{0u, 0u, 0u, 0u};
+    cd[u] = load_nt(row + 16 * jh);
+    if constexpr (FMT == FMT_MXFP4) hd[u] = (u32)__builtin_nontemporal_load(row + I / 2 + jh);
+    else hd[u] = load_nt(row + hdr);
   }
-  __builtin_amdgcn_sched_barrier(0);
+  // compiler fence: the loads above stay above, issued together (not sunk
+  // to their uses behind the per-token branches)
+  asm volatile("" ::: "memory");
+  // lanes past the row contribute nothing: zero codes (and, for MXFP4, scale
+  // code 0, factor 0)
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!has) {
+      cd[u] = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (FMT == FMT_MXFP4) hd[u] = 0u;
+      else hd[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
   for (int c0 = 0; c0 < n; c0 += NT) {
     const int nv = min(NT, n - c0);
     float X[NT][32];
@@ -315,7 +352,16 @@ __global__ __launch_bounds__(BLOCK) void down_egemv_kernel(
     const float s = tsum<V, LG>(v);
     const int idx = tsum_index<V>(lane);
     const int u = idx / NT, tt = idx % NT;
-    if (tsum_owner<V, LG>(lane) && tt < nv) ypair[(size_t)pairs[pos0 + c0 + tt] * H + n0 + u * RPS + rho] = s;
+    if (tsum_owner<V, LG>(lane) && tt < nv) {
+      int p = pairs[pos0 + c0 + min(tt, nv - 1)];
+      if (c0 == 0) {
+        // the first chunk's pair ids, loaded up front
+#pragma unroll
+        for (int q = 0; q < NT; ++q)
+          if (tt == q) p = pq[q];
+      }
+      ypair[(size_t)p * H + n0 + u * RPS + rho] = s;
+    }
   }
 }
 
