@@ -296,7 +296,11 @@ def decode_timeline(plan, blob, graph, stream, L, ms_per_step, q, np, torch, rep
     (sum of squares reduced), gate/up's routing (top-k done) and first row's
     dot products, down's row partials (medians over workgroups, from the
     kernel's start). Medians over layers and over `reps` samples, each the
-    last of `batch` back-to-back replays."""
+    last of `batch` back-to-back replays. For gate/up and down also the
+    10th/50th/90th percentiles over the workgroups of each dispatch group of
+    256 (start and end from the kernel's first start, the marks from the
+    workgroup's own start), and the spread of the per-XCD medians; both over
+    the layers away from the stack's ends."""
     import ctypes
     lib = q.load()
     lib.moe_timeline_reset.restype = ctypes.c_int
@@ -325,6 +329,11 @@ def decode_timeline(plan, blob, graph, stream, L, ms_per_step, q, np, torch, rep
     tick_mhz = (s_b - s_a) / (t_b - t_a) / 1e6
     us_per_tick = 1.0 / tick_mhz
     rows, step_stamps, batch_step_us = [], [], []
+    # per-workgroup distributions of the gate/up and down launches: by
+    # dispatch group (workgroups 0-255 take one CU each, the next 256 share
+    # CUs with them) and by XCD (workgroup id mod 8)
+    wg_kinds = ((1, "gateup", {"routing_known": 5, "row0_dots": 6}), (2, "down", {"row_partials": 6}))
+    by_group, by_xcd = {}, {}
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     assert lib.moe_timeline_reset() == 0
     for _ in range(reps):
@@ -366,10 +375,37 @@ def decode_timeline(plan, blob, graph, stream, L, ms_per_step, q, np, torch, rep
             row["gateup_row0_mark"] = mark(4 * l + 1, 6, gs)
             row["down_partials_mark"] = mark(4 * l + 2, 6, ds)
             rows.append(row)
+            if 2 <= l < L - 2:
+                for kind, name, fields in wg_kinds:
+                    x = r[4 * l + kind]
+                    nwg = int(np.count_nonzero(x[:, 0]))
+                    x = x[:nwg]
+                    st = x[:, 0]
+                    t0 = st.min()
+                    series = {"start": st - t0, "end": x[:, 1:5].max(1) - t0}
+                    series.update({f: np.where(x[:, i] > 0, x[:, i] - st, np.nan) for f, i in fields.items()})
+                    wg = np.arange(nwg)
+                    for g in range((nwg + 255) // 256):
+                        m = wg // 256 == g
+                        for f, v in series.items():
+                            by_group.setdefault((name, g, f), []).append(np.nanpercentile(v[m], [10, 50, 90]) * us_per_tick)
+                    for xcd in range(8):
+                        m = wg % 8 == xcd
+                        for f, v in series.items():
+                            by_xcd.setdefault((name, xcd, f), []).append(np.nanmedian(v[m]) * us_per_tick)
         step_stamps.append((span(3)[1] - base) * us_per_tick)
     keys = list(rows[-1].keys())
     med = {k2: round(float(np.median([rw[k2] for rw in rows if rw.get(k2) is not None])), 3) for k2 in keys}
     parts = ("router", "gap_router_gateup", "gateup", "gap_gateup_down", "down", "gap_down_next")
+    groups = {}
+    for (name, g, f), v in by_group.items():
+        key = f"{name}_wg{256 * g}-{256 * g + 255}"
+        groups.setdefault(key, {})[f] = [round(float(a), 2) for a in np.median(np.array(v), axis=0)]
+    xcd_spread = {}
+    for _, name, fields in wg_kinds:
+        for f in ("start", "end", *fields):
+            meds = [float(np.median(by_xcd[(name, xcd, f)])) for xcd in range(8)]
+            xcd_spread[f"{name}_{f}"] = round(max(meds) - min(meds), 3)
     return {
         "timeline": {
             "per_layer_median_us": med,
@@ -377,6 +413,8 @@ def decode_timeline(plan, blob, graph, stream, L, ms_per_step, q, np, torch, rep
             "layers": L,
             "samples": reps,
             "replays_per_sample": batch,
+            "workgroups_by_dispatch_group_p10_p50_p90_us": groups,
+            "xcd_median_spread_us": xcd_spread,
             "step_us_stamps_median": round(float(np.median(step_stamps)), 1),
             "step_us_events_instrumented": round(ms_per_step * 1e3, 1),
             "step_us_events_sampled_batches": round(float(np.median(batch_step_us)), 1),
