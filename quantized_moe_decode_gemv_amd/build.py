@@ -16,9 +16,14 @@ SOURCES = ["moe_gemv.hip", "moe_egemv.hip", "moe_grouped.hip", "moe_api.cpp", "m
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU forms are kept out of generated code on purpose.
+# MFMA results go to ordinary VGPRs (gfx950 allows either register file):
+# in the AGPR form each 16x16 result of the tile kernels came back through
+# four v_accvgpr_read before its fp32 sub-block affine, 10-18 % of their
+# VALU instructions; outputs are bit-identical either way.
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 
