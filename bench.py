@@ -255,7 +255,41 @@ def main():
         "parity_step0": parity,
         "outputs_finite": finite,
     }
+    bad = plausibility(result)
+    if bad:
+        log(f"implausible figures withheld: {bad}")
     print(json.dumps(result), flush=True)
+
+
+def plausibility(result):
+    """Two-sided plausibility of the reported figures: a bandwidth above the
+    HBM peak (any *_gbps, or a roofline's achieved GB/s) or a fraction or
+    utilisation above 1 cannot come from a correct measurement. Each such
+    figure is replaced by None and its path listed under "implausible";
+    returns that list."""
+    bad = []
+
+    def walk(d, path):
+        for key, v in list(d.items()):
+            p = f"{path}.{key}" if path else key
+            if isinstance(v, dict):
+                walk(v, p)
+                continue
+            if isinstance(v, bool) or not isinstance(v, (int, float)):
+                continue
+            if key.endswith("gbps") or (key == "achieved" and d.get("unit") == "GB/s"):
+                limit = HBM_PEAK_GBPS
+            elif key in ("frac", "frac_of_peak", "mfma_util"):
+                limit = 1.0
+            else:
+                continue
+            if not v <= limit:
+                d[key] = None
+                bad.append(p)
+
+    walk(result, "")
+    result["implausible"] = bad
+    return bad
 
 
 def gate_up_launch_times(plan, blob, xs, L, reps, scratch, stream, torch):
