@@ -660,6 +660,18 @@ def batched_measurements(S, blob, L, dev, stream, q, np, torch, synth, base_flag
     return res
 
 
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(S, L, x0, gpu):
     """The CPU oracle, as it stands (plain scalar C, fp64, one thread), run
     over one full decode step of the same stack from the same seeded input.
@@ -716,6 +728,7 @@ def cpu_baseline(S, L, x0, gpu):
         "value": round(1.0 / t_oracle, 5),
         "unit": "tok/s",
         "cores": 1,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"one full decode step ({L} layers, 1 token) from the same seeded input; "
                   f"oracle arithmetic timed ({t_oracle:.1f} s), expert block generation excluded",
