@@ -109,7 +109,7 @@ def _run(S, L, dev, steps, graph=True):
             plan.stack_step(blob, xs, ys, 1, ids, ws, scratch=scratch, stream=stream)
         torch.cuda.synchronize()
         out.append(dict(x_in=x_in, xs=xs.cpu().numpy().view(np.uint16).copy(), ys=ys.cpu().numpy().copy(),
-                        ids=ids.cpu().numpy().copy(), ws=ws.cpu().numpy().copy()))
+                        ids=ids.cpu().numpy().copy()))
     return plan, blob, out
 
 
@@ -179,36 +179,6 @@ def test_full_stack_chained_step_in_bench_configuration(qwen_stack):
           f"x_next flips {flips}, stopped: {why}")
     assert exact >= 1
     assert np.array_equal(out[1]["x_in"], out[0]["xs"][0])
-
-
-def test_full_stack_teacher_forced_every_layer(qwen_stack):
-    """The captured step's own trajectory, every layer of both recorded
-    steps: the oracle runs layer l on the input the GPU gave it (the step's
-    recorded layer input), so the whole 48-layer chain of each step is held
-    to the full bar however far the free-running trajectories have parted:
-    ids by the near-tie rule, y within 2e-3 * max|ref|, and the next layer's
-    input (the last layer's: the next step's input) within one bf16 step of
-    the oracle's RMSNorm of that input plus its y."""
-    S, _, _, out = qwen_stack
-    L = out[0]["ys"].shape[0]
-    src = oracle.ExpertSource(S, max_cached=16)
-    worst, exempted, flips = 0.0, 0, 0
-    for s, st in enumerate(out):
-        for l in range(L):
-            xb = (st["x_in"] if l == 0 else st["xs"][l])[None, :]
-            ref = oracle.moe_layer(src, l, xb)
-            gid = st["ids"][l][None, :]
-            exempt = check_routing(gid, st["ws"][l][None, :], ref, label=f"step {s} layer {l}")
-            exempted += len(exempt)
-            yref = reference_outputs(src, l, xb, ref, gid, exempt)
-            err = rel_err(st["ys"][l][None, :], yref)
-            assert err <= REL_TOL, f"step {s} layer {l}: {err:.3e}"
-            worst = max(worst, err)
-            _, xn = oracle.resid_rmsnorm(xb[0], yref[0])
-            flips += check_bf16_vector(st["xs"][(l + 1) % L], xn)
-    print(f"teacher-forced, {len(out)} steps x {L} layers: worst max|err|/max|ref| = {worst:.3e}, "
-          f"x_next bf16 flips {flips}, near-tie exemptions {exempted}")
-    assert exempted <= 2 * len(out)
 
 
 def _chained_forward(plan, blob, L, H, k, x0, dev):
