@@ -1,7 +1,8 @@
-"""bench.py's step-0 parity report on the CPU (no GPU): a step record made by
-the oracle itself passes with zero error, both along the oracle's own
-trajectory and teacher-forced; a record with one layer's output off by more
-than the tolerance is refused."""
+"""bench.py's step-0 parity report on the CPU (no GPU), on step records made by
+the oracle itself: such a record passes with zero error; one layer's output
+off by more than the tolerance on identical inputs is refused; once one-step
+bf16 flips have parted the inputs, the comparison follows the trajectories
+and stops, without failing, at the first layer that no longer agrees."""
 import numpy as np
 import pytest
 
@@ -39,8 +40,6 @@ def test_oracle_record_passes_both_ways():
     assert cpu["cores"] == 1 and cpu["value"] > 0
     assert parity["layers_compared"] == L and parity["layers_on_identical_inputs"] == L
     assert parity["worst_rel_err"] < 1e-6 and parity["stopped"] is None
-    tf = parity["teacher_forced"]
-    assert tf["layers"] == L and tf["worst_rel_err"] < 1e-6 and tf["near_tie_layers_skipped"] == 0
 
 
 def test_a_wrong_layer_is_refused():
@@ -72,13 +71,12 @@ def _parted_record():
     return x0, gpu
 
 
-def test_teacher_forced_holds_layers_after_the_trajectories_part():
+def test_parted_trajectories_are_followed_then_left():
     x0, gpu = _parted_record()
     _, parity = bench.cpu_baseline(S, L, x0, gpu)
-    assert parity["layers_on_identical_inputs"] == 3
-    assert parity["teacher_forced"]["worst_rel_err"] < 1e-6
-    # an error after the parting: the free-running comparison can only stop
-    # there; the teacher-forced pass refuses it
+    assert parity["layers_on_identical_inputs"] == 3 and parity["layers_compared"] == L
+    assert parity["stopped"] is None and parity["x_next_bf16_differences"] >= 5
+    # past the parting a layer that no longer agrees ends the comparison
     gpu["ys"][3] *= 1.01
-    with pytest.raises(AssertionError, match="teacher-forced layer 3"):
-        bench.cpu_baseline(S, L, x0, gpu)
+    _, parity = bench.cpu_baseline(S, L, x0, gpu)
+    assert parity["stopped"] == "trajectories parted at layer 3" and parity["layers_compared"] == 3
