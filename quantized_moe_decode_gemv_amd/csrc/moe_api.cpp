@@ -334,7 +334,9 @@ static int route_impl(const moe_plan* plan, const uint8_t* L, const uint16_t* x,
     lg = tmp;
   }
   if (launch_topk(d, lg, ids, w, T, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (counts && launch_dispatch(d, ids, counts, offsets, pairs, T, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (counts && launch_dispatch(d, ids, counts, offsets, pairs, T, stream, 1, nullptr, 0,
+                                reinterpret_cast<int32_t*>(scr + sc.part)) != hipSuccess)
+    return MOE_ERR_HIP;
   return MOE_OK;
 }
 
@@ -411,7 +413,8 @@ static int forward_impl(const moe_plan* plan, const void* blob, int32_t layer, c
   int32_t* pairs = lists ? lists->pairs : reinterpret_cast<int32_t*>(scr + sc.pairs);
   if (path != Path::Gemv) {
     const WorkList wl = work_list(d, path, T, scr, sc);
-    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream, wl.mt, wl.slots, wl.max_slots) != hipSuccess)
+    if (launch_dispatch(d, ids, counts, offsets, pairs, T, stream, wl.mt, wl.slots, wl.max_slots,
+                        reinterpret_cast<int32_t*>(scr + sc.part)) != hipSuccess)
       return MOE_ERR_HIP;
     const int st = batched_impl(plan, path, L, x, T, w, offsets, pairs, out, scr, sc, stream, true);
     if (st) return st;
@@ -419,7 +422,9 @@ static int forward_impl(const moe_plan* plan, const void* blob, int32_t layer, c
     if (launch_gateup(d, L, x, ids, lg, ids, w, h, T, fused, stream) != hipSuccess) return MOE_ERR_HIP;
     if (launch_down(d, L, ids, w, h, out, T, stream) != hipSuccess) return MOE_ERR_HIP;
     // the per-token path needs no dispatch lists; build them when asked for
-    if (lists && launch_dispatch(d, ids, counts, offsets, pairs, T, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (lists && launch_dispatch(d, ids, counts, offsets, pairs, T, stream, 1, nullptr, 0,
+                                 reinterpret_cast<int32_t*>(scr + sc.part)) != hipSuccess)
+      return MOE_ERR_HIP;
   }
   if (x_next && launch_resid_norm(d, x, out, x_next, T, stream) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;

@@ -660,6 +660,30 @@ __device__ __forceinline__ void excl_scan256x2(int a, int b, int& ea, int& eb, i
   tot_b = (wsum[4] + wsum[5]) + (wsum[6] + wsum[7]);
 }
 
+// One wave's group of up to 64 consecutive pairs p (lanes in order; act:
+// the lane holds a pair, routed to expert e): each pair goes to
+// pairs[base[e] + its rank among the group's pairs of e], ranks from ballots
+// over the 8 bits of e (no atomics, so the order is p's), and base[e] moves
+// past the group's pairs of e. base: the wave's own row of first positions.
+__device__ __forceinline__ void place_group(int p, bool act, int e, int* base, int32_t* __restrict__ pairs) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  unsigned long long same = __ballot(act);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const unsigned long long bal = __ballot(act && ((e >> b) & 1));
+    same &= ((e >> b) & 1) ? bal : ~bal;
+  }
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
+  const int rank = __popcll(same & below);
+  const int n = __popcll(same);
+  int b0 = 0;
+  if (act) b0 = base[e];
+  __builtin_amdgcn_wave_barrier();
+  if (act) pairs[b0 + rank] = p;
+  if (act && rank == n - 1) base[e] = b0 + n;
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Single block of 1024 threads (16 waves). counts[e] = #pairs routed to e,
 // offsets = exclusive scan (E+1 entries), pairs = pair indices p = t*k+s
 // ordered by (expert, p), and (slots given) the batched paths' work list:
@@ -720,23 +744,7 @@ __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* _
   __syncthreads();
   // cnt[w][e] is now the first output slot of wave w's pairs for expert e;
   // pairs in increasing p (groups of 64 in order, lanes in order)
-  auto place = [&](int p, bool act, int e) {
-    unsigned long long same = __ballot(act);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const unsigned long long bal = __ballot(act && ((e >> b) & 1));
-      same &= ((e >> b) & 1) ? bal : ~bal;
-    }
-    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
-    const int rank = __popcll(same & below);
-    const int n = __popcll(same);
-    int base = 0;
-    if (act) base = cnt[wid][e];
-    __builtin_amdgcn_wave_barrier();
-    if (act) pairs[base + rank] = p;
-    if (act && rank == n - 1) cnt[wid][e] = base + n;
-    __builtin_amdgcn_wave_barrier();
-  };
+  auto place = [&](int p, bool act, int e) { place_group(p, act, e, cnt[wid], pairs); };
   if constexpr (NPL == 1) {
     for (int pb = p0; pb < p1; pb += WAVE) {
       const int p = pb + lane;
@@ -758,6 +766,111 @@ __global__ __launch_bounds__(DISP_THREADS) void dispatch_kernel(const int32_t* _
         place(p, p < p1, ev[j]);
       }
     }
+  }
+}
+
+// The same lists for large batches, over many workgroups: the pairs in
+// chunks of DISP_CHUNK in pair order, one workgroup of 4 waves per chunk
+// (wave w: the chunk's w-th quarter, in groups of 64). dispatch_hist_kernel
+// counts each chunk's pairs per expert (part[c][e]). dispatch_place_kernel
+// gives each wave, for every expert, the first output position of its pairs
+// (the exclusive scan of the experts' totals, plus the pairs of that expert
+// in the chunks and waves before it) and places them with place_group, so
+// the lists are identical to dispatch_kernel's; workgroup 0 also writes
+// counts, offsets and the work list.
+__global__ __launch_bounds__(BLOCK) void dispatch_hist_kernel(const int32_t* __restrict__ ids,
+                                                              int32_t* __restrict__ part, int E, int P) {
+  static_assert(BLOCK == 256 && DISP_CHUNK % BLOCK == 0, "one histogram entry per thread, whole groups");
+  __shared__ int hist[256];
+  const int tid = threadIdx.x;
+  hist[tid] = 0;
+  __syncthreads();
+  const int p0 = (int)blockIdx.x * DISP_CHUNK, p1 = min(P, p0 + DISP_CHUNK);
+  constexpr int G = DISP_CHUNK / BLOCK;
+  int ev[G];
+  // every load in bounds (slots past the chunk reload its last pair, then
+  // count nothing), so none is conditional and they are in flight together
+#pragma unroll
+  for (int j = 0; j < G; ++j) ev[j] = ids[min(p0 + tid + BLOCK * j, p1 - 1)];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    if (p0 + tid + BLOCK * j < p1) atomicAdd(&hist[ev[j]], 1);
+  __syncthreads();
+  if (tid < E) part[(size_t)blockIdx.x * E + tid] = hist[tid];
+}
+
+__global__ __launch_bounds__(BLOCK) void dispatch_place_kernel(const int32_t* __restrict__ ids,
+                                                               const int32_t* __restrict__ part,
+                                                               int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ pairs, int4* __restrict__ slots,
+                                                               int E, int P, int nchunks, int mt, int max_slots) {
+  constexpr int NW = BLOCK / WAVE, G = DISP_CHUNK / BLOCK;   // waves; groups of 64 per wave
+  __shared__ int cnt[NW][256];
+  __shared__ int wsum[8];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
+  const int c = (int)blockIdx.x;
+  const int p0 = c * DISP_CHUNK, p1 = min(P, p0 + DISP_CHUNK);
+  const int pw = p0 + wid * (DISP_CHUNK / NW);              // the wave's quarter
+  int ev[G];
+  // every load in bounds (slots past the chunk reload its last pair and are
+  // then marked empty), so none is conditional and they are in flight together
+#pragma unroll
+  for (int j = 0; j < G; ++j) ev[j] = ids[min(pw + WAVE * j + lane, p1 - 1)];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    if (pw + WAVE * j + lane >= p1) ev[j] = -1;
+  // thread e: expert e's total and its pairs in the chunks before this one,
+  // the chunks' counts read 16 at a time (all 16 loads in flight)
+  int tot = 0, before = 0;
+  const int te = tid < E ? tid : 0;
+  for (int i0 = 0; i0 < nchunks; i0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = part[(size_t)min(i0 + u, nchunks - 1) * E + te];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int n = i0 + u < nchunks ? v[u] : 0;
+      tot += n;
+      before += i0 + u < c ? n : 0;
+    }
+  }
+  if (tid >= E) tot = before = 0;
+  for (int i = tid; i < NW * 256; i += BLOCK) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    if (ev[j] >= 0) atomicAdd(&cnt[wid][ev[j]], 1);
+  __syncthreads();
+  const int tiles = tid < E ? (tot + mt - 1) / mt : 0;
+  int ex_tot, ex_tiles, all_tot, all_tiles;
+  excl_scan256x2(tid < E ? tot : 0, tiles, ex_tot, ex_tiles, all_tot, all_tiles, wsum);
+  if (c == 0) {
+    if (tid < E) {
+      counts[tid] = tot;
+      offsets[tid] = ex_tot;
+      if (slots)
+        for (int q = 0; q < tiles; ++q) slots[ex_tiles + q] = make_int4(tid, ex_tot + q * mt, min(mt, tot - q * mt), 0);
+    }
+    if (tid == 0) offsets[E] = all_tot;
+    if (slots)
+      for (int i = all_tiles + tid; i < max_slots; i += BLOCK) slots[i] = make_int4(0, 0, 0, 0);
+  }
+  // cnt[w][e]: first output position of wave w's pairs of expert e
+  if (tid < E) {
+    int base = ex_tot + before;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int n = cnt[w][tid];
+      cnt[w][tid] = base;
+      base += n;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    if (pw + WAVE * j >= p1) break;                           // wave-uniform
+    place_group(pw + WAVE * j + lane, ev[j] >= 0, ev[j], cnt[wid], pairs);
   }
 }
 
@@ -946,12 +1059,17 @@ hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y,
 }
 
 hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* pairs, int T,
-                           hipStream_t s, int mt, void* slots, int max_slots) {
+                           hipStream_t s, int mt, void* slots, int max_slots, int32_t* part) {
   if (mt < 1) return hipErrorInvalidValue;
   // the slot records must cover every tile: at most ceil(T*k / mt) + min(E, T*k)
   const int P = T * d.k;
   if (slots && max_slots < (P + mt - 1) / mt + (P < d.E ? P : d.E)) return hipErrorInvalidValue;
-  if (P > 4 * DISP_THREADS)
+  if (part && P > DISP_MULTI_MIN) {
+    const int nchunks = (P + DISP_CHUNK - 1) / DISP_CHUNK;   // part holds nchunks x E counts
+    hipLaunchKernelGGL(dispatch_hist_kernel, dim3(nchunks), dim3(BLOCK), 0, s, ids, part, d.E, P);
+    hipLaunchKernelGGL(dispatch_place_kernel, dim3(nchunks), dim3(BLOCK), 0, s, ids, part, counts, offsets, pairs,
+                       static_cast<int4*>(slots), d.E, P, nchunks, mt, slots ? max_slots : 0);
+  } else if (P > 4 * DISP_THREADS)
     hipLaunchKernelGGL((dispatch_kernel<32>), dim3(1), dim3(DISP_THREADS), 0, s, ids, counts, offsets, pairs,
                        static_cast<int4*>(slots), d.E, P, mt, slots ? max_slots : 0);
   else

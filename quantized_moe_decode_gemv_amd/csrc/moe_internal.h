@@ -75,9 +75,14 @@ struct BlobHeader {
   int32_t weight_format;        // FMT_Q4K or FMT_MXFP4
 };
 
+// Dispatch over many workgroups above DISP_MULTI_MIN routed pairs, one per
+// DISP_CHUNK pairs.
+constexpr int DISP_CHUNK = 1024;
+constexpr int DISP_MULTI_MIN = 4096;
+
 // Scratch carve-up for T tokens (offsets 256-aligned).
 struct Scratch {
-  size_t logits, ids, w, h, counts, offsets, pairs, slots, hbuf, ypair, total;
+  size_t logits, ids, w, h, counts, offsets, pairs, slots, part, hbuf, ypair, total;
   void init(const Layout& d, int T) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
@@ -90,6 +95,8 @@ struct Scratch {
     pairs = take((size_t)T * d.k * 4);
     // work records {expert, first pair, pairs}: one per routed expert, or per 16-pair tile
     slots = take((size_t)((T * d.k + 15) / 16 + d.E) * 16);
+    // per-chunk expert counts of the multi-workgroup dispatch
+    part = take((size_t)((T * d.k + DISP_CHUNK - 1) / DISP_CHUNK) * d.E * 4);
     // batched paths only (T > 1): h in expert-sorted pair order, 4 bytes per
     // value (fp32 on the expert-major GEMV, bf16 hi and lo planes on the MFMA
     // tiles), and one fp32 output row per pair
@@ -122,8 +129,12 @@ hipError_t launch_resid_norm(const Layout& d, const uint16_t* x, const float* y,
 // pairs}, one per tile of mt pairs of every expert in expert order (mt = T*k:
 // one per routed expert), followed by {0, 0, 0} records up to max_slots (at
 // least ceil(T*k / mt) + min(E, T*k)).
+// part: scratch for the per-chunk counts of the multi-workgroup dispatch
+// (ceil(T*k / DISP_CHUNK) x E int32), used above DISP_MULTI_MIN pairs; null:
+// the single-workgroup dispatch at every size.
 hipError_t launch_dispatch(const Layout& d, const int32_t* ids, int32_t* counts, int32_t* offsets,
-                           int32_t* pairs, int T, hipStream_t s, int mt = 1, void* slots = nullptr, int max_slots = 0);
+                           int32_t* pairs, int T, hipStream_t s, int mt = 1, void* slots = nullptr, int max_slots = 0,
+                           int32_t* part = nullptr);
 hipError_t launch_work_list(const Layout& d, const int32_t* offsets, int T, int mt, void* slots, int max_slots,
                             hipStream_t s);
 
