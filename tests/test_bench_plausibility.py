@@ -37,3 +37,13 @@ def test_figures_above_peak_are_withheld():
 def test_nan_is_withheld():
     r = _result(1817.0, float("nan"), 0.1)
     assert bench.plausibility(r) == ["hbm.achieved_gbps", "hbm.frac_of_peak"]
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus above 1 exits at once with a message
+    (before any GPU or library work)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
