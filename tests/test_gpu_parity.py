@@ -400,6 +400,28 @@ def test_route_from_logits_and_dispatch_lists(qwen, T, zipf):
     assert np.array_equal(pairs.cpu().numpy(), np.argsort(flat, kind="stable"))
 
 
+def test_forward_tiles_with_chunked_dispatch(qwen):
+    """1100 tokens through moe_forward (router, top-k, tiles): 8800 routed
+    pairs, so the dispatch runs over nine 1024-pair workgroups, the last one
+    ragged, and writes the tile list the MFMA kernels read. Sampled tokens
+    (including the last, whose pairs sit in the ragged chunk) against the
+    oracle."""
+    S = qwen.shape
+    T = 1100
+    plan = q.Plan(S.hidden, S.n_experts, S.top_k, S.inter, n_layers=1, max_tokens=T)
+    scratch = plan.new_scratch(T, device=qwen.dev)
+    xb = synth.x_bf16(S, 15, T, T=T)
+    out = torch.empty(T, S.hidden, dtype=torch.float32, device=qwen.dev)
+    ids = torch.empty(T, S.top_k, dtype=torch.int32, device=qwen.dev)
+    w = torch.empty(T, S.top_k, dtype=torch.float32, device=qwen.dev)
+    plan.forward(qwen.blob, 0, qwen.xdev(xb), T, out, ids=ids, w=w, scratch=scratch)
+    torch.cuda.synchronize()
+    got = dict(y=out.cpu().numpy(), ids=ids.cpu().numpy(), w=w.cpu().numpy())
+    _check_layer(qwen, xb, got, sample=[0, 1, 127, 128, 511, 512, 1023, 1024, 1097, 1098, 1099],
+                 label="T=1100 forward")
+    assert np.isfinite(got["y"]).all()
+
+
 # ------------------------------------------------------------------ exact ties in the fused routing
 def _tied_router(S, xrow):
     """The seeded router with rows copied so that the layer input's logits
