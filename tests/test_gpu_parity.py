@@ -372,8 +372,9 @@ def test_input_range_every_path(qwen, mx_qwen, mx, case):
 
 # ------------------------------------------------------------------ routing and dispatch lists
 # 513 and 1100 tokens: 4104 and 8800 pairs, the dispatch over several
-# 1024-pair workgroups with a ragged last one (8 and 608 pairs)
-@pytest.mark.parametrize("T,zipf", [(8, None), (128, None), (513, None), (1100, 1.1), (4096, 1.1)])
+# 1024-pair workgroups with a ragged last one (8 and 608 pairs); 16385
+# tokens: 129 workgroups, whose per-chunk counts are read in several batches
+@pytest.mark.parametrize("T,zipf", [(8, None), (128, None), (513, None), (1100, 1.1), (4096, 1.1), (16385, 1.1)])
 def test_route_from_logits_and_dispatch_lists(qwen, T, zipf):
     S = qwen.shape
     d = qwen.dev
