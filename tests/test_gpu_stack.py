@@ -181,6 +181,34 @@ def test_full_stack_chained_step_in_bench_configuration(qwen_stack):
     assert np.array_equal(out[1]["x_in"], out[0]["xs"][0])
 
 
+def test_full_stack_256_step_loop_properties(qwen_stack):
+    """The benchmark's whole greedy loop: 256 replays of the captured step,
+    each feeding the next, and at every step and layer the properties that
+    hold at any size (distinct ids in range, finite y, unit-RMS next input),
+    the routing weights summing to one, and the feedback (the next step's
+    layer-0 input is the last layer's output)."""
+    S, plan, blob, _ = qwen_stack
+    L, H, k = 48, S.hidden, S.top_k
+    dev = blob.device
+    xs = torch.zeros(L, H, dtype=torch.int16, device=dev)
+    ys = torch.zeros(L, H, dtype=torch.float32, device=dev)
+    ids = torch.zeros(L, k, dtype=torch.int32, device=dev)
+    ws = torch.zeros(L, k, dtype=torch.float32, device=dev)
+    scratch = plan.new_scratch(1, device=dev)
+    xs[0].copy_(torch.from_numpy(synth.x_bf16(S, 3, 0)[0].view(np.int16)))
+    stream = torch.cuda.Stream()
+    g = plan.capture_step(blob, xs, ys, 1, ids, ws, scratch=scratch, stream=stream)
+    for step in range(256):
+        x_in = xs[0].clone()
+        g.launch(stream)
+        torch.cuda.synchronize()
+        got = dict(xs=xs.cpu().numpy().view(np.uint16), ys=ys.cpu().numpy(), ids=ids.cpu().numpy())
+        _check_step_properties(S, got)
+        wsum = ws.sum(dim=1).cpu().numpy()
+        assert np.abs(wsum - 1.0).max() <= 1e-5, f"step {step}"
+        assert not torch.equal(x_in, xs[0]), f"step {step}: the input did not move"
+
+
 def _chained_forward(plan, blob, L, H, k, x0, dev):
     """The step as L chained moe_forward calls with the RMSNorm epilogue."""
     xs = torch.zeros(L, H, dtype=torch.int16, device=dev)
