@@ -23,8 +23,9 @@ static bool cfg_ok(const moe_config* c) {
   // device index arithmetic over (token, slot, row) runs in 32 bits
   if ((long long)c->max_tokens * k * (H > I ? H : I) >= (1LL << 31)) return false;
   // gate/up lane mapping: hidden/32 sub-blocks per row either fill a
-  // power-of-two lane group (256, 512, 1024), whole waves (2048 * {1..4}) or
-  // three per lane of 32-lane groups (3072)
+  // power-of-two lane group (256, 512, 1024), half waves with two per lane
+  // (2048), whole waves (2048 * {2..4}) or three per lane of 32-lane groups
+  // (3072)
   const bool h_ok = H == 256 || H == 512 || H == 1024 || H == 3072 || (H % 2048 == 0 && H / 2048 <= 4);
   if (!h_ok) return false;
   // down: k * inter/32 items per output row, one per lane of at most 8 waves

@@ -998,7 +998,10 @@ hipError_t launch_gateup(const Layout& d, const uint8_t* layer, const uint16_t* 
     gateup_go<3, 32, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1);
   } else if (nsb >= 64 && nsb % 64 == 0) {
     switch (nsb / 64) {
-      case 1: gateup_go<1, 64, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
+      // hidden 2048: 32-lane half waves with two sub-blocks each, two rows
+      // per step and one step per wave (one row per 64-lane wave with two
+      // steps was 1.8 % slower per decode step, 4 % with MXFP4 weights)
+      case 1: gateup_go<2, 32, 1>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
       case 2: gateup_go<2, 64, 2>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
       case 3: gateup_go<3, 64, 1>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
       case 4: gateup_go<4, 64, 1>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused_topk, s, ev0, ev1); break;
