@@ -321,8 +321,8 @@ __device__ __forceinline__ int fused_rank_publish(TopkSmem& sm, int p, int k, in
 // ACT: the gate activation as a template argument, so the epilogue on this
 // kernel's critical path carries no branch. FMT: the weight encoding; with
 // MXFP4 a lane's sub-block is one 32-code block with its E8M0 scale byte.
-template <int IPL, int LPR, int U, int ACT, int FMT>
-__global__ __launch_bounds__(BLOCK) void gateup_kernel(
+template <int IPL, int LPR, int U, int ACT, int FMT, int NWB>
+__global__ __launch_bounds__(NWB * WAVE) void gateup_kernel(
     const uint8_t* __restrict__ gu, size_t gu_expert_bytes, int rp_bytes, int H, int I, int E, int k,
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids_in, const float* __restrict__ logits,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ h, int T,
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(BLOCK) void gateup_kernel(
   // grid (I / (4 * RPS * U), k, T): no division stands before a load
   const int t = blockIdx.z;
   const int ts = t * k + blockIdx.y;                      // t*k + s
-  const int r0 = (blockIdx.x * (BLOCK / WAVE) + wid) * (RPS * U);
+  const int r0 = (blockIdx.x * NWB + wid) * (RPS * U);
   const int rho = lane / LPR, lam = lane % LPR;
   // the expert stride in registers and the lane's row offsets (bytes from
   // the expert's base; an expert spans less than 4 GiB) formed before the
@@ -941,6 +941,24 @@ hipError_t launch_topk(const Layout& d, const float* logits, int32_t* ids, float
 // launched in chunks of tokens.
 constexpr int GRID_YZ_MAX = 65535;
 
+template <int IPL, int LPR, int U, int ACT, int FMT, int NWB>
+static void gateup_launch(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids,
+                          const float* logits, int32_t* ids_out, float* w_out, float* h, int T, bool fused,
+                          hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  constexpr int RPS = WAVE / LPR;
+  const dim3 grid(d.I / (NWB * RPS * U), d.k, T);
+  if (ev0 || ev1) {
+    // measurement launch: the events bracket this kernel's execution
+    hipExtLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT, NWB>), grid, dim3(NWB * WAVE), 0, s, ev0, ev1,
+                          0, layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
+                          ids_out, w_out, h, T, fused ? 1 : 0 QMOE_TL_ARGS);
+    return;
+  }
+  hipLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT, NWB>), grid, dim3(NWB * WAVE), 0, s,
+                     layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
+                     ids_out, w_out, h, T, fused ? 1 : 0 QMOE_TL_ARGS);
+}
+
 template <int IPL, int LPR, int U, int ACT, int FMT>
 static void gateup_go_act(const Layout& d, const uint8_t* layer, const uint16_t* x, const int32_t* ids,
                           const float* logits, int32_t* ids_out, float* w_out, float* h, int T, bool fused,
@@ -954,19 +972,17 @@ static void gateup_go_act(const Layout& d, const uint8_t* layer, const uint16_t*
                                            nullptr, nullptr);
     return;
   }
-  // a block's four waves take 4 * RPS * U consecutive rows of one (token,
-  // slot); I is a multiple of 256, so every block is full
-  const dim3 grid(d.I / (4 * RPS * U), d.k, T);
-  if (ev0 || ev1) {
-    // measurement launch: the events bracket this kernel's execution
-    hipExtLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT>), grid, dim3(BLOCK), 0, s, ev0, ev1,
-                          0, layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
-                          ids_out, w_out, h, T, fused ? 1 : 0 QMOE_TL_ARGS);
+  // a block's NWB waves take NWB * RPS * U consecutive rows of one (token,
+  // slot); I is a multiple of 256, so every block of four waves is full.
+  // One token with I a multiple of 12 * RPS * U: twelve waves per block, so
+  // the k * I / (RPS * U) wave units of a 768-row layer at top-8 fill the
+  // 256 CUs with one block each, and each CU searches the routing once
+  // instead of once per block
+  if (T == 1 && d.I % (12 * RPS * U) == 0 && d.k * d.I / (12 * RPS * U) <= 256) {
+    gateup_launch<IPL, LPR, U, ACT, FMT, 12>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1);
     return;
   }
-  hipLaunchKernelGGL((gateup_kernel<IPL, LPR, U, ACT, FMT>), grid, dim3(BLOCK), 0, s,
-                     layer + d.gu_off, d.gu_expert_bytes, (int)d.rp_bytes, d.H, d.I, d.E, d.k, x, ids, logits,
-                     ids_out, w_out, h, T, fused ? 1 : 0 QMOE_TL_ARGS);
+  gateup_launch<IPL, LPR, U, ACT, FMT, 4>(d, layer, x, ids, logits, ids_out, w_out, h, T, fused, s, ev0, ev1);
 }
 
 template <int IPL, int LPR, int U>
