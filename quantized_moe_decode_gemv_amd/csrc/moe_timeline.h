@@ -58,9 +58,12 @@ struct TLScope {
     wg = tl_wg();
     if (threadIdx.x == 0 && slot >= 0 && wg < TL_WGS) tl_rec[slot][wg][0] = t0;
   }
+  // wave w's exit goes to field 1 + w % 4 as a maximum, so blocks of more
+  // than four waves keep their last exit (the clock only grows, so a later
+  // replay's stamps also replace an earlier one's)
   __device__ ~TLScope() {
-    if ((threadIdx.x & 63) == 0 && threadIdx.x < 256 && slot >= 0 && wg < TL_WGS)
-      tl_rec[slot][wg][1 + threadIdx.x / 64] = __builtin_amdgcn_s_memrealtime();
+    if ((threadIdx.x & 63) == 0 && slot >= 0 && wg < TL_WGS)
+      atomicMax(&tl_rec[slot][wg][1 + (threadIdx.x / 64) % 4], __builtin_amdgcn_s_memrealtime());
   }
   __device__ void mark(int field) const {
     if (threadIdx.x == 0 && slot >= 0 && wg < TL_WGS)
