@@ -26,8 +26,9 @@ D_END = (268, 374)
 NORM_SPAN = 50
 
 
-def _write_step(rec, t):
-    """One decode step's stamps from tick t on; returns the tick after it."""
+def _write_step(rec, t, ggroups=3):
+    """One decode step's stamps from tick t on (gate/up in ggroups dispatch
+    groups of 256 workgroups); returns the tick after it."""
     rec[:] = 0
     for l in range(L):
         r = rec[4 * l]
@@ -36,7 +37,7 @@ def _write_step(rec, t):
         r[:ROUTER_WG, 5] = t + R_NORM
         g0 = t + R_SPAN + GAP_RG - G_START[0]          # the launch; its first workgroup starts G_START[0] later
         g = rec[4 * l + 1]
-        for grp in range(3):
+        for grp in range(ggroups):
             wg = slice(256 * grp, 256 * (grp + 1))
             st = g0 + G_START[grp]
             g[wg, 0] = st
@@ -44,7 +45,7 @@ def _write_step(rec, t):
             g[wg, 1:5] = g0 + G_END[grp] - np.array([3, 0, 2, 1], dtype=np.uint64)
             g[wg, 5] = st + G_ROUTE[grp]
             g[wg, 6] = st + G_ROW0[grp]
-        gend = g0 + max(G_END)
+        gend = g0 + max(G_END[:ggroups])
         d0 = gend + GAP_GD - D_START[0]
         d = rec[4 * l + 2]
         for grp in range(2):
@@ -74,14 +75,15 @@ class _Lib:
     """moe_timeline_* stand-ins: read n returns a step starting 1e8 ticks
     (1 s at 100 MHz) after read n-1's."""
 
-    def __init__(self):
+    def __init__(self, ggroups=3):
+        self.ggroups = ggroups
         self.reads = 0
         self.moe_timeline_reset = _Fn(lambda: 0)
         self.moe_timeline_read = _Fn(self._read)
 
     def _read(self, ptr):
         rec = np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ctypes.c_uint64)), shape=(256, 1024, 8))
-        _write_step(rec, 1_000_000 + 100_000_000 * self.reads)
+        _write_step(rec, 1_000_000 + 100_000_000 * self.reads, self.ggroups)
         self.reads += 1
         return 0
 
@@ -97,8 +99,8 @@ class _Event:
         return 0.672 * 48
 
 
-def _run():
-    lib = _Lib()
+def _run(ggroups=3):
+    lib = _Lib(ggroups)
     q = types.SimpleNamespace(load=lambda: lib)
     graph = types.SimpleNamespace(launch=lambda stream: None)
     torch = types.SimpleNamespace(cuda=types.SimpleNamespace(Event=_Event, synchronize=lambda: None))
@@ -163,3 +165,15 @@ def test_dispatch_groups_and_xcds(tl):
         assert s["row_partials"] == [pytest.approx(D_PART[grp] / 100.0)] * 3
     # every XCD (workgroup id mod 8) holds the same mix of groups
     assert all(v == pytest.approx(0.0) for v in tl["xcd_median_spread_us"].values())
+
+
+def test_one_gateup_group_of_256_workgroups():
+    """One-token gate/up launches of 256 workgroups (one per CU) give one
+    dispatch group and the span of that group alone."""
+    tl1 = _run(ggroups=1)
+    groups = tl1["workgroups_by_dispatch_group_p10_p50_p90_us"]
+    assert sorted(k for k in groups if k.startswith("gateup")) == ["gateup_wg0-255"]
+    s = groups["gateup_wg0-255"]
+    assert s["end"] == [pytest.approx((G_END[0] - G_START[0]) / 100.0)] * 3
+    assert s["routing_known"] == [pytest.approx(G_ROUTE[0] / 100.0)] * 3
+    assert tl1["per_layer_median_us"]["gateup"] == pytest.approx((G_END[0] - G_START[0]) / 100.0)
